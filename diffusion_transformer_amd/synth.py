@@ -1,0 +1,174 @@
+"""Seeded synthetic workloads: configuration descriptions, weights and inputs.
+
+This module holds no arithmetic of the method. It only describes the
+workloads (dimensions, token segments, sigma schedules) and draws seeded
+random numbers; both the HIP path and the fp64 oracle receive exactly the
+arrays produced here.
+
+Recipe (the same for every configuration):
+- Weights are drawn N(0, 1/fan_in) in float32 (fan_in = input features of a
+  Linear; norm vectors use their own length), then rounded to bfloat16
+  (round-to-nearest-even); the arrays returned are float32 holding those
+  bf16-exact values. Every named tensor has its own stream
+  ``SeedSequence(seed, spawn_key=(crc32(name),))``.
+- Text prefix hidden states and reference/target latents are N(0, 1)
+  float32, each from its own named stream.
+"""
+from __future__ import annotations
+
+import zlib
+
+import numpy as np
+
+# 8-step Turbo sigma table (page "6B · Scale-Only Final AdaLN ...", §1/§6).
+TURBO_SIGMAS = (1.0, 0.978453, 0.95418, 0.926626, 0.89508, 0.845148,
+                0.704534, 0.414568, 0.0)
+
+_BIG = dict(hidden=4096, n_heads=32, head_dim=128, ffn=16384, latent=64,
+            time_dim=256, rope_dims=(16, 56, 56))
+
+# Workloads. "segments": ("text", n) | ("ref", h, w) | ("target", h, w).
+CONFIGS = {
+    # Lab-scale toy: 11 tokens, 7 prefix + 4 target; fp64 oracle only.
+    # Its 7 prefix hidden states are drawn N(0,1) directly ("prefix_direct").
+    "c0": dict(hidden=8, n_heads=2, head_dim=4, ffn=16, n_layers=2, latent=64,
+               time_dim=8, rope_dims=(0, 2, 2), prefix_direct=True,
+               segments=[("text", 2), ("ref", 2, 2), ("text", 1), ("target", 2, 2)],
+               sigmas=(1.0, 0.85, 0.45, 0.0)),
+    # GPU-shaped twin of the toy: same 11-token layout, head_dim 128.
+    "c0w": dict(hidden=256, n_heads=2, head_dim=128, ffn=512, n_layers=2, latent=64,
+                time_dim=256, rope_dims=(16, 56, 56), prefix_direct=True,
+                segments=[("text", 2), ("ref", 2, 2), ("text", 1), ("target", 2, 2)],
+                sigmas=(1.0, 0.85, 0.45, 0.0)),
+    # One layer, 512 text + 32x32 target; extract at 1.0, cached at 0.978453.
+    "c1": dict(_BIG, n_layers=1,
+               segments=[("text", 512), ("target", 32, 32)],
+               sigmas=(1.0, 0.978453, 0.95418)),
+    # Text-to-image: 256 text + 64x64 target, 32 layers, 8 Turbo steps.
+    "c2": dict(_BIG, n_layers=32,
+               segments=[("text", 256), ("target", 64, 64)],
+               sigmas=TURBO_SIGMAS),
+    # Editing: 256 text + one 64x64 reference + 64x64 target.
+    "c3": dict(_BIG, n_layers=32,
+               segments=[("text", 256), ("ref", 64, 64), ("target", 64, 64)],
+               sigmas=TURBO_SIGMAS),
+    # Multi-reference: 512 text + three 64x64 references + 96x96 target.
+    "c4": dict(_BIG, n_layers=32,
+               segments=[("text", 512), ("ref", 64, 64), ("ref", 64, 64),
+                         ("ref", 64, 64), ("target", 96, 96)],
+               sigmas=TURBO_SIGMAS),
+}
+
+
+def config(name: str, **overrides) -> dict:
+    c = dict(CONFIGS[name])
+    c.update(overrides)
+    c["name"] = name
+    return c
+
+
+def token_counts(cfg: dict):
+    """(P, T, S) implied by the segment list (plain counting)."""
+    n = 0
+    T = 0
+    for seg in cfg["segments"]:
+        cnt = seg[1] if seg[0] == "text" else seg[1] * seg[2]
+        n += cnt
+        if seg[0] == "target":
+            T = cnt
+    return n - T, T, n
+
+
+def _rng(seed: int, name: str) -> np.random.Generator:
+    return np.random.default_rng(np.random.SeedSequence(seed, spawn_key=(zlib.crc32(name.encode()),)))
+
+
+def round_bf16(x: np.ndarray) -> np.ndarray:
+    """float32 -> nearest bfloat16 (ties to even), returned as float32."""
+    b = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    b = (b + (np.uint32(0x7FFF) + ((b >> np.uint32(16)) & np.uint32(1)))) & np.uint32(0xFFFF0000)
+    return b.view(np.float32)
+
+
+def bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Upper 16 bits of float32 values that are already bf16-exact."""
+    b = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    return (b >> np.uint32(16)).astype(np.uint16)
+
+
+def _normal(seed, name, shape, fan_in):
+    g = _rng(seed, name)
+    a = g.standard_normal(size=shape, dtype=np.float32)
+    a *= np.float32(1.0 / np.sqrt(fan_in))
+    return round_bf16(a)
+
+
+def make_weights(cfg: dict, seed: int = 21, n_layers: int | None = None) -> dict:
+    """All weights in nn.Linear layout [out, in], bf16-exact float32.
+
+    Global: t1 [H, D_t], t2 [H, H], mod [4H, H], so [H, H], img_in [H, C],
+    proj_out [C, H]. Per layer: qkv [3H, H] (q rows, then k, then v),
+    q_norm [d], k_norm [d], o [H, H], gate [F, H], up [F, H], down [H, F].
+    """
+    H, d, F = cfg["hidden"], cfg["head_dim"], cfg["ffn"]
+    C, Dt = cfg["latent"], cfg["time_dim"]
+    L = cfg["n_layers"] if n_layers is None else n_layers
+    W = {
+        "t1": _normal(seed, "t1", (H, Dt), Dt),
+        "t2": _normal(seed, "t2", (H, H), H),
+        "mod": _normal(seed, "mod", (4 * H, H), H),
+        "so": _normal(seed, "so", (H, H), H),
+        "img_in": _normal(seed, "img_in", (H, C), C),
+        "proj_out": _normal(seed, "proj_out", (C, H), H),
+        "layers": [],
+    }
+    for l in range(L):
+        W["layers"].append({
+            "qkv": _normal(seed, f"l{l}.qkv", (3 * H, H), H),
+            "q_norm": _normal(seed, f"l{l}.q_norm", (d,), d),
+            "k_norm": _normal(seed, f"l{l}.k_norm", (d,), d),
+            "o": _normal(seed, f"l{l}.o", (H, H), H),
+            "gate": _normal(seed, f"l{l}.gate", (F, H), H),
+            "up": _normal(seed, f"l{l}.up", (F, H), H),
+            "down": _normal(seed, f"l{l}.down", (H, F), F),
+        })
+    return W
+
+
+def make_inputs(cfg: dict, seed: int = 21) -> dict:
+    """Seeded N(0,1) float32 inputs.
+
+    ``text_hidden`` [n_text, H]; ``x0`` [T, C] (initial target latent);
+    for reference tokens either ``ref_hidden`` [n_ref, H] drawn directly
+    (configs with ``prefix_direct``) or ``ref_latents`` [n_ref, C] that the
+    caller embeds with img_in. ``prefix_kind`` gives each prefix row's origin
+    in sequence order (0 text, 1 reference).
+    """
+    H, C = cfg["hidden"], cfg["latent"]
+    n_text = sum(s[1] for s in cfg["segments"] if s[0] == "text")
+    n_ref = sum(s[1] * s[2] for s in cfg["segments"] if s[0] == "ref")
+    T = sum(s[1] * s[2] for s in cfg["segments"] if s[0] == "target")
+    kind = []
+    for s in cfg["segments"]:
+        if s[0] == "text":
+            kind += [0] * s[1]
+        elif s[0] == "ref":
+            kind += [1] * (s[1] * s[2])
+    out = {
+        "text_hidden": _rng(seed, "prefix").standard_normal((n_text, H), dtype=np.float32),
+        "x0": _rng(seed, "x0").standard_normal((T, C), dtype=np.float32),
+        "prefix_kind": np.asarray(kind, dtype=np.int8),
+    }
+    if cfg.get("prefix_direct"):
+        out["ref_hidden"] = _rng(seed, "ref_hidden").standard_normal((n_ref, H), dtype=np.float32)
+    else:
+        out["ref_latents"] = _rng(seed, "ref_latents").standard_normal((n_ref, C), dtype=np.float32)
+    return out
+
+
+def interleave_prefix(kind: np.ndarray, text_rows: np.ndarray, ref_rows: np.ndarray) -> np.ndarray:
+    """Place text rows and reference rows in sequence order (row copies only)."""
+    out = np.empty((len(kind), text_rows.shape[1]), dtype=np.float32)
+    out[kind == 0] = text_rows
+    out[kind == 1] = ref_rows
+    return out

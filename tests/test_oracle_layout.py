@@ -1,0 +1,108 @@
+"""Oracle pins: token metadata, block-causal mask, RoPE coordinates.
+
+Pinned against the values the pages print for the 11-token lab toy
+(tests/golden/lab_toy.json, each entry cited) and against brute force."""
+import json
+import os
+
+import numpy as np
+import pytest
+
+import oracle as O
+from diffusion_transformer_amd import synth
+
+GOLD = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "lab_toy.json")))
+
+
+def c0_layout():
+    return O.build_layout(synth.CONFIGS["c0"]["segments"])
+
+
+def test_c0_image_ids_and_target_mask():
+    lay = c0_layout()
+    assert lay.image_ids.tolist() == GOLD["image_ids"]["value"]
+    assert lay.target_mask.tolist() == GOLD["target_token_mask"]["value"]
+    assert [lay.P, lay.T, lay.S] == GOLD["prefix_target_joint"]["value"]
+
+
+def test_c0_valid_keys_per_row():
+    m = O.block_causal_mask(c0_layout().image_ids)
+    assert m.shape == (11, 11)
+    assert m.sum(axis=1).tolist() == GOLD["valid_keys_per_row"]["value"]
+    assert int(m.sum()) == 78
+    # the target block 7..10 is never visible from the prefix rows 0..6
+    assert not m[:7, 7:].any()
+
+
+def test_mask_brute_force_tiny():
+    # literal double loop over (i, j) on the toy and on a 3-reference toy
+    for ids in (GOLD["image_ids"]["value"], [-1, 0, 0, -1, 1, 1, 1, -1, 2, 2, 3, 3, 3]):
+        m = O.block_causal_mask(ids)
+        for i in range(len(ids)):
+            for j in range(len(ids)):
+                want = (i >= j) or (ids[i] >= 0 and ids[i] == ids[j])
+                assert m[i, j] == want
+
+
+def test_c0_coordinates():
+    lay = c0_layout()
+    text_rows = [i for i, v in enumerate(lay.image_ids) if v < 0]
+    assert lay.coords[text_rows].tolist() == GOLD["text_coords"]["value"]
+    grid = GOLD["image_grid_2x2"]["value"]
+    for blk in (range(2, 6), range(7, 11)):
+        c = lay.coords[list(blk)]
+        assert (c[:, 0] == 0).all()
+        assert c[:, 1:].tolist() == grid
+
+
+@pytest.mark.parametrize("name", ["c0", "c1", "c2", "c3", "c4"])
+def test_row_limit_form_equals_rule(name):
+    """With contiguous image blocks the rule equals j <= limit[i], limit[i] = i
+    for text and the last index of the token's block for image tokens."""
+    cfg = synth.CONFIGS[name]
+    lay = O.build_layout(cfg["segments"])
+    ids = lay.image_ids
+    S = lay.S
+    lim = O.row_limits(ids)
+    # closed form of the limit for contiguous blocks
+    want = np.arange(S)
+    for v in set(ids.tolist()) - {-1}:
+        idx = np.nonzero(ids == v)[0]
+        assert idx[-1] - idx[0] + 1 == len(idx)       # contiguous
+        want[idx] = idx[-1]
+    assert (lim == want).all()
+    j = np.arange(S)
+    for r0 in range(0, S, 2048):
+        rows = np.arange(r0, min(S, r0 + 2048))
+        m = O.block_causal_mask(ids, rows=rows)
+        assert (m == (j[None, :] <= lim[rows][:, None])).all()
+    P, T, Sx = synth.token_counts(cfg)
+    assert (lay.P, lay.T, lay.S) == (P, T, Sx)
+    # target rows see every key
+    assert (lim[lay.P:] == S - 1).all()
+
+
+def test_non_contiguous_block_breaks_limit_form():
+    # an image id split by text: the pairwise rule lets token 0 see token 2
+    ids = [0, -1, 0, 1]
+    m = O.block_causal_mask(ids)
+    assert m[0, 2] and not m[0, 1]
+
+
+def test_layout_rejects_misplaced_target():
+    with pytest.raises(ValueError):
+        O.build_layout([("target", 2, 2), ("text", 3)])
+
+
+def test_image_ids_multi_reference():
+    lay = O.build_layout(synth.CONFIGS["c4"]["segments"])
+    ids = lay.image_ids
+    assert (ids[:512] == -1).all()
+    for r in range(3):
+        assert (ids[512 + 4096 * r: 512 + 4096 * (r + 1)] == r).all()
+    assert (ids[512 + 3 * 4096:] == 3).all()
+    assert lay.T == 9216 and lay.P == 12800
+    # 96x96 target grid: zero-centred offsets -48..47 on both axes
+    c = lay.coords[lay.P:]
+    assert c[:, 1].min() == -48 and c[:, 1].max() == 47
+    assert c[0].tolist() == [0, -48, -48] and c[1].tolist() == [0, -48, -47]
