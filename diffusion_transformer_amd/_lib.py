@@ -1,0 +1,250 @@
+"""ctypes binding of ``libdit.so`` (include/dit.h), one Python function per C
+entry point with the same name. Argument marshalling only: torch tensors
+are passed as raw device pointers, every computation happens in the HIP
+library. Importing this module raises if the library is not built."""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+import numpy as np
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libdit.so")
+
+DIT_OK, DIT_ERR_ARG, DIT_ERR_SHAPE, DIT_ERR_LAYOUT, DIT_ERR_STATE, DIT_ERR_WORKSPACE, \
+    DIT_ERR_HIP, DIT_ERR_UNSUPPORTED = range(8)
+DIT_FLAG_NO_CAUSAL_CONDITION = 1
+PROF = {"off": 0, "gemm_qkv": 1, "gemm_o": 2, "gemm_gateup": 3, "gemm_down": 4,
+        "attention": 5, "ln": 6, "qknorm_rope": 7}
+SEG_TEXT, SEG_REF, SEG_TARGET = 0, 1, 2
+
+EXPORTS = ["dit_build_layout", "dit_load_weights", "dit_free", "dit_workspace_bytes",
+           "dit_kv_capacity", "dit_kv_cache_bytes", "dit_step_extract", "dit_step_cached",
+           "euler_update", "dit_img_in", "dit_debug_mask", "dit_debug_attention",
+           "dit_debug_gemm", "dit_profile_enable", "dit_profile_read", "dit_last_error",
+           "dit_version"]
+
+
+class DitError(RuntimeError):
+    def __init__(self, status, msg):
+        super().__init__(f"dit status {status}: {msg}")
+        self.status = status
+
+
+class dit_config(C.Structure):
+    _fields_ = [("hidden", C.c_int), ("n_heads", C.c_int), ("head_dim", C.c_int),
+                ("ffn", C.c_int), ("n_layers", C.c_int), ("latent", C.c_int),
+                ("time_dim", C.c_int), ("rope_dims", C.c_int * 3),
+                ("rope_base", C.c_float), ("eps", C.c_float)]
+
+
+class dit_weights(C.Structure):
+    _fields_ = [("t1", C.c_void_p), ("t2", C.c_void_p), ("mod", C.c_void_p), ("so", C.c_void_p),
+                ("img_in", C.c_void_p), ("proj_out", C.c_void_p),
+                ("qkv", C.POINTER(C.c_void_p)), ("q_norm", C.POINTER(C.c_void_p)),
+                ("k_norm", C.POINTER(C.c_void_p)), ("o", C.POINTER(C.c_void_p)),
+                ("gate", C.POINTER(C.c_void_p)), ("up", C.POINTER(C.c_void_p)),
+                ("down", C.POINTER(C.c_void_p))]
+
+
+class dit_seq(C.Structure):
+    _fields_ = [("P", C.c_int), ("T", C.c_int), ("d_row_limit", C.c_void_p),
+                ("d_rope_cos", C.c_void_p), ("d_rope_sin", C.c_void_p)]
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build() "
+                          "or python diffusion_transformer_amd/build.py")
+    lib = C.CDLL(LIB_PATH)
+    vp, i, f, sz, ll = C.c_void_p, C.c_int, C.c_float, C.c_size_t, C.c_longlong
+    P = C.POINTER
+    sig = {
+        "dit_build_layout": (i, [P(dit_config), P(i), P(i), P(i), i, vp, vp, vp, vp, vp, P(i), P(i)]),
+        "dit_load_weights": (i, [P(dit_config), P(dit_weights), P(vp)]),
+        "dit_free": (None, [vp]),
+        "dit_workspace_bytes": (sz, [vp, i]),
+        "dit_kv_capacity": (i, [i]),
+        "dit_kv_cache_bytes": (sz, [vp, i]),
+        "dit_step_extract": (i, [vp, P(dit_seq), vp, vp, f, vp, sz, vp, vp, sz, i, vp]),
+        "dit_step_cached": (i, [vp, P(dit_seq), vp, f, vp, sz, vp, vp, sz, vp]),
+        "euler_update": (i, [vp, vp, f, f, ll, vp]),
+        "dit_img_in": (i, [vp, vp, i, vp, vp]),
+        "dit_debug_mask": (i, [P(dit_seq), vp, vp]),
+        "dit_debug_attention": (i, [P(dit_seq), i, vp, i, i, i, vp, vp, vp]),
+        "dit_debug_gemm": (i, [vp, vp, vp, i, i, i, vp]),
+        "dit_profile_enable": (i, [vp, i]),
+        "dit_profile_read": (i, [vp, P(C.c_double), P(ll)]),
+        "dit_last_error": (C.c_char_p, []),
+        "dit_version": (C.c_char_p, []),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib
+
+
+_lib = _load()
+
+
+def _check(st):
+    if st != DIT_OK:
+        raise DitError(st, _lib.dit_last_error().decode())
+
+
+def _ptr(t):
+    """Device (or host) pointer of a torch tensor / numpy array, or None."""
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    if hasattr(t, "data_ptr"):
+        if not t.is_contiguous():
+            raise ValueError("tensor must be contiguous")
+        return t.data_ptr()
+    return t.ctypes.data
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def make_config(hidden, n_heads, head_dim, ffn, n_layers, latent=64, time_dim=256,
+                rope_dims=(16, 56, 56), rope_base=10000.0, eps=1e-6, **_ignored) -> dit_config:
+    c = dit_config()
+    c.hidden, c.n_heads, c.head_dim, c.ffn = hidden, n_heads, head_dim, ffn
+    c.n_layers, c.latent, c.time_dim = n_layers, latent, time_dim
+    c.rope_dims[:] = list(rope_dims)
+    c.rope_base, c.eps = rope_base, eps
+    return c
+
+
+def dit_version() -> str:
+    return _lib.dit_version().decode()
+
+
+def dit_last_error() -> str:
+    return _lib.dit_last_error().decode()
+
+
+def dit_build_layout(cfg: dit_config, segments):
+    """segments: ("text", n) | ("ref", h, w) | ("target", h, w). Returns a
+    dict of host numpy arrays (image_ids, coords, row_limit, rope_cos,
+    rope_sin) and P, T."""
+    kind = {"text": SEG_TEXT, "ref": SEG_REF, "target": SEG_TARGET}
+    n = len(segments)
+    k = (C.c_int * n)(*[kind[s[0]] for s in segments])
+    r = (C.c_int * n)(*[int(s[1]) for s in segments])
+    c = (C.c_int * n)(*[int(s[2]) if len(s) > 2 else 0 for s in segments])
+    P, T = C.c_int(), C.c_int()
+    _check(_lib.dit_build_layout(C.byref(cfg), k, r, c, n, None, None, None, None, None,
+                                 C.byref(P), C.byref(T)))
+    S = P.value + T.value
+    half = cfg.head_dim // 2
+    out = {"image_ids": np.empty(S, np.int32), "coords": np.empty((S, 3), np.int32),
+           "row_limit": np.empty(S, np.int32), "rope_cos": np.empty((S, half), np.float32),
+           "rope_sin": np.empty((S, half), np.float32)}
+    _check(_lib.dit_build_layout(C.byref(cfg), k, r, c, n, _ptr(out["image_ids"]),
+                                 _ptr(out["coords"]), _ptr(out["row_limit"]),
+                                 _ptr(out["rope_cos"]), _ptr(out["rope_sin"]),
+                                 C.byref(P), C.byref(T)))
+    out["P"], out["T"] = P.value, T.value
+    return out
+
+
+def dit_load_weights(cfg: dit_config, w: dict):
+    """w: dict of device tensors (bf16 bits) t1, t2, mod, so, img_in, proj_out
+    and per-layer lists qkv, q_norm, k_norm, o, gate, up, down. Returns an
+    opaque handle (an int); the tensors must outlive it."""
+    L = cfg.n_layers
+    arrs = {}
+    for name in ("qkv", "q_norm", "k_norm", "o", "gate", "up", "down"):
+        arrs[name] = (C.c_void_p * L)(*[_ptr(t) for t in w[name]])
+    ws = dit_weights(_ptr(w["t1"]), _ptr(w["t2"]), _ptr(w["mod"]), _ptr(w["so"]),
+                     _ptr(w["img_in"]), _ptr(w["proj_out"]),
+                     *[C.cast(arrs[n], C.POINTER(C.c_void_p)) for n in
+                       ("qkv", "q_norm", "k_norm", "o", "gate", "up", "down")])
+    h = C.c_void_p()
+    _check(_lib.dit_load_weights(C.byref(cfg), C.byref(ws), C.byref(h)))
+    return h.value
+
+
+def dit_free(model):
+    _lib.dit_free(model)
+
+
+def dit_workspace_bytes(model, n_tokens: int) -> int:
+    return _lib.dit_workspace_bytes(model, n_tokens)
+
+
+def dit_kv_capacity(S: int) -> int:
+    return _lib.dit_kv_capacity(S)
+
+
+def dit_kv_cache_bytes(model, S: int) -> int:
+    return _lib.dit_kv_cache_bytes(model, S)
+
+
+def make_seq(P, T, row_limit, rope_cos, rope_sin) -> dit_seq:
+    return dit_seq(P, T, _ptr(row_limit), _ptr(rope_cos), _ptr(rope_sin))
+
+
+def _nbytes(t):
+    return t.numel() * t.element_size()
+
+
+def dit_step_extract(model, seq: dit_seq, prefix_hidden, x, sigma, kv_cache, v_out, workspace,
+                     flags=0, stream=None):
+    _check(_lib.dit_step_extract(model, C.byref(seq), _ptr(prefix_hidden), _ptr(x), float(sigma),
+                                 _ptr(kv_cache), _nbytes(kv_cache), _ptr(v_out), _ptr(workspace),
+                                 _nbytes(workspace), int(flags), _stream(stream)))
+
+
+def dit_step_cached(model, seq: dit_seq, x, sigma, kv_cache, v_out, workspace, stream=None):
+    _check(_lib.dit_step_cached(model, C.byref(seq), _ptr(x), float(sigma), _ptr(kv_cache),
+                                _nbytes(kv_cache), _ptr(v_out), _ptr(workspace),
+                                _nbytes(workspace), _stream(stream)))
+
+
+def euler_update(x, v, sigma_k, sigma_k1, n=None, stream=None):
+    n = x.numel() if n is None else n
+    _check(_lib.euler_update(_ptr(x), _ptr(v), float(sigma_k), float(sigma_k1), int(n),
+                             _stream(stream)))
+
+
+def dit_img_in(model, latents, hidden, stream=None):
+    _check(_lib.dit_img_in(model, _ptr(latents), int(latents.shape[0]), _ptr(hidden),
+                           _stream(stream)))
+
+
+def dit_debug_mask(seq: dit_seq, mask, stream=None):
+    _check(_lib.dit_debug_mask(C.byref(seq), _ptr(mask), _stream(stream)))
+
+
+def dit_debug_attention(seq: dit_seq, n_heads, q, q_stride, q_off, N, kv_cache, out, stream=None):
+    _check(_lib.dit_debug_attention(C.byref(seq), int(n_heads), _ptr(q), int(q_stride), int(q_off),
+                                    int(N), _ptr(kv_cache), _ptr(out), _stream(stream)))
+
+
+def dit_debug_gemm(A, B, Cmat, M, N, K, stream=None):
+    _check(_lib.dit_debug_gemm(_ptr(A), _ptr(B), _ptr(Cmat), int(M), int(N), int(K),
+                               _stream(stream)))
+
+
+def dit_profile_enable(model, kernel_class):
+    if isinstance(kernel_class, str):
+        kernel_class = PROF[kernel_class]
+    _check(_lib.dit_profile_enable(model, int(kernel_class)))
+
+
+def dit_profile_read(model):
+    ms, n = C.c_double(), C.c_longlong()
+    _check(_lib.dit_profile_read(model, C.byref(ms), C.byref(n)))
+    return ms.value, n.value

@@ -1,0 +1,254 @@
+// Flash-style attention for head_dim 128 on gfx950 bf16 MFMA, with the
+// block-causal mask in row-limit form (key j visible to query i iff
+// j <= limit[i]); masked keys get exactly zero weight.
+//
+// One workgroup = 4 waves = 128 queries of one head; each wave owns 32
+// queries. Scores are computed transposed, Sᵀ = K·Qᵀ (32 keys × 32 queries
+// per MFMA block), so each lane holds 16 keys of ONE query and the softmax
+// row statistics need only in-lane work plus one exchange with lane^32.
+// The output is accumulated transposed as well, Oᵀ = Vᵀ·Pᵀ, which lets the
+// probabilities feed the MFMA B operand straight from registers; V is kept
+// transposed (dim-major) in the cache so the Vᵀ A-operand is a pair of
+// 8-byte LDS reads. K and Vᵀ tiles of 64 keys are staged through LDS,
+// double-buffered with register prefetch. Waves whose queries see none of a
+// key tile skip its arithmetic; tiles past the block's largest limit are
+// never loaded.
+#include "common.h"
+#include "kernels.h"
+
+namespace dit {
+
+namespace {
+
+constexpr int D = 128;
+constexpr int BQ = 128;
+constexpr int BKV = 64;
+constexpr int NT = 256;
+
+__global__ __launch_bounds__(NT) void attn_kernel(AttnArgs a) {
+  __shared__ u32x4 ks[2][BKV * 16];        // [key][16 chunks of 8 dims], chunk ^= key%8
+  __shared__ u32x2 vs[2][D * 16];          // [dim][16 chunks of 4 keys], chunk ^= dim%16
+  __shared__ int red[8];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int h = blockIdx.y;
+  const int q_blk = blockIdx.x * BQ;
+  const int lq = lane & 31, half = lane >> 5;
+  const int qi = min(q_blk + wave * 32 + lq, a.N - 1);   // local query row (clamped)
+  const bool q_valid = q_blk + wave * 32 + lq < a.N;
+  const int lim = a.limit[a.q_off + qi];
+
+  const int wlim_min = wave_min_i(lim), wlim_max = wave_max_i(lim);
+  if (lane == 0) red[wave] = wlim_max;
+  __syncthreads();
+  const int blim_max = max(max(red[0], red[1]), max(red[2], red[3]));
+  const int kv_end = min(a.S, blim_max + 1);
+  const int ntiles = (kv_end + BKV - 1) / BKV;
+
+  // Q fragment as MFMA B operand: lane holds Q[query lq][16s + 8*half .. +7]
+  bf16x8 qf[8];
+  {
+    const u32x4* qp = reinterpret_cast<const u32x4*>(a.q + (size_t)qi * a.q_stride + h * D);
+#pragma unroll
+    for (int s = 0; s < 8; ++s) qf[s] = __builtin_bit_cast(bf16x8, qp[2 * s + half]);
+  }
+
+  const uint16_t* kbase = a.k + (size_t)h * a.cap * D;
+  const uint16_t* vbase = a.vt + (size_t)h * D * a.cap;
+
+  // per-thread load slots: K 4 chunks of 16 B, Vᵀ 4 chunks of 16 B
+  int k_row[4], k_c[4], v_row[4], v_c[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    int q = tid + i * NT;
+    k_row[i] = q >> 4; k_c[i] = q & 15;
+    v_row[i] = q >> 3; v_c[i] = q & 7;
+  }
+  u32x4 rk[4], rv[4];
+  auto gload = [&](int kv0) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      rk[i] = *reinterpret_cast<const u32x4*>(kbase + (size_t)(kv0 + k_row[i]) * D + k_c[i] * 8);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      rv[i] = *reinterpret_cast<const u32x4*>(vbase + (size_t)v_row[i] * a.cap + kv0 + v_c[i] * 8);
+  };
+  auto lstore = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) ks[buf][k_row[i] * 16 + (k_c[i] ^ (k_row[i] & 7))] = rk[i];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int e = v_row[i];
+      const int c0 = 2 * v_c[i], c1 = c0 + 1;
+      u32x2 lo, hi;
+      lo.x = rv[i].x; lo.y = rv[i].y; hi.x = rv[i].z; hi.y = rv[i].w;
+      vs[buf][e * 16 + (c0 ^ (e & 15))] = lo;
+      vs[buf][e * 16 + (c1 ^ (e & 15))] = hi;
+    }
+  };
+
+  f32x16 oacc[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) oacc[j][r] = 0.f;
+  float m_run = -INFINITY, l_run = 0.f;
+  const float sl2 = 1.4426950408889634f * 0.08838834764831845f;   // log2(e)/sqrt(128)
+
+  if (ntiles > 0) {
+    gload(0);
+    lstore(0);
+  }
+  __syncthreads();
+
+  for (int t = 0; t < ntiles; ++t) {
+    const int cur = t & 1;
+    const int kv0 = t * BKV;
+    const bool more = t + 1 < ntiles;
+    if (more) gload(kv0 + BKV);
+
+    const int cls = tile_class<BKV>(kv0, wlim_min, wlim_max, a.S);
+    if (cls != 0) {
+      // ---- Sᵀ = K·Qᵀ for 64 keys ----
+      f32x16 sacc[2];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.f;
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          const int row = kb * 32 + lq;
+          bf16x8 kf = __builtin_bit_cast(bf16x8, ks[cur][row * 16 + ((2 * s + half) ^ (row & 7))]);
+          sacc[kb] = mfma32(kf, qf[s], sacc[kb]);
+        }
+      }
+      // ---- scale, mask, online softmax (lane = one query, 32 of its keys) ----
+      float mt = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          float v = sacc[kb][r] * sl2;
+          if (cls == 2) {
+            const int j = kv0 + kb * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+            if (!key_visible(j, lim, a.S)) v = -INFINITY;
+          }
+          sacc[kb][r] = v;
+          mt = fmaxf(mt, v);
+        }
+      mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+      const float m_new = fmaxf(m_run, mt);
+      // m_new is finite: key 0 is visible to every query and tile 0 is
+      // processed first; later all-masked rows keep m_run.
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      m_run = m_new;
+      float ls = 0.f;
+      uint32_t pk[2][8];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; r += 2) {
+          const float p0 = __builtin_amdgcn_exp2f(sacc[kb][r] - m_new);
+          const float p1 = __builtin_amdgcn_exp2f(sacc[kb][r + 1] - m_new);
+          ls += p0 + p1;
+          pk[kb][r >> 1] = pack2bf(p0, p1);
+        }
+      l_run = l_run * alpha + ls;
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[j][r] *= alpha;
+      // ---- Oᵀ += Vᵀ·Pᵀ over 4 chunks of 16 keys ----
+      // chunk c = registers 8(c%2)..+7 of key block c/2: this lane's keys
+      // 16c + 4*half + {0..3} and 16c + 8 + 4*half + {0..3}.
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        u32x4 pb;
+        pb.x = pk[c >> 1][4 * (c & 1) + 0];
+        pb.y = pk[c >> 1][4 * (c & 1) + 1];
+        pb.z = pk[c >> 1][4 * (c & 1) + 2];
+        pb.w = pk[c >> 1][4 * (c & 1) + 3];
+        const bf16x8 pf = __builtin_bit_cast(bf16x8, pb);
+        const int k8a = 4 * c + half, k8b = 4 * c + 2 + half;
+#pragma unroll
+        for (int db = 0; db < 4; ++db) {
+          const int e = db * 32 + lq;
+          const u32x2 va = vs[cur][e * 16 + (k8a ^ (e & 15))];
+          const u32x2 vb = vs[cur][e * 16 + (k8b ^ (e & 15))];
+          u32x4 vv;
+          vv.x = va.x; vv.y = va.y; vv.z = vb.x; vv.w = vb.y;
+          oacc[db] = mfma32(__builtin_bit_cast(bf16x8, vv), pf, oacc[db]);
+        }
+      }
+    }
+    if (more) lstore(cur ^ 1);
+    __syncthreads();
+  }
+
+  // ---- normalize and store O[query][dim] ----
+  const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+  const float inv = 1.f / l_tot;
+  if (q_valid) {
+    uint16_t* op = a.out + (size_t)qi * a.out_stride + h * D;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int d0 = db * 32 + 8 * g + 4 * half;
+        u32x2 w;
+        w.x = pack2bf(oacc[db][4 * g + 0] * inv, oacc[db][4 * g + 1] * inv);
+        w.y = pack2bf(oacc[db][4 * g + 2] * inv, oacc[db][4 * g + 3] * inv);
+        *reinterpret_cast<u32x2*>(op + d0) = w;
+      }
+  }
+}
+
+// Writes the visibility the attention kernel applies, tile by tile, using
+// the same per-wave classification and per-element predicate.
+__global__ __launch_bounds__(NT) void mask_kernel(const int32_t* limit, int S, uint8_t* mask) {
+  __shared__ int red[8];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int q_blk = blockIdx.x * BQ;
+  const int lq = lane & 31, half = lane >> 5;
+  const int qi = min(q_blk + wave * 32 + lq, S - 1);
+  const bool q_valid = q_blk + wave * 32 + lq < S;
+  const int lim = limit[qi];
+  const int wlim_min = wave_min_i(lim), wlim_max = wave_max_i(lim);
+  if (lane == 0) red[wave] = wlim_max;
+  __syncthreads();
+  const int blim_max = max(max(red[0], red[1]), max(red[2], red[3]));
+  const int kv_end = min(S, blim_max + 1);
+  const int kv0 = blockIdx.y * BKV;
+  const bool loaded = kv0 < kv_end;
+  const int cls = loaded ? tile_class<BKV>(kv0, wlim_min, wlim_max, S) : 0;
+  if (!q_valid) return;
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int j = kv0 + kb * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+      if (j >= S) continue;
+      uint8_t vis = 0;
+      if (cls == 1) vis = 1;
+      else if (cls == 2) vis = key_visible(j, lim, S) ? 1 : 0;
+      mask[(size_t)qi * S + j] = vis;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
+  dim3 grid((a.N + BQ - 1) / BQ, a.nh);
+  hipLaunchKernelGGL(attn_kernel, grid, dim3(NT), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_debug_mask(const int32_t* limit, int S, uint8_t* mask, hipStream_t s) {
+  dim3 grid((S + BQ - 1) / BQ, (S + BKV - 1) / BKV);
+  hipLaunchKernelGGL(mask_kernel, grid, dim3(NT), 0, s, limit, S, mask);
+  return hipGetLastError();
+}
+
+}  // namespace dit

@@ -1,0 +1,58 @@
+// Shared device-side types and helpers for the gfx950 kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dit {
+
+typedef uint16_t bf16_t;                                             // raw bfloat16 bits
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));           // MFMA bf16 operand
+typedef float f32x16 __attribute__((ext_vector_type(16)));           // 32x32 MFMA accumulator
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));          // 16-byte move
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));          // 8-byte move
+
+__device__ __forceinline__ float bf2f(bf16_t b) { return __uint_as_float(((uint32_t)b) << 16); }
+// float -> bf16, round to nearest even (lowers to v_cvt_pk_bf16_f32 on gfx950).
+__device__ __forceinline__ bf16_t f2bf(float f) { return __builtin_bit_cast(bf16_t, (__bf16)f); }
+__device__ __forceinline__ uint32_t pack2bf(float a, float b) {
+  return (uint32_t)f2bf(a) | ((uint32_t)f2bf(b) << 16);
+}
+
+// v_mfma_f32_32x32x16_bf16: C[32x32] += A[32x16] · B[16x32].
+// Lane l supplies A[l%32][8*(l/32) .. +7] and B[8*(l/32) .. +7][l%32];
+// accumulator register r of lane l holds C[8*(r/4) + 4*(l/32) + r%4][l%32].
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+__device__ __forceinline__ int wave_min_i(int v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = min(v, __shfl_xor(v, o, 64));
+  return v;
+}
+__device__ __forceinline__ int wave_max_i(int v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = max(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+// Block-causal visibility in row-limit form: key j is visible to a query
+// whose largest visible key is `lim` (and j must be a real key, j < S).
+__device__ __forceinline__ bool key_visible(int j, int lim, int S) { return j <= lim && j < S; }
+
+// Classification of a key tile [kv0, kv0+BKV) for a group of queries whose
+// limits lie in [lim_min, lim_max]: 0 = nothing visible (skip),
+// 1 = everything visible (no per-element test), 2 = test per element.
+template <int BKV>
+__device__ __forceinline__ int tile_class(int kv0, int lim_min, int lim_max, int S) {
+  if (kv0 > lim_max) return 0;
+  if (kv0 + BKV - 1 <= lim_min && kv0 + BKV <= S) return 1;
+  return 2;
+}
+
+}  // namespace dit

@@ -1,0 +1,529 @@
+// Host side of the C ABI declared in include/dit.h: validation, token
+// layout, workspace plan, per-step kernel orchestration, the extract-state
+// registry behind DIT_ERR_STATE and optional per-kernel event timing.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "../../include/dit.h"
+#include "kernels.h"
+
+using namespace dit;
+
+namespace {
+
+thread_local std::string g_err;
+
+dit_status fail(dit_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return st;
+}
+
+dit_status hip_check(hipError_t e, const char* what) {
+  if (e == hipSuccess) return DIT_OK;
+  return fail(DIT_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+struct ExtractRecord {
+  const void* kv;
+  int P, T;
+};
+
+}  // namespace
+
+struct dit_model {
+  dit_config cfg;
+  const void* t1; const void* t2; const void* mod; const void* so;
+  const void* img_in; const void* proj_out;
+  std::vector<const void*> qkv, qn, kn, o, gate, up, down;
+  std::vector<ExtractRecord> extracted;
+  int prof_class = 0;
+  std::vector<hipEvent_t> ev_start, ev_stop;
+  size_t ev_used = 0;
+};
+
+namespace {
+
+dit_status check_cfg(const dit_config* c) {
+  if (!c) return fail(DIT_ERR_ARG, "config is NULL");
+  if (c->hidden <= 0 || c->n_heads <= 0 || c->head_dim <= 0 || c->ffn <= 0 || c->n_layers <= 0 ||
+      c->latent <= 0 || c->time_dim <= 0)
+    return fail(DIT_ERR_ARG, "dimensions must be positive");
+  if (c->head_dim != 128) return fail(DIT_ERR_SHAPE, "head_dim must be 128 (got %d)", c->head_dim);
+  if (c->hidden != c->n_heads * c->head_dim)
+    return fail(DIT_ERR_SHAPE, "hidden (%d) != n_heads*head_dim (%d)", c->hidden, c->n_heads * c->head_dim);
+  if (c->hidden % 256 || c->hidden > 4096)
+    return fail(DIT_ERR_SHAPE, "hidden must be a multiple of 256 and <= 4096 (got %d)", c->hidden);
+  if (c->ffn % 128) return fail(DIT_ERR_SHAPE, "ffn must be a multiple of 128 (got %d)", c->ffn);
+  if (c->latent != 64) return fail(DIT_ERR_SHAPE, "latent must be 64 (got %d)", c->latent);
+  if (c->time_dim % 8 || c->time_dim > 1024)
+    return fail(DIT_ERR_SHAPE, "time_dim must be a multiple of 8 and <= 1024 (got %d)", c->time_dim);
+  int sum = 0;
+  for (int a = 0; a < 3; ++a) {
+    if (c->rope_dims[a] < 0 || c->rope_dims[a] % 2)
+      return fail(DIT_ERR_SHAPE, "rope_dims[%d] must be even and >= 0", a);
+    sum += c->rope_dims[a];
+  }
+  if (sum != c->head_dim) return fail(DIT_ERR_SHAPE, "rope_dims must sum to head_dim");
+  if (!(c->rope_base > 1.f) || !(c->eps > 0.f)) return fail(DIT_ERR_ARG, "rope_base/eps out of range");
+  return DIT_OK;
+}
+
+dit_status check_seq(const dit_model* m, const dit_seq* s) {
+  if (!s) return fail(DIT_ERR_ARG, "seq is NULL");
+  if (s->P < 0 || s->T <= 0) return fail(DIT_ERR_LAYOUT, "need P >= 0 and T > 0 (P=%d T=%d)", s->P, s->T);
+  if ((long long)s->P + s->T > (1 << 24)) return fail(DIT_ERR_LAYOUT, "sequence too long");
+  if (!s->d_row_limit || !s->d_rope_cos || !s->d_rope_sin)
+    return fail(DIT_ERR_ARG, "seq device tables are NULL");
+  (void)m;
+  return DIT_OK;
+}
+
+// Workspace plan for n tokens.
+struct Plan {
+  size_t mod, scale_out, temb_e, a1, a1s, temb, tembs, h, x, qkv, attn, ffn, total;
+};
+Plan plan(const dit_config& c, int n) {
+  Plan p{};
+  size_t off = 0;
+  auto take = [&](size_t bytes) { size_t o = off; off = align_up(off + bytes); return o; };
+  const size_t H = c.hidden, F = c.ffn, N = (size_t)n;
+  p.mod = take(2 * 4 * H * 4);
+  p.scale_out = take(H * 4);
+  p.temb_e = take(2 * (size_t)c.time_dim * 4);
+  p.a1 = take(2 * H * 4);
+  p.a1s = take(2 * H * 4);
+  p.temb = take(2 * H * 4);
+  p.tembs = take(2 * H * 4);
+  p.h = take(N * H * 4);
+  p.x = take(N * H * 2);
+  p.qkv = take(N * 3 * H * 2);
+  p.attn = take(N * H * 2);
+  p.ffn = take(N * F * 2);
+  p.total = off;
+  return p;
+}
+
+struct Timed {
+  dit_model* m;
+  int cls;
+  hipStream_t s;
+  bool on;
+  Timed(dit_model* m_, int cls_, hipStream_t s_) : m(m_), cls(cls_), s(s_), on(m_ && m_->prof_class == cls_) {
+    if (!on) return;
+    if (m->ev_used == m->ev_start.size()) {
+      hipEvent_t a, b;
+      if (hipEventCreate(&a) != hipSuccess || hipEventCreate(&b) != hipSuccess) { on = false; return; }
+      m->ev_start.push_back(a);
+      m->ev_stop.push_back(b);
+    }
+    hipEventRecord(m->ev_start[m->ev_used], s);
+  }
+  ~Timed() {
+    if (!on) return;
+    hipEventRecord(m->ev_stop[m->ev_used], s);
+    m->ev_used++;
+  }
+};
+
+inline const uint16_t* U(const void* p) { return static_cast<const uint16_t*>(p); }
+
+// One step over N tokens. extract: all S tokens (rows 0..P-1 prefix);
+// cached: the T target tokens (global rows P..S-1).
+dit_status run_step(dit_model* m, const dit_seq* seq, bool extract, const float* prefix,
+                    const float* x, float sigma, void* kv, float* v_out, void* ws, int flags,
+                    hipStream_t st) {
+  const dit_config& c = m->cfg;
+  const int H = c.hidden, F = c.ffn, nh = c.n_heads, L = c.n_layers;
+  const int P = seq->P, T = seq->T, S = P + T;
+  const int cap = dit_kv_capacity(S);
+  const int N = extract ? S : T;
+  const int n_pre = extract ? P : 0;
+  const int q_row0 = extract ? 0 : P;
+  const Plan pl = plan(c, N);
+  char* w = static_cast<char*>(ws);
+  float* mod = reinterpret_cast<float*>(w + pl.mod);
+  float* scale_out = reinterpret_cast<float*>(w + pl.scale_out);
+  float* te = reinterpret_cast<float*>(w + pl.temb_e);
+  float* a1 = reinterpret_cast<float*>(w + pl.a1);
+  float* a1s = reinterpret_cast<float*>(w + pl.a1s);
+  float* tb = reinterpret_cast<float*>(w + pl.temb);
+  float* tbs = reinterpret_cast<float*>(w + pl.tembs);
+  float* hbuf = reinterpret_cast<float*>(w + pl.h);
+  uint16_t* xb = reinterpret_cast<uint16_t*>(w + pl.x);
+  uint16_t* qkv = reinterpret_cast<uint16_t*>(w + pl.qkv);
+  uint16_t* att = reinterpret_cast<uint16_t*>(w + pl.attn);
+  uint16_t* ffn = reinterpret_cast<uint16_t*>(w + pl.ffn);
+  uint16_t* kbase = static_cast<uint16_t*>(kv);
+  uint16_t* vbase = kbase + (size_t)L * nh * cap * 128;
+  dit_status rc;
+#define LAUNCH(expr, what) \
+  do { if ((rc = hip_check((expr), what)) != DIT_OK) return rc; } while (0)
+
+  // ---- conditioning: sinusoid(1000σ) -> MLP -> shared modulation rows ----
+  // Row 0: current t; row 1: t = 0 (prefix rows), or t again without
+  // causal conditioning. The cached step needs row 0 only.
+  const float t = 1000.f * sigma;
+  const int nv = extract ? 2 : 1;
+  const float t_pre = (flags & DIT_FLAG_NO_CAUSAL_CONDITION) ? t : 0.f;
+  LAUNCH(launch_temb(t, t_pre, c.time_dim, c.rope_base, te, st), "temb");
+  LAUNCH(launch_gemv(U(m->t1), H, c.time_dim, te, c.time_dim, nv, a1, H, a1s, st), "gemv t1");
+  LAUNCH(launch_gemv(U(m->t2), H, H, a1s, H, nv, tb, H, tbs, st), "gemv t2");
+  LAUNCH(launch_gemv(U(m->mod), 4 * H, H, tbs, H, nv, mod, 4 * H, nullptr, st), "gemv mod");
+  LAUNCH(launch_gemv(U(m->so), H, H, tbs, H, 1, scale_out, H, nullptr, st), "gemv so");
+  const float* row_t = mod;
+  const float* row_0 = extract ? mod + 4 * H : mod;
+
+  // ---- residual stream init ----
+  if (extract && P > 0)
+    LAUNCH(hipMemcpyAsync(hbuf, prefix, (size_t)P * H * 4, hipMemcpyDeviceToDevice, st), "prefix copy");
+  LAUNCH(launch_img_in(U(m->img_in), x, T, H, hbuf + (size_t)n_pre * H, H, st), "img_in");
+
+  for (int l = 0; l < L; ++l) {
+    uint16_t* kl = kbase + (size_t)l * nh * cap * 128;
+    uint16_t* vl = vbase + (size_t)l * nh * 128 * cap;
+    {
+      Timed tm(m, DIT_PROF_LN, st);
+      LAUNCH(launch_ln_mod(hbuf, H, N, H, row_t, row_0, n_pre, c.eps, xb, H, st), "ln1");
+    }
+    {
+      Timed tm(m, DIT_PROF_GEMM_QKV, st);
+      GemmArgs g{};
+      g.A = xb; g.lda = H; g.B = U(m->qkv[l]); g.ldb = H; g.M = N; g.N = 3 * H; g.K = H;
+      g.C = qkv; g.ldc = 3 * H;
+      LAUNCH(launch_gemm(g, EPI_BF16, st), "gemm qkv");
+    }
+    {
+      Timed tm(m, DIT_PROF_QKNORM_ROPE, st);
+      QkArgs q{};
+      q.qkv = qkv; q.ld = 3 * H; q.q_row0 = q_row0;
+      q.g_begin = extract ? 0 : P; q.g_end = extract ? cap : S;
+      q.S = S; q.cap = cap; q.nh = nh; q.H = H;
+      q.wq = U(m->qn[l]); q.wk = U(m->kn[l]);
+      q.cosv = seq->d_rope_cos; q.sinv = seq->d_rope_sin;
+      q.kc = kl; q.vtc = vl; q.eps = c.eps;
+      LAUNCH(launch_qknorm_rope(q, st), "qknorm_rope");
+    }
+    {
+      Timed tm(m, DIT_PROF_ATTENTION, st);
+      AttnArgs a{};
+      a.q = qkv; a.q_stride = 3 * H; a.q_off = q_row0; a.N = N;
+      a.k = kl; a.vt = vl; a.cap = cap; a.S = S; a.nh = nh; a.limit = seq->d_row_limit;
+      a.out = att; a.out_stride = H;
+      LAUNCH(launch_attention(a, st), "attention");
+    }
+    {
+      Timed tm(m, DIT_PROF_GEMM_O, st);
+      GemmArgs g{};
+      g.A = att; g.lda = H; g.B = U(m->o[l]); g.ldb = H; g.M = N; g.N = H; g.K = H;
+      g.Hres = hbuf; g.ldh = H; g.gate_t = row_t + H; g.gate_0 = row_0 + H; g.n_pre = n_pre;
+      LAUNCH(launch_gemm(g, EPI_RESID, st), "gemm o");
+    }
+    {
+      Timed tm(m, DIT_PROF_LN, st);
+      LAUNCH(launch_ln_mod(hbuf, H, N, H, row_t + 2 * H, row_0 + 2 * H, n_pre, c.eps, xb, H, st), "ln2");
+    }
+    {
+      Timed tm(m, DIT_PROF_GEMM_GATEUP, st);
+      GemmArgs g{};
+      g.A = xb; g.lda = H; g.B = U(m->gate[l]); g.B2 = U(m->up[l]); g.ldb = H;
+      g.M = N; g.N = 2 * F; g.K = H; g.C = ffn; g.ldc = F;
+      LAUNCH(launch_gemm(g, EPI_SWIGLU, st), "gemm gate/up");
+    }
+    {
+      Timed tm(m, DIT_PROF_GEMM_DOWN, st);
+      GemmArgs g{};
+      g.A = ffn; g.lda = F; g.B = U(m->down[l]); g.ldb = F; g.M = N; g.N = H; g.K = F;
+      g.Hres = hbuf; g.ldh = H; g.gate_t = row_t + 3 * H; g.gate_0 = row_0 + 3 * H; g.n_pre = n_pre;
+      LAUNCH(launch_gemm(g, EPI_RESID, st), "gemm down");
+    }
+  }
+
+  // ---- scale-only final AdaLN on target rows, proj_out -> v ----
+  LAUNCH(launch_ln_mod(hbuf + (size_t)n_pre * H, H, T, H, scale_out, scale_out, 0, c.eps, xb, H, st),
+         "final ln");
+  {
+    GemmArgs g{};
+    g.A = xb; g.lda = H; g.B = U(m->proj_out); g.ldb = H; g.M = T; g.N = c.latent; g.K = H;
+    g.C = v_out; g.ldc = c.latent;
+    LAUNCH(launch_gemm(g, EPI_F32, st), "gemm proj_out");
+  }
+#undef LAUNCH
+  return DIT_OK;
+}
+
+dit_status check_step_common(dit_model* m, const dit_seq* seq, const float* x, void* kv,
+                             size_t kv_bytes, float* v_out, void* ws, size_t ws_bytes, int n) {
+  if (!m) return fail(DIT_ERR_ARG, "model is NULL");
+  dit_status rc = check_seq(m, seq);
+  if (rc) return rc;
+  if (!x || !kv || !v_out || !ws) return fail(DIT_ERR_ARG, "x, kv_cache, v_out and workspace must be non-NULL");
+  const size_t need_kv = dit_kv_cache_bytes(m, seq->P + seq->T);
+  if (kv_bytes < need_kv)
+    return fail(DIT_ERR_WORKSPACE, "kv_cache has %zu bytes, needs %zu", kv_bytes, need_kv);
+  const size_t need_ws = dit_workspace_bytes(m, n);
+  if (ws_bytes < need_ws)
+    return fail(DIT_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", ws_bytes, need_ws);
+  if ((reinterpret_cast<uintptr_t>(kv) | reinterpret_cast<uintptr_t>(ws) |
+       reinterpret_cast<uintptr_t>(x) | reinterpret_cast<uintptr_t>(v_out)) & 15)
+    return fail(DIT_ERR_ARG, "device buffers must be 16-byte aligned");
+  return DIT_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* dit_last_error(void) { return g_err.c_str(); }
+const char* dit_version(void) { return "dit-gfx950 0.1"; }
+
+int dit_kv_capacity(int S) { return S <= 0 ? 0 : (S + 127) / 128 * 128; }
+
+size_t dit_kv_cache_bytes(const dit_model* m, int S) {
+  if (!m || S <= 0) return 0;
+  return (size_t)2 * m->cfg.n_layers * m->cfg.n_heads * (size_t)dit_kv_capacity(S) * m->cfg.head_dim * 2;
+}
+
+size_t dit_workspace_bytes(const dit_model* m, int n_tokens) {
+  if (!m || n_tokens <= 0) return 0;
+  return plan(m->cfg, n_tokens).total;
+}
+
+dit_status dit_build_layout(const dit_config* cfg, const int* seg_kind, const int* seg_rows,
+                            const int* seg_cols, int n_seg, int32_t* image_ids, int32_t* coords,
+                            int32_t* row_limit, float* rope_cos, float* rope_sin, int* P_out,
+                            int* T_out) {
+  dit_status rc = check_cfg(cfg);
+  if (rc) return rc;
+  if (!seg_kind || !seg_rows || !seg_cols || n_seg <= 0) return fail(DIT_ERR_ARG, "empty segment list");
+  // validate: sizes positive, exactly one target and it is last
+  long long S = 0;
+  int n_target = 0;
+  for (int i = 0; i < n_seg; ++i) {
+    const int k = seg_kind[i];
+    if (k < 0 || k > 2) return fail(DIT_ERR_LAYOUT, "segment %d: kind %d unknown", i, k);
+    if (seg_rows[i] <= 0 || (k != 0 && seg_cols[i] <= 0))
+      return fail(DIT_ERR_LAYOUT, "segment %d: non-positive size", i);
+    S += (k == 0) ? seg_rows[i] : (long long)seg_rows[i] * seg_cols[i];
+    if (k == 2) {
+      ++n_target;
+      if (i != n_seg - 1) return fail(DIT_ERR_LAYOUT, "the target image must be the last segment");
+    }
+    if (S > (1 << 24)) return fail(DIT_ERR_LAYOUT, "sequence longer than 2^24 tokens");
+  }
+  if (n_target != 1) return fail(DIT_ERR_LAYOUT, "exactly one target segment is required");
+  int n_ref = 0;
+  for (int i = 0; i < n_seg; ++i) n_ref += seg_kind[i] == 1;
+  const int Tt = seg_rows[n_seg - 1] * seg_cols[n_seg - 1];
+  if (P_out) *P_out = (int)S - Tt;
+  if (T_out) *T_out = Tt;
+
+  // per-axis RoPE frequencies base^(-2j/d_a), pairs ordered axis by axis
+  const int npair = cfg->head_dim / 2;
+  std::vector<int> pair_axis(npair);
+  std::vector<double> pair_freq(npair);
+  {
+    int m = 0;
+    for (int a = 0; a < 3; ++a)
+      for (int j = 0; j < cfg->rope_dims[a] / 2; ++j, ++m) {
+        pair_axis[m] = a;
+        pair_freq[m] = std::pow((double)cfg->rope_base, -2.0 * j / (double)cfg->rope_dims[a]);
+      }
+  }
+  int i = 0, text_i = 0, ref_i = 0;
+  for (int sgi = 0; sgi < n_seg; ++sgi) {
+    const int k = seg_kind[sgi];
+    const int rows = seg_rows[sgi], cols = (k == 0) ? 1 : seg_cols[sgi];
+    const int cnt = (k == 0) ? rows : rows * cols;
+    const int id = (k == 0) ? -1 : (k == 1 ? ref_i : n_ref);
+    const int block_end = i + cnt - 1;
+    for (int e = 0; e < cnt; ++e, ++i) {
+      int cf, ch, cw;
+      if (k == 0) { cf = ch = cw = text_i++; }
+      else { cf = 0; ch = e / cols - rows / 2; cw = e % cols - cols / 2; }
+      if (image_ids) image_ids[i] = id;
+      if (coords) { coords[3 * i] = cf; coords[3 * i + 1] = ch; coords[3 * i + 2] = cw; }
+      if (row_limit) row_limit[i] = (k == 0) ? i : block_end;
+      if (rope_cos || rope_sin) {
+        const int cc[3] = {cf, ch, cw};
+        for (int m = 0; m < npair; ++m) {
+          const double ang = (double)cc[pair_axis[m]] * pair_freq[m];
+          if (rope_cos) rope_cos[(size_t)i * npair + m] = (float)std::cos(ang);
+          if (rope_sin) rope_sin[(size_t)i * npair + m] = (float)std::sin(ang);
+        }
+      }
+    }
+    if (k == 1) ++ref_i;
+  }
+  return DIT_OK;
+}
+
+dit_status dit_load_weights(const dit_config* cfg, const dit_weights* w, dit_model** out) {
+  dit_status rc = check_cfg(cfg);
+  if (rc) return rc;
+  if (!w || !out) return fail(DIT_ERR_ARG, "weights or out is NULL");
+  if (!w->t1 || !w->t2 || !w->mod || !w->so || !w->img_in || !w->proj_out)
+    return fail(DIT_ERR_ARG, "a global weight pointer is NULL");
+  if (!w->qkv || !w->q_norm || !w->k_norm || !w->o || !w->gate || !w->up || !w->down)
+    return fail(DIT_ERR_ARG, "a per-layer weight array is NULL");
+  const void* g[] = {w->t1, w->t2, w->mod, w->so, w->img_in, w->proj_out};
+  for (const void* p : g)
+    if (reinterpret_cast<uintptr_t>(p) & 15) return fail(DIT_ERR_ARG, "weights must be 16-byte aligned");
+  dit_model* m = new (std::nothrow) dit_model();
+  if (!m) return fail(DIT_ERR_ARG, "out of host memory");
+  m->cfg = *cfg;
+  m->t1 = w->t1; m->t2 = w->t2; m->mod = w->mod; m->so = w->so; m->img_in = w->img_in;
+  m->proj_out = w->proj_out;
+  const int L = cfg->n_layers;
+  for (int l = 0; l < L; ++l) {
+    const void* p[] = {w->qkv[l], w->q_norm[l], w->k_norm[l], w->o[l], w->gate[l], w->up[l], w->down[l]};
+    for (const void* q : p)
+      if (!q || (reinterpret_cast<uintptr_t>(q) & 15)) {
+        delete m;
+        return fail(DIT_ERR_ARG, "layer %d: weight pointer NULL or not 16-byte aligned", l);
+      }
+    m->qkv.push_back(w->qkv[l]); m->qn.push_back(w->q_norm[l]); m->kn.push_back(w->k_norm[l]);
+    m->o.push_back(w->o[l]); m->gate.push_back(w->gate[l]); m->up.push_back(w->up[l]);
+    m->down.push_back(w->down[l]);
+  }
+  *out = m;
+  return DIT_OK;
+}
+
+void dit_free(dit_model* m) {
+  if (!m) return;
+  for (auto e : m->ev_start) hipEventDestroy(e);
+  for (auto e : m->ev_stop) hipEventDestroy(e);
+  delete m;
+}
+
+dit_status dit_step_extract(dit_model* m, const dit_seq* seq, const float* prefix_hidden,
+                            const float* x, float sigma, void* kv_cache, size_t kv_bytes,
+                            float* v_out, void* workspace, size_t ws_bytes, int flags,
+                            void* stream) {
+  dit_status rc = check_step_common(m, seq, x, kv_cache, kv_bytes, v_out, workspace, ws_bytes,
+                                    seq ? seq->P + seq->T : 0);
+  if (rc) return rc;
+  if (seq->P > 0 && !prefix_hidden) return fail(DIT_ERR_ARG, "prefix_hidden is NULL");
+  if (flags & ~DIT_FLAG_NO_CAUSAL_CONDITION) return fail(DIT_ERR_ARG, "unknown flags 0x%x", flags);
+  if (!std::isfinite(sigma)) return fail(DIT_ERR_ARG, "sigma is not finite");
+  // forget any previous extract of this cache before overwriting it
+  for (size_t i = 0; i < m->extracted.size(); ++i)
+    if (m->extracted[i].kv == kv_cache) { m->extracted.erase(m->extracted.begin() + i); break; }
+  rc = run_step(m, seq, true, prefix_hidden, x, sigma, kv_cache, v_out, workspace, flags,
+                static_cast<hipStream_t>(stream));
+  if (rc) return rc;
+  if (!(flags & DIT_FLAG_NO_CAUSAL_CONDITION)) m->extracted.push_back({kv_cache, seq->P, seq->T});
+  return DIT_OK;
+}
+
+dit_status dit_step_cached(dit_model* m, const dit_seq* seq, const float* x, float sigma,
+                           void* kv_cache, size_t kv_bytes, float* v_out, void* workspace,
+                           size_t ws_bytes, void* stream) {
+  dit_status rc = check_step_common(m, seq, x, kv_cache, kv_bytes, v_out, workspace, ws_bytes,
+                                    seq ? seq->T : 0);
+  if (rc) return rc;
+  if (!std::isfinite(sigma)) return fail(DIT_ERR_ARG, "sigma is not finite");
+  bool ok = false;
+  for (const auto& r : m->extracted)
+    if (r.kv == kv_cache && r.P == seq->P && r.T == seq->T) ok = true;
+  if (!ok)
+    return fail(DIT_ERR_STATE, "no dit_step_extract with t=0 conditioning ran on this cache for P=%d T=%d",
+                seq->P, seq->T);
+  return run_step(m, seq, false, nullptr, x, sigma, kv_cache, v_out, workspace, 0,
+                  static_cast<hipStream_t>(stream));
+}
+
+dit_status euler_update(float* x, const float* v, float sigma_k, float sigma_k1, long long n,
+                        void* stream) {
+  if (!x || !v) return fail(DIT_ERR_ARG, "x or v is NULL");
+  if (n < 0) return fail(DIT_ERR_ARG, "negative length");
+  if (!std::isfinite(sigma_k) || !std::isfinite(sigma_k1)) return fail(DIT_ERR_ARG, "sigma is not finite");
+  return hip_check(launch_euler(x, v, sigma_k1 - sigma_k, n, static_cast<hipStream_t>(stream)), "euler");
+}
+
+dit_status dit_img_in(const dit_model* m, const float* latents, int n, float* hidden, void* stream) {
+  if (!m || !latents || !hidden) return fail(DIT_ERR_ARG, "NULL argument");
+  if (n < 0) return fail(DIT_ERR_ARG, "negative token count");
+  return hip_check(launch_img_in(U(m->img_in), latents, n, m->cfg.hidden, hidden, m->cfg.hidden,
+                                 static_cast<hipStream_t>(stream)),
+                   "img_in");
+}
+
+dit_status dit_debug_mask(const dit_seq* seq, uint8_t* mask, void* stream) {
+  dit_status rc = check_seq(nullptr, seq);
+  if (rc) return rc;
+  if (!mask) return fail(DIT_ERR_ARG, "mask is NULL");
+  return hip_check(launch_debug_mask(seq->d_row_limit, seq->P + seq->T, mask,
+                                     static_cast<hipStream_t>(stream)),
+                   "debug mask");
+}
+
+dit_status dit_debug_attention(const dit_seq* seq, int n_heads, const void* q, int q_stride,
+                               int q_off, int N, const void* kv_cache, void* out, void* stream) {
+  dit_status rc = check_seq(nullptr, seq);
+  if (rc) return rc;
+  const int S = seq->P + seq->T;
+  if (!q || !kv_cache || !out) return fail(DIT_ERR_ARG, "NULL argument");
+  if (n_heads <= 0 || N <= 0 || q_off < 0 || q_off + N > S || q_stride < n_heads * 128 || q_stride % 8)
+    return fail(DIT_ERR_ARG, "bad attention shape");
+  const int cap = dit_kv_capacity(S);
+  AttnArgs a{};
+  a.q = static_cast<const uint16_t*>(q); a.q_stride = q_stride; a.q_off = q_off; a.N = N;
+  a.k = static_cast<const uint16_t*>(kv_cache);
+  a.vt = a.k + (size_t)n_heads * cap * 128;
+  a.cap = cap; a.S = S; a.nh = n_heads; a.limit = seq->d_row_limit;
+  a.out = static_cast<uint16_t*>(out); a.out_stride = n_heads * 128;
+  return hip_check(launch_attention(a, static_cast<hipStream_t>(stream)), "debug attention");
+}
+
+dit_status dit_debug_gemm(const void* A, const void* B, void* C, int M, int N, int K, void* stream) {
+  if (!A || !B || !C) return fail(DIT_ERR_ARG, "NULL argument");
+  if (!gemm_shape_ok(M, N, K, EPI_BF16)) return fail(DIT_ERR_SHAPE, "GEMM needs M>0, N%%256==0, K%%64==0");
+  GemmArgs g{};
+  g.A = static_cast<const uint16_t*>(A); g.lda = K;
+  g.B = static_cast<const uint16_t*>(B); g.ldb = K;
+  g.M = M; g.N = N; g.K = K; g.C = C; g.ldc = N;
+  return hip_check(launch_gemm(g, EPI_BF16, static_cast<hipStream_t>(stream)), "debug gemm");
+}
+
+dit_status dit_profile_enable(dit_model* m, int kernel_class) {
+  if (!m) return fail(DIT_ERR_ARG, "model is NULL");
+  if (kernel_class < DIT_PROF_OFF || kernel_class > DIT_PROF_QKNORM_ROPE)
+    return fail(DIT_ERR_ARG, "unknown kernel class %d", kernel_class);
+  m->prof_class = kernel_class;
+  m->ev_used = 0;
+  return DIT_OK;
+}
+
+dit_status dit_profile_read(dit_model* m, double* total_ms, long long* launches) {
+  if (!m || !total_ms || !launches) return fail(DIT_ERR_ARG, "NULL argument");
+  double tot = 0;
+  for (size_t i = 0; i < m->ev_used; ++i) {
+    hipError_t e = hipEventSynchronize(m->ev_stop[i]);
+    if (e != hipSuccess) return hip_check(e, "event sync");
+    float ms = 0;
+    e = hipEventElapsedTime(&ms, m->ev_start[i], m->ev_stop[i]);
+    if (e != hipSuccess) return hip_check(e, "event elapsed");
+    tot += ms;
+  }
+  *total_ms = tot;
+  *launches = (long long)m->ev_used;
+  m->ev_used = 0;
+  return DIT_OK;
+}
+
+}  // extern "C"

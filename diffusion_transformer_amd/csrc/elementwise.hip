@@ -1,0 +1,277 @@
+// Bandwidth-bound kernels of the step: modulated LayerNorm, QK-RMSNorm +
+// 3D RoPE + KV-cache write, timestep-MLP / modulation GEMVs, img_in and the
+// Euler update. Each streams its operands once with 8–16-byte accesses and
+// reduces within a wavefront (64 lanes) or a 256-thread workgroup.
+#include "common.h"
+#include "kernels.h"
+
+namespace dit {
+
+namespace {
+
+// ---------------------------------------------------------------------------
+// x = LN(h)·(1 + scale[row]) -> bf16. One 256-thread workgroup per row; the
+// row (H <= 4096 floats) stays in registers between the two reductions.
+constexpr int LN_NT = 256;
+constexpr int LN_MAXV = 4;   // float4 per thread -> H <= 4096
+
+__device__ __forceinline__ float block_sum(float v, float* sh) {
+  v = wave_sum(v);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  __syncthreads();
+  if (lane == 0) sh[wave] = v;
+  __syncthreads();
+  return sh[0] + sh[1] + sh[2] + sh[3];
+}
+
+__global__ __launch_bounds__(LN_NT) void ln_mod_kernel(const float* __restrict__ h, int ldh, int H,
+                                                       const float* __restrict__ scale_t,
+                                                       const float* __restrict__ scale_0, int n_pre,
+                                                       float eps, uint16_t* __restrict__ out, int ldo) {
+  __shared__ float sh[4];
+  const int row = blockIdx.x;
+  const float4* hp = reinterpret_cast<const float4*>(h + (size_t)row * ldh);
+  const int nv = H >> 2;
+  float4 v[LN_MAXV];
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < LN_MAXV; ++i) {
+    const int c = threadIdx.x + i * LN_NT;
+    if (c < nv) {
+      v[i] = hp[c];
+      s += (v[i].x + v[i].y) + (v[i].z + v[i].w);
+    }
+  }
+  const float mean = block_sum(s, sh) / (float)H;
+  float q = 0.f;
+#pragma unroll
+  for (int i = 0; i < LN_MAXV; ++i) {
+    const int c = threadIdx.x + i * LN_NT;
+    if (c < nv) {
+      const float a = v[i].x - mean, b = v[i].y - mean, cc = v[i].z - mean, d = v[i].w - mean;
+      q += (a * a + b * b) + (cc * cc + d * d);
+    }
+  }
+  const float var = block_sum(q, sh) / (float)H;
+  const float rstd = rsqrtf(var + eps);
+  const float4* sp = reinterpret_cast<const float4*>(row < n_pre ? scale_0 : scale_t);
+  u32x2* op = reinterpret_cast<u32x2*>(out + (size_t)row * ldo);
+#pragma unroll
+  for (int i = 0; i < LN_MAXV; ++i) {
+    const int c = threadIdx.x + i * LN_NT;
+    if (c < nv) {
+      const float4 sc = sp[c];
+      u32x2 w;
+      w.x = pack2bf((v[i].x - mean) * rstd * (1.f + sc.x), (v[i].y - mean) * rstd * (1.f + sc.y));
+      w.y = pack2bf((v[i].z - mean) * rstd * (1.f + sc.z), (v[i].w - mean) * rstd * (1.f + sc.w));
+      op[c] = w;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// QK-RMSNorm + 3D RoPE + cache write. Workgroup = 64 global tokens of one
+// head, 4 waves × 16 tokens; in a wave, lane m owns rotation pair m
+// (dims 2m, 2m+1) of the 128-wide head. V goes through LDS to be written
+// transposed (dim-major) with 16-byte stores.
+constexpr int QK_TOK = 64;
+
+__global__ __launch_bounds__(256) void qknorm_rope_kernel(QkArgs a) {
+  __shared__ uint32_t vt_s[QK_TOK][65];   // [token][pair] packed bf16x2, padded
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int h = blockIdx.y;
+  const int g0 = (a.g_begin / QK_TOK) * QK_TOK + blockIdx.x * QK_TOK;
+  const float wq0 = 1.f + bf2f(a.wq[2 * lane]), wq1 = 1.f + bf2f(a.wq[2 * lane + 1]);
+  const float wk0 = 1.f + bf2f(a.wk[2 * lane]), wk1 = 1.f + bf2f(a.wk[2 * lane + 1]);
+  uint16_t* kc = a.kc + (size_t)h * a.cap * 128;
+
+  for (int t = wave; t < QK_TOK; t += 4) {
+    const int g = g0 + t;
+    if (g < a.g_begin || g >= a.g_end) continue;       // wave-uniform
+    uint32_t vpair = 0;
+    if (g < a.S) {
+      uint16_t* row = a.qkv + (size_t)(g - a.q_row0) * a.ld;
+      uint32_t* qp = reinterpret_cast<uint32_t*>(row + h * 128) + lane;
+      const uint32_t* kp = reinterpret_cast<const uint32_t*>(row + a.H + h * 128) + lane;
+      const uint32_t* vp = reinterpret_cast<const uint32_t*>(row + 2 * a.H + h * 128) + lane;
+      const uint32_t qraw = *qp, kraw = *kp;
+      vpair = *vp;
+      const float c = a.cosv[(size_t)g * 64 + lane], s = a.sinv[(size_t)g * 64 + lane];
+      float x0 = bf2f(qraw & 0xffff), x1 = bf2f(qraw >> 16);
+      float r = rsqrtf(wave_sum(x0 * x0 + x1 * x1) * (1.f / 128.f) + a.eps);
+      x0 *= r * wq0; x1 *= r * wq1;
+      *qp = pack2bf(x0 * c - x1 * s, x0 * s + x1 * c);
+      float y0 = bf2f(kraw & 0xffff), y1 = bf2f(kraw >> 16);
+      r = rsqrtf(wave_sum(y0 * y0 + y1 * y1) * (1.f / 128.f) + a.eps);
+      y0 *= r * wk0; y1 *= r * wk1;
+      reinterpret_cast<uint32_t*>(kc + (size_t)g * 128)[lane] = pack2bf(y0 * c - y1 * s, y0 * s + y1 * c);
+    } else {
+      reinterpret_cast<uint32_t*>(kc + (size_t)g * 128)[lane] = 0u;   // padding keys
+    }
+    vt_s[t][lane] = vpair;
+  }
+  __syncthreads();
+  // Vᵀ rows: dim e, keys g0..g0+63; 8 chunks of 8 keys per row
+  uint16_t* vt = a.vtc + (size_t)h * 128 * a.cap;
+  for (int q = threadIdx.x; q < 128 * 8; q += 256) {
+    const int e = q >> 3, c = q & 7;
+    const int k0 = g0 + c * 8;
+    uint16_t vals[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const uint32_t p = vt_s[c * 8 + j][e >> 1];
+      vals[j] = (e & 1) ? (uint16_t)(p >> 16) : (uint16_t)(p & 0xffff);
+    }
+    uint16_t* dst = vt + (size_t)e * a.cap + k0;
+    if (k0 >= a.g_begin && k0 + 8 <= a.g_end) {
+      u32x4 w;
+      w.x = vals[0] | ((uint32_t)vals[1] << 16);
+      w.y = vals[2] | ((uint32_t)vals[3] << 16);
+      w.z = vals[4] | ((uint32_t)vals[5] << 16);
+      w.w = vals[6] | ((uint32_t)vals[7] << 16);
+      *reinterpret_cast<u32x4*>(dst) = w;
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        if (k0 + j >= a.g_begin && k0 + j < a.g_end) dst[j] = vals[j];
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// GEMV: one wave per output row, 16-byte weight loads, wave reduction.
+__global__ __launch_bounds__(256) void gemv_kernel(const uint16_t* __restrict__ W, int O, int I,
+                                                   const float* __restrict__ X, int ldx, int nv,
+                                                   float* __restrict__ Y, int ldy, float* Ys) {
+  const int lane = threadIdx.x & 63;
+  const int o = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (o >= O) return;
+  const uint16_t* wr = W + (size_t)o * I;
+  float acc0 = 0.f, acc1 = 0.f;
+  for (int k = lane * 8; k < I; k += 512) {
+    const u32x4 w = *reinterpret_cast<const u32x4*>(wr + k);
+    float wf[8];
+    wf[0] = __uint_as_float(w.x << 16); wf[1] = __uint_as_float(w.x & 0xffff0000u);
+    wf[2] = __uint_as_float(w.y << 16); wf[3] = __uint_as_float(w.y & 0xffff0000u);
+    wf[4] = __uint_as_float(w.z << 16); wf[5] = __uint_as_float(w.z & 0xffff0000u);
+    wf[6] = __uint_as_float(w.w << 16); wf[7] = __uint_as_float(w.w & 0xffff0000u);
+    const float* x0 = X + k;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc0 += wf[j] * x0[j];
+    if (nv > 1) {
+      const float* x1 = X + ldx + k;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) acc1 += wf[j] * x1[j];
+    }
+  }
+  acc0 = wave_sum(acc0);
+  if (nv > 1) acc1 = wave_sum(acc1);
+  if (lane == 0) {
+    Y[o] = acc0;
+    if (Ys) Ys[o] = acc0 / (1.f + __expf(-acc0));
+    if (nv > 1) {
+      Y[ldy + o] = acc1;
+      if (Ys) Ys[ldy + o] = acc1 / (1.f + __expf(-acc1));
+    }
+  }
+}
+
+__global__ void temb_kernel(double t0, double t1, int D, double base, float* out) {
+  const int i = threadIdx.x + blockIdx.x * blockDim.x;
+  const int half = D / 2;
+  if (i >= half) return;
+  const double f = exp(-2.0 * (double)i / (double)D * log(base));
+  out[i] = (float)cos(t0 * f);
+  out[half + i] = (float)sin(t0 * f);
+  out[D + i] = (float)cos(t1 * f);
+  out[D + half + i] = (float)sin(t1 * f);
+}
+
+// ---------------------------------------------------------------------------
+// img_in: each thread owns one output column n (its 64 weights in
+// registers); the workgroup walks 64 tokens whose latents sit in LDS.
+__global__ __launch_bounds__(256) void img_in_kernel(const uint16_t* __restrict__ W,
+                                                     const float* __restrict__ x, int n, int H,
+                                                     float* __restrict__ out, int ldo) {
+  __shared__ float xs[64][64];
+  const int col = blockIdx.x * 256 + threadIdx.x;
+  const int t0 = blockIdx.y * 64;
+  for (int q = threadIdx.x; q < 64 * 64; q += 256) {
+    const int t = q >> 6, c = q & 63;
+    xs[t][c] = (t0 + t < n) ? x[(size_t)(t0 + t) * 64 + c] : 0.f;
+  }
+  float w[64];
+  const u32x4* wp = reinterpret_cast<const u32x4*>(W + (size_t)col * 64);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const u32x4 v = wp[j];
+    w[8 * j + 0] = __uint_as_float(v.x << 16); w[8 * j + 1] = __uint_as_float(v.x & 0xffff0000u);
+    w[8 * j + 2] = __uint_as_float(v.y << 16); w[8 * j + 3] = __uint_as_float(v.y & 0xffff0000u);
+    w[8 * j + 4] = __uint_as_float(v.z << 16); w[8 * j + 5] = __uint_as_float(v.z & 0xffff0000u);
+    w[8 * j + 6] = __uint_as_float(v.w << 16); w[8 * j + 7] = __uint_as_float(v.w & 0xffff0000u);
+  }
+  __syncthreads();
+  const int tend = min(64, n - t0);
+  for (int t = 0; t < tend; ++t) {
+    float acc = 0.f;
+#pragma unroll
+    for (int c = 0; c < 64; ++c) acc += w[c] * xs[t][c];
+    out[(size_t)(t0 + t) * ldo + col] = acc;
+  }
+}
+
+__global__ void euler_kernel(float* __restrict__ x, const float* __restrict__ v, float dsig,
+                             long long n) {
+  for (long long i = threadIdx.x + (long long)blockIdx.x * blockDim.x; i < n;
+       i += (long long)blockDim.x * gridDim.x)
+    x[i] = x[i] + dsig * v[i];
+}
+
+}  // namespace
+
+hipError_t launch_ln_mod(const float* h, int ldh, int rows, int H, const float* scale_t,
+                         const float* scale_0, int n_pre, float eps, uint16_t* out, int ldo,
+                         hipStream_t s) {
+  if (rows <= 0) return hipSuccess;
+  hipLaunchKernelGGL(ln_mod_kernel, dim3(rows), dim3(LN_NT), 0, s, h, ldh, H, scale_t, scale_0,
+                     n_pre, eps, out, ldo);
+  return hipGetLastError();
+}
+
+hipError_t launch_qknorm_rope(const QkArgs& a, hipStream_t s) {
+  const int t_first = a.g_begin / QK_TOK;
+  const int t_last = (a.g_end + QK_TOK - 1) / QK_TOK;
+  dim3 grid(t_last - t_first, a.nh);
+  hipLaunchKernelGGL(qknorm_rope_kernel, grid, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemv(const uint16_t* W, int O, int I, const float* X, int ldx, int nv, float* Y,
+                       int ldy, float* Ys, hipStream_t s) {
+  hipLaunchKernelGGL(gemv_kernel, dim3((O + 3) / 4), dim3(256), 0, s, W, O, I, X, ldx, nv, Y, ldy, Ys);
+  return hipGetLastError();
+}
+
+hipError_t launch_temb(float t0, float t1, int D, float base, float* out, hipStream_t s) {
+  hipLaunchKernelGGL(temb_kernel, dim3((D / 2 + 255) / 256), dim3(256), 0, s, (double)t0,
+                     (double)t1, D, (double)base, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_img_in(const uint16_t* W, const float* x, int n, int H, float* out, int ldo,
+                         hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  dim3 grid(H / 256, (n + 63) / 64);
+  hipLaunchKernelGGL(img_in_kernel, grid, dim3(256), 0, s, W, x, n, H, out, ldo);
+  return hipGetLastError();
+}
+
+hipError_t launch_euler(float* x, const float* v, float dsig, long long n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  long long blocks = (n + 255) / 256;
+  if (blocks > 4096) blocks = 4096;
+  hipLaunchKernelGGL(euler_kernel, dim3((unsigned)blocks), dim3(256), 0, s, x, v, dsig, n);
+  return hipGetLastError();
+}
+
+}  // namespace dit

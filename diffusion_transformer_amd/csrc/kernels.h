@@ -1,0 +1,75 @@
+// Internal launcher interface between the C ABI (dit_api.cpp) and the
+// gfx950 kernels. Every launcher enqueues on `stream` and returns the
+// hipGetLastError() of its launch.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dit {
+
+enum GemmEpi {
+  EPI_BF16 = 0,    // C (bf16) = A·Bᵀ
+  EPI_F32 = 1,     // C (f32)  = A·Bᵀ
+  EPI_RESID = 2,   // Hres (f32) += tanh(gate[row]) ⊙ A·Bᵀ, gate row by n_pre split
+  EPI_SWIGLU = 3   // C (bf16)[:, f] = SiLU(A·Gᵀ)[f] · (A·Uᵀ)[f]  (B = gate, B2 = up)
+};
+
+struct GemmArgs {
+  const uint16_t* A; int lda;       // [M, K] bf16
+  const uint16_t* B; int ldb;       // [N, K] bf16 (gate for SwiGLU)
+  const uint16_t* B2;               // up [N/2, K] for SwiGLU, else unused
+  int M, N, K;                      // N = packed width (2F for SwiGLU)
+  void* C; int ldc;                 // output
+  float* Hres; int ldh;             // residual stream for EPI_RESID
+  const float* gate_t;              // [N] gate row of target / current-t tokens
+  const float* gate_0;              // [N] gate row of prefix tokens (t = 0)
+  int n_pre;                        // rows < n_pre use gate_0
+};
+
+hipError_t launch_gemm(const GemmArgs& g, int epi, hipStream_t s);
+bool gemm_shape_ok(int M, int N, int K, int epi);
+
+struct AttnArgs {
+  const uint16_t* q; int q_stride;  // local query rows 0..N-1, head h at column h*128
+  int q_off;                        // global index of local row 0
+  int N;
+  const uint16_t* k;                // K of this layer: [nh][cap][128]
+  const uint16_t* vt;               // Vᵀ of this layer: [nh][128][cap]
+  int cap, S, nh;
+  const int32_t* limit;             // [S]
+  uint16_t* out; int out_stride;    // [N, nh*128] bf16
+};
+hipError_t launch_attention(const AttnArgs& a, hipStream_t s);
+hipError_t launch_debug_mask(const int32_t* limit, int S, uint8_t* mask, hipStream_t s);
+
+// LN(h)·(1 + scale[row]) -> bf16. rows < n_pre use scale_0, others scale_t.
+hipError_t launch_ln_mod(const float* h, int ldh, int rows, int H, const float* scale_t,
+                         const float* scale_0, int n_pre, float eps, uint16_t* out, int ldo,
+                         hipStream_t s);
+
+// Per-head QK-RMSNorm (1 + w) + 3D RoPE on q (in place) and k, and the K /
+// Vᵀ cache writes for global tokens [g_begin, g_end); tokens >= S are
+// zero-filled in the cache. qkv local row i holds global token q_row0 + i.
+struct QkArgs {
+  uint16_t* qkv; int ld;            // [rows, 3H]
+  int q_row0;
+  int g_begin, g_end, S, cap, nh, H;
+  const uint16_t* wq; const uint16_t* wk;   // [128] bf16
+  const float* cosv; const float* sinv;     // [S, 64]
+  uint16_t* kc; uint16_t* vtc;              // layer bases
+  float eps;
+};
+hipError_t launch_qknorm_rope(const QkArgs& a, hipStream_t s);
+
+// Y[v][o] = W[o]·X[v] for v < nv (W bf16 [O, I]); optionally also writes
+// silu(Y) to Ys.
+hipError_t launch_gemv(const uint16_t* W, int O, int I, const float* X, int ldx, int nv,
+                       float* Y, int ldy, float* Ys, hipStream_t s);
+// [cos(t_v f_i), sin(t_v f_i)], f_i = base^(-2i/D), computed in double.
+hipError_t launch_temb(float t0, float t1, int D, float base, float* out, hipStream_t s);
+// hidden[i][n] = Σ_c W[n][c] x[i][c]; W bf16 [H, 64], x f32 [n, 64].
+hipError_t launch_img_in(const uint16_t* W, const float* x, int n, int H, float* out, int ldo,
+                         hipStream_t s);
+hipError_t launch_euler(float* x, const float* v, float dsig, long long n, hipStream_t s);
+
+}  // namespace dit

@@ -1,0 +1,148 @@
+"""Torch plumbing around the C ABI: device memory for weights, layout
+tables, KV cache, workspace and latents, and the sampler loop (step 1
+extract, steps 2..N cached, Euler after each step). PyTorch only allocates
+and holds memory here; every computation is a call into ``libdit.so``."""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from . import _lib as L
+
+LAYER_KEYS = ("qkv", "q_norm", "k_norm", "o", "gate", "up", "down")
+GLOBAL_KEYS = ("t1", "t2", "mod", "so", "img_in", "proj_out")
+
+
+def to_device_bf16(a, device):
+    """bf16-exact float32 numpy array (or torch tensor) -> contiguous bf16 device tensor."""
+    if isinstance(a, torch.Tensor):
+        return a.to(device=device, dtype=torch.bfloat16).contiguous()
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(
+        device=device).to(torch.bfloat16).contiguous()
+
+
+def upload_weights(W: dict, device) -> dict:
+    out = {k: to_device_bf16(W[k], device) for k in GLOBAL_KEYS}
+    for k in LAYER_KEYS:
+        out[k] = [to_device_bf16(layer[k], device) for layer in W["layers"]]
+    return out
+
+
+def random_weights_device(cfg: dict, seed: int, device, n_layers=None) -> dict:
+    """Seeded N(0, 1/fan_in) bf16 weights drawn directly on the GPU with
+    torch's generator (for full-size throughput runs, where host generation
+    of 17 GB would dominate). Same shapes as synth.make_weights."""
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    H, d, F, C, Dt = cfg["hidden"], cfg["head_dim"], cfg["ffn"], cfg["latent"], cfg["time_dim"]
+    Lc = cfg["n_layers"] if n_layers is None else n_layers
+
+    def n(shape, fan_in):
+        t = torch.empty(shape, device=device, dtype=torch.float32)
+        t.normal_(0.0, 1.0 / float(np.sqrt(fan_in)), generator=g)
+        return t.to(torch.bfloat16)
+
+    out = {"t1": n((H, Dt), Dt), "t2": n((H, H), H), "mod": n((4 * H, H), H),
+           "so": n((H, H), H), "img_in": n((H, C), C), "proj_out": n((C, H), H)}
+    for k in LAYER_KEYS:
+        out[k] = []
+    for _ in range(Lc):
+        out["qkv"].append(n((3 * H, H), H))
+        out["q_norm"].append(n((d,), d))
+        out["k_norm"].append(n((d,), d))
+        out["o"].append(n((H, H), H))
+        out["gate"].append(n((F, H), H))
+        out["up"].append(n((F, H), H))
+        out["down"].append(n((H, F), F))
+    return out
+
+
+class Sequence:
+    """Device copy of one token layout plus its C struct."""
+
+    def __init__(self, cfg_c, segments, device):
+        lay = L.dit_build_layout(cfg_c, segments)
+        self.host = lay
+        self.P, self.T = lay["P"], lay["T"]
+        self.S = self.P + self.T
+        self.row_limit = torch.from_numpy(lay["row_limit"]).to(device)
+        self.rope_cos = torch.from_numpy(lay["rope_cos"]).to(device)
+        self.rope_sin = torch.from_numpy(lay["rope_sin"]).to(device)
+        self.c = L.make_seq(self.P, self.T, self.row_limit, self.rope_cos, self.rope_sin)
+
+
+class DitRuntime:
+    def __init__(self, cfg: dict, weights: dict, device="cuda", on_device=False):
+        self.cfg = cfg
+        self.device = torch.device(device)
+        self.c = L.make_config(**{k: cfg[k] for k in ("hidden", "n_heads", "head_dim", "ffn",
+                                                      "n_layers", "latent", "time_dim",
+                                                      "rope_dims")})
+        self.w = weights if on_device else upload_weights(weights, self.device)
+        self.model = L.dit_load_weights(self.c, self.w)
+
+    def close(self):
+        if self.model:
+            L.dit_free(self.model)
+            self.model = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def sequence(self, segments) -> Sequence:
+        return Sequence(self.c, segments, self.device)
+
+    def alloc_cache(self, seq: Sequence) -> torch.Tensor:
+        nbytes = L.dit_kv_cache_bytes(self.model, seq.S)
+        return torch.empty(nbytes // 2, dtype=torch.int16, device=self.device)
+
+    def alloc_workspace(self, n_tokens: int) -> torch.Tensor:
+        nbytes = L.dit_workspace_bytes(self.model, n_tokens)
+        return torch.empty((nbytes + 3) // 4, dtype=torch.float32, device=self.device)
+
+    def img_in(self, latents: torch.Tensor) -> torch.Tensor:
+        out = torch.empty((latents.shape[0], self.cfg["hidden"]), dtype=torch.float32,
+                          device=self.device)
+        if latents.shape[0]:
+            L.dit_img_in(self.model, latents.contiguous(), out)
+        return out
+
+    def prefix_hidden(self, inputs: dict) -> torch.Tensor:
+        """Prefix rows in sequence order: text hidden states as given,
+        reference tokens drawn directly or embedded from latents by img_in."""
+        kind = torch.from_numpy(inputs["prefix_kind"].astype(np.int64)).to(self.device)
+        text = torch.from_numpy(inputs["text_hidden"]).to(self.device)
+        if "ref_hidden" in inputs:
+            ref = torch.from_numpy(inputs["ref_hidden"]).to(self.device)
+        else:
+            ref = self.img_in(torch.from_numpy(inputs["ref_latents"]).to(self.device))
+        out = torch.empty((kind.numel(), self.cfg["hidden"]), dtype=torch.float32, device=self.device)
+        out[kind == 0] = text
+        out[kind == 1] = ref
+        return out
+
+    def step_extract(self, seq, prefix, x, sigma, cache, v, ws, flags=0, stream=None):
+        L.dit_step_extract(self.model, seq.c, prefix, x, sigma, cache, v, ws, flags, stream)
+
+    def step_cached(self, seq, x, sigma, cache, v, ws, stream=None):
+        L.dit_step_cached(self.model, seq.c, x, sigma, cache, v, ws, stream)
+
+    def run_loop(self, seq, prefix, x0, sigmas, use_cache=True):
+        """Sampler loop; returns (list of v per step, list of x after each step)."""
+        x = x0.clone().contiguous()
+        cache = self.alloc_cache(seq)
+        ws = self.alloc_workspace(seq.S)
+        vs, xs = [], []
+        for k in range(len(sigmas) - 1):
+            v = torch.empty_like(x)
+            if k == 0 or not use_cache:
+                self.step_extract(seq, prefix, x, sigmas[k], cache, v, ws)
+            else:
+                self.step_cached(seq, x, sigmas[k], cache, v, ws)
+            vs.append(v)
+            L.euler_update(x, v, sigmas[k], sigmas[k + 1])
+            xs.append(x.clone())
+        return vs, xs

@@ -1,0 +1,161 @@
+"""C ABI checks that need no GPU: the library loads, exports every entry
+point include/dit.h declares, builds layouts identical to the oracle's, and
+rejects bad arguments on the host before any device work."""
+import ctypes as C
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle as O
+from diffusion_transformer_amd import _lib as L
+from diffusion_transformer_amd import synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def header_functions():
+    src = open(os.path.join(ROOT, "include", "dit.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(\w+)\s*\([^;{]*\)\s*;", src)) - {"if", "for", "while"})
+
+
+def test_every_declared_symbol_is_exported():
+    names = header_functions()
+    assert len(names) >= 17
+    lib = C.CDLL(L.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(L.EXPORTS)
+
+
+def cfg_c(name):
+    c = synth.config(name)
+    return c, L.make_config(**{k: c[k] for k in ("hidden", "n_heads", "head_dim", "ffn",
+                                                  "n_layers", "latent", "time_dim", "rope_dims")})
+
+
+@pytest.mark.parametrize("name", ["c0w", "c1", "c2", "c3", "c4"])
+def test_layout_matches_oracle(name):
+    cfg, c = cfg_c(name)
+    lay = L.dit_build_layout(c, cfg["segments"])
+    ol = O.build_layout(cfg["segments"])
+    assert (lay["P"], lay["T"]) == (ol.P, ol.T)
+    assert np.array_equal(lay["image_ids"], ol.image_ids)
+    assert np.array_equal(lay["coords"], ol.coords)
+    assert np.array_equal(lay["row_limit"], O.row_limits(ol.image_ids))
+    dims = O.DitDims(hidden=cfg["hidden"], n_heads=cfg["n_heads"], head_dim=128, ffn=cfg["ffn"],
+                     n_layers=1, rope_dims=tuple(cfg["rope_dims"]))
+    ang = O.rope_angles(ol.coords, dims)
+    assert np.abs(lay["rope_cos"] - np.cos(ang)).max() < 1e-7
+    assert np.abs(lay["rope_sin"] - np.sin(ang)).max() < 1e-7
+
+
+def test_layout_errors():
+    _, c = cfg_c("c1")
+    with pytest.raises(L.DitError) as e:
+        L.dit_build_layout(c, [("target", 2, 2), ("text", 3)])
+    assert e.value.status == L.DIT_ERR_LAYOUT
+    with pytest.raises(L.DitError) as e:
+        L.dit_build_layout(c, [("text", 3), ("ref", 0, 2), ("target", 2, 2)])
+    assert e.value.status == L.DIT_ERR_LAYOUT
+    with pytest.raises(L.DitError) as e:
+        L.dit_build_layout(c, [("text", 3), ("target", 2, 2), ("target", 2, 2)])
+    assert e.value.status == L.DIT_ERR_LAYOUT
+
+
+FAKE = 1 << 20   # 16-byte aligned stand-in pointer; never dereferenced on these paths
+
+
+def fake_weights(nl):
+    arr = (C.c_void_p * nl)(*([FAKE] * nl))
+    p = C.cast(arr, C.POINTER(C.c_void_p))
+    return L.dit_weights(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, p, p, p, p, p, p, p), arr
+
+
+def load(c):
+    w, keep = fake_weights(c.n_layers)
+    h = C.c_void_p()
+    st = L._lib.dit_load_weights(C.byref(c), C.byref(w), C.byref(h))
+    return st, h.value
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("head_dim", 64, L.DIT_ERR_SHAPE), ("hidden", 4000, L.DIT_ERR_SHAPE),
+    ("latent", 32, L.DIT_ERR_SHAPE), ("ffn", 100, L.DIT_ERR_SHAPE), ("n_layers", 0, L.DIT_ERR_ARG)])
+def test_load_weights_validation(field, value, status):
+    _, c = cfg_c("c1")
+    setattr(c, field, value)
+    st, h = load(c)
+    assert st == status and h is None
+    assert L.dit_last_error()
+
+
+def test_rope_dims_must_sum_to_head_dim():
+    _, c = cfg_c("c1")
+    c.rope_dims[:] = [16, 56, 54]
+    assert load(c)[0] == L.DIT_ERR_SHAPE
+
+
+def test_null_weight_pointer_rejected():
+    _, c = cfg_c("c0w")
+    w, keep = fake_weights(c.n_layers)
+    w.mod = None
+    h = C.c_void_p()
+    assert L._lib.dit_load_weights(C.byref(c), C.byref(w), C.byref(h)) == L.DIT_ERR_ARG
+
+
+def test_step_state_and_workspace_errors():
+    cfg, c = cfg_c("c0w")
+    st, m = load(c)
+    assert st == L.DIT_OK
+    try:
+        seq = L.dit_seq(7, 4, FAKE, FAKE, FAKE)
+        kvb = L.dit_kv_cache_bytes(m, 11)
+        wsb = L.dit_workspace_bytes(m, 11)
+        assert kvb == 2 * 2 * 2 * 128 * 128 * 2     # L * {K,V} * nh * cap(128) * d * bf16
+        assert L.dit_kv_capacity(11) == 128 and L.dit_kv_capacity(128) == 128
+        assert L.dit_kv_capacity(129) == 256
+        # cached before any extract
+        r = L._lib.dit_step_cached(m, C.byref(seq), FAKE, 0.85, FAKE, kvb, FAKE, FAKE, wsb, None)
+        assert r == L.DIT_ERR_STATE
+        # short workspace / cache
+        r = L._lib.dit_step_extract(m, C.byref(seq), FAKE, FAKE, 1.0, FAKE, kvb, FAKE, FAKE,
+                                    wsb - 1, 0, None)
+        assert r == L.DIT_ERR_WORKSPACE
+        r = L._lib.dit_step_extract(m, C.byref(seq), FAKE, FAKE, 1.0, FAKE, kvb - 2, FAKE, FAKE,
+                                    wsb, 0, None)
+        assert r == L.DIT_ERR_WORKSPACE
+        # null pointers, bad flags, bad sigma, bad layout counts
+        r = L._lib.dit_step_extract(m, C.byref(seq), FAKE, None, 1.0, FAKE, kvb, FAKE, FAKE, wsb, 0, None)
+        assert r == L.DIT_ERR_ARG
+        r = L._lib.dit_step_extract(m, C.byref(seq), FAKE, FAKE, 1.0, FAKE, kvb, FAKE, FAKE, wsb, 8, None)
+        assert r == L.DIT_ERR_ARG
+        r = L._lib.dit_step_extract(m, C.byref(seq), FAKE, FAKE, float("nan"), FAKE, kvb, FAKE,
+                                    FAKE, wsb, 0, None)
+        assert r == L.DIT_ERR_ARG
+        bad = L.dit_seq(7, 0, FAKE, FAKE, FAKE)
+        r = L._lib.dit_step_extract(m, C.byref(bad), FAKE, FAKE, 1.0, FAKE, kvb, FAKE, FAKE, wsb, 0, None)
+        assert r == L.DIT_ERR_LAYOUT
+        r = L._lib.dit_step_extract(m, C.byref(seq), FAKE, FAKE + 4, 1.0, FAKE, kvb, FAKE, FAKE,
+                                    wsb, 0, None)
+        assert r == L.DIT_ERR_ARG            # misaligned
+        assert L._lib.euler_update(None, FAKE, 1.0, 0.5, 4, None) == L.DIT_ERR_ARG
+        assert L._lib.dit_debug_gemm(FAKE, FAKE, FAKE, 10, 100, 64, None) == L.DIT_ERR_SHAPE
+        assert L._lib.dit_profile_enable(m, 99) == L.DIT_ERR_ARG
+    finally:
+        L.dit_free(m)
+
+
+def test_workspace_grows_with_tokens():
+    cfg, c = cfg_c("c1")
+    st, m = load(c)
+    try:
+        a, b = L.dit_workspace_bytes(m, 1024), L.dit_workspace_bytes(m, 1536)
+        assert 0 < a < b
+        # activations: f32 residual + bf16 (x, qkv, attn, ffn) per token
+        per_tok = 4096 * 4 + 4096 * 2 + 3 * 4096 * 2 + 4096 * 2 + 16384 * 2
+        assert abs((b - a) - 512 * per_tok) < 64 * 256
+    finally:
+        L.dit_free(m)

@@ -1,0 +1,135 @@
+"""GPU unit parity of individual kernels through the C ABI: the MFMA GEMM,
+the attention kernel's mask and arithmetic, against the fp64 oracle or
+exact integer arithmetic."""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from diffusion_transformer_amd import synth
+from gpu_common import cache_views, rel_err, say
+
+pytestmark = pytest.mark.gpu
+
+L = pytest.importorskip("diffusion_transformer_amd._lib")
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return torch.device("cuda:0")
+
+
+@pytest.mark.parametrize("M,N,K", [(32, 256, 64), (300, 512, 128), (257, 768, 256)])
+def test_gemm_exact_small_integers(dev, M, N, K):
+    """Entries in {-1, 0, 1}: every partial sum is an integer of magnitude
+    <= K <= 256, exact in fp32 and in the bf16 output, so the MFMA GEMM must
+    match integer matrix multiplication bit for bit (checks the MFMA lane
+    layout, the LDS swizzle, the tile order and the ragged M tail)."""
+    say(f"gemm exact M={M} N={N} K={K}")
+    g = torch.Generator().manual_seed(M * 7 + N + K)
+    A = torch.randint(-1, 2, (M, K), generator=g).to(torch.float32)
+    B = torch.randint(-1, 2, (N, K), generator=g).to(torch.float32)
+    want = (A.to(torch.int64) @ B.to(torch.int64).T).to(torch.float32)
+    Ad, Bd = A.to(dev, torch.bfloat16), B.to(dev, torch.bfloat16)
+    Cd = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    L.dit_debug_gemm(Ad, Bd, Cd, M, N, K)
+    torch.cuda.synchronize()
+    assert torch.equal(Cd.float().cpu(), want)
+
+
+def test_gemm_random_full_shape_sampled(dev):
+    """QKV-shaped GEMM (4096 x 12288 x 4096) with N(0,1) bf16 inputs; sampled
+    outputs against fp64 dot products of the same bf16 values."""
+    M, N, K = 4096, 12288, 4096
+    say(f"gemm random M={M} N={N} K={K}")
+    g = torch.Generator(device=dev).manual_seed(5)
+    A = torch.randn((M, K), generator=g, device=dev).to(torch.bfloat16)
+    B = torch.randn((N, K), generator=g, device=dev).to(torch.bfloat16)
+    Cd = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    L.dit_debug_gemm(A, B, Cd, M, N, K)
+    torch.cuda.synchronize()
+    rs = np.random.default_rng(0)
+    rows = rs.choice(M, 64, replace=False)
+    cols = rs.choice(N, 64, replace=False)
+    Ah = A[rows].float().cpu().numpy().astype(np.float64)
+    Bh = B[cols].float().cpu().numpy().astype(np.float64)
+    ref = Ah @ Bh.T
+    got = Cd[rows][:, cols].float().cpu().numpy()
+    # bf16 output rounding (2^-9 relative) dominates
+    assert np.abs(got - ref).max() <= 4e-3 * np.abs(ref).max() + 1e-2
+
+
+LAYOUTS = {
+    "c0w": [("text", 2), ("ref", 2, 2), ("text", 1), ("target", 2, 2)],
+    "c1": synth.CONFIGS["c1"]["segments"],
+    "c3": synth.CONFIGS["c3"]["segments"],
+    "ragged": [("text", 37), ("ref", 5, 7), ("text", 3), ("ref", 3, 3), ("target", 9, 11)],
+}
+
+
+def layout_for(segments):
+    c = L.make_config(hidden=256, n_heads=2, head_dim=128, ffn=512, n_layers=1)
+    return L.dit_build_layout(c, segments)
+
+
+@pytest.mark.parametrize("name", ["c0w", "c1", "c3", "ragged", "c4"])
+def test_attention_mask_bit_exact(dev, name):
+    segs = synth.CONFIGS["c4"]["segments"] if name == "c4" else LAYOUTS[name]
+    lay = layout_for(segs)
+    S = lay["P"] + lay["T"]
+    say(f"mask {name} S={S}")
+    lim = torch.from_numpy(lay["row_limit"]).to(dev)
+    seq = L.make_seq(lay["P"], lay["T"], lim, lim, lim)
+    mask = torch.full((S * S,), 7, dtype=torch.uint8, device=dev)
+    L.dit_debug_mask(seq, mask)
+    torch.cuda.synchronize()
+    got = mask.view(S, S)
+    ids = O.build_layout(segs).image_ids
+    for r0 in range(0, S, 2048):
+        rows = np.arange(r0, min(S, r0 + 2048))
+        want = torch.from_numpy(O.block_causal_mask(ids, rows=rows).astype(np.uint8))
+        assert torch.equal(got[r0:r0 + len(rows)].cpu(), want), f"rows {r0}.."
+
+
+def fill_cache(dev, S, nh, seed):
+    """Random K and V in the library's cache layout (layer 0 only); returns
+    the cache and the bf16-exact float64 K, V [S, nh, 128] it holds."""
+    cap = L.dit_kv_capacity(S)
+    g = torch.Generator().manual_seed(seed)
+    K = torch.randn((S, nh, 128), generator=g).to(torch.bfloat16)
+    V = torch.randn((S, nh, 128), generator=g).to(torch.bfloat16)
+    cache = torch.zeros(2 * nh * cap * 128, dtype=torch.int16)
+    kv, vt = cache_views(cache, 1, nh, cap)
+    kv[0, :, :S, :] = K.transpose(0, 1).view(torch.int16)
+    vt[0, :, :, :S] = V.permute(1, 2, 0).view(torch.int16)
+    return cache.to(dev), K.double().numpy(), V.double().numpy()
+
+
+@pytest.mark.parametrize("name,mode", [("c0w", "extract"), ("c0w", "cached"),
+                                       ("ragged", "extract"), ("ragged", "cached"),
+                                       ("c1", "extract"), ("c1", "cached"),
+                                       ("c3", "cached")])
+def test_attention_matches_oracle(dev, name, mode):
+    nh = 2
+    lay = layout_for(LAYOUTS[name])
+    P, T = lay["P"], lay["T"]
+    S = P + T
+    say(f"attention {name} {mode} S={S}")
+    cache, K, V = fill_cache(dev, S, nh, seed=S)
+    q_off, N = (0, S) if mode == "extract" else (P, T)
+    g = torch.Generator().manual_seed(11)
+    Q = torch.randn((N, nh, 128), generator=g).to(torch.bfloat16)
+    lim = torch.from_numpy(lay["row_limit"]).to(dev)
+    seq = L.make_seq(P, T, lim, lim, lim)
+    out = torch.empty((N, nh * 128), dtype=torch.bfloat16, device=dev)
+    Qd = Q.reshape(N, nh * 128).contiguous().to(dev)
+    L.dit_debug_attention(seq, nh, Qd, nh * 128, q_off, N, cache, out)
+    torch.cuda.synchronize()
+    ids = O.build_layout(LAYOUTS[name]).image_ids
+    allowed = O.block_causal_mask(ids, rows=np.arange(q_off, q_off + N))
+    ref = O.masked_attention(Q.double().numpy(), K, V, allowed)
+    err = rel_err(out.float().cpu().numpy(), ref)
+    say(f"  rel err {err:.3e}")
+    assert err < 1e-2

@@ -1,0 +1,190 @@
+"""GPU parity of the whole step (extract, cached, Euler) through the C ABI
+against the fp64 oracle on the same seeded inputs, plus the cache
+invariants the pages state, checked on the GPU path itself."""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from diffusion_transformer_amd import synth
+from gpu_common import cache_views, i16_to_f32, rel_err, say
+from oracle_inputs import dims_of, oracle_prefix
+
+pytestmark = pytest.mark.gpu
+
+L = pytest.importorskip("diffusion_transformer_amd._lib")
+from diffusion_transformer_amd.runtime import DitRuntime  # noqa: E402
+
+TOL_BF16 = 2e-2          # v_θ and final latent vs the oracle (bf16 path)
+TOL_CACHED = 1e-2        # GPU cached vs GPU full recompute
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return torch.device("cuda:0")
+
+
+def build(name, dev, n_layers=None, seed=21):
+    cfg = synth.config(name)
+    if n_layers is not None:
+        cfg["n_layers"] = n_layers
+    W = synth.make_weights(cfg, seed=seed)
+    I = synth.make_inputs(cfg, seed=seed)
+    rt = DitRuntime(cfg, W, device=dev)
+    seq = rt.sequence(cfg["segments"])
+    pre = rt.prefix_hidden(I)
+    x0 = torch.from_numpy(I["x0"]).to(dev)
+    return cfg, W, I, rt, seq, pre, x0
+
+
+@pytest.mark.parametrize("name", ["c0w", "c1"])
+def test_loop_matches_oracle(dev, name):
+    cfg, W, I, rt, seq, pre, x0 = build(name, dev)
+    sig = cfg["sigmas"]
+    say(f"loop {name} P={seq.P} T={seq.T} L={cfg['n_layers']}")
+    vs_c, xs_c = rt.run_loop(seq, pre, x0, sig, use_cache=True)
+    vs_r, xs_r = rt.run_loop(seq, pre, x0, sig, use_cache=False)
+    torch.cuda.synchronize()
+    dims = dims_of(cfg)
+    lay = O.build_layout(cfg["segments"])
+    ref = O.run_loop(W, dims, lay, oracle_prefix(cfg, W, I), I["x0"], sig, use_cache=True)
+    for k, r in enumerate(ref):
+        e_v = rel_err(vs_c[k].cpu().numpy(), r["v"])
+        e_x = rel_err(xs_c[k].cpu().numpy(), r["x_next"])
+        e_cr = rel_err(vs_c[k].cpu().numpy(), vs_r[k].cpu().numpy())
+        say(f"  step {k} {r['mode']}: v rel {e_v:.3e}  x rel {e_x:.3e}  cached-vs-recompute {e_cr:.3e}")
+        assert e_v < TOL_BF16 and e_x < TOL_BF16
+        assert e_cr < TOL_CACHED
+
+
+@pytest.mark.parametrize("name", ["c2", "c3", "c4"])
+def test_one_layer_full_token_counts_sampled(dev, name):
+    """Real token counts of each workload with one layer: v_θ of 48 sampled
+    target rows from extract (σ = 1) and from a cached step (σ = 0.978453, a
+    fresh seeded latent) against the oracle's row-wise evaluation."""
+    cfg, W, I, rt, seq, pre, x0 = build(name, dev, n_layers=1)
+    say(f"one-layer {name} P={seq.P} T={seq.T}")
+    cache = rt.alloc_cache(seq)
+    ws = rt.alloc_workspace(seq.S)
+    v = torch.empty_like(x0)
+    rt.step_extract(seq, pre, x0, 1.0, cache, v, ws)
+    x1 = synth._rng(99, "x_alt").standard_normal((seq.T, 64), dtype=np.float32)
+    v1 = torch.empty_like(x0)
+    rt.step_cached(seq, torch.from_numpy(x1).to(dev), 0.978453, cache, v1, ws)
+    torch.cuda.synchronize()
+    rows = np.sort(np.random.default_rng(7).choice(seq.T, 48, replace=False))
+    rows = np.unique(np.concatenate([[0, seq.T - 1], rows]))
+    dims = dims_of(cfg)
+    lay = O.build_layout(cfg["segments"])
+    opre = oracle_prefix(cfg, W, I)
+    r0 = O.cached_rows_one_layer(W, dims, lay, opre, I["x0"], 1.0, rows)
+    r1 = O.cached_rows_one_layer(W, dims, lay, opre, x1, 0.978453, rows)
+    e0 = rel_err(v.cpu().numpy()[rows], r0)
+    e1 = rel_err(v1.cpu().numpy()[rows], r1)
+    say(f"  extract rows rel {e0:.3e}  cached rows rel {e1:.3e}")
+    assert e0 < TOL_BF16 and e1 < TOL_BF16
+
+
+def test_cache_rows_land_at_their_token_index(dev):
+    """After extract, K cache row j of every head holds token j's post-norm,
+    post-RoPE key (nearest oracle row is j itself, and values agree to bf16
+    tolerance); V likewise; padding rows S..cap-1 are zero."""
+    cfg, W, I, rt, seq, pre, x0 = build("c1", dev)
+    cache = rt.alloc_cache(seq)
+    cache.fill_(0x3F80)   # 1.0 everywhere before the step
+    ws = rt.alloc_workspace(seq.S)
+    v = torch.empty_like(x0)
+    rt.step_extract(seq, pre, x0, 1.0, cache, v, ws)
+    torch.cuda.synchronize()
+    cap = L.dit_kv_capacity(seq.S)
+    kc, vt = cache_views(cache, 1, 32, cap)
+    lay = O.build_layout(cfg["segments"])
+    e = O.forward_extract(W, dims_of(cfg), lay, oracle_prefix(cfg, W, I), I["x0"], 1.0)
+    k_ref = e["k_all"][0]                               # [S, nh, d]
+    for h in (0, 17, 31):
+        kg = i16_to_f32(kc[0, h, :seq.S])               # [S, d]
+        assert rel_err(kg, k_ref[:, h]) < TOL_BF16
+        d2 = ((kg[:, None, :].astype(np.float64) - k_ref[None, :, h]) ** 2).sum(-1)
+        assert np.array_equal(np.argmin(d2, axis=1), np.arange(seq.S))
+    assert int(kc[0, :, seq.S:].abs().sum()) == 0
+    assert int(vt[0, :, :, seq.S:].abs().sum()) == 0
+
+
+@pytest.fixture(scope="module")
+def c2_full(dev):
+    """32-layer, 4096-wide text-to-image workload (256 text + 64x64 target)
+    with seeded weights drawn on the GPU."""
+    from diffusion_transformer_amd.runtime import random_weights_device
+    cfg = synth.config("c2")
+    Wd = random_weights_device(cfg, 21, dev)
+    rt = DitRuntime(cfg, Wd, device=dev, on_device=True)
+    I = synth.make_inputs(cfg)
+    seq = rt.sequence(cfg["segments"])
+    pre = rt.prefix_hidden(I)
+    x0 = torch.from_numpy(I["x0"]).to(dev)
+    yield cfg, rt, seq, pre, x0
+    rt.close()
+    del Wd
+    torch.cuda.empty_cache()
+
+
+def test_full_depth_cached_matches_recompute(dev, c2_full):
+    cfg, rt, seq, pre, x0 = c2_full
+    say("c2 full depth: 8-step cached loop vs recompute")
+    vs_c, xs_c = rt.run_loop(seq, pre, x0, cfg["sigmas"], use_cache=True)
+    vs_r, xs_r = rt.run_loop(seq, pre, x0, cfg["sigmas"], use_cache=False)
+    torch.cuda.synchronize()
+    for k in range(len(vs_c)):
+        assert torch.isfinite(vs_c[k]).all()
+        e = rel_err(vs_c[k].cpu().numpy(), vs_r[k].cpu().numpy())
+        say(f"  step {k}: cached vs recompute {e:.3e}")
+        assert e < TOL_CACHED
+    assert rel_err(xs_c[-1].cpu().numpy(), xs_r[-1].cpu().numpy()) < TOL_CACHED
+
+
+def test_full_depth_cache_invariants(dev, c2_full):
+    """Prefix K/V independent of σ and x; cached steps never write rows < P;
+    the same cached step twice gives identical bits; without t = 0
+    conditioning the prefix K/V change."""
+    cfg, rt, seq, pre, x0 = c2_full
+    say("c2 full depth: cache invariants")
+    P, S = seq.P, seq.S
+    cap = L.dit_kv_capacity(S)
+    Lc = cfg["n_layers"]
+    ws = rt.alloc_workspace(S)
+    v = torch.empty_like(x0)
+    c1 = rt.alloc_cache(seq)
+    rt.step_extract(seq, pre, x0, 1.0, c1, v, ws)
+    x1 = x0 + 0.37 * v
+    c2 = rt.alloc_cache(seq)
+    rt.step_extract(seq, pre, x1, 0.845148, c2, v, ws)
+    torch.cuda.synchronize()
+    k1, v1 = cache_views(c1, Lc, 32, cap)
+    k2, v2 = cache_views(c2, Lc, 32, cap)
+    assert torch.equal(k1[:, :, :P], k2[:, :, :P])
+    assert torch.equal(v1[:, :, :, :P], v2[:, :, :, :P])
+    # cached steps leave the prefix rows alone, and are deterministic
+    before_k = k1[:, :, :P].clone()
+    before_v = v1[:, :, :, :P].clone()
+    wa = rt.alloc_workspace(seq.T)
+    va, vb = torch.empty_like(x0), torch.empty_like(x0)
+    rt.step_cached(seq, x1, 0.95418, c1, va, wa)
+    rt.step_cached(seq, x1, 0.95418, c1, vb, wa)
+    torch.cuda.synchronize()
+    assert torch.equal(k1[:, :, :P], before_k) and torch.equal(v1[:, :, :, :P], before_v)
+    assert torch.equal(va, vb)
+    # drift without causal conditioning
+    c3 = rt.alloc_cache(seq)
+    c4 = rt.alloc_cache(seq)
+    rt.step_extract(seq, pre, x0, 1.0, c3, v, ws, flags=L.DIT_FLAG_NO_CAUSAL_CONDITION)
+    rt.step_extract(seq, pre, x1, 0.845148, c4, v, ws, flags=L.DIT_FLAG_NO_CAUSAL_CONDITION)
+    torch.cuda.synchronize()
+    k3, _ = cache_views(c3, Lc, 32, cap)
+    k4, _ = cache_views(c4, Lc, 32, cap)
+    for l in (0, Lc - 1):
+        assert not torch.equal(k3[l, :, :P], k4[l, :, :P])
+    with pytest.raises(L.DitError) as e:
+        rt.step_cached(seq, x1, 0.95418, c3, va, wa)
+    assert e.value.status == L.DIT_ERR_STATE
