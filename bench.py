@@ -1,0 +1,330 @@
+"""Throughput of the cached flow-matching DiT step on one MI355X.
+
+Workload: 32-layer, 4096-wide DiT (32 heads x 128, SwiGLU 16384), text-to-
+image layout of 256 text prefix tokens + a 64x64 target latent grid (4096
+target tokens), seeded synthetic bf16 weights N(0, 1/fan_in) and N(0,1)
+inputs. One extract step builds the prefix KV cache; the timed steps are
+cached Euler steps (dit_step_cached + euler_update) walking the 8-step Turbo
+schedule. Prints one JSON line.
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+GEMM_SRC = os.path.join(ROOT, "diffusion_transformer_amd", "csrc", "gemm.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gemm_gateup_c2_cached.json")
+
+
+def source_sha(path):
+    import hashlib
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def measured_traffic():
+    """HBM bytes per gate/up GEMM launch from the committed rocprofv3 PMC
+    runs (FETCH_SIZE and WRITE_SIZE scaled by a copy-kernel calibration), or
+    None when the kernel source changed since those counters were taken."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+        if t.get("source_sha256") != source_sha(GEMM_SRC):
+            return None
+        return t["bytes_per_launch"]
+    except (OSError, ValueError, KeyError):
+        return None
+
+
+def summarize_profiles(trace_dir, fetch_dir, write_dir, command, out_md, out_json):
+    """Turn rocprofv3 CSV output (kernel stats + FETCH_SIZE/WRITE_SIZE
+    counter runs that include the --calib-copy kernel) into the committed
+    summaries."""
+    import csv
+    stats = list(csv.DictReader(open(os.path.join(trace_dir, "run_kernel_stats.csv"))))
+    lines = [f"# rocprofv3 kernel stats: cached DiT step, c2 workload", "",
+             f"Command (from the repository root on the GPU box):", "", "```", command, "```", "",
+             "| kernel | calls | avg us | min us | max us | % time |", "|---|---|---|---|---|---|"]
+    for r in stats[:16]:
+        nm = r["Name"].replace("dit::(anonymous namespace)::", "").replace("|", "/")[:80]
+        lines.append(f"| {nm} | {r['Calls']} | {float(r['AverageNs'])/1e3:.1f} | "
+                     f"{float(r['MinNs'])/1e3:.1f} | {float(r['MaxNs'])/1e3:.1f} | {float(r['Percentage']):.2f} |")
+    res = {}
+    for name, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        rows = list(csv.DictReader(open(os.path.join(d, "run_counter_collection.csv"))))
+        cp = [r for r in rows if "bfloat16_copy" in r["Kernel_Name"]]
+        calib = max(cp, key=lambda r: int(r["Dispatch_Id"]))
+        known_kib = (1 << 28) * (4 if name == "FETCH_SIZE" else 2) / 1024.0
+        factor = known_kib / float(calib["Counter_Value"])
+        gu = [float(r["Counter_Value"]) for r in rows
+              if "gemm_kernel<256, 256, 2, 4, 3>" in r["Kernel_Name"]
+              and int(r["Grid_Size"]) == 2048 * 512]
+        res[name] = {"calib_kib": float(calib["Counter_Value"]), "known_kib": known_kib,
+                     "factor": factor, "gateup_kib_avg": sum(gu) / len(gu), "n": len(gu)}
+    fb = res["FETCH_SIZE"]["gateup_kib_avg"] * res["FETCH_SIZE"]["factor"] * 1024
+    wb = res["WRITE_SIZE"]["gateup_kib_avg"] * res["WRITE_SIZE"]["factor"] * 1024
+    lines += ["", "## HBM traffic of the gate/up GEMM (cached step, 4096 x 32768 x 4096)", "",
+              "Two counter runs of the same command with `--steps 2 --calib-copy`, one counter each:",
+              "`rocprofv3 --pmc FETCH_SIZE ...` and `rocprofv3 --pmc WRITE_SIZE ...`.",
+              "Calibration: the fp32->bf16 copy of 2^28 elements reads 1 GiB and writes 512 MiB.", "",
+              "| counter | copy kernel reads (KiB) | known (KiB) | factor | gate/up per launch (KiB) | scaled bytes |",
+              "|---|---|---|---|---|---|"]
+    for name in ("FETCH_SIZE", "WRITE_SIZE"):
+        r = res[name]
+        lines.append(f"| {name} | {r['calib_kib']:.0f} | {r['known_kib']:.0f} | {r['factor']:.4f} | "
+                     f"{r['gateup_kib_avg']:.0f} (n={r['n']}) | "
+                     f"{r['gateup_kib_avg'] * r['factor'] * 1024:.4g} |")
+    alg = (4096 * 4096 + 2 * 16384 * 4096 + 4096 * 16384) * 2
+    lines += ["", f"Total {fb + wb:.4g} bytes per launch vs {alg:.4g} algorithmic "
+                  f"(A 32 MiB + B 256 MiB read, 128 MiB written): x{(fb + wb) / alg:.2f}."]
+    open(out_md, "w").write("\n".join(lines) + "\n")
+    json.dump({"kernel": "gemm_kernel<256,256,2,4,SwiGLU> gate/up, cached c2 (M=4096)",
+               "source_sha256": source_sha(GEMM_SRC), "fetch": res["FETCH_SIZE"],
+               "write": res["WRITE_SIZE"], "bytes_per_launch": fb + wb,
+               "algorithmic_bytes": alg}, open(out_json, "w"), indent=1)
+
+
+def layer_flops(T, S, H, F, nh, d):
+    """Algorithmic FLOPs of one cached layer: QKV, O, gate/up, down GEMMs
+    (2 flop per MAC) and attention over all S keys (QKᵀ and PV)."""
+    return {"gemm_qkv": 2 * T * H * 3 * H, "gemm_o": 2 * T * H * H,
+            "gemm_gateup": 2 * T * H * 2 * F, "gemm_down": 2 * T * F * H,
+            "attention": 4 * T * S * d * nh}
+
+
+def cpu_baseline(cfg, seconds_hint=True):
+    """The fp64 oracle timed on this host on a bounded sample: one of the
+    32 layers of the cached step (all 4096 target rows against a 256-row
+    prefix cache), scaled x32 to a full cached step."""
+    import oracle as O
+    from diffusion_transformer_amd import synth
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [os.cpu_count()])
+    except Exception:
+        cores = os.cpu_count()
+    c1 = dict(cfg)
+    c1["n_layers"] = 1
+    W = synth.make_weights(c1, seed=21)
+    I = synth.make_inputs(c1, seed=21)
+    dims = O.DitDims(hidden=cfg["hidden"], n_heads=cfg["n_heads"], head_dim=cfg["head_dim"],
+                     ffn=cfg["ffn"], n_layers=1, latent=cfg["latent"], time_dim=cfg["time_dim"],
+                     rope_dims=tuple(cfg["rope_dims"]))
+    lay = O.build_layout(cfg["segments"])
+    rng = np.random.default_rng(3)
+    cache = [(rng.standard_normal((lay.P, dims.n_heads, dims.head_dim)),
+              rng.standard_normal((lay.P, dims.n_heads, dims.head_dim)))]
+    t0 = time.perf_counter()
+    O.forward_cached(W, dims, lay, cache, I["x0"], 0.978453)
+    dt = time.perf_counter() - t0
+    step_s = dt * cfg["n_layers"]
+    return {"value": lay.T / step_s, "unit": "target tokens/s", "cores": int(cores),
+            "kind": "oracle",
+            "sample": (f"1 of {cfg['n_layers']} layers of one cached step (T={lay.T} target rows, "
+                       f"P={lay.P} cached prefix rows, fp64 NumPy), {dt:.1f} s measured, "
+                       f"scaled x{cfg['n_layers']}")}
+
+
+def main():
+    if len(sys.argv) > 1 and sys.argv[1] == "--summarize-prof":
+        # bench.py --summarize-prof TRACE_DIR FETCH_DIR WRITE_DIR "COMMAND"
+        summarize_profiles(sys.argv[2], sys.argv[3], sys.argv[4], sys.argv[5],
+                           os.path.join(ROOT, "profiles", "gemm_gateup_c2_cached.md"), TRAFFIC_FILE)
+        return
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", default="c2")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-breakdown", action="store_true")
+    ap.add_argument("--only-timed", action="store_true",
+                    help="run only cache build + warmup + timed cached steps (for profilers)")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="after timing, run one fp32->bf16 conversion of 2^28 elements "
+                         "(1 GiB read, 512 MiB written) to calibrate byte counters")
+    args = ap.parse_args()
+    if args.only_timed:
+        args.no_breakdown = True
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from diffusion_transformer_amd import _lib as L
+    from diffusion_transformer_amd import synth
+    from diffusion_transformer_amd.runtime import DitRuntime, random_weights_device
+
+    dev = torch.device("cuda:0")
+    cfg = synth.config(args.config)
+    H, F, nh, d, Lc = cfg["hidden"], cfg["ffn"], cfg["n_heads"], cfg["head_dim"], cfg["n_layers"]
+    print(f"[bench] workload {args.config}: generating weights on GPU", file=sys.stderr, flush=True)
+    Wd = random_weights_device(cfg, 21, dev)
+    rt = DitRuntime(cfg, Wd, device=dev, on_device=True)
+    I = synth.make_inputs(cfg, seed=21)
+    seq = rt.sequence(cfg["segments"])
+    P, T, S = seq.P, seq.T, seq.S
+    pre = rt.prefix_hidden(I)
+    x = torch.from_numpy(I["x0"]).to(dev)
+    sig = cfg["sigmas"]
+    cache = rt.alloc_cache(seq)
+    ws = rt.alloc_workspace(S)
+    v = torch.empty_like(x)
+    stream = torch.cuda.current_stream()
+
+    def extract(xx):
+        rt.step_extract(seq, pre, xx, sig[0], cache, v, ws)
+
+    def cached(k, xx):
+        # cached steps walk the Turbo schedule's steps 2..8
+        j = 1 + (k % (len(sig) - 2))
+        rt.step_cached(seq, xx, sig[j], cache, v, ws)
+        L.euler_update(xx, v, sig[j], sig[j + 1])
+
+    print(f"[bench] P={P} T={T} S={S} L={Lc}: warmup", file=sys.stderr, flush=True)
+    extract(x)
+    xw = x.clone()
+    for k in range(args.warmup):
+        cached(k, xw)
+    torch.cuda.synchronize()
+
+    # ---- timed region: K cached Euler steps; dominant kernel timed by
+    # events the library records around each of its launches ----
+    L.dit_profile_enable(rt.model, "gemm_gateup")
+    xt = x.clone()
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    evs[0].record(stream)
+    for k in range(args.steps):
+        cached(k, xt)
+        evs[k + 1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    gu_ms, gu_n = L.dit_profile_read(rt.model)
+    L.dit_profile_enable(rt.model, "off")
+    step_ms = np.array([evs[k].elapsed_time(evs[k + 1]) for k in range(args.steps)])
+    ms_per_step = wall * 1000.0 / args.steps
+    value = T / (ms_per_step / 1000.0)
+    print(f"[bench] cached step {ms_per_step:.3f} ms, {value:.0f} target tok/s", file=sys.stderr,
+          flush=True)
+
+    fl = layer_flops(T, S, H, F, nh, d)
+    gu_avg = gu_ms / max(gu_n, 1)
+    gu_tflops = fl["gemm_gateup"] / (gu_avg / 1e3) / 1e12
+    roofline = {"bound": "mfma", "achieved": round(gu_tflops, 1), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(gu_tflops / PEAK_BF16_TFLOPS, 4),
+                "traffic": measured_traffic(), "kernel": "gemm_kernel<256,256,2,4,SwiGLU> (gate/up)",
+                "avg_launch_ms": round(gu_avg, 4), "launches": gu_n}
+
+    if args.calib_copy:
+        src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+        dst = torch.empty(1 << 28, dtype=torch.bfloat16, device=dev)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    # ---- extract step and full 8-step loop ----
+    extract_ms = loop_ms = float("nan")
+    ex = []
+    for _ in range(0 if args.only_timed else 3):
+        a = torch.cuda.Event(enable_timing=True); b = torch.cuda.Event(enable_timing=True)
+        a.record(stream); extract(x.clone()); b.record(stream); torch.cuda.synchronize()
+        ex.append(a.elapsed_time(b))
+    if not args.only_timed:
+        extract_ms = float(np.median(ex))
+        xl = x.clone()
+        a = torch.cuda.Event(enable_timing=True); b = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        rt.step_extract(seq, pre, xl, sig[0], cache, v, ws)
+        L.euler_update(xl, v, sig[0], sig[1])
+        for j in range(1, len(sig) - 1):
+            rt.step_cached(seq, xl, sig[j], cache, v, ws)
+            L.euler_update(xl, v, sig[j], sig[j + 1])
+        b.record(stream)
+        torch.cuda.synchronize()
+        loop_ms = a.elapsed_time(b)
+
+    # ---- per-kernel breakdown of the cached step (separate passes) ----
+    breakdown = {}
+    if not args.no_breakdown:
+        for name in ("gemm_qkv", "gemm_o", "gemm_gateup", "gemm_down", "attention", "ln",
+                     "qknorm_rope"):
+            L.dit_profile_enable(rt.model, name)
+            xb = x.clone()
+            for k in range(3):
+                cached(k, xb)
+            torch.cuda.synchronize()
+            ms, n = L.dit_profile_read(rt.model)
+            avg = ms / max(n, 1)
+            entry = {"avg_ms": round(avg, 4), "per_step_ms": round(ms / 3, 3)}
+            if name in fl:
+                tf = fl[name] / (avg / 1e3) / 1e12
+                entry.update({"tflops": round(tf, 1), "frac_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4)})
+            elif name == "ln":
+                by = T * H * (4 + 2) + 2 * H * 4
+                gbs = by / (avg / 1e3) / 1e9
+                entry.update({"gbs": round(gbs, 1), "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4)})
+            elif name == "qknorm_rope":
+                by = T * 3 * H * 2 * 2 + T * 64 * 4 * 2
+                gbs = by / (avg / 1e3) / 1e9
+                entry.update({"gbs": round(gbs, 1), "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4)})
+            breakdown[name] = entry
+        L.dit_profile_enable(rt.model, "off")
+
+    step_flops = Lc * sum(fl.values())
+    out = {
+        "metric": "target tokens/s per cached Euler step (32-layer DiT); MFMA % of bf16 peak",
+        "value": round(value, 1),
+        "unit": "target tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1/fan_in) bf16 weights, N(0,1) inputs)",
+        "config": {"workload": f"{args.config}: text-to-image, {P} text prefix + "
+                               f"{int(round(T ** 0.5))}x{int(round(T ** 0.5))} target tokens, "
+                               f"{Lc} layers, hidden {H}, {nh}x{d} heads, SwiGLU {F}, "
+                               f"cached Euler step (Turbo schedule)",
+                   "prefix_tokens": P, "target_tokens": T, "layers": Lc, "batch": 1,
+                   "parallelism": "single GPU"},
+        "latency_ms": {"p50": round(float(np.percentile(step_ms, 50)), 3),
+                       "p95": round(float(np.percentile(step_ms, 95)), 3),
+                       "p99": round(float(np.percentile(step_ms, 99)), 3)},
+        "step_tflops": round(step_flops / (ms_per_step / 1e3) / 1e12, 1),
+        "step_frac_bf16_peak": round(step_flops / (ms_per_step / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+        "extract_ms": None if extract_ms != extract_ms else round(extract_ms, 3),
+        "extract_over_cached": None if extract_ms != extract_ms else round(extract_ms / ms_per_step, 3),
+        "loop_8step_ms": None if loop_ms != loop_ms else round(loop_ms, 3),
+        "roofline": roofline,
+        "kernels": breakdown,
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the fp64 oracle on the host (cpu_baseline)", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(cfg)
+    else:
+        out["cpu_baseline"] = None
+    rt.close()
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()
