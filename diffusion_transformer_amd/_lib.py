@@ -73,7 +73,7 @@ def _load():
         "dit_img_in": (i, [vp, vp, i, vp, vp]),
         "dit_debug_mask": (i, [P(dit_seq), vp, vp]),
         "dit_debug_attention": (i, [P(dit_seq), i, vp, i, i, i, vp, vp, vp]),
-        "dit_debug_gemm": (i, [vp, vp, vp, i, i, i, vp]),
+        "dit_debug_gemm": (i, [vp, vp, vp, i, i, i, i, vp]),
         "dit_profile_enable": (i, [vp, i]),
         "dit_profile_read": (i, [vp, P(C.c_double), P(ll)]),
         "dit_last_error": (C.c_char_p, []),
@@ -233,8 +233,8 @@ def dit_debug_attention(seq: dit_seq, n_heads, q, q_stride, q_off, N, kv_cache, 
                                     int(N), _ptr(kv_cache), _ptr(out), _stream(stream)))
 
 
-def dit_debug_gemm(A, B, Cmat, M, N, K, stream=None):
-    _check(_lib.dit_debug_gemm(_ptr(A), _ptr(B), _ptr(Cmat), int(M), int(N), int(K),
+def dit_debug_gemm(A, B, Cmat, M, N, K, variant=0, stream=None):
+    _check(_lib.dit_debug_gemm(_ptr(A), _ptr(B), _ptr(Cmat), int(M), int(N), int(K), int(variant),
                                _stream(stream)))
 
 

@@ -9,7 +9,9 @@
 // The output is accumulated transposed as well, Oᵀ = Vᵀ·Pᵀ, which lets the
 // probabilities feed the MFMA B operand straight from registers; V is kept
 // transposed (dim-major) in the cache so the Vᵀ A-operand is a pair of
-// 8-byte LDS reads. K and Vᵀ tiles of 64 keys are staged through LDS,
+// 8-byte LDS reads. LDS chunks are XOR-swizzled for gfx950's 64 banks
+// (256 bytes per bank cycle): K rows are 256 bytes, so chunk ^= key%16;
+// Vᵀ rows are 128 bytes (two per bank cycle), so chunk ^= (dim/2)%16. K and Vᵀ tiles of 64 keys are staged through LDS,
 // double-buffered with register prefetch. Waves whose queries see none of a
 // key tile skip its arithmetic; tiles past the block's largest limit are
 // never loaded.
@@ -26,8 +28,8 @@ constexpr int BKV = 64;
 constexpr int NT = 256;
 
 __global__ __launch_bounds__(NT) void attn_kernel(AttnArgs a) {
-  __shared__ u32x4 ks[2][BKV * 16];        // [key][16 chunks of 8 dims], chunk ^= key%8
-  __shared__ u32x2 vs[2][D * 16];          // [dim][16 chunks of 4 keys], chunk ^= dim%16
+  __shared__ u32x4 ks[2][BKV * 16];        // [key][16 chunks of 8 dims], chunk ^= key%16
+  __shared__ u32x2 vs[2][D * 16];          // [dim][16 chunks of 4 keys], chunk ^= (dim/2)%16
   __shared__ int red[8];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -75,15 +77,15 @@ __global__ __launch_bounds__(NT) void attn_kernel(AttnArgs a) {
   };
   auto lstore = [&](int buf) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) ks[buf][k_row[i] * 16 + (k_c[i] ^ (k_row[i] & 7))] = rk[i];
+    for (int i = 0; i < 4; ++i) ks[buf][k_row[i] * 16 + (k_c[i] ^ (k_row[i] & 15))] = rk[i];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int e = v_row[i];
       const int c0 = 2 * v_c[i], c1 = c0 + 1;
       u32x2 lo, hi;
       lo.x = rv[i].x; lo.y = rv[i].y; hi.x = rv[i].z; hi.y = rv[i].w;
-      vs[buf][e * 16 + (c0 ^ (e & 15))] = lo;
-      vs[buf][e * 16 + (c1 ^ (e & 15))] = hi;
+      vs[buf][e * 16 + (c0 ^ ((e >> 1) & 15))] = lo;
+      vs[buf][e * 16 + (c1 ^ ((e >> 1) & 15))] = hi;
     }
   };
 
@@ -120,7 +122,7 @@ __global__ __launch_bounds__(NT) void attn_kernel(AttnArgs a) {
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
           const int row = kb * 32 + lq;
-          bf16x8 kf = __builtin_bit_cast(bf16x8, ks[cur][row * 16 + ((2 * s + half) ^ (row & 7))]);
+          bf16x8 kf = __builtin_bit_cast(bf16x8, ks[cur][row * 16 + ((2 * s + half) ^ (row & 15))]);
           sacc[kb] = mfma32(kf, qf[s], sacc[kb]);
         }
       }
@@ -175,8 +177,8 @@ __global__ __launch_bounds__(NT) void attn_kernel(AttnArgs a) {
 #pragma unroll
         for (int db = 0; db < 4; ++db) {
           const int e = db * 32 + lq;
-          const u32x2 va = vs[cur][e * 16 + (k8a ^ (e & 15))];
-          const u32x2 vb = vs[cur][e * 16 + (k8b ^ (e & 15))];
+          const u32x2 va = vs[cur][e * 16 + (k8a ^ ((e >> 1) & 15))];
+          const u32x2 vb = vs[cur][e * 16 + (k8b ^ ((e >> 1) & 15))];
           u32x4 vv;
           vv.x = va.x; vv.y = va.y; vv.z = vb.x; vv.w = vb.y;
           oacc[db] = mfma32(__builtin_bit_cast(bf16x8, vv), pf, oacc[db]);

@@ -25,6 +25,25 @@ __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
+// s_waitcnt immediates (gfx9 encoding: vmcnt bits [3:0] and [15:14],
+// expcnt [6:4], lgkmcnt [11:8]; a counter at its maximum is not waited on).
+constexpr int waitcnt_vm(int n) { return (n & 0xF) | ((n >> 4) << 14) | 0x70 | 0xF00; }
+constexpr int kWaitLgkm0 = 0xF | 0xC000 | 0x70;
+
+// Workgroup barrier that orders LDS only: waits for this wave's LDS
+// operations, not for its outstanding global loads (a full __syncthreads
+// fence would drain every in-flight prefetch).
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// Raw buffer resource over [p, p + bytes): loads past the end return zero.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
+}
+
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);

@@ -490,14 +490,17 @@ dit_status dit_debug_attention(const dit_seq* seq, int n_heads, const void* q, i
   return hip_check(launch_attention(a, static_cast<hipStream_t>(stream)), "debug attention");
 }
 
-dit_status dit_debug_gemm(const void* A, const void* B, void* C, int M, int N, int K, void* stream) {
+dit_status dit_debug_gemm(const void* A, const void* B, void* C, int M, int N, int K, int variant,
+                          void* stream) {
   if (!A || !B || !C) return fail(DIT_ERR_ARG, "NULL argument");
   if (!gemm_shape_ok(M, N, K, EPI_BF16)) return fail(DIT_ERR_SHAPE, "GEMM needs M>0, N%%256==0, K%%64==0");
   GemmArgs g{};
   g.A = static_cast<const uint16_t*>(A); g.lda = K;
   g.B = static_cast<const uint16_t*>(B); g.ldb = K;
   g.M = M; g.N = N; g.K = K; g.C = C; g.ldc = N;
-  return hip_check(launch_gemm(g, EPI_BF16, static_cast<hipStream_t>(stream)), "debug gemm");
+  if (variant < 0 || variant > 16) return fail(DIT_ERR_ARG, "unknown GEMM variant %d", variant);
+  if (variant == 0) return hip_check(launch_gemm(g, EPI_BF16, static_cast<hipStream_t>(stream)), "debug gemm");
+  return hip_check(launch_gemm_variant(g, variant, static_cast<hipStream_t>(stream)), "debug gemm");
 }
 
 dit_status dit_profile_enable(dit_model* m, int kernel_class) {

@@ -3,9 +3,11 @@
 //
 // Block tile BM×BN×64, WM×WN waves, each wave owns a (BM/WM)×(BN/WN) tile
 // built from v_mfma_f32_32x32x16_bf16 blocks. Operand tiles are staged
-// global -> registers -> LDS, double-buffered (one barrier per K step),
-// with a 16-byte-chunk XOR swizzle (chunk ^ row%8) so that the 8 lanes an
-// LDS read serves together hit 8 different bank groups.
+// global -> registers -> LDS, double-buffered (one barrier per K step).
+// LDS rows are 128 bytes (64 bf16 of K). gfx950 serves a ds_read_b128 16
+// lanes per cycle across 64 banks (256 bytes), i.e. two consecutive rows per
+// bank cycle, so the 16-byte chunk c of row r is stored at c ^ ((r/2)%8):
+// the 16 rows one read phase touches then land on 16 distinct bank groups.
 //
 // Tile order is XCD-aware: the hardware deals workgroups round-robin over
 // the 8 XCDs, so block b is remapped to logical tile (b%8)*(n/8) + b/8,
@@ -22,7 +24,7 @@ namespace {
 constexpr int BK = 64;
 constexpr int GROUP_M = 4;
 
-template <int BM, int BN, int WM, int WN, int EPI>
+template <int BM, int BN, int WM, int WN, int EPI, int SCHED = 0>
 __global__ __launch_bounds__(WM* WN * 64) void gemm_kernel(GemmArgs g) {
   constexpr int NT = WM * WN * 64;
   constexpr int TM = BM / WM, TN = BN / WN;
@@ -54,36 +56,47 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_kernel(GemmArgs g) {
   const int tn = (b % in_group) / gsz;
   const int m0 = tm * BM, n0 = tn * BN;
 
-  // ---- global source pointers for this thread's chunks ----
-  const u32x4* asrc[ACH];
-  int adst[ACH];
-#pragma unroll
-  for (int i = 0; i < ACH; ++i) {
-    int q = tid + i * NT;
-    int row = q >> 3, c = q & 7;
-    int gr = min(m0 + row, g.M - 1);
-    asrc[i] = reinterpret_cast<const u32x4*>(g.A + (size_t)gr * g.lda + c * 8);
-    adst[i] = row * 8 + (c ^ (row & 7));
-  }
-  const u32x4* bsrc[BCH];
-  int bdst[BCH];
-#pragma unroll
-  for (int i = 0; i < BCH; ++i) {
-    int q = tid + i * NT;
-    int row = q >> 3, c = q & 7;
-    int p = n0 + row;
-    const uint16_t* base;
-    if (EPI == EPI_SWIGLU) {
-      // packed column p: 32-wide blocks alternate gate / up for the same
-      // 32 features: block b2 = p/64, half s = (p/32)&1, feature 32*b2 + p%32
-      int f = ((p >> 6) << 5) + (p & 31);
-      base = (((p >> 5) & 1) ? g.B2 : g.B) + (size_t)f * g.ldb;
+  // ---- buffer resources (base at this tile's first row / feature) ----
+  // Rows past M fall outside the A resource and read as zero. Thread t
+  // loads 16-byte chunk c = t%8 of rows r0 + i*RPI (r0 = t/8, RPI = NT/8);
+  // its lane offset is fixed, the row step i and the K position go into
+  // the scalar offset, and the LDS slot of chunk i is a constant offset
+  // (RPI is a multiple of 16, so the swizzle (row/2)%8 is the same for all i).
+  constexpr int RPI = NT / 8;
+  static_assert(RPI % 16 == 0, "swizzle must repeat across chunk passes");
+  const int r0 = tid >> 3, c0 = tid & 7;
+  const int sw0 = (r0 >> 1) & 7;
+  const __amdgpu_buffer_rsrc_t rA = make_rsrc(
+      g.A + (size_t)m0 * g.lda, (uint32_t)min((size_t)(g.M - m0) * g.lda * 2, (size_t)0xFFFFFFF0u));
+  const uint32_t aoff = (uint32_t)((r0 * g.lda + c0 * 8) * 2);
+  const uint32_t astep = (uint32_t)(RPI * g.lda * 2);
+  const int adst = r0 * 8 + (c0 ^ sw0);
+  // B: for SwiGLU the packed column p maps to feature 32*(p/64) + p%32 of
+  // the gate matrix if (p/32) is even, else of the up matrix.
+  __amdgpu_buffer_rsrc_t rB0, rB1;
+  uint32_t boff, bstep;
+  if (EPI == EPI_SWIGLU) {
+    const size_t bytes = min((size_t)(BN / 2) * g.ldb * 2, (size_t)0xFFFFFFF0u);
+    rB0 = make_rsrc(g.B + (size_t)(n0 >> 1) * g.ldb, (uint32_t)bytes);
+    rB1 = make_rsrc(g.B2 + (size_t)(n0 >> 1) * g.ldb, (uint32_t)bytes);
+    if (RPI >= 64) {
+      // every chunk of this thread is in the same 32-row half: pick the
+      // matrix once per wave (8 rows per wave never cross a 32-row block)
+      const int sel = __builtin_amdgcn_readfirstlane((r0 >> 5) & 1);
+      if (sel) rB0 = rB1;
+      boff = (uint32_t)(((32 * (r0 >> 6) + (r0 & 31)) * g.ldb + c0 * 8) * 2);
+      bstep = (uint32_t)((RPI / 2) * g.ldb * 2);
     } else {
-      base = g.B + (size_t)p * g.ldb;
+      // RPI == 32: chunk i is gate for even i, up for odd i, row 32*(i/2) + r0
+      boff = (uint32_t)((r0 * g.ldb + c0 * 8) * 2);
+      bstep = (uint32_t)(32 * g.ldb * 2);
     }
-    bsrc[i] = reinterpret_cast<const u32x4*>(base + c * 8);
-    bdst[i] = BM * 8 + row * 8 + (c ^ (row & 7));
+  } else {
+    rB0 = rB1 = make_rsrc(g.B + (size_t)n0 * g.ldb, (uint32_t)min((size_t)BN * g.ldb * 2, (size_t)0xFFFFFFF0u));
+    boff = (uint32_t)((r0 * g.ldb + c0 * 8) * 2);
+    bstep = (uint32_t)(RPI * g.ldb * 2);
   }
+  const int bdst = BM * 8 + r0 * 8 + (c0 ^ sw0);
 
   f32x16 acc[FM][FN];
 #pragma unroll
@@ -93,60 +106,100 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_kernel(GemmArgs g) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  u32x4 ra[ACH], rb[BCH];
   const int nk = g.K / BK;
-
-  // prologue: stage 0
-#pragma unroll
-  for (int i = 0; i < ACH; ++i) ra[i] = asrc[i][0];
-#pragma unroll
-  for (int i = 0; i < BCH; ++i) rb[i] = bsrc[i][0];
-#pragma unroll
-  for (int i = 0; i < ACH; ++i) smem[0][adst[i]] = ra[i];
-#pragma unroll
-  for (int i = 0; i < BCH; ++i) smem[0][bdst[i]] = rb[i];
-  __syncthreads();
-
   const int lrow = lane & 31;
   const int lhalf = lane >> 5;
-  const int sw = lane & 7;   // row % 8 of every row this lane reads
+  const int sw = (lane >> 1) & 7;   // (row/2) % 8 of every row this lane reads
 
-  for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    const bool more = kt + 1 < nk;
-    if (more) {
-      const int ko = (kt + 1) * (BK / 8);   // in 16-byte units
+  // Two register staging sets: tile kt+1 sits in set (kt+1)&1 while the
+  // loads of tile kt+2 go to set kt&1, so every global load has two K steps
+  // of MFMA work to arrive before its ds_write.
+  u32x4 ra[2][ACH], rb[2][BCH];
+  auto gload = [&](int set, int kt) {
+    const uint32_t ko = (uint32_t)(kt * BK * 2);   // bytes
 #pragma unroll
-      for (int i = 0; i < ACH; ++i) ra[i] = asrc[i][ko];
+    for (int i = 0; i < ACH; ++i)
+      ra[set][i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rA, aoff, ko + i * astep, 0));
 #pragma unroll
-      for (int i = 0; i < BCH; ++i) rb[i] = bsrc[i][ko];
+    for (int i = 0; i < BCH; ++i) {
+      if (EPI == EPI_SWIGLU && RPI < 64)
+        rb[set][i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+            (i & 1) ? rB1 : rB0, boff, ko + (i >> 1) * bstep, 0));
+      else
+        rb[set][i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rB0, boff, ko + i * bstep, 0));
     }
-    const u32x4* As = smem[cur];
-    const u32x4* Bs = smem[cur] + BM * 8;
+  };
+  auto lstore = [&](int set, int buf) {
 #pragma unroll
-    for (int s = 0; s < BK / 16; ++s) {
-      const int ch = (2 * s + lhalf) ^ sw;
-      bf16x8 af[FM], bfr[FN];
+    for (int i = 0; i < ACH; ++i) smem[buf][adst + i * RPI * 8] = ra[set][i];
 #pragma unroll
-      for (int i = 0; i < FM; ++i)
-        af[i] = __builtin_bit_cast(bf16x8, As[(wm * TM + i * 32 + lrow) * 8 + ch]);
+    for (int i = 0; i < BCH; ++i) smem[buf][bdst + i * RPI * 8] = rb[set][i];
+  };
+  // fragments of one 16-wide K slice, double-buffered in registers
+  bf16x8 fa[2][FM], fb[2][FN];
+  auto lread = [&](int fset, int buf, int s) {
+    const u32x4* As = smem[buf];
+    const u32x4* Bs = smem[buf] + BM * 8;
+    const int ch = (2 * s + lhalf) ^ sw;
 #pragma unroll
-      for (int j = 0; j < FN; ++j)
-        bfr[j] = __builtin_bit_cast(bf16x8, Bs[(wn * TN + j * 32 + lrow) * 8 + ch]);
+    for (int i = 0; i < FM; ++i)
+      fa[fset][i] = __builtin_bit_cast(bf16x8, As[(wm * TM + i * 32 + lrow) * 8 + ch]);
 #pragma unroll
-      for (int i = 0; i < FM; ++i)
+    for (int j = 0; j < FN; ++j)
+      fb[fset][j] = __builtin_bit_cast(bf16x8, Bs[(wn * TN + j * 32 + lrow) * 8 + ch]);
+  };
+  auto mma = [&](int fset) {
 #pragma unroll
-        for (int j = 0; j < FN; ++j) acc[i][j] = mfma32(af[i], bfr[j], acc[i][j]);
-    }
-    if (more) {
-      u32x4* nxt = smem[cur ^ 1];
+    for (int i = 0; i < FM; ++i)
 #pragma unroll
-      for (int i = 0; i < ACH; ++i) nxt[adst[i]] = ra[i];
-#pragma unroll
-      for (int i = 0; i < BCH; ++i) nxt[bdst[i]] = rb[i];
-    }
-    __syncthreads();
+      for (int j = 0; j < FN; ++j) acc[i][j] = mfma32(fa[fset][i], fb[fset][j], acc[i][j]);
+  };
+
+  // prologue: tile 0 -> LDS buffer 0; tile 1 in flight in set 1
+  gload(0, 0);
+  gload(1, min(1, nk - 1));
+  lstore(0, 0);
+  lds_barrier();
+  lread(0, 0, 0);
+
+  // One K step of 64 = four 16-wide slices s = 0..3 on LDS buffer par:
+  //  - tile kt+2 is requested into register set par (freed when tile kt
+  //    was stored);
+  //  - slice s+1 is read from LDS while the MFMAs of slice s run;
+  //  - tile kt+1 (register set par^1, requested one step earlier) is
+  //    stored to the other LDS buffer during slice 1;
+  //  - the only barrier sits before slice 3, so the first slice of the next
+  //    tile is read while slice 3 computes. Every read of a buffer is issued
+  //    before the barrier that precedes the next store into it.
+  // All memory operations in the loop are unconditional: past the end the
+  // loads re-read the last tile and the store fills the idle LDS buffer,
+  // which nothing reads again. This keeps the waitcnt analysis exact (the
+  // LDS stores wait only for the older register set).
+  auto step = [&](int kt, int par) {
+    gload(par, min(kt + 2, nk - 1));
+    __builtin_amdgcn_sched_barrier(0);   // keep the prefetch at the top
+    lread(1, par, 1);
+    mma(0);
+    if (SCHED == 1) __builtin_amdgcn_iglp_opt(0);
+    lread(0, par, 2);
+    lstore(par ^ 1, par ^ 1);
+    __builtin_amdgcn_sched_barrier(0);
+    mma(1);
+    if (SCHED == 1) __builtin_amdgcn_iglp_opt(0);
+    lread(1, par, 3);
+    mma(0);
+    if (SCHED == 1) __builtin_amdgcn_iglp_opt(0);
+    lds_barrier();
+    lread(0, par ^ 1, 0);
+    mma(1);
+    if (SCHED == 1) __builtin_amdgcn_iglp_opt(0);
+  };
+  int kt = 0;
+  for (; kt + 1 < nk; kt += 2) {
+    step(kt, 0);
+    step(kt + 1, 1);
   }
+  if (kt < nk) step(kt, 0);
 
   // ---- epilogue ----
 #pragma unroll
@@ -184,10 +237,298 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_kernel(GemmArgs g) {
   }
 }
 
-template <int BM, int BN, int WM, int WN, int EPI>
+// ---------------------------------------------------------------------------
+// Direct-to-LDS variant: BM = BN = 256, BK = 32, a ring of 4 LDS stages of
+// 32 KB (separate arrays, so the compiler's LDS-DMA wait tracking can tell
+// them apart). Tiles are fetched with buffer_load ... lds three stages ahead
+// of their use, so no registers are spent on staging. Each LDS row holds 32
+// bf16 of K (64 bytes = 4 chunks); chunk c of row r sits at c ^ ((r/4)%4),
+// which spreads the 16 rows one ds_read_b128 phase touches over 16 distinct
+// bank groups. One barrier per stage, placed after the first 16-wide slice
+// so the next stage's first fragments are read while the second slice runs.
+#define LDSP(p) ((__attribute__((address_space(3))) void*)(p))
+
+template <int WM, int WN, int EPI, bool SWAP = true>
+__global__ __launch_bounds__(WM* WN * 64) void gemm_dma_kernel(GemmArgs g) {
+  constexpr int BM = 256, BN = 256, DBK = 32;
+  constexpr int NT = WM * WN * 64;
+  constexpr int NW = WM * WN;
+  constexpr int TM = BM / WM, TN = BN / WN;
+  constexpr int FM = TM / 32, FN = TN / 32;
+  constexpr int BLK = (BM + BN) / 16;          // 1 KB blocks (16 rows) per stage
+  constexpr int CH = BLK / NW;                 // DMA instructions per wave per stage
+  static_assert(CH * NW == BLK, "blocks per wave");
+  static_assert(EPI != EPI_SWIGLU || (FN % 2 == 0 && TN % 64 == 0), "SwiGLU pairs 32-col blocks");
+  constexpr int SW = (BM + BN) * DBK / 8;      // u32x4 per stage (2048)
+  __shared__ u32x4 st0[SW], st1[SW], st2[SW], st3[SW];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / WN, wn = wave % WN;
+
+  const int ntm = (g.M + BM - 1) / BM;
+  const int ntn = g.N / BN;
+  const int nblk = ntm * ntn;
+  int b = blockIdx.x;
+  const int per = nblk >> 3;
+  if (b < per * 8) b = (b & 7) * per + (b >> 3);
+  const int in_group = GROUP_M * ntn;
+  const int gid = b / in_group;
+  const int first = gid * GROUP_M;
+  const int gsz = min(ntm - first, GROUP_M);
+  const int tm = first + (b % in_group) % gsz;
+  const int tn = (b % in_group) / gsz;
+  const int m0 = tm * BM, n0 = tn * BN;
+
+  // lane part of every DMA: row l/4 of the 16-row block, logical chunk
+  // (l%4) ^ ((l/16)%4) so the lane's 16 bytes land at physical slot l%4
+  const int lr = lane >> 2;
+  const int lc = (lane & 3) ^ ((lane >> 4) & 3);
+  const __amdgpu_buffer_rsrc_t rA = make_rsrc(
+      g.A + (size_t)m0 * g.lda, (uint32_t)min((size_t)(g.M - m0) * g.lda * 2, (size_t)0xFFFFFFF0u));
+  __amdgpu_buffer_rsrc_t rG, rU;
+  if (EPI == EPI_SWIGLU) {
+    const size_t bytes = min((size_t)(BN / 2) * g.ldb * 2, (size_t)0xFFFFFFF0u);
+    rG = make_rsrc(g.B + (size_t)(n0 >> 1) * g.ldb, (uint32_t)bytes);
+    rU = make_rsrc(g.B2 + (size_t)(n0 >> 1) * g.ldb, (uint32_t)bytes);
+  } else {
+    rG = rU = make_rsrc(g.B + (size_t)n0 * g.ldb, (uint32_t)min((size_t)BN * g.ldb * 2, (size_t)0xFFFFFFF0u));
+  }
+  const uint32_t aoff = (uint32_t)((lr * g.lda + lc * 8) * 2);
+  const uint32_t boff = (uint32_t)((lr * g.ldb + lc * 8) * 2);
+  const int nk = g.K / DBK;
+
+  // DMA blocks: instruction j < CH/2 of a wave loads A block j*NW + wave;
+  // instruction CH/2 + jj loads a 16-row B block whose gate/up choice is a
+  // compile-time function of jj (B block bb = 4*q + 2*mat + half holds
+  // features 32*q + 16*half + r of matrix mat).
+  static_assert(BM == BN && CH % 2 == 0, "A and B blocks split evenly");
+  constexpr int CHB = CH / 2;
+  static_assert(NW * CHB == BN / 16 && (NW == 4 || NW == 8), "B block mapping");
+  auto dma = [&](u32x4* stg, int kt) {
+    const uint32_t ko = (uint32_t)(kt * DBK * 2);
+#pragma unroll
+    for (int j = 0; j < CHB; ++j) {
+      const int blk = j * NW + wave;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rA, LDSP(stg + blk * 64), 16, aoff,
+                                               ko + (uint32_t)(blk * 16 * g.lda * 2), 0, 0);
+    }
+#pragma unroll
+    for (int jj = 0; jj < CHB; ++jj) {
+      int q, mat, hf;
+      if (NW == 4) { q = wave; mat = jj >> 1; hf = jj & 1; }
+      else { q = wave >> 1; mat = jj; hf = wave & 1; }
+      const int bb = 4 * q + 2 * mat + hf;
+      u32x4* dst = stg + (BM / 16 + bb) * 64;
+      if (EPI == EPI_SWIGLU) {
+        const uint32_t so = ko + (uint32_t)((32 * q + 16 * hf) * g.ldb * 2);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(mat ? rU : rG, LDSP(dst), 16, boff, so, 0, 0);
+      } else {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rG, LDSP(dst), 16, boff,
+                                                 ko + (uint32_t)(bb * 16 * g.ldb * 2), 0, 0);
+      }
+    }
+  };
+
+  f32x16 acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  const int lrow = lane & 31, lhalf = lane >> 5;
+  const int swz = (lrow >> 2) & 3;
+  bf16x8 fa[2][FM], fb[2][FN];
+  auto lread = [&](int fs, const u32x4* stg, int s) {
+    const int ph = (2 * s + lhalf) ^ swz;
+#pragma unroll
+    for (int i = 0; i < FM; ++i) fa[fs][i] = __builtin_bit_cast(bf16x8, stg[(wm * TM + i * 32 + lrow) * 4 + ph]);
+#pragma unroll
+    for (int j = 0; j < FN; ++j) fb[fs][j] = __builtin_bit_cast(bf16x8, stg[(BM + wn * TN + j * 32 + lrow) * 4 + ph]);
+  };
+  // Operands swapped (B fragment first): each 32x32 block is accumulated as
+  // Cᵀ, so lane l holds row l%32 of the block and, in registers 4g..4g+3,
+  // the four consecutive columns 8g + 4*(l/32) + {0..3} -> vector stores.
+  auto mma = [&](int fs) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+        acc[i][j] = SWAP ? mfma32(fb[fs][j], fa[fs][i], acc[i][j]) : mfma32(fa[fs][i], fb[fs][j], acc[i][j]);
+  };
+  // wait until this wave's DMA of the stage needed next has landed (the two
+  // younger stages may stay in flight) and its LDS reads are done, then sync
+  static_assert(2 * CH <= 63, "vmcnt range");
+  auto stage_barrier = [&]() {
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * CH));
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+    __builtin_amdgcn_s_barrier();
+  };
+
+  // prologue: stages 0..2 in flight; wait for stage 0
+  dma(st0, 0);
+  dma(st1, min(1, nk - 1));
+  dma(st2, min(2, nk - 1));
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * CH));
+  __builtin_amdgcn_s_barrier();
+  lread(0, st0, 0);
+
+  // iteration on stage `cur`: DMA tile kt+3 into `fut` (freed at the last
+  // barrier), slice 0, barrier (tile kt+1 visible), slice 1 while the next
+  // stage's slice-0 fragments load.
+  // Instruction order is pinned with sched_group_barrier: the fragment
+  // reads for the next slice go out one per MFMA at the front of the
+  // current slice's MFMAs (so they have the rest of the slice to land), and
+  // the DMAs are spread over the remaining MFMAs.
+  constexpr int NMF = FM * FN, NRD = FM + FN;
+  // slice 0: reads paired with MFMAs first, then DMAs paired with the rest
+  constexpr int P0 = NRD < NMF ? NRD : NMF;
+  constexpr int P1 = (NMF - P0) < CH ? (NMF - P0) : CH;
+  auto iter = [&](u32x4* cur, u32x4* nxt, u32x4* fut, int kt) {
+    lread(1, cur, 1);
+    dma(fut, min(kt + 3, nk - 1));
+    mma(0);
+#pragma unroll
+    for (int k = 0; k < P0; ++k) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+    }
+    if (NRD > P0) __builtin_amdgcn_sched_group_barrier(0x100, NRD - P0, 0);
+#pragma unroll
+    for (int k = 0; k < P1; ++k) {
+      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // VMEM read (LDS DMA)
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    }
+    if (CH > P1) __builtin_amdgcn_sched_group_barrier(0x020, CH - P1, 0);
+    if (NMF > P0 + P1) __builtin_amdgcn_sched_group_barrier(0x008, NMF - P0 - P1, 0);
+    stage_barrier();
+    lread(0, nxt, 0);
+    mma(1);
+#pragma unroll
+    for (int k = 0; k < P0; ++k) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+    }
+    if (NRD > P0) __builtin_amdgcn_sched_group_barrier(0x100, NRD - P0, 1);
+    if (NMF > P0) __builtin_amdgcn_sched_group_barrier(0x008, NMF - P0, 1);
+  };
+  int kt = 0;
+  for (; kt + 3 < nk; kt += 4) {
+    iter(st0, st1, st3, kt);
+    iter(st1, st2, st0, kt + 1);
+    iter(st2, st3, st1, kt + 2);
+    iter(st3, st0, st2, kt + 3);
+  }
+  if (kt < nk) iter(st0, st1, st3, kt);
+  if (kt + 1 < nk) iter(st1, st2, st0, kt + 1);
+  if (kt + 2 < nk) iter(st2, st3, st1, kt + 2);
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));   // drain outstanding DMA before exit
+
+  if (!SWAP) {
+    // accumulator register r of lane l holds C[8*(r/4) + 4*(l/32) + r%4][l%32]
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int m = m0 + wm * TM + i * 32 + 8 * (r >> 2) + 4 * lhalf + (r & 3);
+        if (m >= g.M) continue;
+        if (EPI == EPI_SWIGLU) {
+#pragma unroll
+          for (int j = 0; j < FN; j += 2) {
+            const int f = ((n0 + wn * TN + j * 32) >> 1) + lrow;
+            const float gv = acc[i][j][r], uv = acc[i][j + 1][r];
+            reinterpret_cast<bf16_t*>(g.C)[(size_t)m * g.ldc + f] = f2bf(gv / (1.f + __expf(-gv)) * uv);
+          }
+        } else {
+#pragma unroll
+          for (int j = 0; j < FN; ++j) {
+            const int n = n0 + wn * TN + j * 32 + lrow;
+            const float v = acc[i][j][r];
+            if (EPI == EPI_BF16) {
+              reinterpret_cast<bf16_t*>(g.C)[(size_t)m * g.ldc + n] = f2bf(v);
+            } else if (EPI == EPI_F32) {
+              reinterpret_cast<float*>(g.C)[(size_t)m * g.ldc + n] = v;
+            } else {
+              const float gt = (m < g.n_pre ? g.gate_0 : g.gate_t)[n];
+              float* hp = g.Hres + (size_t)m * g.ldh + n;
+              *hp = *hp + tanhf(gt) * v;
+            }
+          }
+        }
+      }
+    }
+    return;
+  }
+  // ---- epilogue: lane owns row m = .. + lrow, columns n0c + 8g + 4*lhalf + {0..3} ----
+#pragma unroll
+  for (int i = 0; i < FM; ++i) {
+    const int m = m0 + wm * TM + i * 32 + lrow;
+    if (m >= g.M) continue;
+    if (EPI == EPI_SWIGLU) {
+#pragma unroll
+      for (int j = 0; j < FN; j += 2) {
+        const int fbase = ((n0 + wn * TN + j * 32) >> 1);     // gate block j, up block j+1
+#pragma unroll
+        for (int gq = 0; gq < 4; ++gq) {
+          float o[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float gv = acc[i][j][4 * gq + e], uv = acc[i][j + 1][4 * gq + e];
+            o[e] = gv / (1.f + __expf(-gv)) * uv;
+          }
+          u32x2 w;
+          w.x = pack2bf(o[0], o[1]);
+          w.y = pack2bf(o[2], o[3]);
+          *reinterpret_cast<u32x2*>(reinterpret_cast<bf16_t*>(g.C) + (size_t)m * g.ldc + fbase + 8 * gq + 4 * lhalf) = w;
+        }
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+#pragma unroll
+        for (int gq = 0; gq < 4; ++gq) {
+          const int n = n0 + wn * TN + j * 32 + 8 * gq + 4 * lhalf;
+          float a4[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) a4[e] = acc[i][j][4 * gq + e];
+          if (EPI == EPI_BF16) {
+            u32x2 w;
+            w.x = pack2bf(a4[0], a4[1]);
+            w.y = pack2bf(a4[2], a4[3]);
+            *reinterpret_cast<u32x2*>(reinterpret_cast<bf16_t*>(g.C) + (size_t)m * g.ldc + n) = w;
+          } else if (EPI == EPI_F32) {
+            *reinterpret_cast<float4*>(reinterpret_cast<float*>(g.C) + (size_t)m * g.ldc + n) =
+                make_float4(a4[0], a4[1], a4[2], a4[3]);
+          } else {
+            const float4 gt = *reinterpret_cast<const float4*>((m < g.n_pre ? g.gate_0 : g.gate_t) + n);
+            float4* hp = reinterpret_cast<float4*>(g.Hres + (size_t)m * g.ldh + n);
+            float4 hv = *hp;
+            hv.x += tanhf(gt.x) * a4[0];
+            hv.y += tanhf(gt.y) * a4[1];
+            hv.z += tanhf(gt.z) * a4[2];
+            hv.w += tanhf(gt.w) * a4[3];
+            *hp = hv;
+          }
+        }
+      }
+    }
+  }
+}
+
+template <int WM, int WN, int EPI, bool SWAP = true>
+hipError_t run_dma(const GemmArgs& g, hipStream_t s) {
+  const int nblk = ((g.M + 255) / 256) * (g.N / 256);
+  hipLaunchKernelGGL((gemm_dma_kernel<WM, WN, EPI, SWAP>), dim3(nblk), dim3(WM * WN * 64), 0, s, g);
+  return hipGetLastError();
+}
+
+template <int BM, int BN, int WM, int WN, int EPI, int SCHED = 0>
 hipError_t run(const GemmArgs& g, hipStream_t s) {
   const int nblk = ((g.M + BM - 1) / BM) * (g.N / BN);
-  hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, EPI>), dim3(nblk), dim3(WM * WN * 64), 0, s, g);
+  hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, EPI, SCHED>), dim3(nblk), dim3(WM * WN * 64), 0, s, g);
   return hipGetLastError();
 }
 
@@ -199,11 +540,30 @@ bool gemm_shape_ok(int M, int N, int K, int epi) {
   return N % 256 == 0;
 }
 
+hipError_t launch_gemm_variant(const GemmArgs& g, int variant, hipStream_t s) {
+  switch (variant) {
+    case 1: return run<256, 256, 2, 4, EPI_BF16>(g, s);
+    case 2: return run<256, 256, 2, 2, EPI_BF16>(g, s);
+    case 3: return run<256, 128, 2, 2, EPI_BF16>(g, s);
+    case 4: return run<128, 256, 2, 2, EPI_BF16>(g, s);
+    case 5: return run<256, 256, 4, 4, EPI_BF16>(g, s);
+    case 6: return run<256, 256, 2, 4, EPI_BF16, 1>(g, s);
+    case 7: return run<256, 256, 2, 2, EPI_BF16, 1>(g, s);
+    case 8: return run<256, 256, 2, 2, EPI_BF16, 2>(g, s);
+    case 9: return run_dma<2, 2, EPI_BF16>(g, s);
+    case 10: return run_dma<2, 4, EPI_BF16>(g, s);
+    case 11: return run_dma<2, 4, EPI_BF16, false>(g, s);
+    case 12: return run_dma<2, 2, EPI_BF16, false>(g, s);
+    case 13: return run<256, 256, 2, 4, EPI_BF16>(g, s);
+  }
+  return hipErrorInvalidValue;
+}
+
 hipError_t launch_gemm(const GemmArgs& g, int epi, hipStream_t s) {
   switch (epi) {
-    case EPI_BF16: return run<256, 256, 2, 4, EPI_BF16>(g, s);
-    case EPI_RESID: return run<256, 256, 2, 4, EPI_RESID>(g, s);
-    case EPI_SWIGLU: return run<256, 256, 2, 4, EPI_SWIGLU>(g, s);
+    case EPI_BF16: return run_dma<2, 4, EPI_BF16, false>(g, s);
+    case EPI_RESID: return run_dma<2, 4, EPI_RESID, true>(g, s);
+    case EPI_SWIGLU: return run_dma<2, 4, EPI_SWIGLU, false>(g, s);
     case EPI_F32: return run<64, 64, 2, 2, EPI_F32>(g, s);
   }
   return hipErrorInvalidValue;

@@ -27,6 +27,7 @@ struct GemmArgs {
 };
 
 hipError_t launch_gemm(const GemmArgs& g, int epi, hipStream_t s);
+hipError_t launch_gemm_variant(const GemmArgs& g, int variant, hipStream_t s);
 bool gemm_shape_ok(int M, int N, int K, int epi);
 
 struct AttnArgs {

@@ -206,9 +206,11 @@ dit_status dit_debug_attention(const dit_seq* seq, int n_heads, const void* q, i
                                void* stream);
 
 /* Test hook: C[M,N] = A[M,K] · B[N,K]ᵀ with the step's bf16 MFMA GEMM
- * (A, B bf16, C bf16). N must be a multiple of 256 and K of 64. */
+ * (A, B bf16, C bf16). N must be a multiple of 256 and K of 64.
+ * variant 0 = the tile configuration the step uses for its bf16-output
+ * GEMMs; 1.. = alternative tile configurations (DIT_ERR_ARG if unknown). */
 dit_status dit_debug_gemm(const void* A, const void* B, void* C, int M, int N, int K,
-                          void* stream);
+                          int variant, void* stream);
 
 /* Per-kernel timing over HIP events recorded on the step's stream around
  * every launch of one kernel class (0 = off). Enabling it adds an event

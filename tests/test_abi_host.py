@@ -142,7 +142,7 @@ def test_step_state_and_workspace_errors():
                                     wsb, 0, None)
         assert r == L.DIT_ERR_ARG            # misaligned
         assert L._lib.euler_update(None, FAKE, 1.0, 0.5, 4, None) == L.DIT_ERR_ARG
-        assert L._lib.dit_debug_gemm(FAKE, FAKE, FAKE, 10, 100, 64, None) == L.DIT_ERR_SHAPE
+        assert L._lib.dit_debug_gemm(FAKE, FAKE, FAKE, 10, 100, 64, 0, None) == L.DIT_ERR_SHAPE
         assert L._lib.dit_profile_enable(m, 99) == L.DIT_ERR_ARG
     finally:
         L.dit_free(m)
