@@ -72,7 +72,7 @@ def _load():
         "euler_update": (i, [vp, vp, f, f, ll, vp]),
         "dit_img_in": (i, [vp, vp, i, vp, vp]),
         "dit_debug_mask": (i, [P(dit_seq), vp, vp]),
-        "dit_debug_attention": (i, [P(dit_seq), i, vp, i, i, i, vp, vp, vp]),
+        "dit_debug_attention": (i, [P(dit_seq), i, vp, i, i, i, vp, vp, i, vp]),
         "dit_debug_gemm": (i, [vp, vp, vp, i, i, i, i, vp]),
         "dit_profile_enable": (i, [vp, i]),
         "dit_profile_read": (i, [vp, P(C.c_double), P(ll)]),
@@ -228,9 +228,10 @@ def dit_debug_mask(seq: dit_seq, mask, stream=None):
     _check(_lib.dit_debug_mask(C.byref(seq), _ptr(mask), _stream(stream)))
 
 
-def dit_debug_attention(seq: dit_seq, n_heads, q, q_stride, q_off, N, kv_cache, out, stream=None):
+def dit_debug_attention(seq: dit_seq, n_heads, q, q_stride, q_off, N, kv_cache, out, variant=0,
+                        stream=None):
     _check(_lib.dit_debug_attention(C.byref(seq), int(n_heads), _ptr(q), int(q_stride), int(q_off),
-                                    int(N), _ptr(kv_cache), _ptr(out), _stream(stream)))
+                                    int(N), _ptr(kv_cache), _ptr(out), int(variant), _stream(stream)))
 
 
 def dit_debug_gemm(A, B, Cmat, M, N, K, variant=0, stream=None):

@@ -239,12 +239,285 @@ __global__ __launch_bounds__(NT) void mask_kernel(const int32_t* limit, int S, u
     }
 }
 
+// ---------------------------------------------------------------------------
+// Second-generation kernel. Differences from attn_kernel:
+//  - each wave owns QW queries (QW/32 sub-blocks of 32) that share every K
+//    and Vᵀ fragment read, halving LDS traffic per FLOP at QW = 64;
+//  - K rows enter the score MFMA in the order π(i) = i with bits 2 and 3
+//    swapped, so that for every 16-key chunk a lane half holds 8 CONTIGUOUS
+//    keys of its query: the Vᵀ operand is then one 16-byte LDS read;
+//  - K / Vᵀ tiles are fetched straight into LDS (buffer_load ... lds) into
+//    a ring of 3 stages, two tiles ahead, one barrier per tile;
+//  - the running max is only raised when a query's tile max exceeds it by
+//    more than 2^8 (wave-uniform decision), so O and l are rescaled rarely;
+//    probabilities stay below 2^8 and the final O/l is unchanged.
+#define LDSP(p) ((__attribute__((address_space(3))) void*)(p))
+
+__device__ __forceinline__ int perm23(int x) {   // swap bits 2 and 3
+  return (x & ~0xC) | ((x & 4) << 1) | ((x & 8) >> 1);
+}
+
+template <int NWV, int QW>
+__global__ __launch_bounds__(NWV * 64) void attn2_kernel(AttnArgs a) {
+  constexpr int NSB = QW / 32;          // 32-query sub-blocks per wave
+  constexpr int BQ2 = NWV * QW;
+  constexpr int KT = BKV * 16;          // u32x4 per K tile (64 keys x 256 B)
+  constexpr int VT = D * 8;             // u32x4 per Vᵀ tile (128 dims x 128 B)
+  constexpr int DMA_PER_WAVE = 32 / NWV;   // 16 K + 16 Vᵀ 1-KB blocks per tile
+  static_assert(32 % NWV == 0 && (DMA_PER_WAVE % 2) == 0, "DMA split");
+  __shared__ u32x4 k0s[KT], k1s[KT], k2s[KT];
+  __shared__ u32x4 v0s[VT], v1s[VT], v2s[VT];
+  __shared__ int red[NWV];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int h = blockIdx.y;
+  const int lq = lane & 31, half = lane >> 5;
+
+  int qi[NSB], lim[NSB];
+  bool qv[NSB];
+  int lmin = 1 << 30, lmax = -1;
+#pragma unroll
+  for (int sb = 0; sb < NSB; ++sb) {
+    const int q = blockIdx.x * BQ2 + wave * QW + sb * 32 + lq;
+    qv[sb] = q < a.N;
+    qi[sb] = min(q, a.N - 1);
+    lim[sb] = a.limit[a.q_off + qi[sb]];
+    lmin = min(lmin, lim[sb]);
+    lmax = max(lmax, lim[sb]);
+  }
+  const int wlim_min = wave_min_i(lmin), wlim_max = wave_max_i(lmax);
+  if (lane == 0) red[wave] = wlim_max;
+  __syncthreads();
+  int blim_max = red[0];
+#pragma unroll
+  for (int w = 1; w < NWV; ++w) blim_max = max(blim_max, red[w]);
+  const int kv_end = min(a.S, blim_max + 1);
+  const int ntiles = (kv_end + BKV - 1) / BKV;
+
+  bf16x8 qf[NSB][8];
+#pragma unroll
+  for (int sb = 0; sb < NSB; ++sb) {
+    const u32x4* qp = reinterpret_cast<const u32x4*>(a.q + (size_t)qi[sb] * a.q_stride + h * D);
+#pragma unroll
+    for (int s = 0; s < 8; ++s) qf[sb][s] = __builtin_bit_cast(bf16x8, qp[2 * s + half]);
+  }
+
+  // ---- DMA setup: wave w loads K blocks w, w+NWV, ... (4 keys each) and Vᵀ
+  // blocks likewise (8 dims each); lane offsets bake in the swizzles ----
+  const __amdgpu_buffer_rsrc_t rK = make_rsrc(a.k + (size_t)h * a.cap * D, (uint32_t)(a.cap * D * 2));
+  const __amdgpu_buffer_rsrc_t rV = make_rsrc(a.vt + (size_t)h * D * a.cap, (uint32_t)(a.cap * D * 2));
+  // K block blk holds keys 4blk + l/16; lane writes physical chunk l%16 of
+  // that row, which must hold logical chunk (l%16) ^ (row%16).
+  uint32_t koff[4];
+#pragma unroll
+  for (int b4 = 0; b4 < 4; ++b4) {
+    const int r = lane >> 4;
+    const int c = (lane & 15) ^ ((4 * b4 + r) & 15);
+    koff[b4] = (uint32_t)(r * 256 + c * 16);
+  }
+  // Vᵀ block blk holds dims 8blk + l/8; physical 16-byte chunk l%8 holds
+  // logical chunk (l%8) ^ ((dim/2)%8).
+  uint32_t voff[2];
+#pragma unroll
+  for (int b2 = 0; b2 < 2; ++b2) {
+    const int r = lane >> 3;
+    const int c = (lane & 7) ^ (((8 * b2 + r) >> 1) & 7);
+    voff[b2] = (uint32_t)(r * a.cap * 2 + c * 16);
+  }
+  auto dma = [&](u32x4* ks, u32x4* vs, int kv0) {
+#pragma unroll
+    for (int j = 0; j < DMA_PER_WAVE / 2; ++j) {
+      const int blk = j * NWV + wave;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rK, LDSP(ks + blk * 64), 16, koff[blk & 3],
+                                               (uint32_t)((kv0 + 4 * blk) * 256), 0, 0);
+    }
+#pragma unroll
+    for (int j = 0; j < DMA_PER_WAVE / 2; ++j) {
+      const int blk = j * NWV + wave;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rV, LDSP(vs + blk * 64), 16, voff[blk & 1],
+                                               (uint32_t)(8 * blk * a.cap * 2 + kv0 * 2), 0, 0);
+    }
+  };
+
+  f32x16 oacc[NSB][4];
+#pragma unroll
+  for (int sb = 0; sb < NSB; ++sb)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) oacc[sb][j][r] = 0.f;
+  float m_run[NSB], l_run[NSB];
+#pragma unroll
+  for (int sb = 0; sb < NSB; ++sb) { m_run[sb] = -INFINITY; l_run[sb] = 0.f; }
+  const float sl2 = 1.4426950408889634f * 0.08838834764831845f;   // log2(e)/sqrt(128)
+
+  auto tile = [&](const u32x4* ks, const u32x4* vs, int kv0) {
+    const int cls = tile_class<BKV>(kv0, wlim_min, wlim_max, a.S);
+    if (cls == 0) return;
+    f32x16 sacc[NSB][2];
+#pragma unroll
+    for (int sb = 0; sb < NSB; ++sb)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sacc[sb][kb][r] = 0.f;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const int row = perm23(kb * 32 + lq);
+        const bf16x8 kf = __builtin_bit_cast(bf16x8, ks[row * 16 + ((2 * s + half) ^ (row & 15))]);
+#pragma unroll
+        for (int sb = 0; sb < NSB; ++sb) sacc[sb][kb] = mfma32(kf, qf[sb][s], sacc[sb][kb]);
+      }
+    }
+    uint32_t pk[NSB][2][8];
+#pragma unroll
+    for (int sb = 0; sb < NSB; ++sb) {
+      float mt = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          float v = sacc[sb][kb][r] * sl2;
+          if (cls == 2) {
+            const int j = kv0 + perm23(kb * 32 + 8 * (r >> 2) + 4 * half + (r & 3));
+            if (!key_visible(j, lim[sb], a.S)) v = -INFINITY;
+          }
+          sacc[sb][kb][r] = v;
+          mt = fmaxf(mt, v);
+        }
+      mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+      // raise the running max only when some query of the wave needs it
+      if (__builtin_amdgcn_ballot_w64(mt > m_run[sb] + 8.f)) {
+        const float m_new = fmaxf(m_run[sb], mt);
+        const float alpha = __builtin_amdgcn_exp2f(m_run[sb] - m_new);
+        m_run[sb] = m_new;
+        l_run[sb] *= alpha;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) oacc[sb][j][r] *= alpha;
+      }
+      const float mr = m_run[sb];
+      float ls = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; r += 2) {
+          const float p0 = __builtin_amdgcn_exp2f(sacc[sb][kb][r] - mr);
+          const float p1 = __builtin_amdgcn_exp2f(sacc[sb][kb][r + 1] - mr);
+          ls += p0 + p1;
+          pk[sb][kb][r >> 1] = pack2bf(p0, p1);
+        }
+      l_run[sb] += ls;
+    }
+    // Oᵀ += Vᵀ·Pᵀ: chunk c = registers 8(c%2).. of key block c/2, which
+    // (through π) are keys 16c + 8*half + {0..7} of this lane's query
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      bf16x8 pf[NSB];
+#pragma unroll
+      for (int sb = 0; sb < NSB; ++sb) {
+        u32x4 pb;
+        pb.x = pk[sb][c >> 1][4 * (c & 1) + 0];
+        pb.y = pk[sb][c >> 1][4 * (c & 1) + 1];
+        pb.z = pk[sb][c >> 1][4 * (c & 1) + 2];
+        pb.w = pk[sb][c >> 1][4 * (c & 1) + 3];
+        pf[sb] = __builtin_bit_cast(bf16x8, pb);
+      }
+#pragma unroll
+      for (int db = 0; db < 4; ++db) {
+        const int e = db * 32 + lq;
+        const bf16x8 vf = __builtin_bit_cast(bf16x8, vs[e * 8 + ((2 * c + half) ^ ((e >> 1) & 7))]);
+#pragma unroll
+        for (int sb = 0; sb < NSB; ++sb) oacc[sb][db] = mfma32(vf, pf[sb], oacc[sb][db]);
+      }
+    }
+  };
+
+  // ring of 3 stages: tile t lives in stage t%3; tiles t+1, t+2 in flight
+  constexpr int PER_TILE = DMA_PER_WAVE;   // DMA instructions per wave per tile
+  auto wait_barrier = [&]() {
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(PER_TILE));   // tile t+1 landed, t+2 may fly
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+    __builtin_amdgcn_s_barrier();
+  };
+  const int last = max(ntiles - 1, 0);
+  if (ntiles > 0) {
+    dma(k0s, v0s, 0);
+    dma(k1s, v1s, min(1, last) * BKV);
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(PER_TILE));
+    __builtin_amdgcn_s_barrier();
+  }
+  // iteration on tile t in stage A: issue tile t+2 into stage C (its last
+  // reader, tile t-1, finished before the previous barrier), compute, then
+  // barrier so tile t+1 (stage B) is visible.
+  auto iter = [&](u32x4* kA, u32x4* vA, u32x4* kC, u32x4* vC, int t) {
+    dma(kC, vC, min(t + 2, last) * BKV);
+    tile(kA, vA, t * BKV);
+    wait_barrier();
+  };
+  int t = 0;
+  for (; t + 2 < ntiles; t += 3) {
+    iter(k0s, v0s, k2s, v2s, t);
+    iter(k1s, v1s, k0s, v0s, t + 1);
+    iter(k2s, v2s, k1s, v1s, t + 2);
+  }
+  if (t < ntiles) iter(k0s, v0s, k2s, v2s, t);
+  if (t + 1 < ntiles) iter(k1s, v1s, k0s, v0s, t + 1);
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+
+  // ---- normalize and store O[query][dim] ----
+#pragma unroll
+  for (int sb = 0; sb < NSB; ++sb) {
+    const float l_tot = l_run[sb] + __shfl_xor(l_run[sb], 32, 64);
+    const float inv = 1.f / l_tot;
+    if (qv[sb]) {
+      uint16_t* op = a.out + (size_t)qi[sb] * a.out_stride + h * D;
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int d0 = db * 32 + 8 * g + 4 * half;
+          u32x2 w;
+          w.x = pack2bf(oacc[sb][db][4 * g + 0] * inv, oacc[sb][db][4 * g + 1] * inv);
+          w.y = pack2bf(oacc[sb][db][4 * g + 2] * inv, oacc[sb][db][4 * g + 3] * inv);
+          *reinterpret_cast<u32x2*>(op + d0) = w;
+        }
+    }
+  }
+}
+
+template <int NWV, int QW>
+hipError_t run_attn2(const AttnArgs& a, hipStream_t s) {
+  dim3 grid((a.N + NWV * QW - 1) / (NWV * QW), a.nh);
+  hipLaunchKernelGGL((attn2_kernel<NWV, QW>), grid, dim3(NWV * 64), 0, s, a);
+  return hipGetLastError();
+}
+
 }  // namespace
 
+hipError_t launch_attention_variant(const AttnArgs& a, int variant, hipStream_t s) {
+  switch (variant) {
+    case 1: {
+      dim3 grid((a.N + BQ - 1) / BQ, a.nh);
+      hipLaunchKernelGGL(attn_kernel, grid, dim3(NT), 0, s, a);
+      return hipGetLastError();
+    }
+    case 2: return run_attn2<4, 64>(a, s);
+    case 3: return run_attn2<4, 32>(a, s);
+    case 4: return run_attn2<8, 32>(a, s);
+    case 5: return run_attn2<2, 64>(a, s);
+  }
+  return hipErrorInvalidValue;
+}
+
 hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
-  dim3 grid((a.N + BQ - 1) / BQ, a.nh);
-  hipLaunchKernelGGL(attn_kernel, grid, dim3(NT), 0, s, a);
-  return hipGetLastError();
+  // 256 queries per workgroup unless that leaves CUs idle
+  const long long blocks256 = (long long)((a.N + 255) / 256) * a.nh;
+  return launch_attention_variant(a, blocks256 >= 256 ? 4 : 3, s);
 }
 
 hipError_t launch_debug_mask(const int32_t* limit, int S, uint8_t* mask, hipStream_t s) {

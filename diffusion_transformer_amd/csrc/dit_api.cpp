@@ -473,7 +473,8 @@ dit_status dit_debug_mask(const dit_seq* seq, uint8_t* mask, void* stream) {
 }
 
 dit_status dit_debug_attention(const dit_seq* seq, int n_heads, const void* q, int q_stride,
-                               int q_off, int N, const void* kv_cache, void* out, void* stream) {
+                               int q_off, int N, const void* kv_cache, void* out, int variant,
+                               void* stream) {
   dit_status rc = check_seq(nullptr, seq);
   if (rc) return rc;
   const int S = seq->P + seq->T;
@@ -487,7 +488,9 @@ dit_status dit_debug_attention(const dit_seq* seq, int n_heads, const void* q, i
   a.vt = a.k + (size_t)n_heads * cap * 128;
   a.cap = cap; a.S = S; a.nh = n_heads; a.limit = seq->d_row_limit;
   a.out = static_cast<uint16_t*>(out); a.out_stride = n_heads * 128;
-  return hip_check(launch_attention(a, static_cast<hipStream_t>(stream)), "debug attention");
+  if (variant < 0 || variant > 16) return fail(DIT_ERR_ARG, "unknown attention variant %d", variant);
+  if (variant == 0) return hip_check(launch_attention(a, static_cast<hipStream_t>(stream)), "debug attention");
+  return hip_check(launch_attention_variant(a, variant, static_cast<hipStream_t>(stream)), "debug attention");
 }
 
 dit_status dit_debug_gemm(const void* A, const void* B, void* C, int M, int N, int K, int variant,

@@ -41,6 +41,7 @@ struct AttnArgs {
   uint16_t* out; int out_stride;    // [N, nh*128] bf16
 };
 hipError_t launch_attention(const AttnArgs& a, hipStream_t s);
+hipError_t launch_attention_variant(const AttnArgs& a, int variant, hipStream_t s);
 hipError_t launch_debug_mask(const int32_t* limit, int S, uint8_t* mask, hipStream_t s);
 
 // LN(h)·(1 + scale[row]) -> bf16. rows < n_pre use scale_0, others scale_t.

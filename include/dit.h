@@ -200,10 +200,11 @@ dit_status dit_debug_mask(const dit_seq* seq, uint8_t* mask, void* stream);
 /* Test hook: one attention layer call on explicit buffers.
  *   q [N, q_stride] bf16 with head h at columns h*128.., kv_cache layer 0
  *   of a cache with capacity dit_kv_capacity(S) for n_heads heads,
- *   queries are global rows q_off..q_off+N-1, out [N, n_heads*128] bf16. */
+ *   queries are global rows q_off..q_off+N-1, out [N, n_heads*128] bf16.
+ *   variant 0 = the kernel the step uses; 1.. = alternative kernels. */
 dit_status dit_debug_attention(const dit_seq* seq, int n_heads, const void* q, int q_stride,
                                int q_off, int N, const void* kv_cache, void* out,
-                               void* stream);
+                               int variant, void* stream);
 
 /* Test hook: C[M,N] = A[M,K] · B[N,K]ᵀ with the step's bf16 MFMA GEMM
  * (A, B bf16, C bf16). N must be a multiple of 256 and K of 64.

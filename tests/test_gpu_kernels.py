@@ -107,16 +107,17 @@ def fill_cache(dev, S, nh, seed):
     return cache.to(dev), K.double().numpy(), V.double().numpy()
 
 
+@pytest.mark.parametrize("variant", [0, 1, 3, 4])
 @pytest.mark.parametrize("name,mode", [("c0w", "extract"), ("c0w", "cached"),
                                        ("ragged", "extract"), ("ragged", "cached"),
                                        ("c1", "extract"), ("c1", "cached"),
                                        ("c3", "cached")])
-def test_attention_matches_oracle(dev, name, mode):
+def test_attention_matches_oracle(dev, name, mode, variant):
     nh = 2
     lay = layout_for(LAYOUTS[name])
     P, T = lay["P"], lay["T"]
     S = P + T
-    say(f"attention {name} {mode} S={S}")
+    say(f"attention {name} {mode} S={S} variant={variant}")
     cache, K, V = fill_cache(dev, S, nh, seed=S)
     q_off, N = (0, S) if mode == "extract" else (P, T)
     g = torch.Generator().manual_seed(11)
@@ -125,7 +126,7 @@ def test_attention_matches_oracle(dev, name, mode):
     seq = L.make_seq(P, T, lim, lim, lim)
     out = torch.empty((N, nh * 128), dtype=torch.bfloat16, device=dev)
     Qd = Q.reshape(N, nh * 128).contiguous().to(dev)
-    L.dit_debug_attention(seq, nh, Qd, nh * 128, q_off, N, cache, out)
+    L.dit_debug_attention(seq, nh, Qd, nh * 128, q_off, N, cache, out, variant)
     torch.cuda.synchronize()
     ids = O.build_layout(LAYOUTS[name]).image_ids
     allowed = O.block_causal_mask(ids, rows=np.arange(q_off, q_off + N))
