@@ -1,19 +1,19 @@
-// bf16 MFMA GEMM for gfx950: C = A·Bᵀ with A [M,K] and B [N,K] both
-// K-contiguous (activations × nn.Linear weights), fp32 accumulation.
+// bf16 MFMA GEMMs for gfx950: C = A·Bᵀ with A [M,K] and B [N,K] both
+// K-contiguous (activations × nn.Linear weights), fp32 accumulation, built
+// from v_mfma_f32_32x32x16_bf16 blocks, with fused epilogues (bf16 store,
+// fp32 store, gated fp32 residual update, SwiGLU).
 //
-// Block tile BM×BN×64, WM×WN waves, each wave owns a (BM/WM)×(BN/WN) tile
-// built from v_mfma_f32_32x32x16_bf16 blocks. Operand tiles are staged
-// global -> registers -> LDS, double-buffered (one barrier per K step).
-// LDS rows are 128 bytes (64 bf16 of K). gfx950 serves a ds_read_b128 16
-// lanes per cycle across 64 banks (256 bytes), i.e. two consecutive rows per
-// bank cycle, so the 16-byte chunk c of row r is stored at c ^ ((r/2)%8):
-// the 16 rows one read phase touches then land on 16 distinct bank groups.
+// gemm_dma_kernel (the step's GEMMs): 256x256 block tile, 8 waves (2x4),
+// K in stages of 32 held in a ring of four 32 KB LDS stages that are filled
+// straight from global memory with buffer_load ... lds three stages ahead.
+// gemm_kernel: register-staged variant (global -> VGPR -> LDS, two stages),
+// used for the narrow proj_out GEMM (64x64 tiles) and kept as a reference.
 //
-// Tile order is XCD-aware: the hardware deals workgroups round-robin over
-// the 8 XCDs, so block b is remapped to logical tile (b%8)*(n/8) + b/8,
-// giving each XCD a contiguous run of logical tiles; logical tiles are then
-// grouped GROUP_M tile-rows at a time so a run covers a compact M×N patch
-// whose A and B panels stay in that XCD's L2.
+// Both use an XCD-aware tile order: the hardware deals workgroups
+// round-robin over the 8 XCDs, so block b is remapped to logical tile
+// (b%8)*(n/8) + b/8, giving each XCD a contiguous run of logical tiles;
+// logical tiles are then grouped GROUP_M tile-rows at a time so a run
+// covers a compact M×N patch whose A and B panels stay in that XCD's L2.
 #include "common.h"
 #include "kernels.h"
 
@@ -24,7 +24,7 @@ namespace {
 constexpr int BK = 64;
 constexpr int GROUP_M = 4;
 
-template <int BM, int BN, int WM, int WN, int EPI, int SCHED = 0>
+template <int BM, int BN, int WM, int WN, int EPI>
 __global__ __launch_bounds__(WM* WN * 64) void gemm_kernel(GemmArgs g) {
   constexpr int NT = WM * WN * 64;
   constexpr int TM = BM / WM, TN = BN / WN;
@@ -180,19 +180,15 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_kernel(GemmArgs g) {
     __builtin_amdgcn_sched_barrier(0);   // keep the prefetch at the top
     lread(1, par, 1);
     mma(0);
-    if (SCHED == 1) __builtin_amdgcn_iglp_opt(0);
     lread(0, par, 2);
     lstore(par ^ 1, par ^ 1);
     __builtin_amdgcn_sched_barrier(0);
     mma(1);
-    if (SCHED == 1) __builtin_amdgcn_iglp_opt(0);
     lread(1, par, 3);
     mma(0);
-    if (SCHED == 1) __builtin_amdgcn_iglp_opt(0);
     lds_barrier();
     lread(0, par ^ 1, 0);
     mma(1);
-    if (SCHED == 1) __builtin_amdgcn_iglp_opt(0);
   };
   int kt = 0;
   for (; kt + 1 < nk; kt += 2) {
@@ -248,7 +244,7 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_kernel(GemmArgs g) {
 // so the next stage's first fragments are read while the second slice runs.
 #define LDSP(p) ((__attribute__((address_space(3))) void*)(p))
 
-template <int WM, int WN, int EPI, bool SWAP = true>
+template <int WM, int WN, int EPI, bool SWAP = true, int GM = GROUP_M>
 __global__ __launch_bounds__(WM* WN * 64) void gemm_dma_kernel(GemmArgs g) {
   constexpr int BM = 256, BN = 256, DBK = 32;
   constexpr int NT = WM * WN * 64;
@@ -273,10 +269,10 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_dma_kernel(GemmArgs g) {
   int b = blockIdx.x;
   const int per = nblk >> 3;
   if (b < per * 8) b = (b & 7) * per + (b >> 3);
-  const int in_group = GROUP_M * ntn;
+  const int in_group = GM * ntn;
   const int gid = b / in_group;
-  const int first = gid * GROUP_M;
-  const int gsz = min(ntm - first, GROUP_M);
+  const int first = gid * GM;
+  const int gsz = min(ntm - first, GM);
   const int tm = first + (b % in_group) % gsz;
   const int tn = (b % in_group) / gsz;
   const int m0 = tm * BM, n0 = tn * BN;
@@ -518,17 +514,17 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_dma_kernel(GemmArgs g) {
   }
 }
 
-template <int WM, int WN, int EPI, bool SWAP = true>
+template <int WM, int WN, int EPI, bool SWAP = true, int GM = GROUP_M>
 hipError_t run_dma(const GemmArgs& g, hipStream_t s) {
   const int nblk = ((g.M + 255) / 256) * (g.N / 256);
-  hipLaunchKernelGGL((gemm_dma_kernel<WM, WN, EPI, SWAP>), dim3(nblk), dim3(WM * WN * 64), 0, s, g);
+  hipLaunchKernelGGL((gemm_dma_kernel<WM, WN, EPI, SWAP, GM>), dim3(nblk), dim3(WM * WN * 64), 0, s, g);
   return hipGetLastError();
 }
 
-template <int BM, int BN, int WM, int WN, int EPI, int SCHED = 0>
+template <int BM, int BN, int WM, int WN, int EPI>
 hipError_t run(const GemmArgs& g, hipStream_t s) {
   const int nblk = ((g.M + BM - 1) / BM) * (g.N / BN);
-  hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, EPI, SCHED>), dim3(nblk), dim3(WM * WN * 64), 0, s, g);
+  hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, EPI>), dim3(nblk), dim3(WM * WN * 64), 0, s, g);
   return hipGetLastError();
 }
 
@@ -542,19 +538,9 @@ bool gemm_shape_ok(int M, int N, int K, int epi) {
 
 hipError_t launch_gemm_variant(const GemmArgs& g, int variant, hipStream_t s) {
   switch (variant) {
-    case 1: return run<256, 256, 2, 4, EPI_BF16>(g, s);
-    case 2: return run<256, 256, 2, 2, EPI_BF16>(g, s);
-    case 3: return run<256, 128, 2, 2, EPI_BF16>(g, s);
-    case 4: return run<128, 256, 2, 2, EPI_BF16>(g, s);
-    case 5: return run<256, 256, 4, 4, EPI_BF16>(g, s);
-    case 6: return run<256, 256, 2, 4, EPI_BF16, 1>(g, s);
-    case 7: return run<256, 256, 2, 2, EPI_BF16, 1>(g, s);
-    case 8: return run<256, 256, 2, 2, EPI_BF16, 2>(g, s);
-    case 9: return run_dma<2, 2, EPI_BF16>(g, s);
-    case 10: return run_dma<2, 4, EPI_BF16>(g, s);
-    case 11: return run_dma<2, 4, EPI_BF16, false>(g, s);
-    case 12: return run_dma<2, 2, EPI_BF16, false>(g, s);
-    case 13: return run<256, 256, 2, 4, EPI_BF16>(g, s);
+    case 1: return run<256, 256, 2, 4, EPI_BF16>(g, s);        // register-staged, 2-stage LDS
+    case 2: return run_dma<2, 4, EPI_BF16, true>(g, s);        // direct-to-LDS, swapped operands
+    case 3: return run_dma<2, 2, EPI_BF16, false>(g, s);       // direct-to-LDS, 4 waves of 128x128
   }
   return hipErrorInvalidValue;
 }

@@ -21,20 +21,21 @@ def dev():
     return torch.device("cuda:0")
 
 
-@pytest.mark.parametrize("M,N,K", [(32, 256, 64), (300, 512, 128), (257, 768, 256)])
-def test_gemm_exact_small_integers(dev, M, N, K):
+@pytest.mark.parametrize("variant", [0, 1, 2, 3])
+@pytest.mark.parametrize("M,N,K", [(32, 256, 64), (300, 512, 128), (257, 768, 256), (600, 1024, 512)])
+def test_gemm_exact_small_integers(dev, M, N, K, variant):
     """Entries in {-1, 0, 1}: every partial sum is an integer of magnitude
     <= K <= 256, exact in fp32 and in the bf16 output, so the MFMA GEMM must
     match integer matrix multiplication bit for bit (checks the MFMA lane
     layout, the LDS swizzle, the tile order and the ragged M tail)."""
-    say(f"gemm exact M={M} N={N} K={K}")
+    say(f"gemm exact M={M} N={N} K={K} variant={variant}")
     g = torch.Generator().manual_seed(M * 7 + N + K)
     A = torch.randint(-1, 2, (M, K), generator=g).to(torch.float32)
     B = torch.randint(-1, 2, (N, K), generator=g).to(torch.float32)
     want = (A.to(torch.int64) @ B.to(torch.int64).T).to(torch.float32)
     Ad, Bd = A.to(dev, torch.bfloat16), B.to(dev, torch.bfloat16)
     Cd = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
-    L.dit_debug_gemm(Ad, Bd, Cd, M, N, K)
+    L.dit_debug_gemm(Ad, Bd, Cd, M, N, K, variant)
     torch.cuda.synchronize()
     assert torch.equal(Cd.float().cpu(), want)
 
