@@ -53,11 +53,12 @@ class dit_seq(C.Structure):
                 ("d_rope_cos", C.c_void_p), ("d_rope_sin", C.c_void_p)]
 
 
-def _load():
-    if not os.path.exists(LIB_PATH):
-        raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build() "
+def _load(path=None):
+    path = path or LIB_PATH
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is not built; run __graft_entry__.build() "
                           "or python diffusion_transformer_amd/build.py")
-    lib = C.CDLL(LIB_PATH)
+    lib = C.CDLL(path)
     vp, i, f, sz, ll = C.c_void_p, C.c_int, C.c_float, C.c_size_t, C.c_longlong
     P = C.POINTER
     sig = {
@@ -84,14 +85,6 @@ def _load():
         fn.restype = res
         fn.argtypes = args
     return lib
-
-
-_lib = _load()
-
-
-def _check(st):
-    if st != DIT_OK:
-        raise DitError(st, _lib.dit_last_error().decode())
 
 
 def _ptr(t):
@@ -126,126 +119,144 @@ def make_config(hidden, n_heads, head_dim, ffn, n_layers, latent=64, time_dim=25
     return c
 
 
-def dit_version() -> str:
-    return _lib.dit_version().decode()
+def _make_api(_lib):
+    """All wrappers bound to one loaded library (the production libdit.so
+    or the fp32 debug build libdit_f32.so)."""
 
+    def _check(st):
+        if st != DIT_OK:
+            raise DitError(st, _lib.dit_last_error().decode())
 
-def dit_last_error() -> str:
-    return _lib.dit_last_error().decode()
+    def dit_version() -> str:
+        return _lib.dit_version().decode()
 
+    def dit_last_error() -> str:
+        return _lib.dit_last_error().decode()
 
-def dit_build_layout(cfg: dit_config, segments):
-    """segments: ("text", n) | ("ref", h, w) | ("target", h, w). Returns a
-    dict of host numpy arrays (image_ids, coords, row_limit, rope_cos,
-    rope_sin) and P, T."""
-    kind = {"text": SEG_TEXT, "ref": SEG_REF, "target": SEG_TARGET}
-    n = len(segments)
-    k = (C.c_int * n)(*[kind[s[0]] for s in segments])
-    r = (C.c_int * n)(*[int(s[1]) for s in segments])
-    c = (C.c_int * n)(*[int(s[2]) if len(s) > 2 else 0 for s in segments])
-    P, T = C.c_int(), C.c_int()
-    _check(_lib.dit_build_layout(C.byref(cfg), k, r, c, n, None, None, None, None, None,
-                                 C.byref(P), C.byref(T)))
-    S = P.value + T.value
-    half = cfg.head_dim // 2
-    out = {"image_ids": np.empty(S, np.int32), "coords": np.empty((S, 3), np.int32),
-           "row_limit": np.empty(S, np.int32), "rope_cos": np.empty((S, half), np.float32),
-           "rope_sin": np.empty((S, half), np.float32)}
-    _check(_lib.dit_build_layout(C.byref(cfg), k, r, c, n, _ptr(out["image_ids"]),
-                                 _ptr(out["coords"]), _ptr(out["row_limit"]),
-                                 _ptr(out["rope_cos"]), _ptr(out["rope_sin"]),
-                                 C.byref(P), C.byref(T)))
-    out["P"], out["T"] = P.value, T.value
-    return out
+    def dit_build_layout(cfg: dit_config, segments):
+        """segments: ("text", n) | ("ref", h, w) | ("target", h, w). Returns a
+        dict of host numpy arrays (image_ids, coords, row_limit, rope_cos,
+        rope_sin) and P, T."""
+        kind = {"text": SEG_TEXT, "ref": SEG_REF, "target": SEG_TARGET}
+        n = len(segments)
+        k = (C.c_int * n)(*[kind[s[0]] for s in segments])
+        r = (C.c_int * n)(*[int(s[1]) for s in segments])
+        c = (C.c_int * n)(*[int(s[2]) if len(s) > 2 else 0 for s in segments])
+        P, T = C.c_int(), C.c_int()
+        _check(_lib.dit_build_layout(C.byref(cfg), k, r, c, n, None, None, None, None, None,
+                                     C.byref(P), C.byref(T)))
+        S = P.value + T.value
+        half = cfg.head_dim // 2
+        out = {"image_ids": np.empty(S, np.int32), "coords": np.empty((S, 3), np.int32),
+               "row_limit": np.empty(S, np.int32), "rope_cos": np.empty((S, half), np.float32),
+               "rope_sin": np.empty((S, half), np.float32)}
+        _check(_lib.dit_build_layout(C.byref(cfg), k, r, c, n, _ptr(out["image_ids"]),
+                                     _ptr(out["coords"]), _ptr(out["row_limit"]),
+                                     _ptr(out["rope_cos"]), _ptr(out["rope_sin"]),
+                                     C.byref(P), C.byref(T)))
+        out["P"], out["T"] = P.value, T.value
+        return out
 
+    def dit_load_weights(cfg: dit_config, w: dict):
+        """w: dict of device tensors (bf16 bits) t1, t2, mod, so, img_in, proj_out
+        and per-layer lists qkv, q_norm, k_norm, o, gate, up, down. Returns an
+        opaque handle (an int); the tensors must outlive it."""
+        L = cfg.n_layers
+        arrs = {}
+        for name in ("qkv", "q_norm", "k_norm", "o", "gate", "up", "down"):
+            arrs[name] = (C.c_void_p * L)(*[_ptr(t) for t in w[name]])
+        ws = dit_weights(_ptr(w["t1"]), _ptr(w["t2"]), _ptr(w["mod"]), _ptr(w["so"]),
+                         _ptr(w["img_in"]), _ptr(w["proj_out"]),
+                         *[C.cast(arrs[n], C.POINTER(C.c_void_p)) for n in
+                           ("qkv", "q_norm", "k_norm", "o", "gate", "up", "down")])
+        h = C.c_void_p()
+        _check(_lib.dit_load_weights(C.byref(cfg), C.byref(ws), C.byref(h)))
+        return h.value
 
-def dit_load_weights(cfg: dit_config, w: dict):
-    """w: dict of device tensors (bf16 bits) t1, t2, mod, so, img_in, proj_out
-    and per-layer lists qkv, q_norm, k_norm, o, gate, up, down. Returns an
-    opaque handle (an int); the tensors must outlive it."""
-    L = cfg.n_layers
-    arrs = {}
-    for name in ("qkv", "q_norm", "k_norm", "o", "gate", "up", "down"):
-        arrs[name] = (C.c_void_p * L)(*[_ptr(t) for t in w[name]])
-    ws = dit_weights(_ptr(w["t1"]), _ptr(w["t2"]), _ptr(w["mod"]), _ptr(w["so"]),
-                     _ptr(w["img_in"]), _ptr(w["proj_out"]),
-                     *[C.cast(arrs[n], C.POINTER(C.c_void_p)) for n in
-                       ("qkv", "q_norm", "k_norm", "o", "gate", "up", "down")])
-    h = C.c_void_p()
-    _check(_lib.dit_load_weights(C.byref(cfg), C.byref(ws), C.byref(h)))
-    return h.value
+    def dit_free(model):
+        _lib.dit_free(model)
 
+    def dit_workspace_bytes(model, n_tokens: int) -> int:
+        return _lib.dit_workspace_bytes(model, n_tokens)
 
-def dit_free(model):
-    _lib.dit_free(model)
+    def dit_kv_capacity(S: int) -> int:
+        return _lib.dit_kv_capacity(S)
 
+    def dit_kv_cache_bytes(model, S: int) -> int:
+        return _lib.dit_kv_cache_bytes(model, S)
 
-def dit_workspace_bytes(model, n_tokens: int) -> int:
-    return _lib.dit_workspace_bytes(model, n_tokens)
+    def make_seq(P, T, row_limit, rope_cos, rope_sin) -> dit_seq:
+        return dit_seq(P, T, _ptr(row_limit), _ptr(rope_cos), _ptr(rope_sin))
 
+    def _nbytes(t):
+        return t.numel() * t.element_size()
 
-def dit_kv_capacity(S: int) -> int:
-    return _lib.dit_kv_capacity(S)
+    def dit_step_extract(model, seq: dit_seq, prefix_hidden, x, sigma, kv_cache, v_out, workspace,
+                         flags=0, stream=None):
+        _check(_lib.dit_step_extract(model, C.byref(seq), _ptr(prefix_hidden), _ptr(x), float(sigma),
+                                     _ptr(kv_cache), _nbytes(kv_cache), _ptr(v_out), _ptr(workspace),
+                                     _nbytes(workspace), int(flags), _stream(stream)))
 
+    def dit_step_cached(model, seq: dit_seq, x, sigma, kv_cache, v_out, workspace, stream=None):
+        _check(_lib.dit_step_cached(model, C.byref(seq), _ptr(x), float(sigma), _ptr(kv_cache),
+                                    _nbytes(kv_cache), _ptr(v_out), _ptr(workspace),
+                                    _nbytes(workspace), _stream(stream)))
 
-def dit_kv_cache_bytes(model, S: int) -> int:
-    return _lib.dit_kv_cache_bytes(model, S)
+    def euler_update(x, v, sigma_k, sigma_k1, n=None, stream=None):
+        n = x.numel() if n is None else n
+        _check(_lib.euler_update(_ptr(x), _ptr(v), float(sigma_k), float(sigma_k1), int(n),
+                                 _stream(stream)))
 
-
-def make_seq(P, T, row_limit, rope_cos, rope_sin) -> dit_seq:
-    return dit_seq(P, T, _ptr(row_limit), _ptr(rope_cos), _ptr(rope_sin))
-
-
-def _nbytes(t):
-    return t.numel() * t.element_size()
-
-
-def dit_step_extract(model, seq: dit_seq, prefix_hidden, x, sigma, kv_cache, v_out, workspace,
-                     flags=0, stream=None):
-    _check(_lib.dit_step_extract(model, C.byref(seq), _ptr(prefix_hidden), _ptr(x), float(sigma),
-                                 _ptr(kv_cache), _nbytes(kv_cache), _ptr(v_out), _ptr(workspace),
-                                 _nbytes(workspace), int(flags), _stream(stream)))
-
-
-def dit_step_cached(model, seq: dit_seq, x, sigma, kv_cache, v_out, workspace, stream=None):
-    _check(_lib.dit_step_cached(model, C.byref(seq), _ptr(x), float(sigma), _ptr(kv_cache),
-                                _nbytes(kv_cache), _ptr(v_out), _ptr(workspace),
-                                _nbytes(workspace), _stream(stream)))
-
-
-def euler_update(x, v, sigma_k, sigma_k1, n=None, stream=None):
-    n = x.numel() if n is None else n
-    _check(_lib.euler_update(_ptr(x), _ptr(v), float(sigma_k), float(sigma_k1), int(n),
-                             _stream(stream)))
-
-
-def dit_img_in(model, latents, hidden, stream=None):
-    _check(_lib.dit_img_in(model, _ptr(latents), int(latents.shape[0]), _ptr(hidden),
-                           _stream(stream)))
-
-
-def dit_debug_mask(seq: dit_seq, mask, stream=None):
-    _check(_lib.dit_debug_mask(C.byref(seq), _ptr(mask), _stream(stream)))
-
-
-def dit_debug_attention(seq: dit_seq, n_heads, q, q_stride, q_off, N, kv_cache, out, variant=0,
-                        stream=None):
-    _check(_lib.dit_debug_attention(C.byref(seq), int(n_heads), _ptr(q), int(q_stride), int(q_off),
-                                    int(N), _ptr(kv_cache), _ptr(out), int(variant), _stream(stream)))
-
-
-def dit_debug_gemm(A, B, Cmat, M, N, K, variant=0, stream=None):
-    _check(_lib.dit_debug_gemm(_ptr(A), _ptr(B), _ptr(Cmat), int(M), int(N), int(K), int(variant),
+    def dit_img_in(model, latents, hidden, stream=None):
+        _check(_lib.dit_img_in(model, _ptr(latents), int(latents.shape[0]), _ptr(hidden),
                                _stream(stream)))
 
+    def dit_debug_mask(seq: dit_seq, mask, stream=None):
+        _check(_lib.dit_debug_mask(C.byref(seq), _ptr(mask), _stream(stream)))
 
-def dit_profile_enable(model, kernel_class):
-    if isinstance(kernel_class, str):
-        kernel_class = PROF[kernel_class]
-    _check(_lib.dit_profile_enable(model, int(kernel_class)))
+    def dit_debug_attention(seq: dit_seq, n_heads, q, q_stride, q_off, N, kv_cache, out, variant=0,
+                            stream=None):
+        _check(_lib.dit_debug_attention(C.byref(seq), int(n_heads), _ptr(q), int(q_stride), int(q_off),
+                                        int(N), _ptr(kv_cache), _ptr(out), int(variant), _stream(stream)))
+
+    def dit_debug_gemm(A, B, Cmat, M, N, K, variant=0, stream=None):
+        _check(_lib.dit_debug_gemm(_ptr(A), _ptr(B), _ptr(Cmat), int(M), int(N), int(K), int(variant),
+                                   _stream(stream)))
+
+    def dit_profile_enable(model, kernel_class):
+        if isinstance(kernel_class, str):
+            kernel_class = PROF[kernel_class]
+        _check(_lib.dit_profile_enable(model, int(kernel_class)))
+
+    def dit_profile_read(model):
+        ms, n = C.c_double(), C.c_longlong()
+        _check(_lib.dit_profile_read(model, C.byref(ms), C.byref(n)))
+        return ms.value, n.value
+
+    return {k: v for k, v in locals().items() if k.startswith(("dit_", "euler_", "make_seq"))}
 
 
-def dit_profile_read(model):
-    ms, n = C.c_double(), C.c_longlong()
-    _check(_lib.dit_profile_read(model, C.byref(ms), C.byref(n)))
-    return ms.value, n.value
+def _bind(path):
+    import types
+    lib = _load(path)
+    ns = types.SimpleNamespace(**_make_api(lib))
+    ns._lib = lib
+    ns.make_config = make_config
+    ns.DitError = DitError
+    for k in ("DIT_OK", "DIT_ERR_ARG", "DIT_ERR_SHAPE", "DIT_ERR_LAYOUT", "DIT_ERR_STATE",
+              "DIT_ERR_WORKSPACE", "DIT_ERR_HIP", "DIT_ERR_UNSUPPORTED", "DIT_FLAG_NO_CAUSAL_CONDITION",
+              "PROF", "dit_seq", "dit_config", "dit_weights"):
+        setattr(ns, k, globals()[k])
+    return ns
+
+
+_default = _bind(LIB_PATH)
+_lib = _default._lib
+globals().update({k: v for k, v in vars(_default).items() if k.startswith(("dit_", "euler_", "make_seq"))})
+
+LIB_F32_PATH = os.path.join(_PKG, "libdit_f32.so")
+
+
+def load_f32():
+    """The same API bound to the fp32 debug build (libdit_f32.so)."""
+    return _bind(LIB_F32_PATH)

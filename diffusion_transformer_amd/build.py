@@ -14,16 +14,19 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OUT = os.path.join(PKG, "libdit.so")
-SOURCES = ["gemm.hip", "attention.hip", "elementwise.hip", "dit_api.cpp"]
+OUT_F32 = os.path.join(PKG, "libdit_f32.so")
+SOURCES = ["gemm.hip", "attention.hip", "mask.hip", "elementwise.hip", "dit_api.cpp"]
+# fp32 debug build: fp32 activations / cache / attention, plain FMA GEMMs
+SOURCES_F32 = ["debug_f32.hip", "mask.hip", "elementwise.hip", "dit_api.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
          "-I", os.path.join(ROOT, "include")]
 
 
-def _compile(src: str, bdir: str) -> str:
+def _compile(src: str, bdir: str, extra=()) -> str:
     obj = os.path.join(bdir, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *FLAGS, *extra, "-c", os.path.join(CSRC, src), "-o", obj]
     if src.endswith(".cpp"):
         cmd[1:1] = ["-x", "hip"]
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -32,19 +35,24 @@ def _compile(src: str, bdir: str) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    bdir = os.path.join(ROOT, "_build")
+def _build_one(sources, out, bdir, extra=()):
     os.makedirs(bdir, exist_ok=True)
-    with cf.ThreadPoolExecutor(max_workers=min(4, len(SOURCES))) as ex:
-        objs = list(ex.map(lambda s: _compile(s, bdir), SOURCES))
-    tmp = OUT + ".tmp"
+    with cf.ThreadPoolExecutor(max_workers=min(4, len(sources))) as ex:
+        objs = list(ex.map(lambda s: _compile(s, bdir, extra), sources))
+    tmp = out + ".tmp"
     r = subprocess.run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp],
                        capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
-    os.replace(tmp, OUT)
+    os.replace(tmp, out)
+
+
+def build(verbose: bool = False) -> str:
+    """Builds libdit.so (bf16) and libdit_f32.so (fp32 debug build)."""
+    _build_one(SOURCES, OUT, os.path.join(ROOT, "_build"))
+    _build_one(SOURCES_F32, OUT_F32, os.path.join(ROOT, "_build", "f32"), ("-DDIT_F32",))
     if verbose:
-        print(f"built {OUT}", file=sys.stderr)
+        print(f"built {OUT} and {OUT_F32}", file=sys.stderr)
     return OUT
 
 

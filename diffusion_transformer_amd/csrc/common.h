@@ -3,6 +3,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "kernels.h"
+
 namespace dit {
 
 typedef uint16_t bf16_t;                                             // raw bfloat16 bits
@@ -16,6 +18,42 @@ __device__ __forceinline__ float bf2f(bf16_t b) { return __uint_as_float(((uint3
 __device__ __forceinline__ bf16_t f2bf(float f) { return __builtin_bit_cast(bf16_t, (__bf16)f); }
 __device__ __forceinline__ uint32_t pack2bf(float a, float b) {
   return (uint32_t)f2bf(a) | ((uint32_t)f2bf(b) << 16);
+}
+
+// Conversions for the activation element type act_t (kernels.h).
+#ifdef DIT_F32
+__device__ __forceinline__ float act2f(act_t v) { return v; }
+__device__ __forceinline__ act_t f2act(float f) { return f; }
+#else
+__device__ __forceinline__ float act2f(act_t v) { return bf2f(v); }
+__device__ __forceinline__ act_t f2act(float f) { return f2bf(f); }
+#endif
+// Store 4 / 8 consecutive activations from floats (16-byte aligned for 8).
+__device__ __forceinline__ void store_act4(act_t* p, float a, float b, float c, float d) {
+#ifdef DIT_F32
+  *reinterpret_cast<float4*>(p) = make_float4(a, b, c, d);
+#else
+  u32x2 w;
+  w.x = pack2bf(a, b);
+  w.y = pack2bf(c, d);
+  *reinterpret_cast<u32x2*>(p) = w;
+#endif
+}
+__device__ __forceinline__ void load_act2(const act_t* p, float& a, float& b) {
+#ifdef DIT_F32
+  const float2 v = *reinterpret_cast<const float2*>(p);
+  a = v.x; b = v.y;
+#else
+  const uint32_t v = *reinterpret_cast<const uint32_t*>(p);
+  a = bf2f((bf16_t)(v & 0xffff)); b = bf2f((bf16_t)(v >> 16));
+#endif
+}
+__device__ __forceinline__ void store_act2(act_t* p, float a, float b) {
+#ifdef DIT_F32
+  *reinterpret_cast<float2*>(p) = make_float2(a, b);
+#else
+  *reinterpret_cast<uint32_t*>(p) = pack2bf(a, b);
+#endif
 }
 
 // v_mfma_f32_32x32x16_bf16: C[32x32] += A[32x16] · B[16x32].

@@ -109,10 +109,11 @@ Plan plan(const dit_config& c, int n) {
   p.temb = take(2 * H * 4);
   p.tembs = take(2 * H * 4);
   p.h = take(N * H * 4);
-  p.x = take(N * H * 2);
-  p.qkv = take(N * 3 * H * 2);
-  p.attn = take(N * H * 2);
-  p.ffn = take(N * F * 2);
+  const size_t A = sizeof(act_t);
+  p.x = take(N * H * A);
+  p.qkv = take(N * 3 * H * A);
+  p.attn = take(N * H * A);
+  p.ffn = take(N * F * A);
   p.total = off;
   return p;
 }
@@ -163,12 +164,12 @@ dit_status run_step(dit_model* m, const dit_seq* seq, bool extract, const float*
   float* tb = reinterpret_cast<float*>(w + pl.temb);
   float* tbs = reinterpret_cast<float*>(w + pl.tembs);
   float* hbuf = reinterpret_cast<float*>(w + pl.h);
-  uint16_t* xb = reinterpret_cast<uint16_t*>(w + pl.x);
-  uint16_t* qkv = reinterpret_cast<uint16_t*>(w + pl.qkv);
-  uint16_t* att = reinterpret_cast<uint16_t*>(w + pl.attn);
-  uint16_t* ffn = reinterpret_cast<uint16_t*>(w + pl.ffn);
-  uint16_t* kbase = static_cast<uint16_t*>(kv);
-  uint16_t* vbase = kbase + (size_t)L * nh * cap * 128;
+  act_t* xb = reinterpret_cast<act_t*>(w + pl.x);
+  act_t* qkv = reinterpret_cast<act_t*>(w + pl.qkv);
+  act_t* att = reinterpret_cast<act_t*>(w + pl.attn);
+  act_t* ffn = reinterpret_cast<act_t*>(w + pl.ffn);
+  act_t* kbase = static_cast<act_t*>(kv);
+  act_t* vbase = kbase + (size_t)L * nh * cap * 128;
   dit_status rc;
 #define LAUNCH(expr, what) \
   do { if ((rc = hip_check((expr), what)) != DIT_OK) return rc; } while (0)
@@ -193,8 +194,8 @@ dit_status run_step(dit_model* m, const dit_seq* seq, bool extract, const float*
   LAUNCH(launch_img_in(U(m->img_in), x, T, H, hbuf + (size_t)n_pre * H, H, st), "img_in");
 
   for (int l = 0; l < L; ++l) {
-    uint16_t* kl = kbase + (size_t)l * nh * cap * 128;
-    uint16_t* vl = vbase + (size_t)l * nh * 128 * cap;
+    act_t* kl = kbase + (size_t)l * nh * cap * 128;
+    act_t* vl = vbase + (size_t)l * nh * 128 * cap;
     {
       Timed tm(m, DIT_PROF_LN, st);
       LAUNCH(launch_ln_mod(hbuf, H, N, H, row_t, row_0, n_pre, c.eps, xb, H, st), "ln1");
@@ -288,13 +289,18 @@ dit_status check_step_common(dit_model* m, const dit_seq* seq, const float* x, v
 extern "C" {
 
 const char* dit_last_error(void) { return g_err.c_str(); }
+#ifdef DIT_F32
+const char* dit_version(void) { return "dit-gfx950 0.1 fp32-debug"; }
+#else
 const char* dit_version(void) { return "dit-gfx950 0.1"; }
+#endif
 
 int dit_kv_capacity(int S) { return S <= 0 ? 0 : (S + 127) / 128 * 128; }
 
 size_t dit_kv_cache_bytes(const dit_model* m, int S) {
   if (!m || S <= 0) return 0;
-  return (size_t)2 * m->cfg.n_layers * m->cfg.n_heads * (size_t)dit_kv_capacity(S) * m->cfg.head_dim * 2;
+  return (size_t)2 * m->cfg.n_layers * m->cfg.n_heads * (size_t)dit_kv_capacity(S) * m->cfg.head_dim *
+         sizeof(act_t);
 }
 
 size_t dit_workspace_bytes(const dit_model* m, int n_tokens) {
@@ -481,29 +487,39 @@ dit_status dit_debug_attention(const dit_seq* seq, int n_heads, const void* q, i
   if (!q || !kv_cache || !out) return fail(DIT_ERR_ARG, "NULL argument");
   if (n_heads <= 0 || N <= 0 || q_off < 0 || q_off + N > S || q_stride < n_heads * 128 || q_stride % 8)
     return fail(DIT_ERR_ARG, "bad attention shape");
+#ifdef DIT_F32
+  (void)variant; (void)stream;
+  return fail(DIT_ERR_UNSUPPORTED, "dit_debug_attention is not part of the fp32 debug build");
+#else
   const int cap = dit_kv_capacity(S);
   AttnArgs a{};
-  a.q = static_cast<const uint16_t*>(q); a.q_stride = q_stride; a.q_off = q_off; a.N = N;
-  a.k = static_cast<const uint16_t*>(kv_cache);
+  a.q = static_cast<const act_t*>(q); a.q_stride = q_stride; a.q_off = q_off; a.N = N;
+  a.k = static_cast<const act_t*>(kv_cache);
   a.vt = a.k + (size_t)n_heads * cap * 128;
   a.cap = cap; a.S = S; a.nh = n_heads; a.limit = seq->d_row_limit;
-  a.out = static_cast<uint16_t*>(out); a.out_stride = n_heads * 128;
+  a.out = static_cast<act_t*>(out); a.out_stride = n_heads * 128;
   if (variant < 0 || variant > 16) return fail(DIT_ERR_ARG, "unknown attention variant %d", variant);
   if (variant == 0) return hip_check(launch_attention(a, static_cast<hipStream_t>(stream)), "debug attention");
   return hip_check(launch_attention_variant(a, variant, static_cast<hipStream_t>(stream)), "debug attention");
+#endif
 }
 
 dit_status dit_debug_gemm(const void* A, const void* B, void* C, int M, int N, int K, int variant,
                           void* stream) {
   if (!A || !B || !C) return fail(DIT_ERR_ARG, "NULL argument");
+#ifdef DIT_F32
+  (void)M; (void)N; (void)K; (void)variant; (void)stream;
+  return fail(DIT_ERR_UNSUPPORTED, "dit_debug_gemm is not part of the fp32 debug build");
+#else
   if (!gemm_shape_ok(M, N, K, EPI_BF16)) return fail(DIT_ERR_SHAPE, "GEMM needs M>0, N%%256==0, K%%64==0");
   GemmArgs g{};
-  g.A = static_cast<const uint16_t*>(A); g.lda = K;
+  g.A = static_cast<const act_t*>(A); g.lda = K;
   g.B = static_cast<const uint16_t*>(B); g.ldb = K;
   g.M = M; g.N = N; g.K = K; g.C = C; g.ldc = N;
   if (variant < 0 || variant > 16) return fail(DIT_ERR_ARG, "unknown GEMM variant %d", variant);
   if (variant == 0) return hip_check(launch_gemm(g, EPI_BF16, static_cast<hipStream_t>(stream)), "debug gemm");
   return hip_check(launch_gemm_variant(g, variant, static_cast<hipStream_t>(stream)), "debug gemm");
+#endif
 }
 
 dit_status dit_profile_enable(dit_model* m, int kernel_class) {

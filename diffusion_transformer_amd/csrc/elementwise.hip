@@ -27,7 +27,7 @@ __device__ __forceinline__ float block_sum(float v, float* sh) {
 __global__ __launch_bounds__(LN_NT) void ln_mod_kernel(const float* __restrict__ h, int ldh, int H,
                                                        const float* __restrict__ scale_t,
                                                        const float* __restrict__ scale_0, int n_pre,
-                                                       float eps, uint16_t* __restrict__ out, int ldo) {
+                                                       float eps, act_t* __restrict__ out, int ldo) {
   __shared__ float sh[4];
   const int row = blockIdx.x;
   const float4* hp = reinterpret_cast<const float4*>(h + (size_t)row * ldh);
@@ -55,16 +55,14 @@ __global__ __launch_bounds__(LN_NT) void ln_mod_kernel(const float* __restrict__
   const float var = block_sum(q, sh) / (float)H;
   const float rstd = rsqrtf(var + eps);
   const float4* sp = reinterpret_cast<const float4*>(row < n_pre ? scale_0 : scale_t);
-  u32x2* op = reinterpret_cast<u32x2*>(out + (size_t)row * ldo);
+  act_t* op = out + (size_t)row * ldo;
 #pragma unroll
   for (int i = 0; i < LN_MAXV; ++i) {
     const int c = threadIdx.x + i * LN_NT;
     if (c < nv) {
       const float4 sc = sp[c];
-      u32x2 w;
-      w.x = pack2bf((v[i].x - mean) * rstd * (1.f + sc.x), (v[i].y - mean) * rstd * (1.f + sc.y));
-      w.y = pack2bf((v[i].z - mean) * rstd * (1.f + sc.z), (v[i].w - mean) * rstd * (1.f + sc.w));
-      op[c] = w;
+      store_act4(op + 4 * c, (v[i].x - mean) * rstd * (1.f + sc.x), (v[i].y - mean) * rstd * (1.f + sc.y),
+                 (v[i].z - mean) * rstd * (1.f + sc.z), (v[i].w - mean) * rstd * (1.f + sc.w));
     }
   }
 }
@@ -77,63 +75,56 @@ __global__ __launch_bounds__(LN_NT) void ln_mod_kernel(const float* __restrict__
 constexpr int QK_TOK = 64;
 
 __global__ __launch_bounds__(256) void qknorm_rope_kernel(QkArgs a) {
-  __shared__ uint32_t vt_s[QK_TOK][65];   // [token][pair] packed bf16x2, padded
+  __shared__ float vt_s[QK_TOK][129];     // [token][dim], padded
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int h = blockIdx.y;
   const int g0 = (a.g_begin / QK_TOK) * QK_TOK + blockIdx.x * QK_TOK;
   const float wq0 = 1.f + bf2f(a.wq[2 * lane]), wq1 = 1.f + bf2f(a.wq[2 * lane + 1]);
   const float wk0 = 1.f + bf2f(a.wk[2 * lane]), wk1 = 1.f + bf2f(a.wk[2 * lane + 1]);
-  uint16_t* kc = a.kc + (size_t)h * a.cap * 128;
+  act_t* kc = a.kc + (size_t)h * a.cap * 128;
 
   for (int t = wave; t < QK_TOK; t += 4) {
     const int g = g0 + t;
     if (g < a.g_begin || g >= a.g_end) continue;       // wave-uniform
-    uint32_t vpair = 0;
+    float v0 = 0.f, v1 = 0.f;
     if (g < a.S) {
-      uint16_t* row = a.qkv + (size_t)(g - a.q_row0) * a.ld;
-      uint32_t* qp = reinterpret_cast<uint32_t*>(row + h * 128) + lane;
-      const uint32_t* kp = reinterpret_cast<const uint32_t*>(row + a.H + h * 128) + lane;
-      const uint32_t* vp = reinterpret_cast<const uint32_t*>(row + 2 * a.H + h * 128) + lane;
-      const uint32_t qraw = *qp, kraw = *kp;
-      vpair = *vp;
+      act_t* row = a.qkv + (size_t)(g - a.q_row0) * a.ld;
+      act_t* qp = row + h * 128 + 2 * lane;
+      const act_t* kp = row + a.H + h * 128 + 2 * lane;
+      load_act2(row + 2 * a.H + h * 128 + 2 * lane, v0, v1);
+      float x0, x1, y0, y1;
+      load_act2(qp, x0, x1);
+      load_act2(kp, y0, y1);
       const float c = a.cosv[(size_t)g * 64 + lane], s = a.sinv[(size_t)g * 64 + lane];
-      float x0 = bf2f(qraw & 0xffff), x1 = bf2f(qraw >> 16);
       float r = rsqrtf(wave_sum(x0 * x0 + x1 * x1) * (1.f / 128.f) + a.eps);
       x0 *= r * wq0; x1 *= r * wq1;
-      *qp = pack2bf(x0 * c - x1 * s, x0 * s + x1 * c);
-      float y0 = bf2f(kraw & 0xffff), y1 = bf2f(kraw >> 16);
+      store_act2(qp, x0 * c - x1 * s, x0 * s + x1 * c);
       r = rsqrtf(wave_sum(y0 * y0 + y1 * y1) * (1.f / 128.f) + a.eps);
       y0 *= r * wk0; y1 *= r * wk1;
-      reinterpret_cast<uint32_t*>(kc + (size_t)g * 128)[lane] = pack2bf(y0 * c - y1 * s, y0 * s + y1 * c);
+      store_act2(kc + (size_t)g * 128 + 2 * lane, y0 * c - y1 * s, y0 * s + y1 * c);
     } else {
-      reinterpret_cast<uint32_t*>(kc + (size_t)g * 128)[lane] = 0u;   // padding keys
+      store_act2(kc + (size_t)g * 128 + 2 * lane, 0.f, 0.f);   // padding keys
     }
-    vt_s[t][lane] = vpair;
+    vt_s[t][2 * lane] = v0;
+    vt_s[t][2 * lane + 1] = v1;
   }
   __syncthreads();
   // Vᵀ rows: dim e, keys g0..g0+63; 8 chunks of 8 keys per row
-  uint16_t* vt = a.vtc + (size_t)h * 128 * a.cap;
+  act_t* vt = a.vtc + (size_t)h * 128 * a.cap;
   for (int q = threadIdx.x; q < 128 * 8; q += 256) {
     const int e = q >> 3, c = q & 7;
     const int k0 = g0 + c * 8;
-    uint16_t vals[8];
+    float vals[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const uint32_t p = vt_s[c * 8 + j][e >> 1];
-      vals[j] = (e & 1) ? (uint16_t)(p >> 16) : (uint16_t)(p & 0xffff);
-    }
-    uint16_t* dst = vt + (size_t)e * a.cap + k0;
+    for (int j = 0; j < 8; ++j) vals[j] = vt_s[c * 8 + j][e];
+    act_t* dst = vt + (size_t)e * a.cap + k0;
     if (k0 >= a.g_begin && k0 + 8 <= a.g_end) {
-      u32x4 w;
-      w.x = vals[0] | ((uint32_t)vals[1] << 16);
-      w.y = vals[2] | ((uint32_t)vals[3] << 16);
-      w.z = vals[4] | ((uint32_t)vals[5] << 16);
-      w.w = vals[6] | ((uint32_t)vals[7] << 16);
-      *reinterpret_cast<u32x4*>(dst) = w;
+      store_act4(dst, vals[0], vals[1], vals[2], vals[3]);
+      store_act4(dst + 4, vals[4], vals[5], vals[6], vals[7]);
     } else {
 #pragma unroll
       for (int j = 0; j < 8; ++j)
-        if (k0 + j >= a.g_begin && k0 + j < a.g_end) dst[j] = vals[j];
+        if (k0 + j >= a.g_begin && k0 + j < a.g_end) dst[j] = f2act(vals[j]);
     }
   }
 }
@@ -230,7 +221,7 @@ __global__ void euler_kernel(float* __restrict__ x, const float* __restrict__ v,
 }  // namespace
 
 hipError_t launch_ln_mod(const float* h, int ldh, int rows, int H, const float* scale_t,
-                         const float* scale_0, int n_pre, float eps, uint16_t* out, int ldo,
+                         const float* scale_0, int n_pre, float eps, act_t* out, int ldo,
                          hipStream_t s) {
   if (rows <= 0) return hipSuccess;
   hipLaunchKernelGGL(ln_mod_kernel, dim3(rows), dim3(LN_NT), 0, s, h, ldh, H, scale_t, scale_0,

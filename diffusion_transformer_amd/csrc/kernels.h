@@ -7,6 +7,14 @@
 
 namespace dit {
 
+// Activation element type: bf16 bits in the production library, fp32 in
+// the debug build compiled with -DDIT_F32 (weights stay bf16 in both).
+#ifdef DIT_F32
+typedef float act_t;
+#else
+typedef uint16_t act_t;
+#endif
+
 enum GemmEpi {
   EPI_BF16 = 0,    // C (bf16) = A·Bᵀ
   EPI_F32 = 1,     // C (f32)  = A·Bᵀ
@@ -15,11 +23,11 @@ enum GemmEpi {
 };
 
 struct GemmArgs {
-  const uint16_t* A; int lda;       // [M, K] bf16
+  const act_t* A; int lda;          // [M, K] activations
   const uint16_t* B; int ldb;       // [N, K] bf16 (gate for SwiGLU)
   const uint16_t* B2;               // up [N/2, K] for SwiGLU, else unused
   int M, N, K;                      // N = packed width (2F for SwiGLU)
-  void* C; int ldc;                 // output
+  void* C; int ldc;                 // output (act_t, or f32 for EPI_F32)
   float* Hres; int ldh;             // residual stream for EPI_RESID
   const float* gate_t;              // [N] gate row of target / current-t tokens
   const float* gate_0;              // [N] gate row of prefix tokens (t = 0)
@@ -31,34 +39,34 @@ hipError_t launch_gemm_variant(const GemmArgs& g, int variant, hipStream_t s);
 bool gemm_shape_ok(int M, int N, int K, int epi);
 
 struct AttnArgs {
-  const uint16_t* q; int q_stride;  // local query rows 0..N-1, head h at column h*128
+  const act_t* q; int q_stride;     // local query rows 0..N-1, head h at column h*128
   int q_off;                        // global index of local row 0
   int N;
-  const uint16_t* k;                // K of this layer: [nh][cap][128]
-  const uint16_t* vt;               // Vᵀ of this layer: [nh][128][cap]
+  const act_t* k;                   // K of this layer: [nh][cap][128]
+  const act_t* vt;                  // Vᵀ of this layer: [nh][128][cap]
   int cap, S, nh;
   const int32_t* limit;             // [S]
-  uint16_t* out; int out_stride;    // [N, nh*128] bf16
+  act_t* out; int out_stride;       // [N, nh*128]
 };
 hipError_t launch_attention(const AttnArgs& a, hipStream_t s);
 hipError_t launch_attention_variant(const AttnArgs& a, int variant, hipStream_t s);
 hipError_t launch_debug_mask(const int32_t* limit, int S, uint8_t* mask, hipStream_t s);
 
-// LN(h)·(1 + scale[row]) -> bf16. rows < n_pre use scale_0, others scale_t.
+// LN(h)·(1 + scale[row]) -> act_t. rows < n_pre use scale_0, others scale_t.
 hipError_t launch_ln_mod(const float* h, int ldh, int rows, int H, const float* scale_t,
-                         const float* scale_0, int n_pre, float eps, uint16_t* out, int ldo,
+                         const float* scale_0, int n_pre, float eps, act_t* out, int ldo,
                          hipStream_t s);
 
 // Per-head QK-RMSNorm (1 + w) + 3D RoPE on q (in place) and k, and the K /
 // Vᵀ cache writes for global tokens [g_begin, g_end); tokens >= S are
 // zero-filled in the cache. qkv local row i holds global token q_row0 + i.
 struct QkArgs {
-  uint16_t* qkv; int ld;            // [rows, 3H]
+  act_t* qkv; int ld;               // [rows, 3H]
   int q_row0;
   int g_begin, g_end, S, cap, nh, H;
   const uint16_t* wq; const uint16_t* wk;   // [128] bf16
   const float* cosv; const float* sinv;     // [S, 64]
-  uint16_t* kc; uint16_t* vtc;              // layer bases
+  act_t* kc; act_t* vtc;                    // layer bases
   float eps;
 };
 hipError_t launch_qknorm_rope(const QkArgs& a, hipStream_t s);

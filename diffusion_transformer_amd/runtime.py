@@ -60,30 +60,34 @@ def random_weights_device(cfg: dict, seed: int, device, n_layers=None) -> dict:
 class Sequence:
     """Device copy of one token layout plus its C struct."""
 
-    def __init__(self, cfg_c, segments, device):
-        lay = L.dit_build_layout(cfg_c, segments)
+    def __init__(self, cfg_c, segments, device, api=L):
+        lay = api.dit_build_layout(cfg_c, segments)
         self.host = lay
         self.P, self.T = lay["P"], lay["T"]
         self.S = self.P + self.T
         self.row_limit = torch.from_numpy(lay["row_limit"]).to(device)
         self.rope_cos = torch.from_numpy(lay["rope_cos"]).to(device)
         self.rope_sin = torch.from_numpy(lay["rope_sin"]).to(device)
-        self.c = L.make_seq(self.P, self.T, self.row_limit, self.rope_cos, self.rope_sin)
+        self.c = api.make_seq(self.P, self.T, self.row_limit, self.rope_cos, self.rope_sin)
 
 
 class DitRuntime:
-    def __init__(self, cfg: dict, weights: dict, device="cuda", on_device=False):
+    """``api``: the binding of the library to use (default: the production
+    bf16 library; ``_lib.load_f32()`` for the fp32 debug build)."""
+
+    def __init__(self, cfg: dict, weights: dict, device="cuda", on_device=False, api=None):
+        self.L = api if api is not None else L
         self.cfg = cfg
         self.device = torch.device(device)
-        self.c = L.make_config(**{k: cfg[k] for k in ("hidden", "n_heads", "head_dim", "ffn",
+        self.c = self.L.make_config(**{k: cfg[k] for k in ("hidden", "n_heads", "head_dim", "ffn",
                                                       "n_layers", "latent", "time_dim",
                                                       "rope_dims")})
         self.w = weights if on_device else upload_weights(weights, self.device)
-        self.model = L.dit_load_weights(self.c, self.w)
+        self.model = self.L.dit_load_weights(self.c, self.w)
 
     def close(self):
         if self.model:
-            L.dit_free(self.model)
+            self.L.dit_free(self.model)
             self.model = None
 
     def __del__(self):
@@ -93,21 +97,21 @@ class DitRuntime:
             pass
 
     def sequence(self, segments) -> Sequence:
-        return Sequence(self.c, segments, self.device)
+        return Sequence(self.c, segments, self.device, self.L)
 
     def alloc_cache(self, seq: Sequence) -> torch.Tensor:
-        nbytes = L.dit_kv_cache_bytes(self.model, seq.S)
+        nbytes = self.L.dit_kv_cache_bytes(self.model, seq.S)
         return torch.empty(nbytes // 2, dtype=torch.int16, device=self.device)
 
     def alloc_workspace(self, n_tokens: int) -> torch.Tensor:
-        nbytes = L.dit_workspace_bytes(self.model, n_tokens)
+        nbytes = self.L.dit_workspace_bytes(self.model, n_tokens)
         return torch.empty((nbytes + 3) // 4, dtype=torch.float32, device=self.device)
 
     def img_in(self, latents: torch.Tensor) -> torch.Tensor:
         out = torch.empty((latents.shape[0], self.cfg["hidden"]), dtype=torch.float32,
                           device=self.device)
         if latents.shape[0]:
-            L.dit_img_in(self.model, latents.contiguous(), out)
+            self.L.dit_img_in(self.model, latents.contiguous(), out)
         return out
 
     def prefix_hidden(self, inputs: dict) -> torch.Tensor:
@@ -125,10 +129,10 @@ class DitRuntime:
         return out
 
     def step_extract(self, seq, prefix, x, sigma, cache, v, ws, flags=0, stream=None):
-        L.dit_step_extract(self.model, seq.c, prefix, x, sigma, cache, v, ws, flags, stream)
+        self.L.dit_step_extract(self.model, seq.c, prefix, x, sigma, cache, v, ws, flags, stream)
 
     def step_cached(self, seq, x, sigma, cache, v, ws, stream=None):
-        L.dit_step_cached(self.model, seq.c, x, sigma, cache, v, ws, stream)
+        self.L.dit_step_cached(self.model, seq.c, x, sigma, cache, v, ws, stream)
 
     def run_loop(self, seq, prefix, x0, sigmas, use_cache=True):
         """Sampler loop; returns (list of v per step, list of x after each step)."""
@@ -143,6 +147,6 @@ class DitRuntime:
             else:
                 self.step_cached(seq, x, sigmas[k], cache, v, ws)
             vs.append(v)
-            L.euler_update(x, v, sigmas[k], sigmas[k + 1])
+            self.L.euler_update(x, v, sigmas[k], sigmas[k + 1])
             xs.append(x.clone())
         return vs, xs
