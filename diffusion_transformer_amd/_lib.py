@@ -1,13 +1,20 @@
 """ctypes binding of ``libdit.so`` (include/dit.h), one Python function per C
 entry point with the same name. Argument marshalling only: torch tensors
 are passed as raw device pointers, every computation happens in the HIP
-library. Importing this module raises if the library is not built."""
+library. Importing this module raises if the library is not built.
+
+torch is imported before the library is opened on purpose: torch ships its
+own HIP runtime (soname libamdhip64.so.7) and the library must bind to that
+same instance, so that torch's device pointers and stream handles are valid
+inside it. Opened first, the library would pull in the system runtime and
+torch would then load a second one next to it."""
 from __future__ import annotations
 
 import ctypes as C
 import os
 
 import numpy as np
+import torch  # noqa: F401  (see above: one HIP runtime per process)
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libdit.so")

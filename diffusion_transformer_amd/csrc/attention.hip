@@ -221,6 +221,13 @@ __global__ __launch_bounds__(NT) void attn_kernel(AttnArgs a) {
 //    probabilities stay below 2^8 and the final O/l is unchanged.
 #define LDSP(p) ((__attribute__((address_space(3))) void*)(p))
 
+// max over the two 32-lane halves of the wave (v_permlane32_swap, no LDS)
+__device__ __forceinline__ float half_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+constexpr bf16x2 kOnes2 = {(__bf16)1.0f, (__bf16)1.0f};
+
 __device__ __forceinline__ int perm23(int x) {   // swap bits 2 and 3
   return (x & ~0xC) | ((x & 4) << 1) | ((x & 8) >> 1);
 }
@@ -228,6 +235,7 @@ __device__ __forceinline__ int perm23(int x) {   // swap bits 2 and 3
 template <int NWV, int QW>
 __global__ __launch_bounds__(NWV * 64) void attn2_kernel(AttnArgs a) {
   constexpr int NSB = QW / 32;          // 32-query sub-blocks per wave
+  constexpr int KAHEAD = 6;             // K fragment reads in flight
   constexpr int BQ2 = NWV * QW;
   constexpr int KT = BKV * 16;          // u32x4 per K tile (64 keys x 256 B)
   constexpr int VT = D * 8;             // u32x4 per Vᵀ tile (128 dims x 128 B)
@@ -239,7 +247,13 @@ __global__ __launch_bounds__(NWV * 64) void attn2_kernel(AttnArgs a) {
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int h = blockIdx.y;
+  // Workgroups are dealt to the 8 XCDs round-robin; renumber them so that
+  // each XCD gets a contiguous run of (head, query block) pairs and its L2
+  // serves the K/Vᵀ of a few heads instead of all of them.
+  const int nqb = (a.N + BQ2 - 1) / BQ2;
+  int bid = blockIdx.x;
+  if ((gridDim.x & 7) == 0) bid = (bid & 7) * (gridDim.x >> 3) + (bid >> 3);
+  const int h = bid / nqb, qblk = bid - h * nqb;
   const int lq = lane & 31, half = lane >> 5;
 
   int qi[NSB], lim[NSB];
@@ -247,14 +261,15 @@ __global__ __launch_bounds__(NWV * 64) void attn2_kernel(AttnArgs a) {
   int lmin = 1 << 30, lmax = -1;
 #pragma unroll
   for (int sb = 0; sb < NSB; ++sb) {
-    const int q = blockIdx.x * BQ2 + wave * QW + sb * 32 + lq;
+    const int q = qblk * BQ2 + wave * QW + sb * 32 + lq;
     qv[sb] = q < a.N;
     qi[sb] = min(q, a.N - 1);
     lim[sb] = a.limit[a.q_off + qi[sb]];
     lmin = min(lmin, lim[sb]);
     lmax = max(lmax, lim[sb]);
   }
-  const int wlim_min = wave_min_i(lmin), wlim_max = wave_max_i(lmax);
+  const int wlim_min = __builtin_amdgcn_readfirstlane(wave_min_i(lmin));
+  const int wlim_max = __builtin_amdgcn_readfirstlane(wave_max_i(lmax));
   if (lane == 0) red[wave] = wlim_max;
   __syncthreads();
   int blim_max = red[0];
@@ -330,16 +345,43 @@ __global__ __launch_bounds__(NWV * 64) void attn2_kernel(AttnArgs a) {
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) sacc[sb][kb][r] = 0.f;
+    // Sᵀ = K·Qᵀ. All 16 K fragments are requested up front and consumed in
+    // order, so LDS latency hides behind the MFMA chain (KAHEAD reads ahead).
+    bf16x8 kf[8][2];
 #pragma unroll
-    for (int s = 0; s < 8; ++s) {
+    for (int s = 0; s < 8; ++s)
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         const int row = perm23(kb * 32 + lq);
-        const bf16x8 kf = __builtin_bit_cast(bf16x8, ks[row * 16 + ((2 * s + half) ^ (row & 15))]);
-#pragma unroll
-        for (int sb = 0; sb < NSB; ++sb) sacc[sb][kb] = mfma32(kf, qf[sb][s], sacc[sb][kb]);
+        kf[s][kb] = __builtin_bit_cast(bf16x8, ks[row * 16 + ((2 * s + half) ^ (row & 15))]);
       }
+#pragma unroll
+    for (int s = 0; s < 8; ++s)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int sb = 0; sb < NSB; ++sb) sacc[sb][kb] = mfma32(kf[s][kb], qf[sb][s], sacc[sb][kb]);
+    __builtin_amdgcn_sched_group_barrier(0x100, KAHEAD, 0);
+#pragma unroll
+    for (int i = 0; i < 16 - KAHEAD; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, NSB, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
+    __builtin_amdgcn_sched_group_barrier(0x008, KAHEAD * NSB, 0);
+    // masking only on tiles that straddle some query's limit (wave-uniform)
+    if (cls == 2) {
+#pragma unroll
+      for (int sb = 0; sb < NSB; ++sb)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int j = kv0 + perm23(kb * 32 + 8 * (r >> 2) + 4 * half + (r & 3));
+            if (!key_visible(j, lim[sb], a.S)) sacc[sb][kb][r] = -INFINITY;
+          }
+    }
+    // Scores stay unscaled; the softmax scale log2(e)/sqrt(d) > 0 commutes
+    // with the max and is folded into the exponent: p = 2^(s*c - m).
     uint32_t pk[NSB][2][8];
 #pragma unroll
     for (int sb = 0; sb < NSB; ++sb) {
@@ -347,16 +389,8 @@ __global__ __launch_bounds__(NWV * 64) void attn2_kernel(AttnArgs a) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float v = sacc[sb][kb][r] * sl2;
-          if (cls == 2) {
-            const int j = kv0 + perm23(kb * 32 + 8 * (r >> 2) + 4 * half + (r & 3));
-            if (!key_visible(j, lim[sb], a.S)) v = -INFINITY;
-          }
-          sacc[sb][kb][r] = v;
-          mt = fmaxf(mt, v);
-        }
-      mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+        for (int r = 0; r < 16; ++r) mt = fmaxf(mt, sacc[sb][kb][r]);
+      mt = half_max(mt) * sl2;
       // raise the running max only when some query of the wave needs it
       if (__builtin_amdgcn_ballot_w64(mt > m_run[sb] + 8.f)) {
         const float m_new = fmaxf(m_run[sb], mt);
@@ -368,18 +402,20 @@ __global__ __launch_bounds__(NWV * 64) void attn2_kernel(AttnArgs a) {
 #pragma unroll
           for (int r = 0; r < 16; ++r) oacc[sb][j][r] *= alpha;
       }
-      const float mr = m_run[sb];
-      float ls = 0.f;
+      const float nm = -m_run[sb];
+      float ls = l_run[sb];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; r += 2) {
-          const float p0 = __builtin_amdgcn_exp2f(sacc[sb][kb][r] - mr);
-          const float p1 = __builtin_amdgcn_exp2f(sacc[sb][kb][r + 1] - mr);
-          ls += p0 + p1;
-          pk[sb][kb][r >> 1] = pack2bf(p0, p1);
+          const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[sb][kb][r], sl2, nm));
+          const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[sb][kb][r + 1], sl2, nm));
+          const uint32_t w = pack2bf(p0, p1);
+          pk[sb][kb][r >> 1] = w;
+          // the row sum takes the same bf16-rounded p the PV product uses
+          ls = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w), kOnes2, ls, false);
         }
-      l_run[sb] += ls;
+      l_run[sb] = ls;
     }
     // Oᵀ += Vᵀ·Pᵀ: chunk c = registers 8(c%2).. of key block c/2, which
     // (through π) are keys 16c + 8*half + {0..7} of this lane's query
@@ -460,7 +496,7 @@ __global__ __launch_bounds__(NWV * 64) void attn2_kernel(AttnArgs a) {
 
 template <int NWV, int QW>
 hipError_t run_attn2(const AttnArgs& a, hipStream_t s) {
-  dim3 grid((a.N + NWV * QW - 1) / (NWV * QW), a.nh);
+  dim3 grid(((a.N + NWV * QW - 1) / (NWV * QW)) * a.nh);
   hipLaunchKernelGGL((attn2_kernel<NWV, QW>), grid, dim3(NWV * 64), 0, s, a);
   return hipGetLastError();
 }

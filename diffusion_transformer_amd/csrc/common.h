@@ -16,8 +16,12 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));          // 8-byte m
 __device__ __forceinline__ float bf2f(bf16_t b) { return __uint_as_float(((uint32_t)b) << 16); }
 // float -> bf16, round to nearest even (lowers to v_cvt_pk_bf16_f32 on gfx950).
 __device__ __forceinline__ bf16_t f2bf(float f) { return __builtin_bit_cast(bf16_t, (__bf16)f); }
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+// Two floats -> packed bf16 pair (a in the low half), one v_cvt_pk_bf16_f32.
 __device__ __forceinline__ uint32_t pack2bf(float a, float b) {
-  return (uint32_t)f2bf(a) | ((uint32_t)f2bf(b) << 16);
+  const f32x2 v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
 }
 
 // Conversions for the activation element type act_t (kernels.h).

@@ -159,3 +159,16 @@ def test_workspace_grows_with_tokens():
         assert abs((b - a) - 512 * per_tok) < 64 * 256
     finally:
         L.dit_free(m)
+
+
+def test_one_hip_runtime_per_process():
+    """The binding opens the library after torch, so both share torch's HIP
+    runtime (a second runtime in the process cannot see the device once the
+    first one holds it, and torch's streams would be foreign to it)."""
+    import subprocess
+    import sys
+    code = ("import diffusion_transformer_amd._lib\n"
+            "print(sorted({l.split()[-1] for l in open('/proc/self/maps') if 'libamdhip64' in l}))")
+    out = subprocess.run([sys.executable, "-c", code], cwd=ROOT, capture_output=True, text=True,
+                         check=True).stdout.strip().splitlines()[-1]
+    assert out.count("libamdhip64") == 1, out
