@@ -233,6 +233,102 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_kernel(GemmArgs g) {
   }
 }
 
+// Epilogue shared by the direct-to-LDS kernels: wave (wm, wn) owns the
+// TM x TN patch at (m0 + wm*TM, n0 + wn*TN) in FM x FN blocks of 32x32.
+template <int FM, int FN, int TM, int TN, int EPI, bool SWAP>
+__device__ __forceinline__ void store_tile(const GemmArgs& g, f32x16 (&acc)[FM][FN], int m0, int n0,
+                                           int wm, int wn, int lrow, int lhalf) {
+  if (!SWAP) {
+    // accumulator register r of lane l holds C[8*(r/4) + 4*(l/32) + r%4][l%32]
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int m = m0 + wm * TM + i * 32 + 8 * (r >> 2) + 4 * lhalf + (r & 3);
+        if (m >= g.M) continue;
+        if (EPI == EPI_SWIGLU) {
+#pragma unroll
+          for (int j = 0; j < FN; j += 2) {
+            const int f = ((n0 + wn * TN + j * 32) >> 1) + lrow;
+            const float gv = acc[i][j][r], uv = acc[i][j + 1][r];
+            reinterpret_cast<bf16_t*>(g.C)[(size_t)m * g.ldc + f] = f2bf(gv / (1.f + __expf(-gv)) * uv);
+          }
+        } else {
+#pragma unroll
+          for (int j = 0; j < FN; ++j) {
+            const int n = n0 + wn * TN + j * 32 + lrow;
+            const float v = acc[i][j][r];
+            if (EPI == EPI_BF16) {
+              reinterpret_cast<bf16_t*>(g.C)[(size_t)m * g.ldc + n] = f2bf(v);
+            } else if (EPI == EPI_F32) {
+              reinterpret_cast<float*>(g.C)[(size_t)m * g.ldc + n] = v;
+            } else {
+              const float gt = (m < g.n_pre ? g.gate_0 : g.gate_t)[n];
+              float* hp = g.Hres + (size_t)m * g.ldh + n;
+              *hp = *hp + tanhf(gt) * v;
+            }
+          }
+        }
+      }
+    }
+    return;
+  }
+  // ---- epilogue: lane owns row m = .. + lrow, columns n0c + 8g + 4*lhalf + {0..3} ----
+#pragma unroll
+  for (int i = 0; i < FM; ++i) {
+    const int m = m0 + wm * TM + i * 32 + lrow;
+    if (m >= g.M) continue;
+    if (EPI == EPI_SWIGLU) {
+#pragma unroll
+      for (int j = 0; j < FN; j += 2) {
+        const int fbase = ((n0 + wn * TN + j * 32) >> 1);     // gate block j, up block j+1
+#pragma unroll
+        for (int gq = 0; gq < 4; ++gq) {
+          float o[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float gv = acc[i][j][4 * gq + e], uv = acc[i][j + 1][4 * gq + e];
+            o[e] = gv / (1.f + __expf(-gv)) * uv;
+          }
+          u32x2 w;
+          w.x = pack2bf(o[0], o[1]);
+          w.y = pack2bf(o[2], o[3]);
+          *reinterpret_cast<u32x2*>(reinterpret_cast<bf16_t*>(g.C) + (size_t)m * g.ldc + fbase + 8 * gq + 4 * lhalf) = w;
+        }
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+#pragma unroll
+        for (int gq = 0; gq < 4; ++gq) {
+          const int n = n0 + wn * TN + j * 32 + 8 * gq + 4 * lhalf;
+          float a4[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) a4[e] = acc[i][j][4 * gq + e];
+          if (EPI == EPI_BF16) {
+            u32x2 w;
+            w.x = pack2bf(a4[0], a4[1]);
+            w.y = pack2bf(a4[2], a4[3]);
+            *reinterpret_cast<u32x2*>(reinterpret_cast<bf16_t*>(g.C) + (size_t)m * g.ldc + n) = w;
+          } else if (EPI == EPI_F32) {
+            *reinterpret_cast<float4*>(reinterpret_cast<float*>(g.C) + (size_t)m * g.ldc + n) =
+                make_float4(a4[0], a4[1], a4[2], a4[3]);
+          } else {
+            const float4 gt = *reinterpret_cast<const float4*>((m < g.n_pre ? g.gate_0 : g.gate_t) + n);
+            float4* hp = reinterpret_cast<float4*>(g.Hres + (size_t)m * g.ldh + n);
+            float4 hv = *hp;
+            hv.x += tanhf(gt.x) * a4[0];
+            hv.y += tanhf(gt.y) * a4[1];
+            hv.z += tanhf(gt.z) * a4[2];
+            hv.w += tanhf(gt.w) * a4[3];
+            *hp = hv;
+          }
+        }
+      }
+    }
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Direct-to-LDS variant: BM = BN = 256, BK = 32, a ring of 4 LDS stages of
 // 32 KB (separate arrays, so the compiler's LDS-DMA wait tracking can tell
@@ -423,95 +519,257 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_dma_kernel(GemmArgs g) {
   if (kt + 2 < nk) iter(st2, st3, st1, kt + 2);
   __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));   // drain outstanding DMA before exit
 
-  if (!SWAP) {
-    // accumulator register r of lane l holds C[8*(r/4) + 4*(l/32) + r%4][l%32]
+  store_tile<FM, FN, TM, TN, EPI, SWAP>(g, acc, m0, n0, wm, wn, lrow, lhalf);
+}
+
+// Epilogue through LDS for the swapped layout (each 32x32 block accumulated
+// as Cᵀ: lane l holds row l%32 and, in registers 4q..4q+3, the four
+// consecutive columns 8q + 4*(l/32) + {0..3}). Storing that layout directly
+// makes every store instruction touch 32 rows. Instead each wave stages its
+// 128 x 128 patch (bf16; 128 x 64 after SwiGLU) row-major in its own LDS
+// region, in 8-byte slots XOR-swizzled by the row so the writes of a half
+// wave hit distinct banks, and then writes whole rows with 16-byte lanes.
+// The caller guarantees every wave has finished reading the stage buffers.
+template <int EPI>
+__device__ __forceinline__ void store_tile_lds(const GemmArgs& g, f32x16 (&acc)[4][4], int m0, int n0,
+                                               int wm, int wn, int lane, char* reg) {
+  static_assert(EPI == EPI_BF16 || EPI == EPI_SWIGLU, "bf16 outputs only");
+  constexpr int OUTC = EPI == EPI_SWIGLU ? 64 : 128;   // output columns of the patch
+  constexpr int ROWB = OUTC * 2;                        // bytes per staged row
+  constexpr int SLOTS = ROWB / 8;                       // 8-byte slots per row
+  const int lrow = lane & 31, lhalf = lane >> 5;
 #pragma unroll
-    for (int i = 0; i < FM; ++i) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int m = m0 + wm * TM + i * 32 + 8 * (r >> 2) + 4 * lhalf + (r & 3);
-        if (m >= g.M) continue;
-        if (EPI == EPI_SWIGLU) {
-#pragma unroll
-          for (int j = 0; j < FN; j += 2) {
-            const int f = ((n0 + wn * TN + j * 32) >> 1) + lrow;
-            const float gv = acc[i][j][r], uv = acc[i][j + 1][r];
-            reinterpret_cast<bf16_t*>(g.C)[(size_t)m * g.ldc + f] = f2bf(gv / (1.f + __expf(-gv)) * uv);
-          }
-        } else {
-#pragma unroll
-          for (int j = 0; j < FN; ++j) {
-            const int n = n0 + wn * TN + j * 32 + lrow;
-            const float v = acc[i][j][r];
-            if (EPI == EPI_BF16) {
-              reinterpret_cast<bf16_t*>(g.C)[(size_t)m * g.ldc + n] = f2bf(v);
-            } else if (EPI == EPI_F32) {
-              reinterpret_cast<float*>(g.C)[(size_t)m * g.ldc + n] = v;
-            } else {
-              const float gt = (m < g.n_pre ? g.gate_0 : g.gate_t)[n];
-              float* hp = g.Hres + (size_t)m * g.ldh + n;
-              *hp = *hp + tanhf(gt) * v;
-            }
-          }
-        }
-      }
-    }
-    return;
-  }
-  // ---- epilogue: lane owns row m = .. + lrow, columns n0c + 8g + 4*lhalf + {0..3} ----
-#pragma unroll
-  for (int i = 0; i < FM; ++i) {
-    const int m = m0 + wm * TM + i * 32 + lrow;
-    if (m >= g.M) continue;
+  for (int i = 0; i < 4; ++i) {
+    const int row = i * 32 + lrow;
+    char* rp = reg + row * ROWB;
     if (EPI == EPI_SWIGLU) {
 #pragma unroll
-      for (int j = 0; j < FN; j += 2) {
-        const int fbase = ((n0 + wn * TN + j * 32) >> 1);     // gate block j, up block j+1
+      for (int j = 0; j < 4; j += 2)
 #pragma unroll
-        for (int gq = 0; gq < 4; ++gq) {
+        for (int q = 0; q < 4; ++q) {
           float o[4];
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            const float gv = acc[i][j][4 * gq + e], uv = acc[i][j + 1][4 * gq + e];
+            const float gv = acc[i][j][4 * q + e], uv = acc[i][j + 1][4 * q + e];
             o[e] = gv / (1.f + __expf(-gv)) * uv;
           }
+          const int slot = (2 * ((j >> 1) * 4 + q) + lhalf) ^ (row & (SLOTS - 1));
           u32x2 w;
           w.x = pack2bf(o[0], o[1]);
           w.y = pack2bf(o[2], o[3]);
-          *reinterpret_cast<u32x2*>(reinterpret_cast<bf16_t*>(g.C) + (size_t)m * g.ldc + fbase + 8 * gq + 4 * lhalf) = w;
+          *reinterpret_cast<u32x2*>(rp + slot * 8) = w;
         }
-      }
     } else {
 #pragma unroll
-      for (int j = 0; j < FN; ++j) {
+      for (int j = 0; j < 4; ++j)
 #pragma unroll
-        for (int gq = 0; gq < 4; ++gq) {
-          const int n = n0 + wn * TN + j * 32 + 8 * gq + 4 * lhalf;
-          float a4[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) a4[e] = acc[i][j][4 * gq + e];
-          if (EPI == EPI_BF16) {
-            u32x2 w;
-            w.x = pack2bf(a4[0], a4[1]);
-            w.y = pack2bf(a4[2], a4[3]);
-            *reinterpret_cast<u32x2*>(reinterpret_cast<bf16_t*>(g.C) + (size_t)m * g.ldc + n) = w;
-          } else if (EPI == EPI_F32) {
-            *reinterpret_cast<float4*>(reinterpret_cast<float*>(g.C) + (size_t)m * g.ldc + n) =
-                make_float4(a4[0], a4[1], a4[2], a4[3]);
-          } else {
-            const float4 gt = *reinterpret_cast<const float4*>((m < g.n_pre ? g.gate_0 : g.gate_t) + n);
-            float4* hp = reinterpret_cast<float4*>(g.Hres + (size_t)m * g.ldh + n);
-            float4 hv = *hp;
-            hv.x += tanhf(gt.x) * a4[0];
-            hv.y += tanhf(gt.y) * a4[1];
-            hv.z += tanhf(gt.z) * a4[2];
-            hv.w += tanhf(gt.w) * a4[3];
-            *hp = hv;
-          }
+        for (int q = 0; q < 4; ++q) {
+          const int slot = (2 * (4 * j + q) + lhalf) ^ (row & (SLOTS - 1));
+          u32x2 w;
+          w.x = pack2bf(acc[i][j][4 * q + 0], acc[i][j][4 * q + 1]);
+          w.y = pack2bf(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
+          *reinterpret_cast<u32x2*>(rp + slot * 8) = w;
         }
-      }
     }
   }
+  __builtin_amdgcn_s_waitcnt(kWaitLgkm0);   // the region is private to this wave
+  // read back: a 16-byte chunk c of row R holds logical slots 2c, 2c+1, at
+  // physical chunk c ^ ((R % SLOTS) / 2), halves exchanged when R is odd
+  constexpr int CPR = ROWB / 16;           // chunks per row
+  constexpr int RPI = 64 / CPR;            // rows per instruction
+  const int cc = lane % CPR;
+  bf16_t* C = reinterpret_cast<bf16_t*>(g.C);
+  const int col0 = (EPI == EPI_SWIGLU ? (n0 >> 1) + wn * 64 : n0 + wn * 128) + 8 * cc;
+#pragma unroll 4
+  for (int q = 0; q < 128 / RPI; ++q) {
+    const int R = q * RPI + lane / CPR;
+    const int pc = cc ^ ((R & (SLOTS - 1)) >> 1);
+    u32x4 v = *reinterpret_cast<const u32x4*>(reg + R * ROWB + pc * 16);
+    if (R & 1) v = (u32x4){v.z, v.w, v.x, v.y};
+    const int m = m0 + wm * 128 + R;
+    if (m < g.M) *reinterpret_cast<u32x4*>(C + (size_t)m * g.ldc + col0) = v;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// One wave per SIMD: 4 waves (2x2) of 128x128 on the 256x256 block tile, K
+// in stages of 64 (rows of 128 bytes), two 64 KB LDS stages. Per 16-wide K
+// slice a wave reads 4 A + 4 B fragments for 16 MFMAs: two thirds of the
+// LDS bytes per MFMA of a 128x64 wave tile; latency is hidden inside the
+// wave by software pipelining instead of by a second wave.
+//  - stage kt+1 is fetched into the other LDS stage during slice 0 of stage
+//    kt (that stage was last read before the previous barrier);
+//  - fragments of slice s+1 are read during the MFMAs of slice s;
+//  - the one barrier per stage sits in the middle of slice 3, so the next
+//    stage's slice-0 fragments load while the second half of slice 3 runs.
+// LDS rows hold 64 bf16 of K (8 chunks of 16 B); chunk c of row r sits at
+// c ^ ((r/2)%8), which puts the 16 rows one ds_read_b128 phase touches on
+// all 64 banks exactly once.
+template <int EPI, bool SWAP>
+__global__ __launch_bounds__(256) void gemm_w4_kernel(GemmArgs g) {
+  constexpr int BM = 256, BN = 256, SBK = 64;
+  constexpr int WN = 2, TM = 128, TN = 128, FM = 4, FN = 4;
+  constexpr int SW = (BM + BN) * SBK / 8;      // u32x4 per stage (64 KB)
+  static_assert(EPI != EPI_SWIGLU || (FN % 2 == 0 && TN % 64 == 0), "SwiGLU pairs 32-col blocks");
+  __shared__ u32x4 st0[SW], st1[SW];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / WN, wn = wave % WN;
+
+  const int ntm = (g.M + BM - 1) / BM;
+  const int ntn = g.N / BN;
+  const int nblk = ntm * ntn;
+  int b = blockIdx.x;
+  const int per = nblk >> 3;
+  if (b < per * 8) b = (b & 7) * per + (b >> 3);
+  const int in_group = GROUP_M * ntn;
+  const int gid = b / in_group;
+  const int first = gid * GROUP_M;
+  const int gsz = min(ntm - first, GROUP_M);
+  const int tm = first + (b % in_group) % gsz;
+  const int tn = (b % in_group) / gsz;
+  const int m0 = tm * BM, n0 = tn * BN;
+
+  // DMA: an instruction moves an 8-row block (1 KB); lane l fills row l/8,
+  // physical chunk l%8, which holds logical chunk (l%8) ^ ((row/2)%8). Wave
+  // w moves blocks 4j + w (j = 0..7) of A and of B, whose row parity (and so
+  // whose lane offsets) are the same for every j.
+  const int lr = lane >> 3;
+  const int lc = (lane & 7) ^ ((4 * (wave & 1) + (lane >> 4)) & 7);
+  const __amdgpu_buffer_rsrc_t rA = make_rsrc(
+      g.A + (size_t)m0 * g.lda, (uint32_t)min((size_t)(g.M - m0) * g.lda * 2, (size_t)0xFFFFFFF0u));
+  __amdgpu_buffer_rsrc_t rG, rU;
+  if (EPI == EPI_SWIGLU) {
+    const size_t bytes = min((size_t)(BN / 2) * g.ldb * 2, (size_t)0xFFFFFFF0u);
+    rG = make_rsrc(g.B + (size_t)(n0 >> 1) * g.ldb, (uint32_t)bytes);
+    rU = make_rsrc(g.B2 + (size_t)(n0 >> 1) * g.ldb, (uint32_t)bytes);
+  } else {
+    rG = rU = make_rsrc(g.B + (size_t)n0 * g.ldb, (uint32_t)min((size_t)BN * g.ldb * 2, (size_t)0xFFFFFFF0u));
+  }
+  const uint32_t aoff = (uint32_t)((lr * g.lda + lc * 8) * 2);
+  const uint32_t boff = (uint32_t)((lr * g.ldb + lc * 8) * 2);
+  const int nk = g.K / SBK;
+
+  // B block bb = 4j + w holds packed columns 8bb .. 8bb+7. For SwiGLU the
+  // packed column p is feature 32*(p/64) + p%32 of gate (p/32 even) or up
+  // (p/32 odd): block 4j + w is rows 32*(j/2) + 8w .. +7 of matrix j%2.
+  auto dma = [&](u32x4* stg, int kt) {
+    const uint32_t ko = (uint32_t)(kt * SBK * 2);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int blk = 4 * j + wave;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rA, LDSP(stg + blk * 64), 16, aoff,
+                                               ko + (uint32_t)(blk * 8 * g.lda * 2), 0, 0);
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int bb = 4 * j + wave;
+      u32x4* dst = stg + (BM / 8 + bb) * 64;
+      if (EPI == EPI_SWIGLU) {
+        const uint32_t so = ko + (uint32_t)((32 * (j >> 1) + 8 * wave) * g.ldb * 2);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds((j & 1) ? rU : rG, LDSP(dst), 16, boff, so, 0, 0);
+      } else {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rG, LDSP(dst), 16, boff,
+                                                 ko + (uint32_t)(bb * 8 * g.ldb * 2), 0, 0);
+      }
+    }
+  };
+
+  f32x16 acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  const int lrow = lane & 31, lhalf = lane >> 5;
+  const int swz = (lrow >> 1) & 7;
+  bf16x8 fa[2][FM], fb[2][FN];
+  auto lread = [&](int fs, const u32x4* stg, int s) {
+    const int ph = (2 * s + lhalf) ^ swz;
+#pragma unroll
+    for (int i = 0; i < FM; ++i) fa[fs][i] = __builtin_bit_cast(bf16x8, stg[(wm * TM + i * 32 + lrow) * 8 + ph]);
+#pragma unroll
+    for (int j = 0; j < FN; ++j) fb[fs][j] = __builtin_bit_cast(bf16x8, stg[(BM + wn * TN + j * 32 + lrow) * 8 + ph]);
+  };
+  auto mma = [&](int fs, int i0, int i1) {
+#pragma unroll
+    for (int i = i0; i < i1; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+        acc[i][j] = SWAP ? mfma32(fb[fs][j], fa[fs][i], acc[i][j]) : mfma32(fa[fs][i], fb[fs][j], acc[i][j]);
+  };
+
+  dma(st0, 0);
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+  __builtin_amdgcn_s_barrier();
+  lread(0, st0, 0);
+
+  // Each slice is its own scheduling region (sched_barrier), inside which
+  // the fragment reads / DMAs are paired one-to-one with the MFMAs.
+  auto pair = [&](int n_ds, int n_vm) {
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      if (k < n_ds) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                 // MFMA
+      if (k < n_vm) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // VMEM (LDS DMA)
+    }
+  };
+  auto iter = [&](const u32x4* cur, u32x4* nxt, int kt) {
+    // slice 0: next slice's fragments and the whole next-stage DMA
+    lread(1, cur, 1);
+    dma(nxt, min(kt + 1, nk - 1));
+    mma(0, 0, FM);
+    pair(8, 16);
+    __builtin_amdgcn_sched_barrier(0);
+    lread(0, cur, 2);
+    mma(1, 0, FM);
+    pair(8, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    lread(1, cur, 3);
+    mma(0, 0, FM);
+    pair(8, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    // slice 3: half, barrier (next stage landed and visible), next stage's
+    // slice-0 reads under the second half
+    mma(1, 0, FM / 2);
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+    lds_barrier();
+    lread(0, nxt, 0);
+    mma(1, FM / 2, FM);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  int kt = 0;
+  for (; kt + 1 < nk; kt += 2) {
+    iter(st0, st1, kt);
+    iter(st1, st0, kt + 1);
+  }
+  if (kt < nk) iter(st0, st1, kt);
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));   // drain the final (redundant) DMA before exit
+
+  if (SWAP && (EPI == EPI_BF16 || EPI == EPI_SWIGLU)) {
+    lds_barrier();   // every wave is done with the stage buffers
+    char* reg = reinterpret_cast<char*>((wave < 2 ? st0 : st1)) + (wave & 1) * 32768;
+    store_tile_lds<(EPI == EPI_SWIGLU ? EPI_SWIGLU : EPI_BF16)>(g, acc, m0, n0, wm, wn, lane, reg);
+  } else {
+    store_tile<FM, FN, TM, TN, EPI, SWAP>(g, acc, m0, n0, wm, wn, lrow, lhalf);
+  }
+}
+
+template <int EPI, bool SWAP>
+hipError_t run_w4(const GemmArgs& g, hipStream_t s) {
+  const int nblk = ((g.M + 255) / 256) * (g.N / 256);
+  hipLaunchKernelGGL((gemm_w4_kernel<EPI, SWAP>), dim3(nblk), dim3(256), 0, s, g);
+  return hipGetLastError();
 }
 
 template <int WM, int WN, int EPI, bool SWAP = true, int GM = GROUP_M>
@@ -541,15 +799,17 @@ hipError_t launch_gemm_variant(const GemmArgs& g, int variant, hipStream_t s) {
     case 1: return run<256, 256, 2, 4, EPI_BF16>(g, s);        // register-staged, 2-stage LDS
     case 2: return run_dma<2, 4, EPI_BF16, true>(g, s);        // direct-to-LDS, swapped operands
     case 3: return run_dma<2, 2, EPI_BF16, false>(g, s);       // direct-to-LDS, 4 waves of 128x128
+    case 4: return run_w4<EPI_BF16, false>(g, s);              // 4 waves of 128x128, K stages of 64
+    case 5: return run_dma<2, 4, EPI_BF16, false>(g, s);       // 8 waves of 128x64
   }
   return hipErrorInvalidValue;
 }
 
 hipError_t launch_gemm(const GemmArgs& g, int epi, hipStream_t s) {
   switch (epi) {
-    case EPI_BF16: return run_dma<2, 4, EPI_BF16, false>(g, s);
-    case EPI_RESID: return run_dma<2, 4, EPI_RESID, true>(g, s);
-    case EPI_SWIGLU: return run_dma<2, 4, EPI_SWIGLU, false>(g, s);
+    case EPI_BF16: return run_w4<EPI_BF16, true>(g, s);
+    case EPI_RESID: return run_w4<EPI_RESID, true>(g, s);
+    case EPI_SWIGLU: return run_w4<EPI_SWIGLU, true>(g, s);
     case EPI_F32: return run<64, 64, 2, 2, EPI_F32>(g, s);
   }
   return hipErrorInvalidValue;
