@@ -68,7 +68,7 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs g, int Nout) {
       } else if (EPI == EPI_RESID) {
         const float gt = (m < g.n_pre ? g.gate_0 : g.gate_t)[n];
         float* hp = g.Hres + (size_t)m * g.ldh + n;
-        *hp = *hp + tanhf(gt) * v;
+        *hp = *hp + gt * v;
       } else {
         reinterpret_cast<float*>(g.C)[(size_t)m * g.ldc + n] = v / (1.f + expf(-v)) * accu[i][j];
       }

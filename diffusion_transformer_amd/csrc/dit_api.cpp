@@ -184,6 +184,7 @@ dit_status run_step(dit_model* m, const dit_seq* seq, bool extract, const float*
   LAUNCH(launch_gemv(U(m->t1), H, c.time_dim, te, c.time_dim, nv, a1, H, a1s, st), "gemv t1");
   LAUNCH(launch_gemv(U(m->t2), H, H, a1s, H, nv, tb, H, tbs, st), "gemv t2");
   LAUNCH(launch_gemv(U(m->mod), 4 * H, H, tbs, H, nv, mod, 4 * H, nullptr, st), "gemv mod");
+  LAUNCH(launch_gate_tanh(mod, H, nv, st), "gate tanh");
   LAUNCH(launch_gemv(U(m->so), H, H, tbs, H, 1, scale_out, H, nullptr, st), "gemv so");
   const float* row_t = mod;
   const float* row_0 = extract ? mod + 4 * H : mod;

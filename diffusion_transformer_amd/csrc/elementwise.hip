@@ -243,6 +243,22 @@ hipError_t launch_gemv(const uint16_t* W, int O, int I, const float* X, int ldx,
   return hipGetLastError();
 }
 
+// In place: the gate sections [H, 2H) and [3H, 4H) of each of the nv
+// modulation rows (4H floats each) -> tanh(gate), once per step, so the
+// residual epilogues multiply by it directly.
+__global__ void gate_tanh_kernel(float* mod, int H, int nv) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= 2 * H * nv) return;
+  const int v = i / (2 * H), r = i % (2 * H);
+  float* p = mod + (size_t)v * 4 * H + (r < H ? H + r : 3 * H + (r - H));
+  *p = tanhf(*p);
+}
+
+hipError_t launch_gate_tanh(float* mod, int H, int nv, hipStream_t s) {
+  hipLaunchKernelGGL(gate_tanh_kernel, dim3((2 * H * nv + 255) / 256), dim3(256), 0, s, mod, H, nv);
+  return hipGetLastError();
+}
+
 hipError_t launch_temb(float t0, float t1, int D, float base, float* out, hipStream_t s) {
   hipLaunchKernelGGL(temb_kernel, dim3((D / 2 + 255) / 256), dim3(256), 0, s, (double)t0,
                      (double)t1, D, (double)base, out);

@@ -225,7 +225,7 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_kernel(GemmArgs g) {
           } else {
             const float gt = (m < g.n_pre ? g.gate_0 : g.gate_t)[n];
             float* hp = g.Hres + (size_t)m * g.ldh + n;
-            *hp = *hp + tanhf(gt) * v;
+            *hp = *hp + gt * v;
           }
         }
       }
@@ -265,7 +265,7 @@ __device__ __forceinline__ void store_tile(const GemmArgs& g, f32x16 (&acc)[FM][
             } else {
               const float gt = (m < g.n_pre ? g.gate_0 : g.gate_t)[n];
               float* hp = g.Hres + (size_t)m * g.ldh + n;
-              *hp = *hp + tanhf(gt) * v;
+              *hp = *hp + gt * v;
             }
           }
         }
@@ -317,10 +317,10 @@ __device__ __forceinline__ void store_tile(const GemmArgs& g, f32x16 (&acc)[FM][
             const float4 gt = *reinterpret_cast<const float4*>((m < g.n_pre ? g.gate_0 : g.gate_t) + n);
             float4* hp = reinterpret_cast<float4*>(g.Hres + (size_t)m * g.ldh + n);
             float4 hv = *hp;
-            hv.x += tanhf(gt.x) * a4[0];
-            hv.y += tanhf(gt.y) * a4[1];
-            hv.z += tanhf(gt.z) * a4[2];
-            hv.w += tanhf(gt.w) * a4[3];
+            hv.x += gt.x * a4[0];
+            hv.y += gt.y * a4[1];
+            hv.z += gt.z * a4[2];
+            hv.w += gt.w * a4[3];
             *hp = hv;
           }
         }
@@ -591,6 +591,60 @@ __device__ __forceinline__ void store_tile_lds(const GemmArgs& g, f32x16 (&acc)[
   }
 }
 
+// Residual epilogue through LDS (swapped layout): Hres[m, n] += gate[n] *
+// acc, fp32. The 128 x 128 fp32 patch of a wave (64 KB) is staged in two
+// halves of 64 rows x 512 bytes, 16-byte chunks XOR-swizzled by the row;
+// each half is then read back as whole rows (2 rows = 1 KB per instruction).
+// All 32 Hres loads of a half are issued before any is used, so a wave keeps
+// 32 KB of residual reads in flight.
+__device__ __forceinline__ void store_tile_lds_resid(const GemmArgs& g, f32x16 (&acc)[4][4], int m0,
+                                                     int n0, int wm, int wn, int lane, char* reg) {
+  const int lrow = lane & 31, lhalf = lane >> 5;
+  const int cc = lane & 31;
+  const int n = n0 + wn * 128 + 4 * cc;
+  const float4 gate_t = *reinterpret_cast<const float4*>(g.gate_t + n);
+  const float4 gate_0 = *reinterpret_cast<const float4*>(g.gate_0 + n);
+#pragma unroll
+  for (int hf = 0; hf < 2; ++hf) {
+    const int mb = m0 + wm * 128 + hf * 64 + (lane >> 5);
+    float4 hv[32];
+#pragma unroll
+    for (int t = 0; t < 32; ++t) {
+      const int m = mb + 2 * t;
+      hv[t] = m < g.M ? *reinterpret_cast<const float4*>(g.Hres + (size_t)m * g.ldh + n)
+                      : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+#pragma unroll
+    for (int ii = 0; ii < 2; ++ii) {
+      const int i = 2 * hf + ii;
+      const int row = ii * 32 + lrow;
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int k = (8 * j + 2 * q + lhalf) ^ (row & 31);
+          *reinterpret_cast<float4*>(reg + row * 512 + k * 16) =
+              make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
+        }
+    }
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+#pragma unroll
+    for (int t = 0; t < 32; ++t) {
+      const int R = 2 * t + (lane >> 5);
+      const float4 a = *reinterpret_cast<const float4*>(reg + R * 512 + ((cc ^ (R & 31)) * 16));
+      const int m = mb + 2 * t;
+      const float4 gt = m < g.n_pre ? gate_0 : gate_t;
+      float4 h = hv[t];
+      h.x += gt.x * a.x;
+      h.y += gt.y * a.y;
+      h.z += gt.z * a.z;
+      h.w += gt.w * a.w;
+      if (m < g.M) *reinterpret_cast<float4*>(g.Hres + (size_t)m * g.ldh + n) = h;
+    }
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);   // reads done before the next half overwrites
+  }
+}
+
 // ---------------------------------------------------------------------------
 // One wave per SIMD: 4 waves (2x2) of 128x128 on the 256x256 block tile, K
 // in stages of 64 (rows of 128 bytes), two 64 KB LDS stages. Per 16-wide K
@@ -756,10 +810,11 @@ __global__ __launch_bounds__(256) void gemm_w4_kernel(GemmArgs g) {
   if (kt < nk) iter(st0, st1, kt);
   __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));   // drain the final (redundant) DMA before exit
 
-  if (SWAP && (EPI == EPI_BF16 || EPI == EPI_SWIGLU)) {
+  if (SWAP && EPI != EPI_F32) {
     lds_barrier();   // every wave is done with the stage buffers
     char* reg = reinterpret_cast<char*>((wave < 2 ? st0 : st1)) + (wave & 1) * 32768;
-    store_tile_lds<(EPI == EPI_SWIGLU ? EPI_SWIGLU : EPI_BF16)>(g, acc, m0, n0, wm, wn, lane, reg);
+    if (EPI == EPI_RESID) store_tile_lds_resid(g, acc, m0, n0, wm, wn, lane, reg);
+    else store_tile_lds<(EPI == EPI_SWIGLU ? EPI_SWIGLU : EPI_BF16)>(g, acc, m0, n0, wm, wn, lane, reg);
   } else {
     store_tile<FM, FN, TM, TN, EPI, SWAP>(g, acc, m0, n0, wm, wn, lrow, lhalf);
   }

@@ -29,8 +29,8 @@ struct GemmArgs {
   int M, N, K;                      // N = packed width (2F for SwiGLU)
   void* C; int ldc;                 // output (act_t, or f32 for EPI_F32)
   float* Hres; int ldh;             // residual stream for EPI_RESID
-  const float* gate_t;              // [N] gate row of target / current-t tokens
-  const float* gate_0;              // [N] gate row of prefix tokens (t = 0)
+  const float* gate_t;              // [N] tanh(gate) of target / current-t tokens
+  const float* gate_0;              // [N] tanh(gate) of prefix tokens (t = 0)
   int n_pre;                        // rows < n_pre use gate_0
 };
 
@@ -77,6 +77,8 @@ hipError_t launch_gemv(const uint16_t* W, int O, int I, const float* X, int ldx,
                        float* Y, int ldy, float* Ys, hipStream_t s);
 // [cos(t_v f_i), sin(t_v f_i)], f_i = base^(-2i/D), computed in double.
 hipError_t launch_temb(float t0, float t1, int D, float base, float* out, hipStream_t s);
+// tanh of the gate sections of nv modulation rows [scale1 | gate1 | scale2 | gate2].
+hipError_t launch_gate_tanh(float* mod, int H, int nv, hipStream_t s);
 // hidden[i][n] = Σ_c W[n][c] x[i][c]; W bf16 [H, 64], x f32 [n, 64].
 hipError_t launch_img_in(const uint16_t* W, const float* x, int n, int H, float* out, int ldo,
                          hipStream_t s);
