@@ -52,6 +52,32 @@ __device__ __forceinline__ void load_act2(const act_t* p, float& a, float& b) {
   a = bf2f((bf16_t)(v & 0xffff)); b = bf2f((bf16_t)(v >> 16));
 #endif
 }
+// 8 consecutive activations <-> floats (16-byte aligned for bf16, 32 for fp32).
+__device__ __forceinline__ void load_act8(const act_t* p, float (&f)[8]) {
+#ifdef DIT_F32
+  const float4 a = reinterpret_cast<const float4*>(p)[0], b = reinterpret_cast<const float4*>(p)[1];
+  f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w; f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
+#else
+  const u32x4 v = *reinterpret_cast<const u32x4*>(p);
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f[2 * i] = __uint_as_float(w[i] << 16);
+    f[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+  }
+#endif
+}
+__device__ __forceinline__ void store_act8(act_t* p, const float (&f)[8]) {
+#ifdef DIT_F32
+  reinterpret_cast<float4*>(p)[0] = make_float4(f[0], f[1], f[2], f[3]);
+  reinterpret_cast<float4*>(p)[1] = make_float4(f[4], f[5], f[6], f[7]);
+#else
+  u32x4 v;
+  v.x = pack2bf(f[0], f[1]); v.y = pack2bf(f[2], f[3]);
+  v.z = pack2bf(f[4], f[5]); v.w = pack2bf(f[6], f[7]);
+  *reinterpret_cast<u32x4*>(p) = v;
+#endif
+}
 __device__ __forceinline__ void store_act2(act_t* p, float a, float b) {
 #ifdef DIT_F32
   *reinterpret_cast<float2*>(p) = make_float2(a, b);

@@ -69,44 +69,76 @@ __global__ __launch_bounds__(LN_NT) void ln_mod_kernel(const float* __restrict__
 
 // ---------------------------------------------------------------------------
 // QK-RMSNorm + 3D RoPE + cache write. Workgroup = 64 global tokens of one
-// head, 4 waves × 16 tokens; in a wave, lane m owns rotation pair m
-// (dims 2m, 2m+1) of the 128-wide head. V goes through LDS to be written
-// transposed (dim-major) with 16-byte stores.
+// head. A token's 128-wide head row is handled by 16 consecutive lanes, 8
+// dims (16 bytes) each, so a wave covers 4 tokens per pass and the RMS sums
+// reduce over 16 lanes; lane p of a token owns rotation pairs 4p..4p+3
+// (dims 8p..8p+7). V goes through LDS to be written transposed (dim-major)
+// with 16-byte stores.
 constexpr int QK_TOK = 64;
+
+__device__ __forceinline__ float sum16(float v) {
+#pragma unroll
+  for (int o = 8; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
 
 __global__ __launch_bounds__(256) void qknorm_rope_kernel(QkArgs a) {
   __shared__ float vt_s[QK_TOK][129];     // [token][dim], padded
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int p = threadIdx.x & 15;           // 8-dim chunk of the head row
+  const int tl = threadIdx.x >> 4;          // token slot 0..15 of a pass
   const int h = blockIdx.y;
   const int g0 = (a.g_begin / QK_TOK) * QK_TOK + blockIdx.x * QK_TOK;
-  const float wq0 = 1.f + bf2f(a.wq[2 * lane]), wq1 = 1.f + bf2f(a.wq[2 * lane + 1]);
-  const float wk0 = 1.f + bf2f(a.wk[2 * lane]), wk1 = 1.f + bf2f(a.wk[2 * lane + 1]);
+  float wq[8], wk[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    wq[j] = 1.f + bf2f(a.wq[8 * p + j]);
+    wk[j] = 1.f + bf2f(a.wk[8 * p + j]);
+  }
   act_t* kc = a.kc + (size_t)h * a.cap * 128;
 
-  for (int t = wave; t < QK_TOK; t += 4) {
+#pragma unroll
+  for (int pass = 0; pass < QK_TOK / 16; ++pass) {
+    const int t = pass * 16 + tl;
     const int g = g0 + t;
-    if (g < a.g_begin || g >= a.g_end) continue;       // wave-uniform
-    float v0 = 0.f, v1 = 0.f;
-    if (g < a.S) {
-      act_t* row = a.qkv + (size_t)(g - a.q_row0) * a.ld;
-      act_t* qp = row + h * 128 + 2 * lane;
-      const act_t* kp = row + a.H + h * 128 + 2 * lane;
-      load_act2(row + 2 * a.H + h * 128 + 2 * lane, v0, v1);
-      float x0, x1, y0, y1;
-      load_act2(qp, x0, x1);
-      load_act2(kp, y0, y1);
-      const float c = a.cosv[(size_t)g * 64 + lane], s = a.sinv[(size_t)g * 64 + lane];
-      float r = rsqrtf(wave_sum(x0 * x0 + x1 * x1) * (1.f / 128.f) + a.eps);
-      x0 *= r * wq0; x1 *= r * wq1;
-      store_act2(qp, x0 * c - x1 * s, x0 * s + x1 * c);
-      r = rsqrtf(wave_sum(y0 * y0 + y1 * y1) * (1.f / 128.f) + a.eps);
-      y0 *= r * wk0; y1 *= r * wk1;
-      store_act2(kc + (size_t)g * 128 + 2 * lane, y0 * c - y1 * s, y0 * s + y1 * c);
-    } else {
-      store_act2(kc + (size_t)g * 128 + 2 * lane, 0.f, 0.f);   // padding keys
+    float vv[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) vv[j] = 0.f;
+    // the 16 lanes of a token agree on every branch below
+    if (g >= a.g_begin && g < a.g_end) {
+      if (g < a.S) {
+        act_t* row = a.qkv + (size_t)(g - a.q_row0) * a.ld;
+        act_t* qp = row + h * 128 + 8 * p;
+        const act_t* kp = row + a.H + h * 128 + 8 * p;
+        float x[8], y[8];
+        load_act8(row + 2 * a.H + h * 128 + 8 * p, vv);
+        load_act8(qp, x);
+        load_act8(kp, y);
+        const float4 c = *reinterpret_cast<const float4*>(a.cosv + (size_t)g * 64 + 4 * p);
+        const float4 sn = *reinterpret_cast<const float4*>(a.sinv + (size_t)g * 64 + 4 * p);
+        const float cs[4] = {c.x, c.y, c.z, c.w}, ss[4] = {sn.x, sn.y, sn.z, sn.w};
+        float sx = 0.f, sy = 0.f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) { sx += x[j] * x[j]; sy += y[j] * y[j]; }
+        const float rx = rsqrtf(sum16(sx) * (1.f / 128.f) + a.eps);
+        const float ry = rsqrtf(sum16(sy) * (1.f / 128.f) + a.eps);
+        float xo[8], yo[8];
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          const float x0 = x[2 * m] * rx * wq[2 * m], x1 = x[2 * m + 1] * rx * wq[2 * m + 1];
+          const float y0 = y[2 * m] * ry * wk[2 * m], y1 = y[2 * m + 1] * ry * wk[2 * m + 1];
+          xo[2 * m] = x0 * cs[m] - x1 * ss[m];
+          xo[2 * m + 1] = x0 * ss[m] + x1 * cs[m];
+          yo[2 * m] = y0 * cs[m] - y1 * ss[m];
+          yo[2 * m + 1] = y0 * ss[m] + y1 * cs[m];
+        }
+        store_act8(qp, xo);
+        store_act8(kc + (size_t)g * 128 + 8 * p, yo);
+      } else {
+        store_act8(kc + (size_t)g * 128 + 8 * p, vv);   // padding keys (zeros)
+      }
     }
-    vt_s[t][2 * lane] = v0;
-    vt_s[t][2 * lane + 1] = v1;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) vt_s[t][8 * p + j] = vv[j];
   }
   __syncthreads();
   // Vᵀ rows: dim e, keys g0..g0+63; 8 chunks of 8 keys per row
@@ -119,8 +151,7 @@ __global__ __launch_bounds__(256) void qknorm_rope_kernel(QkArgs a) {
     for (int j = 0; j < 8; ++j) vals[j] = vt_s[c * 8 + j][e];
     act_t* dst = vt + (size_t)e * a.cap + k0;
     if (k0 >= a.g_begin && k0 + 8 <= a.g_end) {
-      store_act4(dst, vals[0], vals[1], vals[2], vals[3]);
-      store_act4(dst + 4, vals[4], vals[5], vals[6], vals[7]);
+      store_act8(dst, vals);
     } else {
 #pragma unroll
       for (int j = 0; j < 8; ++j)
