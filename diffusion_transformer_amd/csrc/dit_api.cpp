@@ -94,7 +94,7 @@ dit_status check_seq(const dit_model* m, const dit_seq* s) {
 
 // Workspace plan for n tokens.
 struct Plan {
-  size_t mod, scale_out, temb_e, a1, a1s, temb, tembs, h, x, qkv, attn, ffn, total;
+  size_t mod, scale_out, temb_e, a1, a1s, temb, tembs, h, x, qkv, attn, ffn, part, total;
 };
 Plan plan(const dit_config& c, int n) {
   Plan p{};
@@ -114,6 +114,7 @@ Plan plan(const dit_config& c, int n) {
   p.qkv = take(N * 3 * H * A);
   p.attn = take(N * H * A);
   p.ffn = take(N * F * A);
+  p.part = take(kGemmPartBytes);
   p.total = off;
   return p;
 }
@@ -168,6 +169,7 @@ dit_status run_step(dit_model* m, const dit_seq* seq, bool extract, const float*
   act_t* qkv = reinterpret_cast<act_t*>(w + pl.qkv);
   act_t* att = reinterpret_cast<act_t*>(w + pl.attn);
   act_t* ffn = reinterpret_cast<act_t*>(w + pl.ffn);
+  float* part = reinterpret_cast<float*>(w + pl.part);
   act_t* kbase = static_cast<act_t*>(kv);
   act_t* vbase = kbase + (size_t)L * nh * cap * 128;
   dit_status rc;
@@ -206,6 +208,7 @@ dit_status run_step(dit_model* m, const dit_seq* seq, bool extract, const float*
       GemmArgs g{};
       g.A = xb; g.lda = H; g.B = U(m->qkv[l]); g.ldb = H; g.M = N; g.N = 3 * H; g.K = H;
       g.C = qkv; g.ldc = 3 * H;
+      g.part = part; g.part_bytes = kGemmPartBytes;
       LAUNCH(launch_gemm(g, EPI_BF16, st), "gemm qkv");
     }
     {
@@ -232,6 +235,7 @@ dit_status run_step(dit_model* m, const dit_seq* seq, bool extract, const float*
       GemmArgs g{};
       g.A = att; g.lda = H; g.B = U(m->o[l]); g.ldb = H; g.M = N; g.N = H; g.K = H;
       g.Hres = hbuf; g.ldh = H; g.gate_t = row_t + H; g.gate_0 = row_0 + H; g.n_pre = n_pre;
+      g.part = part; g.part_bytes = kGemmPartBytes;
       LAUNCH(launch_gemm(g, EPI_RESID, st), "gemm o");
     }
     {
@@ -243,6 +247,7 @@ dit_status run_step(dit_model* m, const dit_seq* seq, bool extract, const float*
       GemmArgs g{};
       g.A = xb; g.lda = H; g.B = U(m->gate[l]); g.B2 = U(m->up[l]); g.ldb = H;
       g.M = N; g.N = 2 * F; g.K = H; g.C = ffn; g.ldc = F;
+      g.part = part; g.part_bytes = kGemmPartBytes;
       LAUNCH(launch_gemm(g, EPI_SWIGLU, st), "gemm gate/up");
     }
     {
@@ -250,6 +255,7 @@ dit_status run_step(dit_model* m, const dit_seq* seq, bool extract, const float*
       GemmArgs g{};
       g.A = ffn; g.lda = F; g.B = U(m->down[l]); g.ldb = F; g.M = N; g.N = H; g.K = F;
       g.Hres = hbuf; g.ldh = H; g.gate_t = row_t + 3 * H; g.gate_0 = row_0 + 3 * H; g.n_pre = n_pre;
+      g.part = part; g.part_bytes = kGemmPartBytes;
       LAUNCH(launch_gemm(g, EPI_RESID, st), "gemm down");
     }
   }
@@ -519,6 +525,19 @@ dit_status dit_debug_gemm(const void* A, const void* B, void* C, int M, int N, i
   g.M = M; g.N = N; g.K = K; g.C = C; g.ldc = N;
   if (variant < 0 || variant > 16) return fail(DIT_ERR_ARG, "unknown GEMM variant %d", variant);
   if (variant == 0) return hip_check(launch_gemm(g, EPI_BF16, static_cast<hipStream_t>(stream)), "debug gemm");
+  if (variant == 6) {
+    // split-K path: scratch for up to 4 splits of the last 256-row block,
+    // allocated here and released after the launch completes
+    const size_t bytes = (size_t)4 * 256 * N * 4;
+    float* part = nullptr;
+    dit_status rc = hip_check(hipMalloc(&part, bytes), "debug gemm scratch");
+    if (rc) return rc;
+    g.part = part; g.part_bytes = bytes;
+    rc = hip_check(launch_gemm_variant(g, variant, static_cast<hipStream_t>(stream)), "debug gemm");
+    const dit_status rs = hip_check(hipStreamSynchronize(static_cast<hipStream_t>(stream)), "debug gemm sync");
+    hipFree(part);
+    return rc ? rc : rs;
+  }
   return hip_check(launch_gemm_variant(g, variant, static_cast<hipStream_t>(stream)), "debug gemm");
 #endif
 }

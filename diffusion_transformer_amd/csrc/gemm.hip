@@ -591,19 +591,28 @@ __device__ __forceinline__ void store_tile_lds(const GemmArgs& g, f32x16 (&acc)[
   }
 }
 
-// Residual epilogue through LDS (swapped layout): Hres[m, n] += gate[n] *
+// fp32 epilogue through LDS (swapped layout): Hres[m, n] += gate[n] *
 // acc, fp32. The 128 x 128 fp32 patch of a wave (64 KB) is staged in two
 // halves of 64 rows x 512 bytes, 16-byte chunks XOR-swizzled by the row;
 // each half is then read back as whole rows (2 rows = 1 KB per instruction).
 // All 32 Hres loads of a half are issued before any is used, so a wave keeps
 // 32 KB of residual reads in flight.
-__device__ __forceinline__ void store_tile_lds_resid(const GemmArgs& g, f32x16 (&acc)[4][4], int m0,
-                                                     int n0, int wm, int wn, int lane, char* reg) {
+// With PART, the patch is instead stored as fp32 partial sums of K split
+// `split` into part[split][M][N] (no residual read).
+template <bool PART>
+__device__ __forceinline__ void store_tile_lds_f32(const GemmArgs& g, f32x16 (&acc)[4][4], int m0,
+                                                   int n0, int wm, int wn, int lane, char* reg,
+                                                   int split) {
   const int lrow = lane & 31, lhalf = lane >> 5;
   const int cc = lane & 31;
   const int n = n0 + wn * 128 + 4 * cc;
-  const float4 gate_t = *reinterpret_cast<const float4*>(g.gate_t + n);
-  const float4 gate_0 = *reinterpret_cast<const float4*>(g.gate_0 + n);
+  float4 gate_t = make_float4(0.f, 0.f, 0.f, 0.f), gate_0 = gate_t;
+  if (!PART) {
+    gate_t = *reinterpret_cast<const float4*>(g.gate_t + n);
+    gate_0 = *reinterpret_cast<const float4*>(g.gate_0 + n);
+  }
+  float* out = PART ? g.part + (size_t)split * g.M * g.N : g.Hres;
+  const int ldo = PART ? g.N : g.ldh;
 #pragma unroll
   for (int hf = 0; hf < 2; ++hf) {
     const int mb = m0 + wm * 128 + hf * 64 + (lane >> 5);
@@ -611,8 +620,8 @@ __device__ __forceinline__ void store_tile_lds_resid(const GemmArgs& g, f32x16 (
 #pragma unroll
     for (int t = 0; t < 32; ++t) {
       const int m = mb + 2 * t;
-      hv[t] = m < g.M ? *reinterpret_cast<const float4*>(g.Hres + (size_t)m * g.ldh + n)
-                      : make_float4(0.f, 0.f, 0.f, 0.f);
+      hv[t] = (!PART && m < g.M) ? *reinterpret_cast<const float4*>(g.Hres + (size_t)m * g.ldh + n)
+                                 : make_float4(0.f, 0.f, 0.f, 0.f);
     }
 #pragma unroll
     for (int ii = 0; ii < 2; ++ii) {
@@ -633,13 +642,17 @@ __device__ __forceinline__ void store_tile_lds_resid(const GemmArgs& g, f32x16 (
       const int R = 2 * t + (lane >> 5);
       const float4 a = *reinterpret_cast<const float4*>(reg + R * 512 + ((cc ^ (R & 31)) * 16));
       const int m = mb + 2 * t;
-      const float4 gt = m < g.n_pre ? gate_0 : gate_t;
       float4 h = hv[t];
-      h.x += gt.x * a.x;
-      h.y += gt.y * a.y;
-      h.z += gt.z * a.z;
-      h.w += gt.w * a.w;
-      if (m < g.M) *reinterpret_cast<float4*>(g.Hres + (size_t)m * g.ldh + n) = h;
+      if (PART) {
+        h = a;
+      } else {
+        const float4 gt = m < g.n_pre ? gate_0 : gate_t;
+        h.x += gt.x * a.x;
+        h.y += gt.y * a.y;
+        h.z += gt.z * a.z;
+        h.w += gt.w * a.w;
+      }
+      if (m < g.M) *reinterpret_cast<float4*>(out + (size_t)m * ldo + n) = h;
     }
     __builtin_amdgcn_s_waitcnt(kWaitLgkm0);   // reads done before the next half overwrites
   }
@@ -659,7 +672,7 @@ __device__ __forceinline__ void store_tile_lds_resid(const GemmArgs& g, f32x16 (
 // LDS rows hold 64 bf16 of K (8 chunks of 16 B); chunk c of row r sits at
 // c ^ ((r/2)%8), which puts the 16 rows one ds_read_b128 phase touches on
 // all 64 banks exactly once.
-template <int EPI, bool SWAP>
+template <int EPI, bool SWAP, bool PACKED = (EPI == EPI_SWIGLU)>
 __global__ __launch_bounds__(256) void gemm_w4_kernel(GemmArgs g) {
   constexpr int BM = 256, BN = 256, SBK = 64;
   constexpr int WN = 2, TM = 128, TN = 128, FM = 4, FN = 4;
@@ -672,12 +685,17 @@ __global__ __launch_bounds__(256) void gemm_w4_kernel(GemmArgs g) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / WN, wn = wave % WN;
 
+  // Grid = tiles x splits (splits = 1 unless EPI_PART): block b works on
+  // tile b % tiles over K range split * K/splits .. (split+1) * K/splits.
   const int ntm = (g.M + BM - 1) / BM;
   const int ntn = g.N / BN;
-  const int nblk = ntm * ntn;
+  const int ntiles = ntm * ntn;
+  const int nblk = gridDim.x;
   int b = blockIdx.x;
   const int per = nblk >> 3;
   if (b < per * 8) b = (b & 7) * per + (b >> 3);
+  const int split = EPI == EPI_PART ? b / ntiles : 0;
+  b -= split * ntiles;
   const int in_group = GROUP_M * ntn;
   const int gid = b / in_group;
   const int first = gid * GROUP_M;
@@ -685,6 +703,8 @@ __global__ __launch_bounds__(256) void gemm_w4_kernel(GemmArgs g) {
   const int tm = first + (b % in_group) % gsz;
   const int tn = (b % in_group) / gsz;
   const int m0 = tm * BM, n0 = tn * BN;
+  const int klen = EPI == EPI_PART ? g.K / g.splits : g.K;
+  const int kbeg = split * klen;
 
   // DMA: an instruction moves an 8-row block (1 KB); lane l fills row l/8,
   // physical chunk l%8, which holds logical chunk (l%8) ^ ((row/2)%8). Wave
@@ -695,7 +715,7 @@ __global__ __launch_bounds__(256) void gemm_w4_kernel(GemmArgs g) {
   const __amdgpu_buffer_rsrc_t rA = make_rsrc(
       g.A + (size_t)m0 * g.lda, (uint32_t)min((size_t)(g.M - m0) * g.lda * 2, (size_t)0xFFFFFFF0u));
   __amdgpu_buffer_rsrc_t rG, rU;
-  if (EPI == EPI_SWIGLU) {
+  if (PACKED) {
     const size_t bytes = min((size_t)(BN / 2) * g.ldb * 2, (size_t)0xFFFFFFF0u);
     rG = make_rsrc(g.B + (size_t)(n0 >> 1) * g.ldb, (uint32_t)bytes);
     rU = make_rsrc(g.B2 + (size_t)(n0 >> 1) * g.ldb, (uint32_t)bytes);
@@ -704,13 +724,13 @@ __global__ __launch_bounds__(256) void gemm_w4_kernel(GemmArgs g) {
   }
   const uint32_t aoff = (uint32_t)((lr * g.lda + lc * 8) * 2);
   const uint32_t boff = (uint32_t)((lr * g.ldb + lc * 8) * 2);
-  const int nk = g.K / SBK;
+  const int nk = klen / SBK;
 
   // B block bb = 4j + w holds packed columns 8bb .. 8bb+7. For SwiGLU the
   // packed column p is feature 32*(p/64) + p%32 of gate (p/32 even) or up
   // (p/32 odd): block 4j + w is rows 32*(j/2) + 8w .. +7 of matrix j%2.
   auto dma = [&](u32x4* stg, int kt) {
-    const uint32_t ko = (uint32_t)(kt * SBK * 2);
+    const uint32_t ko = (uint32_t)((kbeg + kt * SBK) * 2);
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const int blk = 4 * j + wave;
@@ -721,7 +741,7 @@ __global__ __launch_bounds__(256) void gemm_w4_kernel(GemmArgs g) {
     for (int j = 0; j < 8; ++j) {
       const int bb = 4 * j + wave;
       u32x4* dst = stg + (BM / 8 + bb) * 64;
-      if (EPI == EPI_SWIGLU) {
+      if (PACKED) {
         const uint32_t so = ko + (uint32_t)((32 * (j >> 1) + 8 * wave) * g.ldb * 2);
         __builtin_amdgcn_raw_ptr_buffer_load_lds((j & 1) ? rU : rG, LDSP(dst), 16, boff, so, 0, 0);
       } else {
@@ -813,18 +833,115 @@ __global__ __launch_bounds__(256) void gemm_w4_kernel(GemmArgs g) {
   if (SWAP && EPI != EPI_F32) {
     lds_barrier();   // every wave is done with the stage buffers
     char* reg = reinterpret_cast<char*>((wave < 2 ? st0 : st1)) + (wave & 1) * 32768;
-    if (EPI == EPI_RESID) store_tile_lds_resid(g, acc, m0, n0, wm, wn, lane, reg);
+    if (EPI == EPI_RESID) store_tile_lds_f32<false>(g, acc, m0, n0, wm, wn, lane, reg, 0);
+    else if (EPI == EPI_PART) store_tile_lds_f32<true>(g, acc, m0, n0, wm, wn, lane, reg, split);
     else store_tile_lds<(EPI == EPI_SWIGLU ? EPI_SWIGLU : EPI_BF16)>(g, acc, m0, n0, wm, wn, lane, reg);
   } else {
     store_tile<FM, FN, TM, TN, EPI, SWAP>(g, acc, m0, n0, wm, wn, lrow, lhalf);
   }
 }
 
-template <int EPI, bool SWAP>
+template <int EPI, bool SWAP, bool PACKED = (EPI == EPI_SWIGLU)>
 hipError_t run_w4(const GemmArgs& g, hipStream_t s) {
-  const int nblk = ((g.M + 255) / 256) * (g.N / 256);
-  hipLaunchKernelGGL((gemm_w4_kernel<EPI, SWAP>), dim3(nblk), dim3(256), 0, s, g);
+  const int nblk = ((g.M + 255) / 256) * (g.N / 256) * (EPI == EPI_PART ? g.splits : 1);
+  hipLaunchKernelGGL((gemm_w4_kernel<EPI, SWAP, PACKED>), dim3(nblk), dim3(256), 0, s, g);
   return hipGetLastError();
+}
+
+// Sum of the K-split partial sums part[0..splits) of a (tail) GEMM, then the
+// epilogue EPI on it. One thread per 4 consecutive output columns of a row.
+template <int EPI>
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(GemmArgs g) {
+  const int outc = EPI == EPI_SWIGLU ? g.N / 2 : g.N;
+  const int per_row = outc / 4;
+  const long long q = (long long)blockIdx.x * 256 + threadIdx.x;
+  const int m = (int)(q / per_row);
+  if (m >= g.M) return;
+  const int c = (int)(q - (long long)m * per_row) * 4;
+  const size_t MN = (size_t)g.M * g.N;
+  auto sum4 = [&](int col) {
+    float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int sp = 0; sp < g.splits; ++sp) {
+      const float4 v = *reinterpret_cast<const float4*>(g.part + sp * MN + (size_t)m * g.N + col);
+      a.x += v.x; a.y += v.y; a.z += v.z; a.w += v.w;
+    }
+    return a;
+  };
+  if (EPI == EPI_SWIGLU) {
+    // output feature c is packed column 64*(c/32) + c%32 (gate); up is 32 later
+    const int pg = 64 * (c >> 5) + (c & 31);
+    const float4 gv = sum4(pg), uv = sum4(pg + 32);
+    const float o0 = gv.x / (1.f + __expf(-gv.x)) * uv.x, o1 = gv.y / (1.f + __expf(-gv.y)) * uv.y;
+    const float o2 = gv.z / (1.f + __expf(-gv.z)) * uv.z, o3 = gv.w / (1.f + __expf(-gv.w)) * uv.w;
+    u32x2 w;
+    w.x = pack2bf(o0, o1);
+    w.y = pack2bf(o2, o3);
+    *reinterpret_cast<u32x2*>(reinterpret_cast<bf16_t*>(g.C) + (size_t)m * g.ldc + c) = w;
+  } else if (EPI == EPI_BF16) {
+    const float4 a = sum4(c);
+    u32x2 w;
+    w.x = pack2bf(a.x, a.y);
+    w.y = pack2bf(a.z, a.w);
+    *reinterpret_cast<u32x2*>(reinterpret_cast<bf16_t*>(g.C) + (size_t)m * g.ldc + c) = w;
+  } else {
+    const float4 a = sum4(c);
+    const float4 gt = *reinterpret_cast<const float4*>((m < g.n_pre ? g.gate_0 : g.gate_t) + c);
+    float4* hp = reinterpret_cast<float4*>(g.Hres + (size_t)m * g.ldh + c);
+    float4 h = *hp;
+    h.x += gt.x * a.x;
+    h.y += gt.y * a.y;
+    h.z += gt.z * a.z;
+    h.w += gt.w * a.w;
+    *hp = h;
+  }
+}
+
+template <int EPI>
+hipError_t run_reduce(const GemmArgs& g, hipStream_t s) {
+  const long long n4 = (long long)g.M * ((EPI == EPI_SWIGLU ? g.N / 2 : g.N) / 4);
+  hipLaunchKernelGGL((splitk_reduce_kernel<EPI>), dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, s, g);
+  return hipGetLastError();
+}
+
+template <int EPI>
+hipError_t run_main(const GemmArgs& g, hipStream_t s) { return run_w4<EPI, true>(g, s); }
+
+hipError_t run_epi(const GemmArgs& g, int epi, hipStream_t s) {
+  switch (epi) {
+    case EPI_BF16: return run_main<EPI_BF16>(g, s);
+    case EPI_RESID: return run_main<EPI_RESID>(g, s);
+    case EPI_SWIGLU: return run_main<EPI_SWIGLU>(g, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+// The last r row blocks (256 rows each) are computed as `splits` K-split
+// GEMMs into g.part and reduced with the epilogue; the rows before them in
+// one ordinary launch.
+hipError_t launch_gemm_split(const GemmArgs& g, int epi, int r, int splits, hipStream_t s) {
+  const int ntm = (g.M + 255) / 256;
+  GemmArgs gm = g;
+  gm.M = (ntm - r) * 256;
+  if (gm.M > 0) {
+    const hipError_t e = run_epi(gm, epi, s);
+    if (e != hipSuccess) return e;
+  }
+  GemmArgs gt = g;
+  gt.A = g.A + (size_t)gm.M * g.lda;
+  gt.M = g.M - gm.M;
+  if (g.C) gt.C = reinterpret_cast<bf16_t*>(g.C) + (size_t)gm.M * g.ldc;
+  if (g.Hres) gt.Hres = g.Hres + (size_t)gm.M * g.ldh;
+  gt.n_pre = g.n_pre - gm.M;
+  gt.splits = splits;
+  // the partial sums of a SwiGLU GEMM keep its packed gate/up columns
+  hipError_t e = epi == EPI_SWIGLU ? run_w4<EPI_PART, true, true>(gt, s) : run_w4<EPI_PART, true, false>(gt, s);
+  if (e != hipSuccess) return e;
+  switch (epi) {
+    case EPI_BF16: return run_reduce<EPI_BF16>(gt, s);
+    case EPI_RESID: return run_reduce<EPI_RESID>(gt, s);
+    case EPI_SWIGLU: return run_reduce<EPI_SWIGLU>(gt, s);
+  }
+  return hipErrorInvalidValue;
 }
 
 template <int WM, int WN, int EPI, bool SWAP = true, int GM = GROUP_M>
@@ -856,18 +973,33 @@ hipError_t launch_gemm_variant(const GemmArgs& g, int variant, hipStream_t s) {
     case 3: return run_dma<2, 2, EPI_BF16, false>(g, s);       // direct-to-LDS, 4 waves of 128x128
     case 4: return run_w4<EPI_BF16, false>(g, s);              // 4 waves of 128x128, K stages of 64
     case 5: return run_dma<2, 4, EPI_BF16, false>(g, s);       // 8 waves of 128x64
+    case 6: {                                                  // split-K path for the last row block
+      int sp = 1;
+      while (sp < 4 && (g.K / 64) % (2 * sp) == 0) sp *= 2;
+      return launch_gemm_split(g, EPI_BF16, 1, sp, s);
+    }
   }
   return hipErrorInvalidValue;
 }
 
 hipError_t launch_gemm(const GemmArgs& g, int epi, hipStream_t s) {
-  switch (epi) {
-    case EPI_BF16: return run_w4<EPI_BF16, true>(g, s);
-    case EPI_RESID: return run_w4<EPI_RESID, true>(g, s);
-    case EPI_SWIGLU: return run_w4<EPI_SWIGLU, true>(g, s);
-    case EPI_F32: return run<64, 64, 2, 2, EPI_F32>(g, s);
+  if (epi == EPI_F32) return run<64, 64, 2, 2, EPI_F32>(g, s);
+  // One block tile per CU per round: when the tiles leave the last round
+  // mostly idle and dropping the last r row blocks makes the rest whole
+  // rounds, those r row blocks are spread over the idle CUs by splitting K.
+  const int ntm = (g.M + 255) / 256, ntn = g.N / 256;
+  constexpr int kRound = 256;
+  if (g.part && (ntm * ntn) % kRound) {
+    int r = 0;
+    for (int rr = 1; rr < ntm && rr * ntn <= kRound; ++rr)
+      if (((ntm - rr) * ntn) % kRound == 0) { r = rr; break; }
+    int splits = 1;
+    while (r && 2 * splits * r * ntn <= kRound && (g.K / 64) % (2 * splits) == 0 &&
+           (size_t)(2 * splits) * g.N * (size_t)(g.M - (ntm - r) * 256) * 4 <= g.part_bytes)
+      splits *= 2;
+    if (r && splits > 1) return launch_gemm_split(g, epi, r, splits, s);
   }
-  return hipErrorInvalidValue;
+  return run_epi(g, epi, s);
 }
 
 }  // namespace dit

@@ -18,8 +18,9 @@ typedef uint16_t act_t;
 enum GemmEpi {
   EPI_BF16 = 0,    // C (bf16) = A·Bᵀ
   EPI_F32 = 1,     // C (f32)  = A·Bᵀ
-  EPI_RESID = 2,   // Hres (f32) += tanh(gate[row]) ⊙ A·Bᵀ, gate row by n_pre split
-  EPI_SWIGLU = 3   // C (bf16)[:, f] = SiLU(A·Gᵀ)[f] · (A·Uᵀ)[f]  (B = gate, B2 = up)
+  EPI_RESID = 2,   // Hres (f32) += g[row] ⊙ A·Bᵀ, g = tanh(gate) chosen by the n_pre split
+  EPI_SWIGLU = 3,  // C (bf16)[:, f] = SiLU(A·Gᵀ)[f] · (A·Uᵀ)[f]  (B = gate, B2 = up)
+  EPI_PART = 4     // internal: fp32 partial sums of one K split -> part[split][M][N]
 };
 
 struct GemmArgs {
@@ -32,7 +33,12 @@ struct GemmArgs {
   const float* gate_t;              // [N] tanh(gate) of target / current-t tokens
   const float* gate_0;              // [N] tanh(gate) of prefix tokens (t = 0)
   int n_pre;                        // rows < n_pre use gate_0
+  float* part; size_t part_bytes;   // scratch for split-K partial sums (may be null)
+  int splits;                       // internal: K splits of an EPI_PART launch
 };
+// Bytes of split-K scratch the GEMM launcher can use: at most one round of
+// 256 tiles of 256 x 256 fp32 partial sums.
+constexpr size_t kGemmPartBytes = (size_t)256 * 256 * 256 * 4;
 
 hipError_t launch_gemm(const GemmArgs& g, int epi, hipStream_t s);
 hipError_t launch_gemm_variant(const GemmArgs& g, int variant, hipStream_t s);

@@ -209,7 +209,9 @@ dit_status dit_debug_attention(const dit_seq* seq, int n_heads, const void* q, i
 /* Test hook: C[M,N] = A[M,K] · B[N,K]ᵀ with the step's bf16 MFMA GEMM
  * (A, B bf16, C bf16). N must be a multiple of 256 and K of 64.
  * variant 0 = the tile configuration the step uses for its bf16-output
- * GEMMs; 1.. = alternative tile configurations (DIT_ERR_ARG if unknown). */
+ * GEMMs; 1.. = alternative tile configurations (DIT_ERR_ARG if unknown);
+ * 6 = the split-K path for the last 256-row block (the library allocates
+ * and frees its partial-sum scratch and waits for the stream). */
 dit_status dit_debug_gemm(const void* A, const void* B, void* C, int M, int N, int K,
                           int variant, void* stream);
 

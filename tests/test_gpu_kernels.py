@@ -21,7 +21,7 @@ def dev():
     return torch.device("cuda:0")
 
 
-@pytest.mark.parametrize("variant", [0, 1, 2, 3, 4, 5])
+@pytest.mark.parametrize("variant", [0, 1, 2, 3, 4, 5, 6])
 @pytest.mark.parametrize("M,N,K", [(32, 256, 64), (300, 512, 128), (257, 768, 256), (600, 1024, 512)])
 def test_gemm_exact_small_integers(dev, M, N, K, variant):
     """Entries in {-1, 0, 1}: every partial sum is an integer of magnitude
