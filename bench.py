@@ -26,6 +26,9 @@ PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 GEMM_SRC = os.path.join(ROOT, "diffusion_transformer_amd", "csrc", "gemm.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gemm_gateup_c2_cached.json")
+# the dominant kernel of the cached step: the fused gate/up GEMM + SwiGLU
+GATEUP_KERNEL = "gemm_w4_kernel<3, true, true>"
+GATEUP_LABEL = "gemm_w4_kernel<SwiGLU> (gate/up, 256x256 tiles, 4 waves of 128x128)"
 
 
 def source_sha(path):
@@ -69,8 +72,7 @@ def summarize_profiles(trace_dir, fetch_dir, write_dir, command, out_md, out_jso
         known_kib = (1 << 28) * (4 if name == "FETCH_SIZE" else 2) / 1024.0
         factor = known_kib / float(calib["Counter_Value"])
         gu = [float(r["Counter_Value"]) for r in rows
-              if "gemm_kernel<256, 256, 2, 4, 3>" in r["Kernel_Name"]
-              and int(r["Grid_Size"]) == 2048 * 512]
+              if GATEUP_KERNEL in r["Kernel_Name"] and int(r["Grid_Size"]) == 2048 * 256]
         res[name] = {"calib_kib": float(calib["Counter_Value"]), "known_kib": known_kib,
                      "factor": factor, "gateup_kib_avg": sum(gu) / len(gu), "n": len(gu)}
     fb = res["FETCH_SIZE"]["gateup_kib_avg"] * res["FETCH_SIZE"]["factor"] * 1024
@@ -90,7 +92,7 @@ def summarize_profiles(trace_dir, fetch_dir, write_dir, command, out_md, out_jso
     lines += ["", f"Total {fb + wb:.4g} bytes per launch vs {alg:.4g} algorithmic "
                   f"(A 32 MiB + B 256 MiB read, 128 MiB written): x{(fb + wb) / alg:.2f}."]
     open(out_md, "w").write("\n".join(lines) + "\n")
-    json.dump({"kernel": "gemm_kernel<256,256,2,4,SwiGLU> gate/up, cached c2 (M=4096)",
+    json.dump({"kernel": GATEUP_LABEL + ", cached c2 (M=4096)",
                "source_sha256": source_sha(GEMM_SRC), "fetch": res["FETCH_SIZE"],
                "write": res["WRITE_SIZE"], "bytes_per_launch": fb + wb,
                "algorithmic_bytes": alg}, open(out_json, "w"), indent=1)
@@ -227,7 +229,7 @@ def main():
     gu_tflops = fl["gemm_gateup"] / (gu_avg / 1e3) / 1e12
     roofline = {"bound": "mfma", "achieved": round(gu_tflops, 1), "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(gu_tflops / PEAK_BF16_TFLOPS, 4),
-                "traffic": measured_traffic(), "kernel": "gemm_kernel<256,256,2,4,SwiGLU> (gate/up)",
+                "traffic": measured_traffic(), "kernel": GATEUP_LABEL,
                 "avg_launch_ms": round(gu_avg, 4), "launches": gu_n}
 
     if args.calib_copy:
