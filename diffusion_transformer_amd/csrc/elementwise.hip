@@ -10,60 +10,71 @@ namespace dit {
 namespace {
 
 // ---------------------------------------------------------------------------
-// x = LN(h)·(1 + scale[row]) -> bf16. One 256-thread workgroup per row; the
-// row (H <= 4096 floats) stays in registers between the two reductions.
+// x = LN(h)·(1 + scale[row]) -> act_t. A 256-thread workgroup handles
+// LN_ROWS consecutive rows; each row (H <= 4096 floats) stays in registers
+// between the two reductions, and the next row's loads are issued before
+// the current row is reduced, so every workgroup keeps a row in flight.
 constexpr int LN_NT = 256;
 constexpr int LN_MAXV = 4;   // float4 per thread -> H <= 4096
+constexpr int LN_ROWS = 2;
 
-__device__ __forceinline__ float block_sum(float v, float* sh) {
-  v = wave_sum(v);
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  __syncthreads();
-  if (lane == 0) sh[wave] = v;
-  __syncthreads();
-  return sh[0] + sh[1] + sh[2] + sh[3];
-}
-
-__global__ __launch_bounds__(LN_NT) void ln_mod_kernel(const float* __restrict__ h, int ldh, int H,
-                                                       const float* __restrict__ scale_t,
+__global__ __launch_bounds__(LN_NT) void ln_mod_kernel(const float* __restrict__ h, int ldh, int rows,
+                                                       int H, const float* __restrict__ scale_t,
                                                        const float* __restrict__ scale_0, int n_pre,
                                                        float eps, act_t* __restrict__ out, int ldo) {
-  __shared__ float sh[4];
-  const int row = blockIdx.x;
-  const float4* hp = reinterpret_cast<const float4*>(h + (size_t)row * ldh);
+  __shared__ float sh[2][2][4];   // [row parity][sum, sum of squares][wave]
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int nv = H >> 2;
-  float4 v[LN_MAXV];
-  float s = 0.f;
+  const int r0 = blockIdx.x * LN_ROWS;
+  float4 cur[LN_MAXV], nxt[LN_MAXV];
+  auto load = [&](float4 (&v)[LN_MAXV], int row) {
+    const float4* hp = reinterpret_cast<const float4*>(h + (size_t)row * ldh);
 #pragma unroll
-  for (int i = 0; i < LN_MAXV; ++i) {
-    const int c = threadIdx.x + i * LN_NT;
-    if (c < nv) {
-      v[i] = hp[c];
-      s += (v[i].x + v[i].y) + (v[i].z + v[i].w);
+    for (int i = 0; i < LN_MAXV; ++i) {
+      const int c = threadIdx.x + i * LN_NT;
+      v[i] = c < nv ? hp[c] : make_float4(0.f, 0.f, 0.f, 0.f);
     }
-  }
-  const float mean = block_sum(s, sh) / (float)H;
-  float q = 0.f;
+  };
+  load(cur, r0);   // r0 < rows: the grid covers ceil(rows / LN_ROWS) workgroups
 #pragma unroll
-  for (int i = 0; i < LN_MAXV; ++i) {
-    const int c = threadIdx.x + i * LN_NT;
-    if (c < nv) {
-      const float a = v[i].x - mean, b = v[i].y - mean, cc = v[i].z - mean, d = v[i].w - mean;
-      q += (a * a + b * b) + (cc * cc + d * d);
-    }
-  }
-  const float var = block_sum(q, sh) / (float)H;
-  const float rstd = rsqrtf(var + eps);
-  const float4* sp = reinterpret_cast<const float4*>(row < n_pre ? scale_0 : scale_t);
-  act_t* op = out + (size_t)row * ldo;
+  for (int rr = 0; rr < LN_ROWS; ++rr) {
+    const int row = r0 + rr;
+    if (row >= rows) break;                               // uniform over the workgroup
+    if (rr + 1 < LN_ROWS && row + 1 < rows) load(nxt, row + 1);
+    float s = 0.f;
 #pragma unroll
-  for (int i = 0; i < LN_MAXV; ++i) {
-    const int c = threadIdx.x + i * LN_NT;
-    if (c < nv) {
-      const float4 sc = sp[c];
-      store_act4(op + 4 * c, (v[i].x - mean) * rstd * (1.f + sc.x), (v[i].y - mean) * rstd * (1.f + sc.y),
-                 (v[i].z - mean) * rstd * (1.f + sc.z), (v[i].w - mean) * rstd * (1.f + sc.w));
+    for (int i = 0; i < LN_MAXV; ++i) s += (cur[i].x + cur[i].y) + (cur[i].z + cur[i].w);
+    s = wave_sum(s);
+    if (lane == 0) sh[rr & 1][0][wave] = s;
+    __syncthreads();
+    const float mean = (sh[rr & 1][0][0] + sh[rr & 1][0][1] + sh[rr & 1][0][2] + sh[rr & 1][0][3]) / (float)H;
+    float q = 0.f;
+#pragma unroll
+    for (int i = 0; i < LN_MAXV; ++i) {
+      const int c = threadIdx.x + i * LN_NT;
+      if (c < nv) {
+        const float a = cur[i].x - mean, b = cur[i].y - mean, cc = cur[i].z - mean, d = cur[i].w - mean;
+        q += (a * a + b * b) + (cc * cc + d * d);
+      }
     }
+    q = wave_sum(q);
+    if (lane == 0) sh[rr & 1][1][wave] = q;
+    __syncthreads();
+    const float var = (sh[rr & 1][1][0] + sh[rr & 1][1][1] + sh[rr & 1][1][2] + sh[rr & 1][1][3]) / (float)H;
+    const float rstd = rsqrtf(var + eps);
+    const float4* sp = reinterpret_cast<const float4*>(row < n_pre ? scale_0 : scale_t);
+    act_t* op = out + (size_t)row * ldo;
+#pragma unroll
+    for (int i = 0; i < LN_MAXV; ++i) {
+      const int c = threadIdx.x + i * LN_NT;
+      if (c < nv) {
+        const float4 sc = sp[c];
+        store_act4(op + 4 * c, (cur[i].x - mean) * rstd * (1.f + sc.x), (cur[i].y - mean) * rstd * (1.f + sc.y),
+                   (cur[i].z - mean) * rstd * (1.f + sc.z), (cur[i].w - mean) * rstd * (1.f + sc.w));
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < LN_MAXV; ++i) cur[i] = nxt[i];
   }
 }
 
@@ -96,36 +107,50 @@ __global__ __launch_bounds__(256) void qknorm_rope_kernel(QkArgs a) {
   }
   act_t* kc = a.kc + (size_t)h * a.cap * 128;
 
+  // All loads of the workgroup's 4 passes are issued before any store (the
+  // in-place Q store could otherwise alias later loads for the compiler).
+  constexpr int NP = QK_TOK / 16;
+  float x[NP][8], y[NP][8], vv[NP][8];
+  float4 cs4[NP], sn4[NP];
+  bool live[NP], real[NP];
 #pragma unroll
-  for (int pass = 0; pass < QK_TOK / 16; ++pass) {
+  for (int pass = 0; pass < NP; ++pass) {
+    const int g = g0 + pass * 16 + tl;
+    // the 16 lanes of a token agree on both flags
+    live[pass] = g >= a.g_begin && g < a.g_end;
+    real[pass] = live[pass] && g < a.S;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) { x[pass][j] = 0.f; y[pass][j] = 0.f; vv[pass][j] = 0.f; }
+    cs4[pass] = make_float4(1.f, 1.f, 1.f, 1.f);
+    sn4[pass] = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (real[pass]) {
+      const act_t* row = a.qkv + (size_t)(g - a.q_row0) * a.ld + h * 128 + 8 * p;
+      load_act8(row, x[pass]);
+      load_act8(row + a.H, y[pass]);
+      load_act8(row + 2 * a.H, vv[pass]);
+      cs4[pass] = *reinterpret_cast<const float4*>(a.cosv + (size_t)g * 64 + 4 * p);
+      sn4[pass] = *reinterpret_cast<const float4*>(a.sinv + (size_t)g * 64 + 4 * p);
+    }
+  }
+#pragma unroll
+  for (int pass = 0; pass < NP; ++pass) {
     const int t = pass * 16 + tl;
     const int g = g0 + t;
-    float vv[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) vv[j] = 0.f;
-    // the 16 lanes of a token agree on every branch below
-    if (g >= a.g_begin && g < a.g_end) {
-      if (g < a.S) {
-        act_t* row = a.qkv + (size_t)(g - a.q_row0) * a.ld;
-        act_t* qp = row + h * 128 + 8 * p;
-        const act_t* kp = row + a.H + h * 128 + 8 * p;
-        float x[8], y[8];
-        load_act8(row + 2 * a.H + h * 128 + 8 * p, vv);
-        load_act8(qp, x);
-        load_act8(kp, y);
-        const float4 c = *reinterpret_cast<const float4*>(a.cosv + (size_t)g * 64 + 4 * p);
-        const float4 sn = *reinterpret_cast<const float4*>(a.sinv + (size_t)g * 64 + 4 * p);
-        const float cs[4] = {c.x, c.y, c.z, c.w}, ss[4] = {sn.x, sn.y, sn.z, sn.w};
+    if (live[pass]) {
+      if (real[pass]) {
+        act_t* qp = a.qkv + (size_t)(g - a.q_row0) * a.ld + h * 128 + 8 * p;
+        const float cs[4] = {cs4[pass].x, cs4[pass].y, cs4[pass].z, cs4[pass].w};
+        const float ss[4] = {sn4[pass].x, sn4[pass].y, sn4[pass].z, sn4[pass].w};
         float sx = 0.f, sy = 0.f;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) { sx += x[j] * x[j]; sy += y[j] * y[j]; }
+        for (int j = 0; j < 8; ++j) { sx += x[pass][j] * x[pass][j]; sy += y[pass][j] * y[pass][j]; }
         const float rx = rsqrtf(sum16(sx) * (1.f / 128.f) + a.eps);
         const float ry = rsqrtf(sum16(sy) * (1.f / 128.f) + a.eps);
         float xo[8], yo[8];
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
-          const float x0 = x[2 * m] * rx * wq[2 * m], x1 = x[2 * m + 1] * rx * wq[2 * m + 1];
-          const float y0 = y[2 * m] * ry * wk[2 * m], y1 = y[2 * m + 1] * ry * wk[2 * m + 1];
+          const float x0 = x[pass][2 * m] * rx * wq[2 * m], x1 = x[pass][2 * m + 1] * rx * wq[2 * m + 1];
+          const float y0 = y[pass][2 * m] * ry * wk[2 * m], y1 = y[pass][2 * m + 1] * ry * wk[2 * m + 1];
           xo[2 * m] = x0 * cs[m] - x1 * ss[m];
           xo[2 * m + 1] = x0 * ss[m] + x1 * cs[m];
           yo[2 * m] = y0 * cs[m] - y1 * ss[m];
@@ -134,11 +159,11 @@ __global__ __launch_bounds__(256) void qknorm_rope_kernel(QkArgs a) {
         store_act8(qp, xo);
         store_act8(kc + (size_t)g * 128 + 8 * p, yo);
       } else {
-        store_act8(kc + (size_t)g * 128 + 8 * p, vv);   // padding keys (zeros)
+        store_act8(kc + (size_t)g * 128 + 8 * p, vv[pass]);   // padding keys (zeros)
       }
     }
 #pragma unroll
-    for (int j = 0; j < 8; ++j) vt_s[t][8 * p + j] = vv[j];
+    for (int j = 0; j < 8; ++j) vt_s[t][8 * p + j] = vv[pass][j];
   }
   __syncthreads();
   // Vᵀ rows: dim e, keys g0..g0+63; 8 chunks of 8 keys per row
@@ -255,8 +280,8 @@ hipError_t launch_ln_mod(const float* h, int ldh, int rows, int H, const float* 
                          const float* scale_0, int n_pre, float eps, act_t* out, int ldo,
                          hipStream_t s) {
   if (rows <= 0) return hipSuccess;
-  hipLaunchKernelGGL(ln_mod_kernel, dim3(rows), dim3(LN_NT), 0, s, h, ldh, H, scale_t, scale_0,
-                     n_pre, eps, out, ldo);
+  hipLaunchKernelGGL(ln_mod_kernel, dim3((rows + LN_ROWS - 1) / LN_ROWS), dim3(LN_NT), 0, s, h, ldh, rows,
+                     H, scale_t, scale_0, n_pre, eps, out, ldo);
   return hipGetLastError();
 }
 
