@@ -98,6 +98,19 @@ def summarize_profiles(trace_dir, fetch_dir, write_dir, command, out_md, out_jso
                "algorithmic_bytes": alg}, open(out_json, "w"), indent=1)
 
 
+def describe(cfg):
+    """Token layout of a workload in words, e.g. '256 text + 64x64 target'."""
+    parts = []
+    for seg in cfg["segments"]:
+        if seg[0] == "text":
+            parts.append(f"{seg[1]} text")
+        else:
+            parts.append(f"{seg[1]}x{seg[2]} {'reference' if seg[0] == 'ref' else 'target'}")
+    kind = {0: "text-to-image", 1: "image editing"}.get(sum(s[0] == "ref" for s in cfg["segments"]),
+                                                       "multi-reference")
+    return f"{kind}, " + " + ".join(parts) + " tokens"
+
+
 def layer_flops(T, S, H, F, nh, d):
     """Algorithmic FLOPs of one cached layer: QKV, O, gate/up, down GEMMs
     (2 flop per MAC) and attention over all S keys (QKᵀ and PV)."""
@@ -302,10 +315,8 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic (seeded N(0,1/fan_in) bf16 weights, N(0,1) inputs)",
-        "config": {"workload": f"{args.config}: text-to-image, {P} text prefix + "
-                               f"{int(round(T ** 0.5))}x{int(round(T ** 0.5))} target tokens, "
-                               f"{Lc} layers, hidden {H}, {nh}x{d} heads, SwiGLU {F}, "
-                               f"cached Euler step (Turbo schedule)",
+        "config": {"workload": f"{args.config}: {describe(cfg)}, {Lc} layers, hidden {H}, "
+                               f"{nh}x{d} heads, SwiGLU {F}, cached Euler step (Turbo schedule)",
                    "prefix_tokens": P, "target_tokens": T, "layers": Lc, "batch": 1,
                    "parallelism": "single GPU"},
         "latency_ms": {"p50": round(float(np.percentile(step_ms, 50)), 3),

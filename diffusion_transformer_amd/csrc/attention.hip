@@ -2,19 +2,18 @@
 // block-causal mask in row-limit form (key j visible to query i iff
 // j <= limit[i]); masked keys get exactly zero weight.
 //
-// One workgroup = 4 waves = 128 queries of one head; each wave owns 32
-// queries. Scores are computed transposed, Sᵀ = K·Qᵀ (32 keys × 32 queries
-// per MFMA block), so each lane holds 16 keys of ONE query and the softmax
-// row statistics need only in-lane work plus one exchange with lane^32.
-// The output is accumulated transposed as well, Oᵀ = Vᵀ·Pᵀ, which lets the
-// probabilities feed the MFMA B operand straight from registers; V is kept
-// transposed (dim-major) in the cache so the Vᵀ A-operand is a pair of
-// 8-byte LDS reads. LDS chunks are XOR-swizzled for gfx950's 64 banks
-// (256 bytes per bank cycle): K rows are 256 bytes, so chunk ^= key%16;
-// Vᵀ rows are 128 bytes (two per bank cycle), so chunk ^= (dim/2)%16. K and Vᵀ tiles of 64 keys are staged through LDS,
-// double-buffered with register prefetch. Waves whose queries see none of a
-// key tile skip its arithmetic; tiles past the block's largest limit are
-// never loaded.
+// Both kernels compute scores transposed, Sᵀ = K·Qᵀ (32 keys × 32 queries
+// per MFMA block), so each lane holds keys of ONE query and the row max/sum
+// need in-lane work plus one exchange between the wave halves; the output is
+// accumulated transposed as well, Oᵀ = Vᵀ·Pᵀ, which lets the probabilities
+// feed the MFMA B operand straight from registers. V is kept transposed
+// (dim-major) in the cache. Waves whose queries see none of a key tile skip
+// its arithmetic; tiles past the workgroup's largest limit are never loaded.
+//
+// attn_kernel: first version (4 waves × 32 queries, K/Vᵀ tiles staged
+// through registers), kept as a reference variant.
+// attn2_kernel: the step's kernel; its own comment below lists the
+// differences.
 #include "common.h"
 #include "kernels.h"
 
@@ -232,8 +231,8 @@ __device__ __forceinline__ int perm23(int x) {   // swap bits 2 and 3
   return (x & ~0xC) | ((x & 4) << 1) | ((x & 8) >> 1);
 }
 
-template <int NWV, int QW>
-__global__ __launch_bounds__(NWV * 64) void attn2_kernel(AttnArgs a) {
+template <int NWV, int QW, int NST>
+__global__ __launch_bounds__(NWV * 64, (NWV == 4 && NST == 2) ? 2 : 1) void attn2_kernel(AttnArgs a) {
   constexpr int NSB = QW / 32;          // 32-query sub-blocks per wave
   constexpr int KAHEAD = 6;             // K fragment reads in flight
   constexpr int BQ2 = NWV * QW;
@@ -241,8 +240,9 @@ __global__ __launch_bounds__(NWV * 64) void attn2_kernel(AttnArgs a) {
   constexpr int VT = D * 8;             // u32x4 per Vᵀ tile (128 dims x 128 B)
   constexpr int DMA_PER_WAVE = 32 / NWV;   // 16 K + 16 Vᵀ 1-KB blocks per tile
   static_assert(32 % NWV == 0 && (DMA_PER_WAVE % 2) == 0, "DMA split");
-  __shared__ u32x4 k0s[KT], k1s[KT], k2s[KT];
-  __shared__ u32x4 v0s[VT], v1s[VT], v2s[VT];
+  static_assert(NST == 2 || NST == 3, "ring of 2 or 3 stages");
+  __shared__ u32x4 k0s[KT], k1s[KT], k2s[NST == 3 ? KT : 1];
+  __shared__ u32x4 v0s[VT], v1s[VT], v2s[NST == 3 ? VT : 1];
   __shared__ int red[NWV];
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -441,36 +441,60 @@ __global__ __launch_bounds__(NWV * 64) void attn2_kernel(AttnArgs a) {
     }
   };
 
-  // ring of 3 stages: tile t lives in stage t%3; tiles t+1, t+2 in flight
-  constexpr int PER_TILE = DMA_PER_WAVE;   // DMA instructions per wave per tile
-  auto wait_barrier = [&]() {
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm(PER_TILE));   // tile t+1 landed, t+2 may fly
-    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
-    __builtin_amdgcn_s_barrier();
-  };
   const int last = max(ntiles - 1, 0);
-  if (ntiles > 0) {
-    dma(k0s, v0s, 0);
-    dma(k1s, v1s, min(1, last) * BKV);
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm(PER_TILE));
-    __builtin_amdgcn_s_barrier();
+  if constexpr (NST == 3) {
+    // ring of 3 stages: tile t lives in stage t%3; tiles t+1, t+2 in flight
+    constexpr int PER_TILE = DMA_PER_WAVE;   // DMA instructions per wave per tile
+    auto wait_barrier = [&]() {
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm(PER_TILE));   // tile t+1 landed, t+2 may fly
+      __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+      __builtin_amdgcn_s_barrier();
+    };
+    if (ntiles > 0) {
+      dma(k0s, v0s, 0);
+      dma(k1s, v1s, min(1, last) * BKV);
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm(PER_TILE));
+      __builtin_amdgcn_s_barrier();
+    }
+    // iteration on tile t in stage A: issue tile t+2 into stage C (its last
+    // reader, tile t-1, finished before the previous barrier), compute, then
+    // barrier so tile t+1 (stage B) is visible.
+    auto iter = [&](u32x4* kA, u32x4* vA, u32x4* kC, u32x4* vC, int t) {
+      dma(kC, vC, min(t + 2, last) * BKV);
+      tile(kA, vA, t * BKV);
+      wait_barrier();
+    };
+    int t = 0;
+    for (; t + 2 < ntiles; t += 3) {
+      iter(k0s, v0s, k2s, v2s, t);
+      iter(k1s, v1s, k0s, v0s, t + 1);
+      iter(k2s, v2s, k1s, v1s, t + 2);
+    }
+    if (t < ntiles) iter(k0s, v0s, k2s, v2s, t);
+    if (t + 1 < ntiles) iter(k1s, v1s, k0s, v0s, t + 1);
+  } else {
+    // double buffer (64 KB, so two workgroups share a CU and their barriers
+    // fall at different times): tile t+1 is fetched into the other stage,
+    // whose previous tile was read before the last barrier
+    if (ntiles > 0) {
+      dma(k0s, v0s, 0);
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+      __builtin_amdgcn_s_barrier();
+    }
+    auto iter = [&](u32x4* kA, u32x4* vA, u32x4* kB, u32x4* vB, int t) {
+      dma(kB, vB, min(t + 1, last) * BKV);
+      tile(kA, vA, t * BKV);
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+      __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+      __builtin_amdgcn_s_barrier();
+    };
+    int t = 0;
+    for (; t + 1 < ntiles; t += 2) {
+      iter(k0s, v0s, k1s, v1s, t);
+      iter(k1s, v1s, k0s, v0s, t + 1);
+    }
+    if (t < ntiles) iter(k0s, v0s, k1s, v1s, t);
   }
-  // iteration on tile t in stage A: issue tile t+2 into stage C (its last
-  // reader, tile t-1, finished before the previous barrier), compute, then
-  // barrier so tile t+1 (stage B) is visible.
-  auto iter = [&](u32x4* kA, u32x4* vA, u32x4* kC, u32x4* vC, int t) {
-    dma(kC, vC, min(t + 2, last) * BKV);
-    tile(kA, vA, t * BKV);
-    wait_barrier();
-  };
-  int t = 0;
-  for (; t + 2 < ntiles; t += 3) {
-    iter(k0s, v0s, k2s, v2s, t);
-    iter(k1s, v1s, k0s, v0s, t + 1);
-    iter(k2s, v2s, k1s, v1s, t + 2);
-  }
-  if (t < ntiles) iter(k0s, v0s, k2s, v2s, t);
-  if (t + 1 < ntiles) iter(k1s, v1s, k0s, v0s, t + 1);
   __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
 
   // ---- normalize and store O[query][dim] ----
@@ -494,10 +518,10 @@ __global__ __launch_bounds__(NWV * 64) void attn2_kernel(AttnArgs a) {
   }
 }
 
-template <int NWV, int QW>
+template <int NWV, int QW, int NST>
 hipError_t run_attn2(const AttnArgs& a, hipStream_t s) {
   dim3 grid(((a.N + NWV * QW - 1) / (NWV * QW)) * a.nh);
-  hipLaunchKernelGGL((attn2_kernel<NWV, QW>), grid, dim3(NWV * 64), 0, s, a);
+  hipLaunchKernelGGL((attn2_kernel<NWV, QW, NST>), grid, dim3(NWV * 64), 0, s, a);
   return hipGetLastError();
 }
 
@@ -510,16 +534,21 @@ hipError_t launch_attention_variant(const AttnArgs& a, int variant, hipStream_t 
       hipLaunchKernelGGL(attn_kernel, grid, dim3(NT), 0, s, a);
       return hipGetLastError();
     }
-    case 3: return run_attn2<4, 32>(a, s);
-    case 4: return run_attn2<8, 32>(a, s);
+    case 3: return run_attn2<4, 32, 3>(a, s);
+    case 4: return run_attn2<8, 32, 3>(a, s);
+    case 5: return run_attn2<4, 32, 2>(a, s);   // two workgroups per CU
   }
   return hipErrorInvalidValue;
 }
 
 hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
-  // 256 queries per workgroup unless that leaves CUs idle
+  // 256 queries per workgroup (8 waves, one workgroup per CU) unless that
+  // leaves CUs idle; 128-query workgroups two per CU (their barriers fall at
+  // different times) for small grids and for target rows that all stream a
+  // long key range (measured: 22016 keys 3.35 -> 3.13 ms, 4352 keys slower)
   const long long blocks256 = (long long)((a.N + 255) / 256) * a.nh;
-  return launch_attention_variant(a, blocks256 >= 256 ? 4 : 3, s);
+  if (blocks256 < 256 || (a.q_off > 0 && a.S >= 8192)) return launch_attention_variant(a, 5, s);
+  return launch_attention_variant(a, 4, s);
 }
 
 

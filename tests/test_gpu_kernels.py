@@ -108,7 +108,7 @@ def fill_cache(dev, S, nh, seed):
     return cache.to(dev), K.double().numpy(), V.double().numpy()
 
 
-@pytest.mark.parametrize("variant", [0, 1, 3, 4])
+@pytest.mark.parametrize("variant", [0, 1, 3, 4, 5])
 @pytest.mark.parametrize("name,mode", [("c0w", "extract"), ("c0w", "cached"),
                                        ("ragged", "extract"), ("ragged", "cached"),
                                        ("c1", "extract"), ("c1", "cached"),
