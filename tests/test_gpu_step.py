@@ -188,3 +188,33 @@ def test_full_depth_cache_invariants(dev, c2_full):
     with pytest.raises(L.DitError) as e:
         rt.step_cached(seq, x1, 0.95418, c3, va, wa)
     assert e.value.status == L.DIT_ERR_STATE
+
+
+@pytest.mark.parametrize("name", ["c3", "c4"])
+def test_full_depth_largest_workloads_cached_matches_recompute(dev, name):
+    """The editing (4352-row prefix) and multi-reference (12800-row prefix,
+    96x96 target, 22016 keys: the largest workload, 11.6 GB of KV cache)
+    workloads at full depth: the first three Turbo steps, cached against full
+    recompute, finite and within the cached-path bound."""
+    from diffusion_transformer_amd.runtime import random_weights_device
+    cfg = synth.config(name)
+    Wd = random_weights_device(cfg, 21, dev)
+    rt = DitRuntime(cfg, Wd, device=dev, on_device=True)
+    I = synth.make_inputs(cfg)
+    seq = rt.sequence(cfg["segments"])
+    pre = rt.prefix_hidden(I)
+    x0 = torch.from_numpy(I["x0"]).to(dev)
+    sig = cfg["sigmas"][:4]
+    say(f"{name} full depth P={seq.P} T={seq.T}: 3-step cached loop vs recompute")
+    vs_c, xs_c = rt.run_loop(seq, pre, x0, sig, use_cache=True)
+    vs_r, xs_r = rt.run_loop(seq, pre, x0, sig, use_cache=False)
+    torch.cuda.synchronize()
+    for k in range(len(vs_c)):
+        assert torch.isfinite(vs_c[k]).all()
+        e = rel_err(vs_c[k].cpu().numpy(), vs_r[k].cpu().numpy())
+        say(f"  step {k}: cached vs recompute {e:.3e}")
+        assert e < TOL_CACHED
+    assert rel_err(xs_c[-1].cpu().numpy(), xs_r[-1].cpu().numpy()) < TOL_CACHED
+    rt.close()
+    del Wd
+    torch.cuda.empty_cache()
