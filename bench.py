@@ -163,6 +163,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", default="c2")
+    ap.add_argument("--batch", type=int, default=1,
+                    help="target latents denoised together against one shared prefix")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-breakdown", action="store_true")
     ap.add_argument("--only-timed", action="store_true",
@@ -190,13 +192,17 @@ def main():
     Wd = random_weights_device(cfg, 21, dev)
     rt = DitRuntime(cfg, Wd, device=dev, on_device=True)
     I = synth.make_inputs(cfg, seed=21)
-    seq = rt.sequence(cfg["segments"])
-    P, T, S = seq.P, seq.T, seq.S
+    B = args.batch
+    seq = rt.sequence(cfg["segments"], batch=B)
+    P, T1, S = seq.P, seq.T, seq.S
+    T = B * T1          # target rows of all elements
     pre = rt.prefix_hidden(I)
-    x = torch.from_numpy(I["x0"]).to(dev)
+    x = torch.cat([torch.from_numpy(I["x0"])] +
+                  [torch.from_numpy(synth._rng(100 + b, "x_batch").standard_normal(
+                      (T1, cfg["latent"]), dtype=np.float32)) for b in range(1, B)]).to(dev)
     sig = cfg["sigmas"]
     cache = rt.alloc_cache(seq)
-    ws = rt.alloc_workspace(S)
+    ws = rt.alloc_workspace(seq.S_all)
     v = torch.empty_like(x)
     stream = torch.cuda.current_stream()
 
@@ -237,7 +243,7 @@ def main():
     print(f"[bench] cached step {ms_per_step:.3f} ms, {value:.0f} target tok/s", file=sys.stderr,
           flush=True)
 
-    fl = layer_flops(T, S, H, F, nh, d)
+    fl = layer_flops(T, S, H, F, nh, d)   # T = all elements' target rows, each over S keys
     gu_avg = gu_ms / max(gu_n, 1)
     gu_tflops = fl["gemm_gateup"] / (gu_avg / 1e3) / 1e12
     roofline = {"bound": "mfma", "achieved": round(gu_tflops, 1), "peak": PEAK_BF16_TFLOPS,
@@ -315,9 +321,11 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic (seeded N(0,1/fan_in) bf16 weights, N(0,1) inputs)",
-        "config": {"workload": f"{args.config}: {describe(cfg)}, {Lc} layers, hidden {H}, "
+        "config": {"workload": f"{args.config}: {describe(cfg)}"
+                               + (f", {B} target latents sharing the prefix" if B > 1 else "")
+                               + f", {Lc} layers, hidden {H}, "
                                f"{nh}x{d} heads, SwiGLU {F}, cached Euler step (Turbo schedule)",
-                   "prefix_tokens": P, "target_tokens": T, "layers": Lc, "batch": 1,
+                   "prefix_tokens": P, "target_tokens": T1, "layers": Lc, "batch": B,
                    "parallelism": "single GPU"},
         "latency_ms": {"p50": round(float(np.percentile(step_ms, 50)), 3),
                        "p95": round(float(np.percentile(step_ms, 95)), 3),

@@ -57,7 +57,7 @@ class dit_weights(C.Structure):
 
 class dit_seq(C.Structure):
     _fields_ = [("P", C.c_int), ("T", C.c_int), ("d_row_limit", C.c_void_p),
-                ("d_rope_cos", C.c_void_p), ("d_rope_sin", C.c_void_p)]
+                ("d_rope_cos", C.c_void_p), ("d_rope_sin", C.c_void_p), ("B", C.c_int)]
 
 
 def _load(path=None):
@@ -192,8 +192,9 @@ def _make_api(_lib):
     def dit_kv_cache_bytes(model, S: int) -> int:
         return _lib.dit_kv_cache_bytes(model, S)
 
-    def make_seq(P, T, row_limit, rope_cos, rope_sin) -> dit_seq:
-        return dit_seq(P, T, _ptr(row_limit), _ptr(rope_cos), _ptr(rope_sin))
+    def make_seq(P, T, row_limit, rope_cos, rope_sin, B=1) -> dit_seq:
+        """B target latents share the prefix (rows P + b*T .. of x, v, cache)."""
+        return dit_seq(P, T, _ptr(row_limit), _ptr(rope_cos), _ptr(rope_sin), B)
 
     def _nbytes(t):
         return t.numel() * t.element_size()

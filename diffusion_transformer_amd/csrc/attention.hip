@@ -255,6 +255,12 @@ __global__ __launch_bounds__(NWV * 64, (NWV == 4 && NST == 2) ? 2 : 1) void attn
   if ((gridDim.x & 7) == 0) bid = (bid & 7) * (gridDim.x >> 3) + (bid >> 3);
   const int h = bid / nqb, qblk = bid - h * nqb;
   const int lq = lane & 31, half = lane >> 5;
+  // Target element of this workgroup's queries (one element per workgroup:
+  // with several elements P and T_el are multiples of the query block): its
+  // query rows and its cached keys past the prefix sit e*T_el rows further
+  // than the logical rows of the layout.
+  const int gq0 = a.q_off + qblk * BQ2;
+  const int eoff = (a.T_el > 0 && gq0 >= a.P) ? (gq0 - a.P) / a.T_el * a.T_el : 0;
 
   int qi[NSB], lim[NSB];
   bool qv[NSB];
@@ -264,7 +270,7 @@ __global__ __launch_bounds__(NWV * 64, (NWV == 4 && NST == 2) ? 2 : 1) void attn
     const int q = qblk * BQ2 + wave * QW + sb * 32 + lq;
     qv[sb] = q < a.N;
     qi[sb] = min(q, a.N - 1);
-    lim[sb] = a.limit[a.q_off + qi[sb]];
+    lim[sb] = a.limit[a.q_off + qi[sb] - eoff];
     lmin = min(lmin, lim[sb]);
     lmax = max(lmax, lim[sb]);
   }
@@ -308,18 +314,21 @@ __global__ __launch_bounds__(NWV * 64, (NWV == 4 && NST == 2) ? 2 : 1) void attn
     const int c = (lane & 7) ^ (((8 * b2 + r) >> 1) & 7);
     voff[b2] = (uint32_t)(r * a.cap * 2 + c * 16);
   }
+  // tile of logical keys kv0 .. kv0+63 (P is a multiple of 64 whenever the
+  // element offset is non-zero, so a tile never straddles the prefix end)
   auto dma = [&](u32x4* ks, u32x4* vs, int kv0) {
+    const int kp = kv0 >= a.P ? kv0 + eoff : kv0;
 #pragma unroll
     for (int j = 0; j < DMA_PER_WAVE / 2; ++j) {
       const int blk = j * NWV + wave;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rK, LDSP(ks + blk * 64), 16, koff[blk & 3],
-                                               (uint32_t)((kv0 + 4 * blk) * 256), 0, 0);
+                                               (uint32_t)((kp + 4 * blk) * 256), 0, 0);
     }
 #pragma unroll
     for (int j = 0; j < DMA_PER_WAVE / 2; ++j) {
       const int blk = j * NWV + wave;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rV, LDSP(vs + blk * 64), 16, voff[blk & 1],
-                                               (uint32_t)(8 * blk * a.cap * 2 + kv0 * 2), 0, 0);
+                                               (uint32_t)(8 * blk * a.cap * 2 + kp * 2), 0, 0);
     }
   };
 

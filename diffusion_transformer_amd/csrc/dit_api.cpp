@@ -39,7 +39,7 @@ size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 struct ExtractRecord {
   const void* kv;
-  int P, T;
+  int P, T, B;
 };
 
 }  // namespace
@@ -82,10 +82,25 @@ dit_status check_cfg(const dit_config* c) {
   return DIT_OK;
 }
 
+// Number of target latents sharing the prefix (B <= 1 means one).
+inline int n_elem(const dit_seq* s) { return s->B > 1 ? s->B : 1; }
+// Rows of every per-token tensor and keys of the cache: P + B*T.
+inline int s_all(const dit_seq* s) { return s->P + n_elem(s) * s->T; }
+
 dit_status check_seq(const dit_model* m, const dit_seq* s) {
   if (!s) return fail(DIT_ERR_ARG, "seq is NULL");
   if (s->P < 0 || s->T <= 0) return fail(DIT_ERR_LAYOUT, "need P >= 0 and T > 0 (P=%d T=%d)", s->P, s->T);
-  if ((long long)s->P + s->T > (1 << 24)) return fail(DIT_ERR_LAYOUT, "sequence too long");
+  if (s->B < 0) return fail(DIT_ERR_ARG, "negative batch %d", s->B);
+  if ((long long)s->P + (long long)(s->B > 1 ? s->B : 1) * s->T > (1 << 24))
+    return fail(DIT_ERR_LAYOUT, "sequence too long");
+  if (s->B > 1) {
+#ifdef DIT_F32
+    return fail(DIT_ERR_UNSUPPORTED, "several target latents are not part of the fp32 debug build");
+#endif
+    if (s->P % 256 || s->T % 256)
+      return fail(DIT_ERR_SHAPE, "several target latents need P and T multiples of 256 (P=%d T=%d)",
+                  s->P, s->T);
+  }
   if (!s->d_row_limit || !s->d_rope_cos || !s->d_rope_sin)
     return fail(DIT_ERR_ARG, "seq device tables are NULL");
   (void)m;
@@ -150,9 +165,11 @@ dit_status run_step(dit_model* m, const dit_seq* seq, bool extract, const float*
                     hipStream_t st) {
   const dit_config& c = m->cfg;
   const int H = c.hidden, F = c.ffn, nh = c.n_heads, L = c.n_layers;
-  const int P = seq->P, T = seq->T, S = P + T;
-  const int cap = dit_kv_capacity(S);
-  const int N = extract ? S : T;
+  // S: one element's sequence (layout tables, mask); SA: all rows/keys with
+  // the B target latents; TB: target rows of all elements
+  const int P = seq->P, T = seq->T, S = P + T, SA = s_all(seq), TB = SA - P;
+  const int cap = dit_kv_capacity(SA);
+  const int N = extract ? SA : TB;
   const int n_pre = extract ? P : 0;
   const int q_row0 = extract ? 0 : P;
   const Plan pl = plan(c, N);
@@ -194,7 +211,7 @@ dit_status run_step(dit_model* m, const dit_seq* seq, bool extract, const float*
   // ---- residual stream init ----
   if (extract && P > 0)
     LAUNCH(hipMemcpyAsync(hbuf, prefix, (size_t)P * H * 4, hipMemcpyDeviceToDevice, st), "prefix copy");
-  LAUNCH(launch_img_in(U(m->img_in), x, T, H, hbuf + (size_t)n_pre * H, H, st), "img_in");
+  LAUNCH(launch_img_in(U(m->img_in), x, TB, H, hbuf + (size_t)n_pre * H, H, st), "img_in");
 
   for (int l = 0; l < L; ++l) {
     act_t* kl = kbase + (size_t)l * nh * cap * 128;
@@ -215,8 +232,8 @@ dit_status run_step(dit_model* m, const dit_seq* seq, bool extract, const float*
       Timed tm(m, DIT_PROF_QKNORM_ROPE, st);
       QkArgs q{};
       q.qkv = qkv; q.ld = 3 * H; q.q_row0 = q_row0;
-      q.g_begin = extract ? 0 : P; q.g_end = extract ? cap : S;
-      q.S = S; q.cap = cap; q.nh = nh; q.H = H;
+      q.g_begin = extract ? 0 : P; q.g_end = extract ? cap : SA;
+      q.S = SA; q.cap = cap; q.nh = nh; q.H = H; q.P = P; q.T_el = T;
       q.wq = U(m->qn[l]); q.wk = U(m->kn[l]);
       q.cosv = seq->d_rope_cos; q.sinv = seq->d_rope_sin;
       q.kc = kl; q.vtc = vl; q.eps = c.eps;
@@ -227,7 +244,7 @@ dit_status run_step(dit_model* m, const dit_seq* seq, bool extract, const float*
       AttnArgs a{};
       a.q = qkv; a.q_stride = 3 * H; a.q_off = q_row0; a.N = N;
       a.k = kl; a.vt = vl; a.cap = cap; a.S = S; a.nh = nh; a.limit = seq->d_row_limit;
-      a.out = att; a.out_stride = H;
+      a.out = att; a.out_stride = H; a.P = P; a.T_el = T;
       LAUNCH(launch_attention(a, st), "attention");
     }
     {
@@ -261,11 +278,11 @@ dit_status run_step(dit_model* m, const dit_seq* seq, bool extract, const float*
   }
 
   // ---- scale-only final AdaLN on target rows, proj_out -> v ----
-  LAUNCH(launch_ln_mod(hbuf + (size_t)n_pre * H, H, T, H, scale_out, scale_out, 0, c.eps, xb, H, st),
+  LAUNCH(launch_ln_mod(hbuf + (size_t)n_pre * H, H, TB, H, scale_out, scale_out, 0, c.eps, xb, H, st),
          "final ln");
   {
     GemmArgs g{};
-    g.A = xb; g.lda = H; g.B = U(m->proj_out); g.ldb = H; g.M = T; g.N = c.latent; g.K = H;
+    g.A = xb; g.lda = H; g.B = U(m->proj_out); g.ldb = H; g.M = TB; g.N = c.latent; g.K = H;
     g.C = v_out; g.ldc = c.latent;
     LAUNCH(launch_gemm(g, EPI_F32, st), "gemm proj_out");
   }
@@ -279,7 +296,7 @@ dit_status check_step_common(dit_model* m, const dit_seq* seq, const float* x, v
   dit_status rc = check_seq(m, seq);
   if (rc) return rc;
   if (!x || !kv || !v_out || !ws) return fail(DIT_ERR_ARG, "x, kv_cache, v_out and workspace must be non-NULL");
-  const size_t need_kv = dit_kv_cache_bytes(m, seq->P + seq->T);
+  const size_t need_kv = dit_kv_cache_bytes(m, s_all(seq));
   if (kv_bytes < need_kv)
     return fail(DIT_ERR_WORKSPACE, "kv_cache has %zu bytes, needs %zu", kv_bytes, need_kv);
   const size_t need_ws = dit_workspace_bytes(m, n);
@@ -428,7 +445,7 @@ dit_status dit_step_extract(dit_model* m, const dit_seq* seq, const float* prefi
                             float* v_out, void* workspace, size_t ws_bytes, int flags,
                             void* stream) {
   dit_status rc = check_step_common(m, seq, x, kv_cache, kv_bytes, v_out, workspace, ws_bytes,
-                                    seq ? seq->P + seq->T : 0);
+                                    seq ? s_all(seq) : 0);
   if (rc) return rc;
   if (seq->P > 0 && !prefix_hidden) return fail(DIT_ERR_ARG, "prefix_hidden is NULL");
   if (flags & ~DIT_FLAG_NO_CAUSAL_CONDITION) return fail(DIT_ERR_ARG, "unknown flags 0x%x", flags);
@@ -439,7 +456,7 @@ dit_status dit_step_extract(dit_model* m, const dit_seq* seq, const float* prefi
   rc = run_step(m, seq, true, prefix_hidden, x, sigma, kv_cache, v_out, workspace, flags,
                 static_cast<hipStream_t>(stream));
   if (rc) return rc;
-  if (!(flags & DIT_FLAG_NO_CAUSAL_CONDITION)) m->extracted.push_back({kv_cache, seq->P, seq->T});
+  if (!(flags & DIT_FLAG_NO_CAUSAL_CONDITION)) m->extracted.push_back({kv_cache, seq->P, seq->T, n_elem(seq)});
   return DIT_OK;
 }
 
@@ -447,15 +464,16 @@ dit_status dit_step_cached(dit_model* m, const dit_seq* seq, const float* x, flo
                            void* kv_cache, size_t kv_bytes, float* v_out, void* workspace,
                            size_t ws_bytes, void* stream) {
   dit_status rc = check_step_common(m, seq, x, kv_cache, kv_bytes, v_out, workspace, ws_bytes,
-                                    seq ? seq->T : 0);
+                                    seq ? s_all(seq) - seq->P : 0);
   if (rc) return rc;
   if (!std::isfinite(sigma)) return fail(DIT_ERR_ARG, "sigma is not finite");
   bool ok = false;
   for (const auto& r : m->extracted)
-    if (r.kv == kv_cache && r.P == seq->P && r.T == seq->T) ok = true;
+    if (r.kv == kv_cache && r.P == seq->P && r.T == seq->T && r.B == n_elem(seq)) ok = true;
   if (!ok)
-    return fail(DIT_ERR_STATE, "no dit_step_extract with t=0 conditioning ran on this cache for P=%d T=%d",
-                seq->P, seq->T);
+    return fail(DIT_ERR_STATE,
+                "no dit_step_extract with t=0 conditioning ran on this cache for P=%d T=%d B=%d",
+                seq->P, seq->T, n_elem(seq));
   return run_step(m, seq, false, nullptr, x, sigma, kv_cache, v_out, workspace, 0,
                   static_cast<hipStream_t>(stream));
 }
@@ -505,6 +523,7 @@ dit_status dit_debug_attention(const dit_seq* seq, int n_heads, const void* q, i
   a.vt = a.k + (size_t)n_heads * cap * 128;
   a.cap = cap; a.S = S; a.nh = n_heads; a.limit = seq->d_row_limit;
   a.out = static_cast<act_t*>(out); a.out_stride = n_heads * 128;
+  a.P = seq->P; a.T_el = seq->T;
   if (variant < 0 || variant > 16) return fail(DIT_ERR_ARG, "unknown attention variant %d", variant);
   if (variant == 0) return hip_check(launch_attention(a, static_cast<hipStream_t>(stream)), "debug attention");
   return hip_check(launch_attention_variant(a, variant, static_cast<hipStream_t>(stream)), "debug attention");

@@ -128,8 +128,11 @@ __global__ __launch_bounds__(256) void qknorm_rope_kernel(QkArgs a) {
       load_act8(row, x[pass]);
       load_act8(row + a.H, y[pass]);
       load_act8(row + 2 * a.H, vv[pass]);
-      cs4[pass] = *reinterpret_cast<const float4*>(a.cosv + (size_t)g * 64 + 4 * p);
-      sn4[pass] = *reinterpret_cast<const float4*>(a.sinv + (size_t)g * 64 + 4 * p);
+      // RoPE position: the logical row of the layout (target rows of every
+      // element share one table)
+      const int gl = (a.T_el > 0 && g >= a.P) ? a.P + (g - a.P) % a.T_el : g;
+      cs4[pass] = *reinterpret_cast<const float4*>(a.cosv + (size_t)gl * 64 + 4 * p);
+      sn4[pass] = *reinterpret_cast<const float4*>(a.sinv + (size_t)gl * 64 + 4 * p);
     }
   }
 #pragma unroll

@@ -987,11 +987,12 @@ hipError_t launch_gemm(const GemmArgs& g, int epi, hipStream_t s) {
   // One block tile per CU per round: when the tiles leave the last round
   // mostly idle and dropping the last r row blocks makes the rest whole
   // rounds, those r row blocks are spread over the idle CUs by splitting K.
+  // A GEMM with less than one round of tiles is split whole (r = ntm).
   const int ntm = (g.M + 255) / 256, ntn = g.N / 256;
   constexpr int kRound = 256;
   if (g.part && (ntm * ntn) % kRound) {
-    int r = 0;
-    for (int rr = 1; rr < ntm && rr * ntn <= kRound; ++rr)
+    int r = ntm * ntn < kRound ? ntm : 0;
+    for (int rr = 1; !r && rr < ntm && rr * ntn <= kRound; ++rr)
       if (((ntm - rr) * ntn) % kRound == 0) { r = rr; break; }
     int splits = 1;
     while (r && 2 * splits * r * ntn <= kRound && (g.K / 64) % (2 * splits) == 0 &&

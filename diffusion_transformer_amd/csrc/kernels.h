@@ -53,6 +53,11 @@ struct AttnArgs {
   int cap, S, nh;
   const int32_t* limit;             // [S]
   act_t* out; int out_stride;       // [N, nh*128]
+  // Target latents sharing the prefix: global rows and cache keys >= P of
+  // element e = (row - P) / T_el are that element's, its logical index is
+  // row - e*T_el (layout tables and the mask describe one element). T_el = 0
+  // or S - P: a single latent.
+  int P, T_el;
 };
 hipError_t launch_attention(const AttnArgs& a, hipStream_t s);
 hipError_t launch_attention_variant(const AttnArgs& a, int variant, hipStream_t s);
@@ -74,6 +79,7 @@ struct QkArgs {
   const float* cosv; const float* sinv;     // [S, 64]
   act_t* kc; act_t* vtc;                    // layer bases
   float eps;
+  int P, T_el;   // rows >= P: RoPE of logical row P + (g - P) % T_el (T_el = 0: g)
 };
 hipError_t launch_qknorm_rope(const QkArgs& a, hipStream_t s);
 

@@ -58,17 +58,21 @@ def random_weights_device(cfg: dict, seed: int, device, n_layers=None) -> dict:
 
 
 class Sequence:
-    """Device copy of one token layout plus its C struct."""
+    """Device copy of one token layout plus its C struct. ``batch`` target
+    latents share the prefix: x and v hold batch*T rows, the cache
+    S_all = P + batch*T keys."""
 
-    def __init__(self, cfg_c, segments, device, api=L):
+    def __init__(self, cfg_c, segments, device, api=L, batch=1):
         lay = api.dit_build_layout(cfg_c, segments)
         self.host = lay
         self.P, self.T = lay["P"], lay["T"]
         self.S = self.P + self.T
+        self.B = batch
+        self.S_all = self.P + batch * self.T
         self.row_limit = torch.from_numpy(lay["row_limit"]).to(device)
         self.rope_cos = torch.from_numpy(lay["rope_cos"]).to(device)
         self.rope_sin = torch.from_numpy(lay["rope_sin"]).to(device)
-        self.c = api.make_seq(self.P, self.T, self.row_limit, self.rope_cos, self.rope_sin)
+        self.c = api.make_seq(self.P, self.T, self.row_limit, self.rope_cos, self.rope_sin, batch)
 
 
 class DitRuntime:
@@ -96,11 +100,11 @@ class DitRuntime:
         except Exception:
             pass
 
-    def sequence(self, segments) -> Sequence:
-        return Sequence(self.c, segments, self.device, self.L)
+    def sequence(self, segments, batch=1) -> Sequence:
+        return Sequence(self.c, segments, self.device, self.L, batch)
 
     def alloc_cache(self, seq: Sequence) -> torch.Tensor:
-        nbytes = self.L.dit_kv_cache_bytes(self.model, seq.S)
+        nbytes = self.L.dit_kv_cache_bytes(self.model, seq.S_all)
         return torch.empty(nbytes // 2, dtype=torch.int16, device=self.device)
 
     def alloc_workspace(self, n_tokens: int) -> torch.Tensor:
@@ -138,7 +142,7 @@ class DitRuntime:
         """Sampler loop; returns (list of v per step, list of x after each step)."""
         x = x0.clone().contiguous()
         cache = self.alloc_cache(seq)
-        ws = self.alloc_workspace(seq.S)
+        ws = self.alloc_workspace(seq.S_all)
         vs, xs = [], []
         for k in range(len(sigmas) - 1):
             v = torch.empty_like(x)

@@ -108,13 +108,23 @@ typedef struct dit_model dit_model; /* opaque host-side handle */
  *   P prefix tokens (text and references) followed by T target tokens.
  *   d_row_limit [S] int32: largest key index visible to each query row.
  *   d_rope_cos, d_rope_sin [S, head_dim/2] float32: per-token, per-pair
- *   RoPE rotation. */
+ *   RoPE rotation.
+ *   B: number of target latents denoised together against ONE shared prefix
+ *   (independent requests or seeds; 0 or 1 = a single latent). Element b's
+ *   target tokens are rows P + b*T .. P + (b+1)*T - 1 of every per-token
+ *   tensor and of the KV cache; each sees the prefix and its own target
+ *   block, never another element's (the layout tables describe one element:
+ *   S = P + T entries). x and v_out are [B*T, C], the cache holds
+ *   S_all = P + B*T keys, extract workspaces n_tokens = S_all, cached
+ *   n_tokens = B*T. B > 1 needs P and T to be multiples of 256
+ *   (DIT_ERR_SHAPE otherwise) and is not part of the fp32 debug build. */
 typedef struct dit_seq {
   int P;
   int T;
   const int32_t* d_row_limit;
   const float* d_rope_cos;
   const float* d_rope_sin;
+  int B;
 } dit_seq;
 
 /* Token layout from a segment list (host only, no device work).

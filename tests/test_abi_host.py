@@ -74,10 +74,10 @@ def fake_weights(nl):
     return L.dit_weights(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, p, p, p, p, p, p, p), arr
 
 
-def load(c):
+def load(c, api=L):
     w, keep = fake_weights(c.n_layers)
     h = C.c_void_p()
-    st = L._lib.dit_load_weights(C.byref(c), C.byref(w), C.byref(h))
+    st = api._lib.dit_load_weights(C.byref(c), C.byref(w), C.byref(h))
     return st, h.value
 
 
@@ -146,6 +146,49 @@ def test_step_state_and_workspace_errors():
         assert L._lib.dit_profile_enable(m, 99) == L.DIT_ERR_ARG
     finally:
         L.dit_free(m)
+
+
+def test_batch_of_targets_validation():
+    """Several target latents sharing one prefix: the cache and workspace
+    cover P + B*T rows, B > 1 needs P and T multiples of 256, and a cached
+    step needs an extract of the same batch."""
+    cfg, c = cfg_c("c1")
+    st, m = load(c)
+    assert st == L.DIT_OK
+    try:
+        P, T, B = 512, 1024, 3
+        seq = L.dit_seq(P, T, FAKE, FAKE, FAKE, B)
+        kvb = L.dit_kv_cache_bytes(m, P + B * T)
+        ws_x, ws_c = L.dit_workspace_bytes(m, P + B * T), L.dit_workspace_bytes(m, B * T)
+        # a cache sized for one latent is too small for three
+        r = L._lib.dit_step_extract(m, C.byref(seq), FAKE, FAKE, 1.0, FAKE,
+                                    L.dit_kv_cache_bytes(m, P + T), FAKE, FAKE, ws_x, 0, None)
+        assert r == L.DIT_ERR_WORKSPACE
+        r = L._lib.dit_step_extract(m, C.byref(seq), FAKE, FAKE, 1.0, FAKE, kvb, FAKE, FAKE,
+                                    ws_c, 0, None)
+        assert r == L.DIT_ERR_WORKSPACE          # extract needs the P + B*T workspace
+        r = L._lib.dit_step_cached(m, C.byref(seq), FAKE, 0.9, FAKE, kvb, FAKE, FAKE, ws_c, None)
+        assert r == L.DIT_ERR_STATE
+        for bad in (L.dit_seq(500, T, FAKE, FAKE, FAKE, 2), L.dit_seq(P, 1000, FAKE, FAKE, FAKE, 2)):
+            r = L._lib.dit_step_extract(m, C.byref(bad), FAKE, FAKE, 1.0, FAKE, kvb, FAKE, FAKE,
+                                        ws_x, 0, None)
+            assert r == L.DIT_ERR_SHAPE
+        neg = L.dit_seq(P, T, FAKE, FAKE, FAKE, -1)
+        r = L._lib.dit_step_extract(m, C.byref(neg), FAKE, FAKE, 1.0, FAKE, kvb, FAKE, FAKE, ws_x, 0, None)
+        assert r == L.DIT_ERR_ARG
+    finally:
+        L.dit_free(m)
+    # the fp32 debug build refuses several latents
+    f32 = L.load_f32()
+    st, m = load(c, api=f32)
+    assert st == L.DIT_OK
+    try:
+        seq = L.dit_seq(512, 1024, FAKE, FAKE, FAKE, 2)
+        r = f32._lib.dit_step_extract(m, C.byref(seq), FAKE, FAKE, 1.0, FAKE, 1 << 40, FAKE,
+                                      FAKE, 1 << 40, 0, None)
+        assert r == L.DIT_ERR_UNSUPPORTED
+    finally:
+        f32.dit_free(m)
 
 
 def test_workspace_grows_with_tokens():

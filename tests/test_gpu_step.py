@@ -218,3 +218,51 @@ def test_full_depth_largest_workloads_cached_matches_recompute(dev, name):
     rt.close()
     del Wd
     torch.cuda.empty_cache()
+
+
+def test_batch_of_targets_shares_one_prefix(dev):
+    """Three target latents denoised together against one shared prefix
+    cache (512 text + 32x32 target, one layer): each element's v from the
+    batched extract and cached steps equals the same element run alone, the
+    shared prefix K/V rows are identical to a single run's and each
+    element's target K rows sit at P + b*T; the middle element's cached rows
+    also match the oracle."""
+    cfg, W, I, rt, seq1, pre, x0 = build("c1", dev)
+    B, P, T = 3, seq1.P, seq1.T
+    seqb = rt.sequence(cfg["segments"], batch=B)
+    say(f"batch of {B} targets sharing P={P} (T={T})")
+    rng = [synth._rng(100 + b, "x_batch") for b in range(B)]
+    xs = [x0] + [torch.from_numpy(rng[b].standard_normal((T, 64), dtype=np.float32)).to(dev)
+                 for b in range(1, B)]
+    x2 = [torch.from_numpy(rng[b].standard_normal((T, 64), dtype=np.float32)).to(dev)
+          for b in range(B)]
+    cb, wb = rt.alloc_cache(seqb), rt.alloc_workspace(seqb.S_all)
+    xb, x2b = torch.cat(xs).contiguous(), torch.cat(x2).contiguous()
+    vb, vbc = torch.empty_like(xb), torch.empty_like(xb)
+    rt.step_extract(seqb, pre, xb, 1.0, cb, vb, wb)
+    rt.step_cached(seqb, x2b, 0.978453, cb, vbc, wb)
+    torch.cuda.synchronize()
+    Lc, nh = cfg["n_layers"], cfg["n_heads"]
+    kb, _ = cache_views(cb, Lc, nh, L.dit_kv_capacity(seqb.S_all))
+    for b in range(B):
+        c1, w1 = rt.alloc_cache(seq1), rt.alloc_workspace(seq1.S)
+        v1, v1c = torch.empty_like(x0), torch.empty_like(x0)
+        rt.step_extract(seq1, pre, xs[b], 1.0, c1, v1, w1)
+        k_after_extract = cache_views(c1, Lc, nh, L.dit_kv_capacity(seq1.S))[0].clone()
+        rt.step_cached(seq1, x2[b], 0.978453, c1, v1c, w1)
+        torch.cuda.synchronize()
+        k1, _ = cache_views(c1, Lc, nh, L.dit_kv_capacity(seq1.S))
+        ex = rel_err(vb[b * T:(b + 1) * T].cpu().numpy(), v1.cpu().numpy())
+        ec = rel_err(vbc[b * T:(b + 1) * T].cpu().numpy(), v1c.cpu().numpy())
+        say(f"  element {b}: extract vs alone {ex:.2e}, cached vs alone {ec:.2e}")
+        assert ex < TOL_CACHED and ec < TOL_CACHED
+        assert torch.equal(kb[:, :, :P], k_after_extract[:, :, :P])
+        # the batched cache holds the cached step's target K of element b
+        et = rel_err(i16_to_f32(kb[:, :, P + b * T:P + (b + 1) * T]), i16_to_f32(k1[:, :, P:P + T]))
+        assert et < TOL_CACHED
+    rows = np.sort(np.random.default_rng(5).choice(T, 32, replace=False))
+    r1 = O.cached_rows_one_layer(W, dims_of(cfg), O.build_layout(cfg["segments"]),
+                                 oracle_prefix(cfg, W, I), x2[1].cpu().numpy(), 0.978453, rows)
+    e = rel_err(vbc[T:2 * T].cpu().numpy()[rows], r1)
+    say(f"  element 1 cached rows vs oracle {e:.2e}")
+    assert e < TOL_BF16
