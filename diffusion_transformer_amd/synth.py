@@ -166,6 +166,14 @@ def make_inputs(cfg: dict, seed: int = 21) -> dict:
     return out
 
 
+def latent_stats(C: int = 64, seed: int = 21):
+    """Synthetic per-channel VAE latent statistics (mean [C], std [C]) standing
+    in for a checkpoint's: mean N(0, 0.5²), std exp(N(0, 0.3²)), float32."""
+    mean = (0.5 * _rng(seed, "latents_mean").standard_normal(C)).astype(np.float32)
+    std = np.exp(0.3 * _rng(seed, "latents_std").standard_normal(C)).astype(np.float32)
+    return mean, std
+
+
 def interleave_prefix(kind: np.ndarray, text_rows: np.ndarray, ref_rows: np.ndarray) -> np.ndarray:
     """Place text rows and reference rows in sequence order (row copies only)."""
     out = np.empty((len(kind), text_rows.shape[1]), dtype=np.float32)

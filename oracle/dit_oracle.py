@@ -13,6 +13,8 @@ Sources (five course pages on Qwen-Image-2.1, cited by page title and section):
   [3B]    "3B · Causal condition (t=0 vs t) & shared modulation":
           §1 Definition, §2 Flow, §3 Solution, §6 Glossary.
   [2A]    "2A · 4× image-slot expansion & joint sequence packing": §1, §2.
+  [1A]    "1A · RGBA 64-Ch VAE & Unpatched Latents" (the end-to-end lab's first
+          diagram step: per-channel standardization before img_in).
   [INDEX] "Bài Lab tổng hợp — Qwen-Image-2.1 Architecture" (lab index page):
           the 1:1 mapping table (rows 3A, 3B, 3C, 4A, 5A, 6A, 6B) and the
           script qwen-image-21.py, cited by its banner blocks
@@ -39,7 +41,7 @@ __all__ = [
     "row_limits", "rope_angles", "timestep_embedding", "conditioning",
     "layernorm", "rmsnorm", "silu", "rope_rotate", "masked_attention",
     "forward_extract", "forward_cached", "euler_step", "run_loop",
-    "cached_rows_one_layer",
+    "cached_rows_one_layer", "standardize", "unstandardize",
 ]
 
 # [6B] §1 Definition / §6 Glossary: the 8-step Turbo sigma table (9 marks).
@@ -381,6 +383,20 @@ def forward_cached(W, dims: DitDims, layout: Layout, cache, x, sigma, n_layers=N
                          k_prefix=np.asarray(kp, np.float64),
                          v_prefix=np.asarray(vp, np.float64))
     return {"v": _output(h, cond, W, dims), "cond": cond}
+
+
+def standardize(z, mean, std):
+    """[1A] and the [INDEX] script's helper of that name: each of the C
+    latent channels is standardized with its own statistics before img_in,
+    ẑ = (z − mean_c) / std_c. z [n, C], mean and std [C]."""
+    z = np.asarray(z, np.float64)
+    return (z - np.asarray(mean, np.float64)) / np.asarray(std, np.float64)
+
+
+def unstandardize(z_std, mean, std):
+    """[6B] §1 Definition: after the last Euler step the latent returns to the
+    VAE's space, z = ẑ·std_c + mean_c per channel (the inverse of [1A])."""
+    return np.asarray(z_std, np.float64) * np.asarray(std, np.float64) + np.asarray(mean, np.float64)
 
 
 def euler_step(x, v, sigma_k, sigma_k1):

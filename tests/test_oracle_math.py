@@ -124,3 +124,25 @@ def test_timestep_embedding_closed_forms():
     assert abs(np.sum(e ** 2) - 128.0) < 1e-10
     # first frequency is 1: entries cos(t), sin(t)
     assert e[0] == math.cos(850.0) and e[128] == math.sin(850.0)
+
+
+def test_standardize_closed_forms_and_inverse():
+    """[1A] standardize and [6B] unstandardize: the channel mean maps to 0 and
+    mean + std to 1, channels are independent, and the two are inverses;
+    checked against hand values, not by re-running the formula."""
+    mean = np.array([0.5, -2.0, 0.0, 3.0])
+    std = np.array([2.0, 0.25, 1.0, 4.0])
+    np.testing.assert_array_equal(O.standardize(mean[None, :], mean, std), np.zeros((1, 4)))
+    np.testing.assert_array_equal(O.standardize((mean + std)[None, :], mean, std), np.ones((1, 4)))
+    z = np.array([[1.5, -1.5, 7.0, -1.0]])
+    np.testing.assert_allclose(O.standardize(z, mean, std), [[0.5, 2.0, 7.0, -1.0]])
+    np.testing.assert_allclose(O.unstandardize([[0.5, 2.0, 7.0, -1.0]], mean, std), z)
+    rng = np.random.default_rng(1)
+    zz = rng.standard_normal((9, 4)) * 3
+    np.testing.assert_allclose(O.unstandardize(O.standardize(zz, mean, std), mean, std), zz,
+                               rtol=0, atol=1e-12)
+    # changing one channel of the input changes only that channel
+    z2 = zz.copy()
+    z2[:, 2] += 1.0
+    d = O.standardize(z2, mean, std) - O.standardize(zz, mean, std)
+    assert np.all(d[:, [0, 1, 3]] == 0) and np.allclose(d[:, 2], 1.0)
