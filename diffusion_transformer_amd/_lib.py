@@ -28,7 +28,7 @@ SEG_TEXT, SEG_REF, SEG_TARGET = 0, 1, 2
 
 EXPORTS = ["dit_build_layout", "dit_load_weights", "dit_free", "dit_workspace_bytes",
            "dit_kv_capacity", "dit_kv_cache_bytes", "dit_step_extract", "dit_step_cached",
-           "euler_update", "dit_img_in", "dit_debug_mask", "dit_debug_attention",
+           "euler_update", "dit_img_in", "dit_latent_standardize", "dit_debug_mask", "dit_debug_attention",
            "dit_debug_gemm", "dit_profile_enable", "dit_profile_read", "dit_last_error",
            "dit_version"]
 
@@ -79,6 +79,7 @@ def _load(path=None):
         "dit_step_cached": (i, [vp, P(dit_seq), vp, f, vp, sz, vp, vp, sz, vp]),
         "euler_update": (i, [vp, vp, f, f, ll, vp]),
         "dit_img_in": (i, [vp, vp, i, vp, vp]),
+        "dit_latent_standardize": (i, [vp, vp, vp, ll, i, i, vp]),
         "dit_debug_mask": (i, [P(dit_seq), vp, vp]),
         "dit_debug_attention": (i, [P(dit_seq), i, vp, i, i, i, vp, vp, i, vp]),
         "dit_debug_gemm": (i, [vp, vp, vp, i, i, i, i, vp]),
@@ -218,6 +219,11 @@ def _make_api(_lib):
     def dit_img_in(model, latents, hidden, stream=None):
         _check(_lib.dit_img_in(model, _ptr(latents), int(latents.shape[0]), _ptr(hidden),
                                _stream(stream)))
+
+    def dit_latent_standardize(z, mean, std, inverse=False, stream=None):
+        """In place on a contiguous float32 [rows, C] device tensor."""
+        _check(_lib.dit_latent_standardize(_ptr(z), _ptr(mean), _ptr(std), int(z.shape[0]),
+                                           int(z.shape[1]), int(bool(inverse)), _stream(stream)))
 
     def dit_debug_mask(seq: dit_seq, mask, stream=None):
         _check(_lib.dit_debug_mask(C.byref(seq), _ptr(mask), _stream(stream)))

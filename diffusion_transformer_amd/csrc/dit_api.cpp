@@ -486,6 +486,18 @@ dit_status euler_update(float* x, const float* v, float sigma_k, float sigma_k1,
   return hip_check(launch_euler(x, v, sigma_k1 - sigma_k, n, static_cast<hipStream_t>(stream)), "euler");
 }
 
+dit_status dit_latent_standardize(float* z, const float* mean, const float* std, long long rows,
+                                  int channels, int inverse, void* stream) {
+  if (!z || !mean || !std) return fail(DIT_ERR_ARG, "NULL argument");
+  if (rows < 0 || channels < 1 || channels > 1024) return fail(DIT_ERR_ARG, "bad rows/channels");
+  if (inverse != 0 && inverse != 1) return fail(DIT_ERR_ARG, "inverse must be 0 or 1");
+  if ((channels & 3) == 0 &&
+      ((reinterpret_cast<uintptr_t>(z) | reinterpret_cast<uintptr_t>(mean) | reinterpret_cast<uintptr_t>(std)) & 15))
+    return fail(DIT_ERR_ARG, "z, mean and std must be 16-byte aligned");
+  return hip_check(launch_standardize(z, mean, std, rows, channels, inverse, static_cast<hipStream_t>(stream)),
+                   "standardize");
+}
+
 dit_status dit_img_in(const dit_model* m, const float* latents, int n, float* hidden, void* stream) {
   if (!m || !latents || !hidden) return fail(DIT_ERR_ARG, "NULL argument");
   if (n < 0) return fail(DIT_ERR_ARG, "negative token count");

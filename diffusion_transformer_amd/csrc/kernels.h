@@ -89,6 +89,9 @@ hipError_t launch_gemv(const uint16_t* W, int O, int I, const float* X, int ldx,
                        float* Y, int ldy, float* Ys, hipStream_t s);
 // [cos(t_v f_i), sin(t_v f_i)], f_i = base^(-2i/D), computed in double.
 hipError_t launch_temb(float t0, float t1, int D, float base, float* out, hipStream_t s);
+// z[r][c] = (z - mean[c]) / std[c] (inverse: z * std[c] + mean[c]), in place.
+hipError_t launch_standardize(float* z, const float* mean, const float* std, long long rows,
+                              int channels, int inverse, hipStream_t s);
 // tanh of the gate sections of nv modulation rows [scale1 | gate1 | scale2 | gate2].
 hipError_t launch_gate_tanh(float* mod, int H, int nv, hipStream_t s);
 // hidden[i][n] = Σ_c W[n][c] x[i][c]; W bf16 [H, 64], x f32 [n, 64].

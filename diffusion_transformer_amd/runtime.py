@@ -118,12 +118,23 @@ class DitRuntime:
             self.L.dit_img_in(self.model, latents.contiguous(), out)
         return out
 
-    def prefix_hidden(self, inputs: dict) -> torch.Tensor:
+    def standardize(self, z: torch.Tensor, stats, inverse=False) -> torch.Tensor:
+        """Per-channel latent (un)standardization on the GPU, in place;
+        ``stats`` = (mean [C], std [C]) device float32 tensors."""
+        self.L.dit_latent_standardize(z, stats[0], stats[1], inverse)
+        return z
+
+    def prefix_hidden(self, inputs: dict, raw_latents=None, stats=None) -> torch.Tensor:
         """Prefix rows in sequence order: text hidden states as given,
-        reference tokens drawn directly or embedded from latents by img_in."""
+        reference tokens drawn directly or embedded from latents by img_in.
+        With ``raw_latents`` [n_ref, C] (VAE space) and ``stats`` the
+        reference latents are standardized on the GPU first (page 1A)."""
         kind = torch.from_numpy(inputs["prefix_kind"].astype(np.int64)).to(self.device)
         text = torch.from_numpy(inputs["text_hidden"]).to(self.device)
-        if "ref_hidden" in inputs:
+        if raw_latents is not None:
+            z = raw_latents.to(self.device, torch.float32).contiguous().clone()
+            ref = self.img_in(self.standardize(z, stats))
+        elif "ref_hidden" in inputs:
             ref = torch.from_numpy(inputs["ref_hidden"]).to(self.device)
         else:
             ref = self.img_in(torch.from_numpy(inputs["ref_latents"]).to(self.device))

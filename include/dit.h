@@ -196,6 +196,17 @@ dit_status dit_step_cached(dit_model* m, const dit_seq* seq, const float* x, flo
 dit_status euler_update(float* x, const float* v, float sigma_k, float sigma_k1, long long n,
                         void* stream);
 
+/* Per-channel latent (un)standardization, in place, float32.
+ * Page "1A · RGBA 64-Ch VAE & Unpatched Latents": each latent channel of a
+ * reference image is standardized with its own statistics before img_in,
+ * z_hat = (z - mean[c]) / std[c]; page 6B §1: after the last Euler step the
+ * latent returns to the VAE's space, z = z_hat * std[c] + mean[c].
+ *   z [rows, channels] f32 (device, in place), mean, std [channels] f32
+ *   (device); inverse 0 = standardize, 1 = unstandardize; channels in
+ *   1..1024. std entries are used as given (a zero std divides by zero). */
+dit_status dit_latent_standardize(float* z, const float* mean, const float* std, long long rows,
+                                  int channels, int inverse, void* stream);
+
 /* img_in (end-to-end lab, block 1A: one latent cell -> one H-wide token):
  * hidden[i] = W_in · latents[i], latents [n, C] f32 -> hidden [n, H] f32.
  * Used to embed reference latents into prefix hidden states. */

@@ -135,3 +135,22 @@ def test_attention_matches_oracle(dev, name, mode, variant):
     err = rel_err(out.float().cpu().numpy(), ref)
     say(f"  rel err {err:.3e}")
     assert err < 1e-2
+
+
+@pytest.mark.parametrize("C", [64, 5])
+def test_latent_standardize_matches_oracle(dev, C):
+    """Per-channel standardize / unstandardize (pages 1A and 6B) on a ragged
+    row count, against the oracle in fp64; C = 5 takes the scalar path."""
+    rows = 4099
+    say(f"latent standardize rows={rows} C={C}")
+    mean, std = synth.latent_stats(C)
+    z = (2.0 * np.random.default_rng(C).standard_normal((rows, C)) + 1.0).astype(np.float32)
+    md, sd = torch.from_numpy(mean).to(dev), torch.from_numpy(std).to(dev)
+    zd = torch.from_numpy(z).to(dev)
+    L.dit_latent_standardize(zd, md, sd)
+    torch.cuda.synchronize()
+    ref = O.standardize(z, mean, std)
+    assert rel_err(zd.cpu().numpy(), ref) < 1e-6
+    L.dit_latent_standardize(zd, md, sd, inverse=True)
+    torch.cuda.synchronize()
+    assert rel_err(zd.cpu().numpy(), O.unstandardize(ref, mean, std)) < 1e-6

@@ -266,3 +266,30 @@ def test_batch_of_targets_shares_one_prefix(dev):
     e = rel_err(vbc[T:2 * T].cpu().numpy()[rows], r1)
     say(f"  element 1 cached rows vs oracle {e:.2e}")
     assert e < TOL_BF16
+
+
+def test_prefix_front_end_and_unstandardized_output(dev):
+    """Reference latents given in VAE space are standardized per channel on
+    the GPU before img_in (page 1A): the prefix equals the one built from the
+    standardized latents. After a short loop the final latent is returned to
+    VAE space (page 6B) and matches the oracle's unstandardized latent."""
+    cfg, W, I, rt, seq, pre, x0 = build("c0w", dev)
+    mean, std = synth.latent_stats(cfg["latent"])
+    md, sd = torch.from_numpy(mean).to(dev), torch.from_numpy(std).to(dev)
+    cfg1, W1, I1, rt1, seq1, pre1, _ = build("c3", dev, n_layers=1)
+    raw = O.unstandardize(I1["ref_latents"], mean, std).astype(np.float32)
+    say(f"c3 prefix from {raw.shape[0]} raw reference latents")
+    pre_raw = rt1.prefix_hidden(I1, raw_latents=torch.from_numpy(raw), stats=(md, sd))
+    torch.cuda.synchronize()
+    assert rel_err(pre_raw.cpu().numpy(), pre1.cpu().numpy()) < 1e-5
+    rt1.close()
+    say("c0w loop, final latent unstandardized")
+    sig = cfg["sigmas"]
+    vs, xs = rt.run_loop(seq, pre, x0, sig, use_cache=True)
+    xf = rt.standardize(xs[-1].clone(), (md, sd), inverse=True)
+    torch.cuda.synchronize()
+    ref = O.run_loop(W, dims_of(cfg), O.build_layout(cfg["segments"]), oracle_prefix(cfg, W, I),
+                     I["x0"], sig, use_cache=True)
+    e = rel_err(xf.cpu().numpy(), O.unstandardize(ref[-1]["x_next"], mean, std))
+    say(f"  unstandardized final latent vs oracle {e:.2e}")
+    assert e < TOL_BF16
