@@ -149,8 +149,13 @@ class DitRuntime:
     def step_cached(self, seq, x, sigma, cache, v, ws, stream=None):
         self.L.dit_step_cached(self.model, seq.c, x, sigma, cache, v, ws, stream)
 
-    def run_loop(self, seq, prefix, x0, sigmas, use_cache=True):
-        """Sampler loop; returns (list of v per step, list of x after each step)."""
+    def run_loop(self, seq, prefix, x0, sigmas, use_cache=True, causal_condition=True):
+        """Sampler loop over any decreasing sigma schedule; returns (list of v
+        per step, list of x after each step). Without causal conditioning
+        every step recomputes (the prefix follows t, so no cache)."""
+        if not causal_condition and use_cache:
+            raise ValueError("without causal conditioning the prefix cache is invalid")
+        flags = 0 if causal_condition else self.L.DIT_FLAG_NO_CAUSAL_CONDITION
         x = x0.clone().contiguous()
         cache = self.alloc_cache(seq)
         ws = self.alloc_workspace(seq.S_all)
@@ -158,7 +163,7 @@ class DitRuntime:
         for k in range(len(sigmas) - 1):
             v = torch.empty_like(x)
             if k == 0 or not use_cache:
-                self.step_extract(seq, prefix, x, sigmas[k], cache, v, ws)
+                self.step_extract(seq, prefix, x, sigmas[k], cache, v, ws, flags=flags)
             else:
                 self.step_cached(seq, x, sigmas[k], cache, v, ws)
             vs.append(v)

@@ -405,17 +405,23 @@ def euler_step(x, v, sigma_k, sigma_k1):
 
 
 def run_loop(W, dims, layout, prefix_hidden, x0, sigmas=TURBO_SIGMAS, use_cache=True,
-             n_layers=None):
+             n_layers=None, causal_condition=True):
     """The sampler loop: step 1 extract, steps 2..N cached (use_cache=True),
     or extract at every step (full recompute). [LAB] §4 Profiling and the
-    [INDEX] script's pipeline driver. Returns list of dict(v, x_next, mode)."""
+    [INDEX] script's pipeline driver. Any decreasing sigma list is a schedule
+    ([6B] §1: Turbo fixes 8 steps; more steps are the general case). With
+    causal_condition False ([3B] §4 Limits) the prefix follows t, its K/V
+    change every step, so the cache is invalid and every step recomputes.
+    Returns list of dict(v, x_next, mode)."""
+    if not causal_condition and use_cache:
+        raise ValueError("without causal conditioning the prefix cache is invalid")
     x = np.asarray(x0, np.float64)
     cache = None
     recs = []
     for k in range(len(sigmas) - 1):
         if k == 0 or not use_cache:
             out = forward_extract(W, dims, layout, prefix_hidden, x, sigmas[k],
-                                  n_layers=n_layers)
+                                  causal_condition=causal_condition, n_layers=n_layers)
             if cache is None:
                 cache = out["cache"]
             mode = "extract"

@@ -293,3 +293,25 @@ def test_prefix_front_end_and_unstandardized_output(dev):
     e = rel_err(xf.cpu().numpy(), O.unstandardize(ref[-1]["x_next"], mean, std))
     say(f"  unstandardized final latent vs oracle {e:.2e}")
     assert e < TOL_BF16
+
+
+@pytest.mark.parametrize("mode", ["linear12", "no_causal"])
+def test_general_schedules_and_no_causal_condition(dev, mode):
+    """The GPU loop over a 12-step linear schedule (cached after step 1), and
+    the loop without t = 0 conditioning (every step recomputes, page 3B §4),
+    against the oracle's loops: v and the latent after every step."""
+    cfg, W, I, rt, seq, pre, x0 = build("c0w", dev)
+    if mode == "linear12":
+        sig, use_cache, cc = tuple(float(s) for s in np.linspace(1.0, 0.0, 13)), True, True
+    else:
+        sig, use_cache, cc = cfg["sigmas"], False, False
+    say(f"c0w loop {mode}: {len(sig) - 1} steps")
+    vs, xs = rt.run_loop(seq, pre, x0, sig, use_cache=use_cache, causal_condition=cc)
+    torch.cuda.synchronize()
+    ref = O.run_loop(W, dims_of(cfg), O.build_layout(cfg["segments"]), oracle_prefix(cfg, W, I),
+                     I["x0"], sig, use_cache=use_cache, causal_condition=cc)
+    for k, r in enumerate(ref):
+        ev = rel_err(vs[k].cpu().numpy(), r["v"])
+        ex = rel_err(xs[k].cpu().numpy(), r["x_next"])
+        assert ev < TOL_BF16 and ex < TOL_BF16, (k, ev, ex)
+    say(f"  last step: v {ev:.2e}, x {ex:.2e}")
