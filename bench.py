@@ -101,11 +101,19 @@ def summarize_profiles(trace_dir, fetch_dir, write_dir, command, out_md, out_jso
 def describe(cfg):
     """Token layout of a workload in words, e.g. '256 text + 64x64 target'."""
     parts = []
-    for seg in cfg["segments"]:
+    segs = list(cfg["segments"])
+    i = 0
+    while i < len(segs):
+        seg, n = segs[i], 1
+        while i + n < len(segs) and segs[i + n] == seg:
+            n += 1
         if seg[0] == "text":
-            parts.append(f"{seg[1]} text")
+            w = f"{seg[1] * n} text"
         else:
-            parts.append(f"{seg[1]}x{seg[2]} {'reference' if seg[0] == 'ref' else 'target'}")
+            w = f"{seg[1]}x{seg[2]} {'reference' if seg[0] == 'ref' else 'target'}"
+            w = f"{n} x {w}s" if n > 1 else w
+        parts.append(w)
+        i += n
     kind = {0: "text-to-image", 1: "image editing"}.get(sum(s[0] == "ref" for s in cfg["segments"]),
                                                        "multi-reference")
     return f"{kind}, " + " + ".join(parts) + " tokens"

@@ -35,6 +35,10 @@ dit_status hip_check(hipError_t e, const char* what) {
 }
 
 constexpr size_t kAlign = 256;
+// Longest joint sequence (all tokens, every target latent): the attention
+// kernels address one head's K or Vᵀ block (capacity x 128 bf16) with 32-bit
+// signed byte offsets, which holds up to 2^23 keys; 2^22 leaves a margin.
+constexpr int kMaxTokens = 1 << 22;
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 struct ExtractRecord {
@@ -91,8 +95,8 @@ dit_status check_seq(const dit_model* m, const dit_seq* s) {
   if (!s) return fail(DIT_ERR_ARG, "seq is NULL");
   if (s->P < 0 || s->T <= 0) return fail(DIT_ERR_LAYOUT, "need P >= 0 and T > 0 (P=%d T=%d)", s->P, s->T);
   if (s->B < 0) return fail(DIT_ERR_ARG, "negative batch %d", s->B);
-  if ((long long)s->P + (long long)(s->B > 1 ? s->B : 1) * s->T > (1 << 24))
-    return fail(DIT_ERR_LAYOUT, "sequence too long");
+  if ((long long)s->P + (long long)(s->B > 1 ? s->B : 1) * s->T > kMaxTokens)
+    return fail(DIT_ERR_LAYOUT, "P + B*T exceeds %d tokens", kMaxTokens);
   if (s->B > 1) {
 #ifdef DIT_F32
     return fail(DIT_ERR_UNSUPPORTED, "several target latents are not part of the fp32 debug build");
@@ -352,7 +356,7 @@ dit_status dit_build_layout(const dit_config* cfg, const int* seg_kind, const in
       ++n_target;
       if (i != n_seg - 1) return fail(DIT_ERR_LAYOUT, "the target image must be the last segment");
     }
-    if (S > (1 << 24)) return fail(DIT_ERR_LAYOUT, "sequence longer than 2^24 tokens");
+    if (S > kMaxTokens) return fail(DIT_ERR_LAYOUT, "sequence longer than %d tokens", kMaxTokens);
   }
   if (n_target != 1) return fail(DIT_ERR_LAYOUT, "exactly one target segment is required");
   int n_ref = 0;

@@ -57,6 +57,21 @@ CONFIGS = {
                segments=[("text", 512), ("ref", 64, 64), ("ref", 64, 64),
                          ("ref", 64, 64), ("target", 96, 96)],
                sigmas=TURBO_SIGMAS),
+    # Many references: 512 text + ten 64x64 references + 96x96 target
+    # (41472 prefix tokens, 50688 in all; 26.6 GB of KV cache).
+    "c5": dict(_BIG, n_layers=32,
+               segments=[("text", 512)] + [("ref", 64, 64)] * 10 + [("target", 96, 96)],
+               sigmas=TURBO_SIGMAS),
+}
+
+# Token layouts (segments only) whose block edges fall off the 64/128/256
+# tile boundaries, for mask and attention tests.
+RAGGED_LAYOUTS = {
+    "ragged": [("text", 37), ("ref", 5, 7), ("text", 3), ("ref", 3, 3), ("target", 9, 11)],
+    # ten references of mixed shapes (one a single cell), text between some
+    "many_ragged": [("text", 61), ("ref", 9, 13), ("ref", 16, 16), ("text", 5), ("ref", 5, 40),
+                    ("ref", 1, 1), ("ref", 33, 7), ("ref", 12, 12), ("text", 2), ("ref", 20, 3),
+                    ("ref", 8, 8), ("ref", 3, 50), ("ref", 17, 17), ("target", 19, 23)],
 }
 
 

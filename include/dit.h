@@ -117,7 +117,8 @@ typedef struct dit_model dit_model; /* opaque host-side handle */
  *   S = P + T entries). x and v_out are [B*T, C], the cache holds
  *   S_all = P + B*T keys, extract workspaces n_tokens = S_all, cached
  *   n_tokens = B*T. B > 1 needs P and T to be multiples of 256
- *   (DIT_ERR_SHAPE otherwise) and is not part of the fp32 debug build. */
+ *   (DIT_ERR_SHAPE otherwise) and is not part of the fp32 debug build.
+ *   S_all above 2^22 tokens is DIT_ERR_LAYOUT. */
 typedef struct dit_seq {
   int P;
   int T;
@@ -142,8 +143,9 @@ typedef struct dit_seq {
  *   [S * head_dim/2] (angles evaluated in double, stored as float),
  *   P_out, T_out.
  * Returns DIT_ERR_LAYOUT for an empty or misplaced target, a non-positive
- * segment size or S > 2^24. With contiguous segments the block-causal rule
- * is exactly j <= row_limit[i]; the library relies on that. */
+ * segment size or S > 2^22 (4194304 tokens, the library's limit). With
+ * contiguous segments the block-causal rule is exactly j <= row_limit[i];
+ * the library relies on that. */
 dit_status dit_build_layout(const dit_config* cfg, const int* seg_kind, const int* seg_rows,
                             const int* seg_cols, int n_seg, int32_t* image_ids,
                             int32_t* coords, int32_t* row_limit, float* rope_cos,

@@ -36,9 +36,13 @@ def cfg_c(name):
                                                   "n_layers", "latent", "time_dim", "rope_dims")})
 
 
-@pytest.mark.parametrize("name", ["c0w", "c1", "c2", "c3", "c4"])
+@pytest.mark.parametrize("name", ["c0w", "c1", "c2", "c3", "c4", "c5", "ragged", "many_ragged"])
 def test_layout_matches_oracle(name):
-    cfg, c = cfg_c(name)
+    if name in synth.RAGGED_LAYOUTS:
+        cfg, c = cfg_c("c1")
+        cfg = dict(cfg, segments=synth.RAGGED_LAYOUTS[name])
+    else:
+        cfg, c = cfg_c(name)
     lay = L.dit_build_layout(c, cfg["segments"])
     ol = O.build_layout(cfg["segments"])
     assert (lay["P"], lay["T"]) == (ol.P, ol.T)
@@ -62,6 +66,10 @@ def test_layout_errors():
     assert e.value.status == L.DIT_ERR_LAYOUT
     with pytest.raises(L.DitError) as e:
         L.dit_build_layout(c, [("text", 3), ("target", 2, 2), ("target", 2, 2)])
+    assert e.value.status == L.DIT_ERR_LAYOUT
+    # the library's sequence limit: 2^22 tokens in all (ten 700x700 references exceed it)
+    with pytest.raises(L.DitError) as e:
+        L.dit_build_layout(c, [("text", 512)] + [("ref", 700, 700)] * 10 + [("target", 96, 96)])
     assert e.value.status == L.DIT_ERR_LAYOUT
 
 
@@ -176,6 +184,11 @@ def test_batch_of_targets_validation():
         neg = L.dit_seq(P, T, FAKE, FAKE, FAKE, -1)
         r = L._lib.dit_step_extract(m, C.byref(neg), FAKE, FAKE, 1.0, FAKE, kvb, FAKE, FAKE, ws_x, 0, None)
         assert r == L.DIT_ERR_ARG
+        # P + B*T beyond 2^22 tokens is refused before any size check
+        long_seq = L.dit_seq(1 << 21, 1 << 20, FAKE, FAKE, FAKE, 3)
+        r = L._lib.dit_step_extract(m, C.byref(long_seq), FAKE, FAKE, 1.0, FAKE, 1 << 60, FAKE,
+                                    FAKE, 1 << 60, 0, None)
+        assert r == L.DIT_ERR_LAYOUT
     finally:
         L.dit_free(m)
     # the fp32 debug build refuses several latents

@@ -66,7 +66,9 @@ LAYOUTS = {
     "c0w": [("text", 2), ("ref", 2, 2), ("text", 1), ("target", 2, 2)],
     "c1": synth.CONFIGS["c1"]["segments"],
     "c3": synth.CONFIGS["c3"]["segments"],
-    "ragged": [("text", 37), ("ref", 5, 7), ("text", 3), ("ref", 3, 3), ("target", 9, 11)],
+    **synth.RAGGED_LAYOUTS,
+    "c4": synth.CONFIGS["c4"]["segments"],
+    "c5": synth.CONFIGS["c5"]["segments"],
 }
 
 
@@ -75,9 +77,9 @@ def layout_for(segments):
     return L.dit_build_layout(c, segments)
 
 
-@pytest.mark.parametrize("name", ["c0w", "c1", "c3", "ragged", "c4"])
+@pytest.mark.parametrize("name", ["c0w", "c1", "c3", "ragged", "many_ragged", "c4", "c5"])
 def test_attention_mask_bit_exact(dev, name):
-    segs = synth.CONFIGS["c4"]["segments"] if name == "c4" else LAYOUTS[name]
+    segs = LAYOUTS[name]
     lay = layout_for(segs)
     S = lay["P"] + lay["T"]
     say(f"mask {name} S={S}")
@@ -111,6 +113,7 @@ def fill_cache(dev, S, nh, seed):
 @pytest.mark.parametrize("variant", [0, 1, 3, 4, 5])
 @pytest.mark.parametrize("name,mode", [("c0w", "extract"), ("c0w", "cached"),
                                        ("ragged", "extract"), ("ragged", "cached"),
+                                       ("many_ragged", "extract"), ("many_ragged", "cached"),
                                        ("c1", "extract"), ("c1", "cached"),
                                        ("c3", "cached")])
 def test_attention_matches_oracle(dev, name, mode, variant):

@@ -59,7 +59,7 @@ def test_loop_matches_oracle(dev, name):
         assert e_cr < TOL_CACHED
 
 
-@pytest.mark.parametrize("name", ["c2", "c3", "c4"])
+@pytest.mark.parametrize("name", ["c2", "c3", "c4", "c5"])
 def test_one_layer_full_token_counts_sampled(dev, name):
     """Real token counts of each workload with one layer: v_θ of 48 sampled
     target rows from extract (σ = 1) and from a cached step (σ = 0.978453, a
@@ -190,12 +190,13 @@ def test_full_depth_cache_invariants(dev, c2_full):
     assert e.value.status == L.DIT_ERR_STATE
 
 
-@pytest.mark.parametrize("name", ["c3", "c4"])
+@pytest.mark.parametrize("name", ["c3", "c4", "c5"])
 def test_full_depth_largest_workloads_cached_matches_recompute(dev, name):
-    """The editing (4352-row prefix) and multi-reference (12800-row prefix,
-    96x96 target, 22016 keys: the largest workload, 11.6 GB of KV cache)
-    workloads at full depth: the first three Turbo steps, cached against full
-    recompute, finite and within the cached-path bound."""
+    """The editing (4352-row prefix), multi-reference (12800-row prefix, 96x96
+    target, 22016 keys, 11.6 GB of KV cache) and ten-reference (41472-row
+    prefix, 50688 keys, 26.6 GB of KV cache) workloads at full depth: the
+    first three Turbo steps, cached against full recompute, finite and within
+    the cached-path bound."""
     from diffusion_transformer_amd.runtime import random_weights_device
     cfg = synth.config(name)
     Wd = random_weights_device(cfg, 21, dev)

@@ -55,11 +55,11 @@ def test_c0_coordinates():
         assert c[:, 1:].tolist() == grid
 
 
-@pytest.mark.parametrize("name", ["c0", "c1", "c2", "c3", "c4"])
+@pytest.mark.parametrize("name", ["c0", "c1", "c2", "c3", "c4", "c5", "ragged", "many_ragged"])
 def test_row_limit_form_equals_rule(name):
     """With contiguous image blocks the rule equals j <= limit[i], limit[i] = i
     for text and the last index of the token's block for image tokens."""
-    cfg = synth.CONFIGS[name]
+    cfg = synth.CONFIGS.get(name) or {"segments": synth.RAGGED_LAYOUTS[name]}
     lay = O.build_layout(cfg["segments"])
     ids = lay.image_ids
     S = lay.S
@@ -72,8 +72,14 @@ def test_row_limit_form_equals_rule(name):
         want[idx] = idx[-1]
     assert (lim == want).all()
     j = np.arange(S)
-    for r0 in range(0, S, 2048):
-        rows = np.arange(r0, min(S, r0 + 2048))
+    check = np.arange(S)
+    if S > 30000:
+        # every row next to a block edge plus 6000 random rows
+        edges = np.nonzero(np.diff(ids))[0]
+        near = np.clip(np.concatenate([edges - 1, edges, edges + 1, edges + 2]), 0, S - 1)
+        check = np.unique(np.concatenate([near, np.random.default_rng(3).choice(S, 6000)]))
+    for r0 in range(0, len(check), 2048):
+        rows = check[r0:r0 + 2048]
         m = O.block_causal_mask(ids, rows=rows)
         assert (m == (j[None, :] <= lim[rows][:, None])).all()
     P, T, Sx = synth.token_counts(cfg)
@@ -106,3 +112,23 @@ def test_image_ids_multi_reference():
     c = lay.coords[lay.P:]
     assert c[:, 1].min() == -48 and c[:, 1].max() == 47
     assert c[0].tolist() == [0, -48, -48] and c[1].tolist() == [0, -48, -47]
+
+
+def test_image_ids_ten_references():
+    """512 text + ten 64x64 references + 96x96 target: reference r is id r on
+    rows 512 + 4096 r .. 512 + 4096 (r+1) - 1, the target is id 10, every
+    reference restarts the zero-centred grid, and each reference row sees
+    all earlier tokens plus its own block only."""
+    lay = O.build_layout(synth.CONFIGS["c5"]["segments"])
+    ids = lay.image_ids
+    assert (lay.P, lay.T, lay.S) == (512 + 10 * 4096, 9216, 512 + 10 * 4096 + 9216)
+    assert (ids[:512] == -1).all()
+    for r in range(10):
+        blk = slice(512 + 4096 * r, 512 + 4096 * (r + 1))
+        assert (ids[blk] == r).all()
+        c = lay.coords[blk]
+        assert c[0].tolist() == [0, -32, -32] and c[-1].tolist() == [0, 31, 31]
+    assert (ids[lay.P:] == 10).all()
+    rows = np.array([512, 512 + 4095, 512 + 4096 * 9, lay.P - 1])
+    m = O.block_causal_mask(ids, rows=rows)
+    assert m.sum(axis=1).tolist() == [512 + 4096, 512 + 4096, 512 + 4096 * 10, 512 + 4096 * 10]
