@@ -291,8 +291,7 @@ def main():
     # ---- per-kernel breakdown of the cached step (separate passes) ----
     breakdown = {}
     if not args.no_breakdown:
-        for name in ("gemm_qkv", "gemm_o", "gemm_gateup", "gemm_down", "attention", "ln",
-                     "qknorm_rope"):
+        for name in ("gemm_qkv", "gemm_o", "gemm_gateup", "gemm_down", "attention", "ln"):
             L.dit_profile_enable(rt.model, name)
             xb = x.clone()
             for k in range(3):
@@ -306,10 +305,6 @@ def main():
                 entry.update({"tflops": round(tf, 1), "frac_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4)})
             elif name == "ln":
                 by = T * H * (4 + 2) + 2 * H * 4
-                gbs = by / (avg / 1e3) / 1e9
-                entry.update({"gbs": round(gbs, 1), "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4)})
-            elif name == "qknorm_rope":
-                by = T * 3 * H * 2 * 2 + T * 64 * 4 * 2
                 gbs = by / (avg / 1e3) / 1e9
                 entry.update({"gbs": round(gbs, 1), "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4)})
             breakdown[name] = entry

@@ -126,6 +126,14 @@ hipError_t launch_gemm(const GemmArgs& g, int epi, hipStream_t s) {
     case EPI_RESID: return run_f32<EPI_RESID>(g, s);
     case EPI_SWIGLU: return run_f32<EPI_SWIGLU>(g, s);
     case EPI_F32: return run_f32<EPI_F32>(g, s);
+    case EPI_QKV: {   // plain GEMM, then the standalone norm / RoPE / cache kernel
+      const hipError_t e = run_f32<EPI_BF16>(g, s);
+      if (e != hipSuccess) return e;
+      QkArgs q = g.qk;
+      q.g_begin = q.q_row0;
+      q.g_end = q.q_row0 + g.M;
+      return launch_qknorm_rope(q, s);
+    }
   }
   return hipErrorInvalidValue;
 }

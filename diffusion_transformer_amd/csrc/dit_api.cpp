@@ -224,24 +224,30 @@ dit_status run_step(dit_model* m, const dit_seq* seq, bool extract, const float*
       Timed tm(m, DIT_PROF_LN, st);
       LAUNCH(launch_ln_mod(hbuf, H, N, H, row_t, row_0, n_pre, c.eps, xb, H, st), "ln1");
     }
+    // QKV projection with the per-head QK-RMSNorm, RoPE and K / Vᵀ cache
+    // writes of tokens q_row0 .. q_row0+N-1 fused into its epilogue
+    QkArgs q{};
+    q.qkv = qkv; q.ld = 3 * H; q.q_row0 = q_row0;
+    q.g_begin = q_row0; q.g_end = q_row0 + N;
+    q.S = SA; q.cap = cap; q.nh = nh; q.H = H; q.P = P; q.T_el = T;
+    q.wq = U(m->qn[l]); q.wk = U(m->kn[l]);
+    q.cosv = seq->d_rope_cos; q.sinv = seq->d_rope_sin;
+    q.kc = kl; q.vtc = vl; q.eps = c.eps;
     {
       Timed tm(m, DIT_PROF_GEMM_QKV, st);
       GemmArgs g{};
       g.A = xb; g.lda = H; g.B = U(m->qkv[l]); g.ldb = H; g.M = N; g.N = 3 * H; g.K = H;
       g.C = qkv; g.ldc = 3 * H;
       g.part = part; g.part_bytes = kGemmPartBytes;
-      LAUNCH(launch_gemm(g, EPI_BF16, st), "gemm qkv");
+      g.qk = q;
+      LAUNCH(launch_gemm(g, EPI_QKV, st), "gemm qkv");
     }
-    {
+    if (extract && cap > SA) {
+      // cache keys SA .. cap-1 (capacity padding) are zero-filled
       Timed tm(m, DIT_PROF_QKNORM_ROPE, st);
-      QkArgs q{};
-      q.qkv = qkv; q.ld = 3 * H; q.q_row0 = q_row0;
-      q.g_begin = extract ? 0 : P; q.g_end = extract ? cap : SA;
-      q.S = SA; q.cap = cap; q.nh = nh; q.H = H; q.P = P; q.T_el = T;
-      q.wq = U(m->qn[l]); q.wk = U(m->kn[l]);
-      q.cosv = seq->d_rope_cos; q.sinv = seq->d_rope_sin;
-      q.kc = kl; q.vtc = vl; q.eps = c.eps;
-      LAUNCH(launch_qknorm_rope(q, st), "qknorm_rope");
+      QkArgs z = q;
+      z.g_begin = SA; z.g_end = cap;
+      LAUNCH(launch_qknorm_rope(z, st), "cache padding");
     }
     {
       Timed tm(m, DIT_PROF_ATTENTION, st);

@@ -591,6 +591,176 @@ __device__ __forceinline__ void store_tile_lds(const GemmArgs& g, f32x16 (&acc)[
   }
 }
 
+// EPI_QKV epilogue. A wave's 128 x 128 patch is one head of q, k or v (the
+// output columns are [q | k | v], 128 per head); the accumulators are
+// rounded to bf16 exactly as EPI_BF16 stores them, so the norm sees the
+// values the unfused path would have read back.
+//  - q, k: the patch is staged row-major in LDS; the 16 lanes of a row (8
+//    dims each) form the RMS over the head's 128 dims, apply (1 + w) and the
+//    row token's 3D RoPE (interleaved pairs), and write q to its row of C
+//    and k to its cache row;
+//  - v: the patch is staged transposed (dim-major) and written to the
+//    transposed cache, 16 lanes (256 bytes of consecutive tokens) per dim.
+// Sum over the 16 lanes of a row (DPP: quad swaps, then half-row and row
+// mirrors), the result in every lane.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, true));
+}
+__device__ __forceinline__ float row16_sum(float v) {
+  v += dpp_f<0xB1>(v);    // quad_perm [1,0,3,2]
+  v += dpp_f<0x4E>(v);    // quad_perm [2,3,0,1]
+  v += dpp_f<0x141>(v);   // row_half_mirror
+  v += dpp_f<0x140>(v);   // row_mirror
+  return v;
+}
+
+__device__ __forceinline__ void store_tile_qkv(const GemmArgs& g, f32x16 (&acc)[4][4], int m0, int n0,
+                                               int wm, int wn, int lane, char* reg) {
+  constexpr int ROWB = 256;                 // bytes per staged row (128 bf16)
+  constexpr int SLOTS = ROWB / 8;
+  const int lrow = lane & 31, lhalf = lane >> 5;
+  const QkArgs& a = g.qk;
+  const int c0 = n0 + wn * 128;
+  const int sec = c0 / a.H;                  // 0 q, 1 k, 2 v (uniform over the wave)
+  const int hh = (c0 - sec * a.H) >> 7;      // head
+  const int rbase = m0 + wm * 128;           // local row of patch row 0
+  const int cc = lane & 15;                  // 16-byte chunk of a staged row
+  if (sec < 2) {
+    // row-major staging, 8-byte slots XOR-swizzled by the row (as EPI_BF16)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = i * 32 + lrow;
+      char* rp = reg + row * ROWB;
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int slot = (2 * (4 * j + q) + lhalf) ^ (row & (SLOTS - 1));
+          u32x2 w;
+          w.x = pack2bf(acc[i][j][4 * q + 0], acc[i][j][4 * q + 1]);
+          w.y = pack2bf(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
+          *reinterpret_cast<u32x2*>(rp + slot * 8) = w;
+        }
+    }
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);   // the region is private to this wave
+    const uint16_t* wv = sec == 0 ? a.wq : a.wk;
+    float w[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) w[j] = 1.f + bf2f(wv[8 * cc + j]);
+    bf16_t* C = reinterpret_cast<bf16_t*>(g.C);
+    // RoPE tables of the lane's 32 rows (R = 4 it + lane/16), loaded up
+    // front. Table row of token gq: gq itself before the prefix end P, else
+    // P + (gq - P) % T_el (the latent's own layout row); it advances by 4
+    // per row step and wraps by T_el.
+    float4 cs[32], sn[32];
+    {
+      const int gq0 = a.q_row0 + rbase + (lane >> 4);
+      int gl = (a.T_el > 0 && gq0 >= a.P) ? a.P + (gq0 - a.P) % a.T_el : gq0;
+      // one subtraction per step wraps when T_el >= 4; tinier latents take
+      // the modulo per row
+      const bool tiny = a.T_el > 0 && a.T_el < 4;
+      const int wrap = a.T_el > 0 ? a.P + a.T_el : 0x7FFFFFFF;
+#pragma unroll
+      for (int it = 0; it < 32; ++it) {
+        const int m = rbase + it * 4 + (lane >> 4);
+        int row = gl;
+        if (tiny) {
+          const int gq = gq0 + it * 4;
+          row = gq >= a.P ? a.P + (gq - a.P) % a.T_el : gq;
+        }
+        row = m < g.M ? row : 0;                // rows past M read a valid row
+        cs[it] = *reinterpret_cast<const float4*>(a.cosv + (size_t)row * 64 + 4 * cc);
+        sn[it] = *reinterpret_cast<const float4*>(a.sinv + (size_t)row * 64 + 4 * cc);
+        gl += 4;
+        gl = gl >= wrap ? gl - a.T_el : gl;
+      }
+    }
+#pragma unroll
+    for (int it = 0; it < 32; ++it) {
+      const int R = it * 4 + (lane >> 4);
+      const int m = rbase + R;
+      // chunk cc of row R (see store_tile_lds)
+      const int pc = cc ^ ((R & (SLOTS - 1)) >> 1);
+      u32x4 v = *reinterpret_cast<const u32x4*>(reg + R * ROWB + pc * 16);
+      if (R & 1) v = (u32x4){v.z, v.w, v.x, v.y};
+      const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+      float x[8];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        x[2 * k] = __uint_as_float(u[k] << 16);
+        x[2 * k + 1] = __uint_as_float(u[k] & 0xFFFF0000u);
+      }
+      float ss = 0.f;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) ss += x[j] * x[j];
+      const float r = rsqrtf(row16_sum(ss) * (1.f / 128.f) + a.eps);
+      const float c4[4] = {cs[it].x, cs[it].y, cs[it].z, cs[it].w};
+      const float s4[4] = {sn[it].x, sn[it].y, sn[it].z, sn[it].w};
+      uint32_t o[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const float x0 = x[2 * k] * r * w[2 * k], x1 = x[2 * k + 1] * r * w[2 * k + 1];
+        o[k] = pack2bf(x0 * c4[k] - x1 * s4[k], x0 * s4[k] + x1 * c4[k]);
+      }
+      const u32x4 ov = {o[0], o[1], o[2], o[3]};
+      if (m < g.M) {
+        if (sec == 0) *reinterpret_cast<u32x4*>(C + (size_t)m * g.ldc + c0 + 8 * cc) = ov;
+        else *reinterpret_cast<u32x4*>(a.kc + ((size_t)hh * a.cap + a.q_row0 + m) * 128 + 8 * cc) = ov;
+      }
+    }
+  } else {
+    // transposed staging: dim row d (128 tokens, 256 bytes), 16-byte token
+    // chunk c at c ^ (d % 16). A lane holds 4 consecutive dims of token t;
+    // the pair of lanes with tokens t, t^1 swaps half of them, so that each
+    // lane writes 2 dims x 2 tokens as two 4-byte words (the even-token lane
+    // dims +0, +1, the odd-token lane dims +2, +3).
+    const bool odd = lrow & 1;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int te = i * 32 + (lrow & ~1);     // even token of the pair
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const uint32_t p01 = pack2bf(acc[i][j][4 * q + 0], acc[i][j][4 * q + 1]);
+          const uint32_t p23 = pack2bf(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
+          // quad_perm [1,0,3,2]: exchange with the neighbouring lane
+          const uint32_t nb = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(odd ? p01 : p23), 0xB1, 0xF, 0xF,
+                                                                    true);
+          const uint32_t mine = odd ? p23 : p01;
+          // words (token te, token te+1) for the lane's two dims
+          const uint32_t lo = odd ? ((nb & 0xFFFFu) | (mine << 16)) : ((mine & 0xFFFFu) | (nb << 16));
+          const uint32_t hi = odd ? ((nb >> 16) | (mine & 0xFFFF0000u)) : ((mine >> 16) | (nb & 0xFFFF0000u));
+          const int d = j * 32 + 8 * q + 4 * lhalf + (odd ? 2 : 0);
+          const int off = (((te >> 3) ^ (d & 15)) << 4) + (te & 7) * 2;
+          *reinterpret_cast<uint32_t*>(reg + d * ROWB + off) = lo;
+          *reinterpret_cast<uint32_t*>(reg + (d + 1) * ROWB + ((((te >> 3) ^ ((d + 1) & 15)) << 4) +
+                                                                (te & 7) * 2)) = hi;
+        }
+    }
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+    act_t* vt = a.vtc + (size_t)hh * 128 * a.cap;
+    const int g0 = a.q_row0 + rbase + 8 * cc;  // first token of the lane's chunk
+    const int mv = rbase + 8 * cc;
+    const bool full = mv + 8 <= g.M && (g0 & 7) == 0;
+#pragma unroll 4
+    for (int it = 0; it < 32; ++it) {
+      const int d = it * 4 + (lane >> 4);
+      const u32x4 v = *reinterpret_cast<const u32x4*>(reg + d * ROWB + ((cc ^ (d & 15)) << 4));
+      act_t* dst = vt + (size_t)d * a.cap + g0;
+      if (full) {
+        *reinterpret_cast<u32x4*>(dst) = v;
+      } else {
+        const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          if (mv + j < g.M) dst[j] = (act_t)((j & 1) ? (u[j >> 1] >> 16) : (u[j >> 1] & 0xFFFF));
+      }
+    }
+  }
+}
+
 // fp32 epilogue through LDS (swapped layout): Hres[m, n] += gate[n] *
 // acc, fp32. The 128 x 128 fp32 patch of a wave (64 KB) is staged in two
 // halves of 64 rows x 512 bytes, 16-byte chunks XOR-swizzled by the row;
@@ -835,6 +1005,7 @@ __global__ __launch_bounds__(256) void gemm_w4_kernel(GemmArgs g) {
     char* reg = reinterpret_cast<char*>((wave < 2 ? st0 : st1)) + (wave & 1) * 32768;
     if (EPI == EPI_RESID) store_tile_lds_f32<false>(g, acc, m0, n0, wm, wn, lane, reg, 0);
     else if (EPI == EPI_PART) store_tile_lds_f32<true>(g, acc, m0, n0, wm, wn, lane, reg, split);
+    else if (EPI == EPI_QKV) store_tile_qkv(g, acc, m0, n0, wm, wn, lane, reg);
     else store_tile_lds<(EPI == EPI_SWIGLU ? EPI_SWIGLU : EPI_BF16)>(g, acc, m0, n0, wm, wn, lane, reg);
   } else {
     store_tile<FM, FN, TM, TN, EPI, SWAP>(g, acc, m0, n0, wm, wn, lrow, lhalf);
@@ -911,6 +1082,7 @@ hipError_t run_epi(const GemmArgs& g, int epi, hipStream_t s) {
     case EPI_BF16: return run_main<EPI_BF16>(g, s);
     case EPI_RESID: return run_main<EPI_RESID>(g, s);
     case EPI_SWIGLU: return run_main<EPI_SWIGLU>(g, s);
+    case EPI_QKV: return run_main<EPI_QKV>(g, s);
   }
   return hipErrorInvalidValue;
 }
@@ -940,6 +1112,16 @@ hipError_t launch_gemm_split(const GemmArgs& g, int epi, int r, int splits, hipS
     case EPI_BF16: return run_reduce<EPI_BF16>(gt, s);
     case EPI_RESID: return run_reduce<EPI_RESID>(gt, s);
     case EPI_SWIGLU: return run_reduce<EPI_SWIGLU>(gt, s);
+    case EPI_QKV: {
+      // the reduced rows are stored as plain bf16 q|k|v, then normalized,
+      // rotated and written to the cache by the standalone kernel
+      e = run_reduce<EPI_BF16>(gt, s);
+      if (e != hipSuccess) return e;
+      QkArgs q = g.qk;
+      q.g_begin = q.q_row0 + gm.M;
+      q.g_end = q.q_row0 + g.M;
+      return launch_qknorm_rope(q, s);
+    }
   }
   return hipErrorInvalidValue;
 }

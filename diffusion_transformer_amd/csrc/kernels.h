@@ -15,12 +15,29 @@ typedef float act_t;
 typedef uint16_t act_t;
 #endif
 
+// Per-head QK-RMSNorm (1 + w) + 3D RoPE on q (in place) and k, and the K /
+// Vᵀ cache writes for global tokens [g_begin, g_end); tokens >= S are
+// zero-filled in the cache. qkv local row i holds global token q_row0 + i.
+struct QkArgs {
+  act_t* qkv; int ld;               // [rows, 3H]
+  int q_row0;
+  int g_begin, g_end, S, cap, nh, H;
+  const uint16_t* wq; const uint16_t* wk;   // [128] bf16
+  const float* cosv; const float* sinv;     // [S, 64]
+  act_t* kc; act_t* vtc;                    // layer bases
+  float eps;
+  int P, T_el;   // rows >= P: RoPE of logical row P + (g - P) % T_el (T_el = 0: g)
+};
+hipError_t launch_qknorm_rope(const QkArgs& a, hipStream_t s);
+
 enum GemmEpi {
   EPI_BF16 = 0,    // C (bf16) = A·Bᵀ
   EPI_F32 = 1,     // C (f32)  = A·Bᵀ
   EPI_RESID = 2,   // Hres (f32) += g[row] ⊙ A·Bᵀ, g = tanh(gate) chosen by the n_pre split
   EPI_SWIGLU = 3,  // C (bf16)[:, f] = SiLU(A·Gᵀ)[f] · (A·Uᵀ)[f]  (B = gate, B2 = up)
-  EPI_PART = 4     // internal: fp32 partial sums of one K split -> part[split][M][N]
+  EPI_PART = 4,    // internal: fp32 partial sums of one K split -> part[split][M][N]
+  EPI_QKV = 5      // C = A·Bᵀ (bf16) with the QK-RMSNorm + RoPE + cache write of `qk` fused:
+                   // q columns to C, k rows and transposed v to the cache
 };
 
 struct GemmArgs {
@@ -35,6 +52,7 @@ struct GemmArgs {
   int n_pre;                        // rows < n_pre use gate_0
   float* part; size_t part_bytes;   // scratch for split-K partial sums (may be null)
   int splits;                       // internal: K splits of an EPI_PART launch
+  QkArgs qk;                        // EPI_QKV: norm weights, RoPE tables, cache, row mapping
 };
 // Bytes of split-K scratch the GEMM launcher can use: at most one round of
 // 256 tiles of 256 x 256 fp32 partial sums.
@@ -68,20 +86,6 @@ hipError_t launch_ln_mod(const float* h, int ldh, int rows, int H, const float* 
                          const float* scale_0, int n_pre, float eps, act_t* out, int ldo,
                          hipStream_t s);
 
-// Per-head QK-RMSNorm (1 + w) + 3D RoPE on q (in place) and k, and the K /
-// Vᵀ cache writes for global tokens [g_begin, g_end); tokens >= S are
-// zero-filled in the cache. qkv local row i holds global token q_row0 + i.
-struct QkArgs {
-  act_t* qkv; int ld;               // [rows, 3H]
-  int q_row0;
-  int g_begin, g_end, S, cap, nh, H;
-  const uint16_t* wq; const uint16_t* wk;   // [128] bf16
-  const float* cosv; const float* sinv;     // [S, 64]
-  act_t* kc; act_t* vtc;                    // layer bases
-  float eps;
-  int P, T_el;   // rows >= P: RoPE of logical row P + (g - P) % T_el (T_el = 0: g)
-};
-hipError_t launch_qknorm_rope(const QkArgs& a, hipStream_t s);
 
 // Y[v][o] = W[o]·X[v] for v < nv (W bf16 [O, I]); optionally also writes
 // silu(Y) to Ys.
