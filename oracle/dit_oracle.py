@@ -340,7 +340,7 @@ def forward_extract(W, dims: DitDims, layout: Layout, prefix_hidden, x, sigma,
     target_token_mask). ``perturb``: optional list of (token, dim, delta)
     added to the joint input (the lab's isolation experiment, [INDEX]
     mapping row 3C). Returns dict(v, cache=[(K [P,nh,d], V [P,nh,d])],
-    k_all=[K [S,nh,d]], h_final [S,H], cond).
+    k_all=[K [S,nh,d]], v_all=[V [S,nh,d]], h_final [S,H], cond).
     """
     W = _f64(W)
     Lc = dims.n_layers if n_layers is None else n_layers
@@ -358,13 +358,14 @@ def forward_extract(W, dims: DitDims, layout: Layout, prefix_hidden, x, sigma,
     s1, g1, s2, g2 = s1.T, g1.T, s2.T, g2.T
     angles = rope_angles(layout.coords, dims)
     allowed = block_causal_mask(layout.image_ids)
-    cache, k_all = [], []
+    cache, k_all, v_all = [], [], []
     for l in range(Lc):
         h, k, v = _layer(h, s1, g1, s2, g2, W["layers"][l], dims, angles, allowed)
         cache.append((k[:P].copy(), v[:P].copy()))
         k_all.append(k)
+        v_all.append(v)
     vel = _output(h[P:], cond, W, dims)
-    return {"v": vel, "cache": cache, "k_all": k_all, "h_final": h, "cond": cond}
+    return {"v": vel, "cache": cache, "k_all": k_all, "v_all": v_all, "h_final": h, "cond": cond}
 
 
 def forward_cached(W, dims: DitDims, layout: Layout, cache, x, sigma, n_layers=None):

@@ -87,6 +87,13 @@ def test_one_layer_full_token_counts_sampled(dev, name):
     assert e0 < TOL_BF16 and e1 < TOL_BF16
 
 
+def nearest_rows(got, ref):
+    """Index of the nearest ref row (squared distance) for every got row."""
+    g = got.astype(np.float64)
+    d2 = (g * g).sum(1)[:, None] + (ref * ref).sum(1)[None, :] - 2.0 * g @ ref.T
+    return np.argmin(d2, axis=1)
+
+
 def test_cache_rows_land_at_their_token_index(dev):
     """After extract, K cache row j of every head holds token j's post-norm,
     post-RoPE key (nearest oracle row is j itself, and values agree to bf16
@@ -103,11 +110,14 @@ def test_cache_rows_land_at_their_token_index(dev):
     lay = O.build_layout(cfg["segments"])
     e = O.forward_extract(W, dims_of(cfg), lay, oracle_prefix(cfg, W, I), I["x0"], 1.0)
     k_ref = e["k_all"][0]                               # [S, nh, d]
+    v_ref = e["v_all"][0]
     for h in (0, 17, 31):
         kg = i16_to_f32(kc[0, h, :seq.S])               # [S, d]
         assert rel_err(kg, k_ref[:, h]) < TOL_BF16
-        d2 = ((kg[:, None, :].astype(np.float64) - k_ref[None, :, h]) ** 2).sum(-1)
-        assert np.array_equal(np.argmin(d2, axis=1), np.arange(seq.S))
+        assert np.array_equal(nearest_rows(kg, k_ref[:, h]), np.arange(seq.S))
+        vg = i16_to_f32(vt[0, h, :, :seq.S].T.contiguous())   # Vᵀ stored dim-major
+        assert rel_err(vg, v_ref[:, h]) < TOL_BF16
+        assert np.array_equal(nearest_rows(vg, v_ref[:, h]), np.arange(seq.S))
     assert int(kc[0, :, seq.S:].abs().sum()) == 0
     assert int(vt[0, :, :, seq.S:].abs().sum()) == 0
 
