@@ -228,3 +228,34 @@ def test_one_hip_runtime_per_process():
     out = subprocess.run([sys.executable, "-c", code], cwd=ROOT, capture_output=True, text=True,
                          check=True).stdout.strip().splitlines()[-1]
     assert out.count("libamdhip64") == 1, out
+
+
+# Random token layouts: text runs and reference images in any order, then
+# one target image; every output of the C layout builder must equal the
+# oracle's plain construction (ids, coordinates, row limits read off the
+# pairwise mask, RoPE tables).
+try:
+    from hypothesis import given, settings, strategies as st
+except ImportError:   # pragma: no cover
+    given = None
+
+if given is not None:
+    _seg = st.one_of(st.tuples(st.just("text"), st.integers(1, 40)),
+                     st.tuples(st.just("ref"), st.integers(1, 12), st.integers(1, 12)))
+
+    @settings(max_examples=60, deadline=None)
+    @given(st.lists(_seg, min_size=0, max_size=12),
+           st.tuples(st.just("target"), st.integers(1, 12), st.integers(1, 12)))
+    def test_random_layouts_match_oracle(prefix, target):
+        segs = list(prefix) + [target]
+        _, c = cfg_c("c1")
+        lay = L.dit_build_layout(c, segs)
+        ol = O.build_layout(segs)
+        assert (lay["P"], lay["T"]) == (ol.P, ol.T)
+        assert np.array_equal(lay["image_ids"], ol.image_ids)
+        assert np.array_equal(lay["coords"], ol.coords)
+        assert np.array_equal(lay["row_limit"], O.row_limits(ol.image_ids))
+        dims = O.DitDims(hidden=4096, n_heads=32, head_dim=128, ffn=16384, n_layers=1)
+        ang = O.rope_angles(ol.coords, dims)
+        assert np.abs(lay["rope_cos"] - np.cos(ang)).max() < 1e-7
+        assert np.abs(lay["rope_sin"] - np.sin(ang)).max() < 1e-7

@@ -140,6 +140,55 @@ def test_attention_matches_oracle(dev, name, mode, variant):
     assert err < 1e-2
 
 
+def random_layout(seed):
+    """Seeded random token layout: 1-10 text runs / reference images of
+    mixed sizes in random order, then a target image (about 300-2500 tokens)."""
+    r = np.random.default_rng(1000 + seed)
+    segs = []
+    for _ in range(int(r.integers(1, 11))):
+        if r.random() < 0.4:
+            segs.append(("text", int(r.integers(1, 80))))
+        else:
+            segs.append(("ref", int(r.integers(1, 24)), int(r.integers(1, 24))))
+    segs.append(("target", int(r.integers(4, 30)), int(r.integers(4, 30))))
+    return segs
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2, 3])
+def test_attention_random_layouts(dev, seed):
+    """Random layouts: the materialized mask is the oracle's rule bit for
+    bit, and every attention variant matches the oracle in extract and
+    cached mode."""
+    nh = 2
+    segs = random_layout(seed)
+    lay = layout_for(segs)
+    P, T = lay["P"], lay["T"]
+    S = P + T
+    say(f"random layout {seed}: {len(segs)} segments, P={P} T={T}")
+    lim = torch.from_numpy(lay["row_limit"]).to(dev)
+    seq = L.make_seq(P, T, lim, lim, lim)
+    mask = torch.full((S * S,), 7, dtype=torch.uint8, device=dev)
+    L.dit_debug_mask(seq, mask)
+    torch.cuda.synchronize()
+    ids = O.build_layout(segs).image_ids
+    want = torch.from_numpy(O.block_causal_mask(ids).astype(np.uint8))
+    assert torch.equal(mask.view(S, S).cpu(), want)
+    cache, K, V = fill_cache(dev, S, nh, seed=S + seed)
+    g = torch.Generator().manual_seed(seed)
+    for mode in ("extract", "cached"):
+        q_off, N = (0, S) if mode == "extract" else (P, T)
+        Q = torch.randn((N, nh, 128), generator=g).to(torch.bfloat16)
+        Qd = Q.reshape(N, nh * 128).contiguous().to(dev)
+        allowed = O.block_causal_mask(ids, rows=np.arange(q_off, q_off + N))
+        ref = O.masked_attention(Q.double().numpy(), K, V, allowed)
+        for variant in (0, 1, 3, 4, 5):
+            out = torch.empty((N, nh * 128), dtype=torch.bfloat16, device=dev)
+            L.dit_debug_attention(seq, nh, Qd, nh * 128, q_off, N, cache, out, variant)
+            torch.cuda.synchronize()
+            err = rel_err(out.float().cpu().numpy(), ref)
+            assert err < 1e-2, (mode, variant, err)
+
+
 @pytest.mark.parametrize("C", [64, 5])
 def test_latent_standardize_matches_oracle(dev, C):
     """Per-channel standardize / unstandardize (pages 1A and 6B) on a ragged
