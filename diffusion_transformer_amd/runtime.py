@@ -149,6 +149,23 @@ class DitRuntime:
     def step_cached(self, seq, x, sigma, cache, v, ws, stream=None):
         self.L.dit_step_cached(self.model, seq.c, x, sigma, cache, v, ws, stream)
 
+    def cached_step_graph(self, seq, x, sigma, sigma_next, cache, v, ws):
+        """Record one cached Euler step -- dit_step_cached(x, sigma) into v,
+        then euler_update(x, v, sigma, sigma_next) in place -- into a HIP
+        graph and return it; graph.replay() re-issues exactly those launches
+        on the current stream (same buffers, same sigmas) without per-launch
+        host work. The step must be valid when recorded (an extract into
+        `cache` before), and the buffers must outlive the graph."""
+        import torch
+        g = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.graph(g, stream=side):
+            self.step_cached(seq, x, sigma, cache, v, ws)
+            self.L.euler_update(x, v, sigma, sigma_next)
+        torch.cuda.current_stream().wait_stream(side)
+        return g
+
     def run_loop(self, seq, prefix, x0, sigmas, use_cache=True, causal_condition=True):
         """Sampler loop over any decreasing sigma schedule; returns (list of v
         per step, list of x after each step). Without causal conditioning

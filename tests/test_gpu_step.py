@@ -326,3 +326,31 @@ def test_general_schedules_and_no_causal_condition(dev, mode):
         ex = rel_err(xs[k].cpu().numpy(), r["x_next"])
         assert ev < TOL_BF16 and ex < TOL_BF16, (k, ev, ex)
     say(f"  last step: v {ev:.2e}, x {ex:.2e}")
+
+
+def test_cached_step_graph_replays_match_eager(dev):
+    """The cached Euler step recorded into a HIP graph: every replay (with
+    eager work and synchronizations between replays) gives the eager step's
+    v and x bit for bit."""
+    cfg, W, I, rt, seq, pre, x0 = build("c1", dev)
+    sig = cfg["sigmas"]
+    cache = rt.alloc_cache(seq)
+    ws = rt.alloc_workspace(seq.S_all)
+    v = torch.empty_like(x0)
+    rt.step_extract(seq, pre, x0.clone(), sig[0], cache, v, ws)
+    xe, ve = x0.clone(), torch.empty_like(x0)
+    rt.step_cached(seq, xe, sig[1], cache, ve, ws)
+    L.euler_update(xe, ve, sig[1], sig[2])
+    torch.cuda.synchronize()
+    xg, vg = x0.clone(), torch.empty_like(x0)
+    g = rt.cached_step_graph(seq, xg, sig[1], sig[2], cache, vg, ws)
+    say("c1 cached step graph: 3 replays")
+    for r in range(3):
+        xg.copy_(x0)
+        vg.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(vg, ve), r
+        assert torch.equal(xg, xe), r
+        assert float((xe * 2).sum()) != 0.0   # eager work between replays
