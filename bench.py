@@ -98,6 +98,104 @@ def summarize_profiles(trace_dir, fetch_dir, write_dir, command, out_md, out_jso
                "algorithmic_bytes": alg}, open(out_json, "w"), indent=1)
 
 
+def summarize_counters(counter_dir, fetch_dir, write_dir, command, out_md):
+    """Per-kernel rocprofv3 counter evidence for the cached step: MFMA
+    instructions (all v_mfma_f32_32x32x16_bf16, 32768 flop each) over the
+    dispatch's own duration against the dense bf16 peak, the matrix-core
+    busy counter, LDS traffic, and for the LayerNorm the calibrated HBM bytes
+    (FETCH_SIZE / WRITE_SIZE runs) against the HBM peak."""
+    import csv
+    from collections import defaultdict
+
+    def per_dispatch(d):
+        rows = list(csv.DictReader(open(os.path.join(d, "run_counter_collection.csv"))))
+        out = defaultdict(lambda: {"counters": defaultdict(float)})
+        for r in rows:
+            e = out[r["Dispatch_Id"]]
+            e["name"] = r["Kernel_Name"]
+            e["grid"] = int(r["Grid_Size"])
+            e["counters"][r["Counter_Name"]] += float(r["Counter_Value"])
+            if r.get("End_Timestamp"):
+                e["ns"] = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+        kt = os.path.join(d, "run_kernel_trace.csv")
+        if os.path.exists(kt):
+            for r in csv.DictReader(open(kt)):
+                if r["Dispatch_Id"] in out:
+                    out[r["Dispatch_Id"]]["ns"] = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+        return out
+
+    disp = per_dispatch(counter_dir)
+    mf = [e["counters"]["SQ_INSTS_MFMA"] for e in disp.values() if "gemm_w4_kernel<2" in e["name"]]
+    split = (min(mf) + max(mf)) / 2 if mf else 0
+
+    def cls(e):
+        n = e["name"]
+        if "gemm_w4_kernel<5" in n:
+            return "QKV GEMM + norm/RoPE/cache epilogue"
+        if GATEUP_KERNEL in n:
+            return "gate/up GEMM (SwiGLU epilogue)"
+        if "gemm_w4_kernel<2" in n:
+            return "O GEMM (residual epilogue)" if e["counters"]["SQ_INSTS_MFMA"] < split else \
+                "down GEMM (residual epilogue)"
+        if "attn2_kernel" in n:
+            return "attention"
+        return None
+
+    groups = defaultdict(list)
+    for e in disp.values():
+        c = cls(e)
+        if c and "ns" in e:
+            groups[c].append(e)
+    lines = ["# rocprofv3 counters per kernel: cached DiT step, c2 workload", "",
+             "Commands (from the repository root on the GPU box; R = repository root):", "", "```",
+             command, "```", "",
+             "MFMA: `SQ_INSTS_MFMA` x 32768 flop (every MFMA here is v_mfma_f32_32x32x16_bf16) over "
+             "each dispatch's own duration, against the dense bf16 peak of 2.5 PFLOP/s. "
+             "`SQ_VALU_MFMA_BUSY_CYCLES` is shown as a fraction of 1024 SIMDs x "
+             "`GRBM_GUI_ACTIVE`/8 (eight XCDs), i.e. per cycle at the clock the kernel actually ran.", "",
+             "| kernel | dispatches | avg us | MFMA instr | TFLOP/s | % bf16 peak | MFMA busy / SIMD-cycle "
+             "| clock GHz | LDS instr | LDS bank conflicts |",
+             "|---|---|---|---|---|---|---|---|---|---|"]
+    for c in ("QKV GEMM + norm/RoPE/cache epilogue", "O GEMM (residual epilogue)",
+              "gate/up GEMM (SwiGLU epilogue)", "down GEMM (residual epilogue)", "attention"):
+        es = groups.get(c)
+        if not es:
+            continue
+        n = len(es)
+        ns = sum(e["ns"] for e in es) / n
+        cs = {k: sum(e["counters"][k] for e in es) / n for k in es[0]["counters"]}
+        tf = cs["SQ_INSTS_MFMA"] * 32768 / (ns * 1e-9) / 1e12
+        cyc = cs["GRBM_GUI_ACTIVE"] / 8
+        busy = cs["SQ_VALU_MFMA_BUSY_CYCLES"] / (1024 * cyc) if cyc else float("nan")
+        lines.append(f"| {c} | {n} | {ns / 1e3:.1f} | {cs['SQ_INSTS_MFMA']:.4g} | {tf:.0f} | "
+                     f"{tf / PEAK_BF16_TFLOPS * 100:.1f} | {busy * 100:.1f}% | {cyc / ns:.2f} | "
+                     f"{cs['SQ_INSTS_LDS']:.4g} | {cs['SQ_LDS_BANK_CONFLICT']:.3g} |")
+    # LayerNorm: calibrated HBM bytes per dispatch
+    res = {}
+    for name, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        dd = per_dispatch(d)
+        cp = [e for e in dd.values() if "bfloat16_copy" in e["name"]]
+        calib = cp[-1]["counters"][name]
+        known_kib = (1 << 28) * (4 if name == "FETCH_SIZE" else 2) / 1024.0
+        ln = [e for e in dd.values() if "ln_mod_kernel" in e["name"] and "ns" in e and e["grid"] == 2048 * 256]
+        res[name] = (known_kib / calib, ln)
+    ff, lnf = res["FETCH_SIZE"]
+    wf, lnw = res["WRITE_SIZE"]
+    if lnf and lnw:
+        fb = sum(e["counters"]["FETCH_SIZE"] for e in lnf) / len(lnf) * ff * 1024
+        wb = sum(e["counters"]["WRITE_SIZE"] for e in lnw) / len(lnw) * wf * 1024
+        ns = (sum(e["ns"] for e in lnf) + sum(e["ns"] for e in lnw)) / (len(lnf) + len(lnw))
+        alg = 4096 * 4096 * 6
+        lines += ["", "## LayerNorm + modulation (4096 rows x 4096): HBM bytes", "",
+                  "| dispatches | avg us | fetched bytes | written bytes | algorithmic | GB/s (measured bytes) "
+                  "| % of 8 TB/s |", "|---|---|---|---|---|---|---|",
+                  f"| {len(lnf)}+{len(lnw)} | {ns / 1e3:.1f} | {fb:.4g} | {wb:.4g} | {alg:.4g} | "
+                  f"{(fb + wb) / (ns * 1e-9) / 1e9:.0f} | {(fb + wb) / (ns * 1e-9) / 1e9 / PEAK_HBM_GBS * 100:.1f} |",
+                  "", f"(FETCH_SIZE x{ff:.3f}, WRITE_SIZE x{wf:.3f} from the fp32->bf16 copy calibration; "
+                  "durations are those of the counter runs.)"]
+    open(out_md, "w").write("\n".join(lines) + "\n")
+
+
 def describe(cfg):
     """Token layout of a workload in words, e.g. '256 text + 64x64 target'."""
     parts = []
@@ -161,6 +259,11 @@ def cpu_baseline(cfg, seconds_hint=True):
 
 
 def main():
+    if len(sys.argv) > 1 and sys.argv[1] == "--summarize-counters":
+        # bench.py --summarize-counters COUNTER_DIR FETCH_DIR WRITE_DIR "COMMAND"
+        summarize_counters(sys.argv[2], sys.argv[3], sys.argv[4], sys.argv[5],
+                           os.path.join(ROOT, "profiles", "counters_c2_cached.md"))
+        return
     if len(sys.argv) > 1 and sys.argv[1] == "--summarize-prof":
         # bench.py --summarize-prof TRACE_DIR FETCH_DIR WRITE_DIR "COMMAND"
         summarize_profiles(sys.argv[2], sys.argv[3], sys.argv[4], sys.argv[5],
