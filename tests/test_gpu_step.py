@@ -354,3 +354,28 @@ def test_cached_step_graph_replays_match_eager(dev):
         assert torch.equal(vg, ve), r
         assert torch.equal(xg, xe), r
         assert float((xe * 2).sum()) != 0.0   # eager work between replays
+
+
+@pytest.mark.parametrize("tgt", [(4, 4), (20, 20)])
+def test_loop_without_prefix(dev, tgt):
+    """A layout with no text and no reference (P = 0): the extract step and
+    the cached steps see only the target tokens, and match the oracle."""
+    cfg = synth.config("c0w", segments=[("target", *tgt)])
+    W = synth.make_weights(cfg)
+    I = synth.make_inputs(cfg)
+    rt = DitRuntime(cfg, W, device=dev)
+    seq = rt.sequence(cfg["segments"])
+    assert seq.P == 0
+    pre = rt.prefix_hidden(I)
+    x0 = torch.from_numpy(I["x0"]).to(dev)
+    sig = cfg["sigmas"]
+    say(f"no prefix: target {tgt}, T={seq.T}")
+    vs, xs = rt.run_loop(seq, pre, x0, sig, use_cache=True)
+    torch.cuda.synchronize()
+    ref = O.run_loop(W, dims_of(cfg), O.build_layout(cfg["segments"]), oracle_prefix(cfg, W, I),
+                     I["x0"], sig, use_cache=True)
+    for k, r in enumerate(ref):
+        e_v = rel_err(vs[k].cpu().numpy(), r["v"])
+        say(f"  step {k} {r['mode']}: v rel {e_v:.3e}")
+        assert e_v < TOL_BF16
+    rt.close()
