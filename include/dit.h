@@ -245,13 +245,13 @@ dit_status dit_debug_gemm(const void* A, const void* B, void* C, int M, int N, i
  * and resets the totals. */
 enum {
   DIT_PROF_OFF = 0,
-  DIT_PROF_GEMM_QKV = 1,
+  DIT_PROF_GEMM_QKV = 1,     /* includes the fused QK norm, RoPE and cache write */
   DIT_PROF_GEMM_O = 2,
   DIT_PROF_GEMM_GATEUP = 3,
   DIT_PROF_GEMM_DOWN = 4,
   DIT_PROF_ATTENTION = 5,
   DIT_PROF_LN = 6,
-  DIT_PROF_QKNORM_ROPE = 7
+  DIT_PROF_QKNORM_ROPE = 7   /* the standalone kernel: cache padding of an extract step */
 };
 dit_status dit_profile_enable(dit_model* m, int kernel_class);
 dit_status dit_profile_read(dit_model* m, double* total_ms, long long* launches);
