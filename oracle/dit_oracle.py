@@ -140,15 +140,17 @@ def block_causal_mask(image_ids, rows=None) -> np.ndarray:
     return causal | same
 
 
-def row_limits(image_ids, chunk: int = 4096) -> np.ndarray:
+def row_limits(image_ids, rows=None, chunk: int = 1024) -> np.ndarray:
     """Largest visible key index per query row under the block-causal rule,
-    read off the pairwise mask (the last True in each row). The mask is
-    formed ``chunk`` query rows at a time only to bound memory."""
+    read off the pairwise mask (the last True in each row), for all rows or
+    the given ``rows``. The mask is formed ``chunk`` query rows at a time
+    only to bound memory."""
     ids = np.asarray(image_ids)
     S = len(ids)
-    out = np.empty(S, dtype=np.int64)
-    for r0 in range(0, S, chunk):
-        m = block_causal_mask(ids, rows=np.arange(r0, min(S, r0 + chunk)))
+    qi = np.arange(S) if rows is None else np.asarray(rows)
+    out = np.empty(len(qi), dtype=np.int64)
+    for r0 in range(0, len(qi), chunk):
+        m = block_causal_mask(ids, rows=qi[r0:r0 + chunk])
         out[r0:r0 + m.shape[0]] = S - 1 - np.argmax(m[:, ::-1], axis=1)
     return out
 

@@ -48,7 +48,14 @@ def test_layout_matches_oracle(name):
     assert (lay["P"], lay["T"]) == (ol.P, ol.T)
     assert np.array_equal(lay["image_ids"], ol.image_ids)
     assert np.array_equal(lay["coords"], ol.coords)
-    assert np.array_equal(lay["row_limit"], O.row_limits(ol.image_ids))
+    S = ol.S
+    rows = np.arange(S)
+    if S > 20000:
+        # the pairwise read-off on every row next to a block edge and 4000 random rows
+        edges = np.nonzero(np.diff(ol.image_ids))[0]
+        near = np.clip(np.concatenate([edges - 1, edges, edges + 1, edges + 2]), 0, S - 1)
+        rows = np.unique(np.concatenate([near, [0, S - 1], np.random.default_rng(5).choice(S, 4000)]))
+    assert np.array_equal(lay["row_limit"][rows], O.row_limits(ol.image_ids, rows=rows))
     dims = O.DitDims(hidden=cfg["hidden"], n_heads=cfg["n_heads"], head_dim=128, ffn=cfg["ffn"],
                      n_layers=1, rope_dims=tuple(cfg["rope_dims"]))
     ang = O.rope_angles(ol.coords, dims)
