@@ -259,6 +259,21 @@ def cpu_baseline(cfg, seconds_hint=True):
 
 
 def main():
+    if len(sys.argv) > 1 and sys.argv[1] == "--summarize-trace":
+        # bench.py --summarize-trace TRACE_DIR TITLE "COMMAND" OUT_MD
+        import csv
+        stats = list(csv.DictReader(open(os.path.join(sys.argv[2], "run_kernel_stats.csv"))))
+        lines = [f"# rocprofv3 kernel stats: {sys.argv[3]}", "",
+                 "Command (from the repository root on the GPU box; R = repository root):", "",
+                 "```", sys.argv[4], "```", "",
+                 "| kernel | calls | avg us | min us | max us | % time |", "|---|---|---|---|---|---|"]
+        for r in stats[:14]:
+            nm = r["Name"].replace("dit::(anonymous namespace)::", "").replace("|", "/")[:80]
+            lines.append(f"| {nm} | {r['Calls']} | {float(r['AverageNs'])/1e3:.1f} | "
+                         f"{float(r['MinNs'])/1e3:.1f} | {float(r['MaxNs'])/1e3:.1f} | "
+                         f"{float(r['Percentage']):.2f} |")
+        open(sys.argv[5], "w").write("\n".join(lines) + "\n")
+        return
     if len(sys.argv) > 1 and sys.argv[1] == "--summarize-counters":
         # bench.py --summarize-counters COUNTER_DIR FETCH_DIR WRITE_DIR "COMMAND"
         summarize_counters(sys.argv[2], sys.argv[3], sys.argv[4], sys.argv[5],
