@@ -37,10 +37,13 @@ def source_sha(path):
         return hashlib.sha256(f.read()).hexdigest()
 
 
-def measured_traffic():
+def measured_traffic(config, batch):
     """HBM bytes per gate/up GEMM launch from the committed rocprofv3 PMC
     runs (FETCH_SIZE and WRITE_SIZE scaled by a copy-kernel calibration), or
-    None when the kernel source changed since those counters were taken."""
+    None when the kernel source changed since those counters were taken or
+    the workload is not the one they were taken on (c2, one latent)."""
+    if config != "c2" or batch != 1:
+        return None
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
@@ -374,7 +377,7 @@ def main():
     gu_tflops = fl["gemm_gateup"] / (gu_avg / 1e3) / 1e12
     roofline = {"bound": "mfma", "achieved": round(gu_tflops, 1), "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(gu_tflops / PEAK_BF16_TFLOPS, 4),
-                "traffic": measured_traffic(), "kernel": GATEUP_LABEL,
+                "traffic": measured_traffic(args.config, B), "kernel": GATEUP_LABEL,
                 "avg_launch_ms": round(gu_avg, 4), "launches": gu_n}
 
     if args.calib_copy:

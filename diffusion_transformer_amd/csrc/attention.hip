@@ -217,7 +217,12 @@ __global__ __launch_bounds__(NT) void attn_kernel(AttnArgs a) {
 //    a ring of 3 stages, two tiles ahead, one barrier per tile;
 //  - the running max is only raised when a query's tile max exceeds it by
 //    more than 2^8 (wave-uniform decision), so O and l are rescaled rarely;
-//    probabilities stay below 2^8 and the final O/l is unchanged.
+//    probabilities stay below 2^8 and the final O/l is unchanged;
+//  - optionally, the last (head, query block) units of the grid are split
+//    over key ranges (AttnArgs::split_*): each piece writes its normalized
+//    O and log2-sum-exp in fp32 and attn_combine_kernel merges them. With
+//    every unit streaming the same keys (target rows of a cached step) this
+//    turns a last, partly filled round of workgroups into a shorter one.
 #define LDSP(p) ((__attribute__((address_space(3))) void*)(p))
 
 // max over the two 32-lane halves of the wave (v_permlane32_swap, no LDS)
@@ -251,8 +256,15 @@ __global__ __launch_bounds__(NWV * 64, (NWV == 4 && NST == 2) ? 2 : 1) void attn
   // each XCD gets a contiguous run of (head, query block) pairs and its L2
   // serves the K/Vᵀ of a few heads instead of all of them.
   const int nqb = (a.N + BQ2 - 1) / BQ2;
-  int bid = blockIdx.x;
-  if ((gridDim.x & 7) == 0) bid = (bid & 7) * (gridDim.x >> 3) + (bid >> 3);
+  int bid = blockIdx.x, piece = -1;
+  if (a.split_s > 1 && bid >= a.split_base) {
+    // piece of a split unit: consecutive blocks are the key ranges of one unit
+    piece = bid - a.split_base;
+    bid = a.split_base + piece / a.split_s;
+  } else {
+    const int nwhole = a.split_s > 1 ? a.split_base : (int)gridDim.x;
+    if ((nwhole & 7) == 0) bid = (bid & 7) * (nwhole >> 3) + (bid >> 3);
+  }
   const int h = bid / nqb, qblk = bid - h * nqb;
   const int lq = lane & 31, half = lane >> 5;
   // Target element of this workgroup's queries (one element per workgroup:
@@ -282,7 +294,15 @@ __global__ __launch_bounds__(NWV * 64, (NWV == 4 && NST == 2) ? 2 : 1) void attn
 #pragma unroll
   for (int w = 1; w < NWV; ++w) blim_max = max(blim_max, red[w]);
   const int kv_end = min(a.S, blim_max + 1);
-  const int ntiles = (kv_end + BKV - 1) / BKV;
+  const int ntiles_all = (kv_end + BKV - 1) / BKV;
+  // a piece j of a split unit takes key tiles [j*n/s, (j+1)*n/s)
+  int ntiles = ntiles_all, kt0 = 0;
+  if (piece >= 0) {
+    const int j = piece % a.split_s;
+    const int t_lo = j * ntiles_all / a.split_s;
+    ntiles = (j + 1) * ntiles_all / a.split_s - t_lo;
+    kt0 = t_lo * BKV;
+  }
 
   bf16x8 qf[NSB][8];
 #pragma unroll
@@ -403,7 +423,8 @@ __global__ __launch_bounds__(NWV * 64, (NWV == 4 && NST == 2) ? 2 : 1) void attn
       // raise the running max only when some query of the wave needs it
       if (__builtin_amdgcn_ballot_w64(mt > m_run[sb] + 8.f)) {
         const float m_new = fmaxf(m_run[sb], mt);
-        const float alpha = __builtin_amdgcn_exp2f(m_run[sb] - m_new);
+        // a query that has seen no key yet keeps m = -inf and alpha = 1
+        const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_run[sb] - m_new);
         m_run[sb] = m_new;
         l_run[sb] *= alpha;
 #pragma unroll
@@ -411,7 +432,9 @@ __global__ __launch_bounds__(NWV * 64, (NWV == 4 && NST == 2) ? 2 : 1) void attn
 #pragma unroll
           for (int r = 0; r < 16; ++r) oacc[sb][j][r] *= alpha;
       }
-      const float nm = -m_run[sb];
+      // (m = -inf: every score so far is -inf and every p below is 0; a key
+      // range that starts past key 0 can have such queries)
+      const float nm = m_run[sb] == -INFINITY ? 0.f : -m_run[sb];
       float ls = l_run[sb];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
@@ -460,8 +483,8 @@ __global__ __launch_bounds__(NWV * 64, (NWV == 4 && NST == 2) ? 2 : 1) void attn
       __builtin_amdgcn_s_barrier();
     };
     if (ntiles > 0) {
-      dma(k0s, v0s, 0);
-      dma(k1s, v1s, min(1, last) * BKV);
+      dma(k0s, v0s, kt0);
+      dma(k1s, v1s, kt0 + min(1, last) * BKV);
       __builtin_amdgcn_s_waitcnt(waitcnt_vm(PER_TILE));
       __builtin_amdgcn_s_barrier();
     }
@@ -469,8 +492,8 @@ __global__ __launch_bounds__(NWV * 64, (NWV == 4 && NST == 2) ? 2 : 1) void attn
     // reader, tile t-1, finished before the previous barrier), compute, then
     // barrier so tile t+1 (stage B) is visible.
     auto iter = [&](u32x4* kA, u32x4* vA, u32x4* kC, u32x4* vC, int t) {
-      dma(kC, vC, min(t + 2, last) * BKV);
-      tile(kA, vA, t * BKV);
+      dma(kC, vC, kt0 + min(t + 2, last) * BKV);
+      tile(kA, vA, kt0 + t * BKV);
       wait_barrier();
     };
     int t = 0;
@@ -486,13 +509,13 @@ __global__ __launch_bounds__(NWV * 64, (NWV == 4 && NST == 2) ? 2 : 1) void attn
     // fall at different times): tile t+1 is fetched into the other stage,
     // whose previous tile was read before the last barrier
     if (ntiles > 0) {
-      dma(k0s, v0s, 0);
+      dma(k0s, v0s, kt0);
       __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
       __builtin_amdgcn_s_barrier();
     }
     auto iter = [&](u32x4* kA, u32x4* vA, u32x4* kB, u32x4* vB, int t) {
-      dma(kB, vB, min(t + 1, last) * BKV);
-      tile(kA, vA, t * BKV);
+      dma(kB, vB, kt0 + min(t + 1, last) * BKV);
+      tile(kA, vA, kt0 + t * BKV);
       __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
       __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
       __builtin_amdgcn_s_barrier();
@@ -505,6 +528,34 @@ __global__ __launch_bounds__(NWV * 64, (NWV == 4 && NST == 2) ? 2 : 1) void attn
     if (t < ntiles) iter(k0s, v0s, k1s, v1s, t);
   }
   __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+
+  if (piece >= 0) {
+    // ---- split piece: normalized O and log2(sum 2^(s*c)) of its keys, fp32;
+    // a piece that saw no key leaves O = 0 and -inf ----
+    const int npieces = (int)gridDim.x - a.split_base;
+    float* po = a.part + (size_t)piece * BQ2 * D;
+    float* pl = a.part + (size_t)npieces * BQ2 * D + (size_t)piece * BQ2;
+#pragma unroll
+    for (int sb = 0; sb < NSB; ++sb) {
+      const float l_tot = l_run[sb] + __shfl_xor(l_run[sb], 32, 64);
+      const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+      const int rl = wave * QW + sb * 32 + lq;
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int d0 = db * 32 + 8 * g + 4 * half;
+          f32x4 w;
+          w[0] = oacc[sb][db][4 * g + 0] * inv;
+          w[1] = oacc[sb][db][4 * g + 1] * inv;
+          w[2] = oacc[sb][db][4 * g + 2] * inv;
+          w[3] = oacc[sb][db][4 * g + 3] * inv;
+          *reinterpret_cast<f32x4*>(po + (size_t)rl * D + d0) = w;
+        }
+      if (half == 0) pl[rl] = l_tot > 0.f ? m_run[sb] + __log2f(l_tot) : -INFINITY;
+    }
+    return;
+  }
 
   // ---- normalize and store O[query][dim] ----
 #pragma unroll
@@ -527,10 +578,83 @@ __global__ __launch_bounds__(NWV * 64, (NWV == 4 && NST == 2) ? 2 : 1) void attn
   }
 }
 
+// Merges the pieces of each split unit: with L = max_j lse_j, the output row
+// is sum_j 2^(lse_j - L) O_j / sum_j 2^(lse_j - L) (the pieces' O_j are
+// already normalized by their own sums). One thread per 4 dims of a row.
+__global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a, int bq) {
+  const int rows_per_blk = 8;
+  const int blks_per_unit = bq / rows_per_blk;
+  const int ui = blockIdx.x / blks_per_unit;
+  const int rl = (blockIdx.x - ui * blks_per_unit) * rows_per_blk + (threadIdx.x >> 5);
+  const int d0 = (threadIdx.x & 31) * 4;
+  const int nqb = (a.N + bq - 1) / bq;
+  const int unit = a.split_base + ui;
+  const int h = unit / nqb, qblk = unit - h * nqb;
+  const int q = qblk * bq + rl;
+  if (q >= a.N) return;
+  const int npieces = (int)gridDim.x / blks_per_unit * a.split_s;
+  const float* lse = a.part + (size_t)npieces * bq * D;
+  float lmax = -INFINITY;
+  for (int j = 0; j < a.split_s; ++j) lmax = fmaxf(lmax, lse[(size_t)(ui * a.split_s + j) * bq + rl]);
+  float acc[4] = {0.f, 0.f, 0.f, 0.f}, wsum = 0.f;
+  if (lmax > -INFINITY) {
+    for (int j = 0; j < a.split_s; ++j) {
+      const int pc = ui * a.split_s + j;
+      const float w = exp2f(lse[(size_t)pc * bq + rl] - lmax);
+      const f32x4 o = *reinterpret_cast<const f32x4*>(a.part + ((size_t)pc * bq + rl) * D + d0);
+      wsum += w;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[i] += w * o[i];
+    }
+  }
+  const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+  u32x2 w;
+  w.x = pack2bf(acc[0] * inv, acc[1] * inv);
+  w.y = pack2bf(acc[2] * inv, acc[3] * inv);
+  *reinterpret_cast<u32x2*>(a.out + (size_t)q * a.out_stride + h * D + d0) = w;
+}
+
+// Compute units of the current device (cached per device).
+int device_cus() {
+  static int cus[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  if (cus[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    cus[dev] = n;
+  }
+  return cus[dev];
+}
+
+// split = 0: never; 1: when it shortens the last round; the grid has
+// units = query blocks x heads workgroups, `per_cu` of them resident per CU.
 template <int NWV, int QW, int NST>
-hipError_t run_attn2(const AttnArgs& a, hipStream_t s) {
-  dim3 grid(((a.N + NWV * QW - 1) / (NWV * QW)) * a.nh);
-  hipLaunchKernelGGL((attn2_kernel<NWV, QW, NST>), grid, dim3(NWV * 64), 0, s, a);
+hipError_t run_attn2(const AttnArgs& a0, hipStream_t s, bool split) {
+  constexpr int BQ2 = NWV * QW;
+  constexpr int per_cu = (NWV == 4 && NST == 2) ? 2 : 1;
+  AttnArgs a = a0;
+  const int units = ((a.N + BQ2 - 1) / BQ2) * a.nh;
+  a.split_base = units; a.split_s = 1;
+  if (split && a.part) {
+    const int slots = device_cus() * per_cu;
+    const int rem = slots > 0 ? units % slots : 0;
+    if (rem > 0) {
+      // pieces of the remaining units fill one round; each keeps >= 8 key tiles
+      int sp = min(slots / rem, 8);
+      sp = min(sp, ((a.S + BKV - 1) / BKV) / 8);
+      const size_t need = (size_t)rem * sp * BQ2 * (D + 1) * sizeof(float);
+      if (sp >= 2 && need <= a.part_bytes) { a.split_base = units - rem; a.split_s = sp; }
+    }
+  }
+  const int nblk = a.split_s > 1 ? a.split_base + (units - a.split_base) * a.split_s : units;
+  hipLaunchKernelGGL((attn2_kernel<NWV, QW, NST>), dim3(nblk), dim3(NWV * 64), 0, s, a);
+  if (a.split_s > 1) {
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(attn_combine_kernel, dim3((units - a.split_base) * (BQ2 / 8)), dim3(256), 0, s,
+                       a, BQ2);
+  }
   return hipGetLastError();
 }
 
@@ -543,21 +667,27 @@ hipError_t launch_attention_variant(const AttnArgs& a, int variant, hipStream_t 
       hipLaunchKernelGGL(attn_kernel, grid, dim3(NT), 0, s, a);
       return hipGetLastError();
     }
-    case 3: return run_attn2<4, 32, 3>(a, s);
-    case 4: return run_attn2<8, 32, 3>(a, s);
-    case 5: return run_attn2<4, 32, 2>(a, s);   // two workgroups per CU
+    case 3: return run_attn2<4, 32, 3>(a, s, false);
+    case 4: return run_attn2<8, 32, 3>(a, s, false);
+    case 5: return run_attn2<4, 32, 2>(a, s, false);   // two workgroups per CU
+    case 6: return run_attn2<8, 32, 3>(a, s, true);    // 4 with the last round split
+    case 7: return run_attn2<4, 32, 2>(a, s, true);    // 5 with the last round split
   }
   return hipErrorInvalidValue;
 }
 
 hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
   // 256 queries per workgroup (8 waves, one workgroup per CU) unless that
-  // leaves CUs idle; 128-query workgroups two per CU (their barriers fall at
-  // different times) for small grids and for target rows that all stream a
-  // long key range (measured: 22016 keys 3.35 -> 3.13 ms, 4352 keys slower)
+  // leaves CUs idle, then 128-query workgroups two per CU. Target rows of a
+  // cached step (q_off > 0) all stream the same keys, so a last, partly
+  // filled round of workgroups is split over key ranges (measured on 32
+  // heads: 9216 queries x 22016 keys 3.11 -> 2.91 ms, x 50688 keys 7.42 ->
+  // 6.71 ms). The rows of an extract step differ in length; there the split
+  // measured slower and is not used.
   const long long blocks256 = (long long)((a.N + 255) / 256) * a.nh;
-  if (blocks256 < 256 || (a.q_off > 0 && a.S >= 8192)) return launch_attention_variant(a, 5, s);
-  return launch_attention_variant(a, 4, s);
+  const bool split = a.q_off > 0;
+  if (blocks256 < 256) return run_attn2<4, 32, 2>(a, s, split);
+  return run_attn2<8, 32, 3>(a, s, split);
 }
 
 

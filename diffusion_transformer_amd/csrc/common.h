@@ -18,6 +18,7 @@ __device__ __forceinline__ float bf2f(bf16_t b) { return __uint_as_float(((uint3
 __device__ __forceinline__ bf16_t f2bf(float f) { return __builtin_bit_cast(bf16_t, (__bf16)f); }
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));           // 16-byte fp32 move
 // Two floats -> packed bf16 pair (a in the low half), one v_cvt_pk_bf16_f32.
 __device__ __forceinline__ uint32_t pack2bf(float a, float b) {
   const f32x2 v = {a, b};

@@ -255,6 +255,7 @@ dit_status run_step(dit_model* m, const dit_seq* seq, bool extract, const float*
       a.q = qkv; a.q_stride = 3 * H; a.q_off = q_row0; a.N = N;
       a.k = kl; a.vt = vl; a.cap = cap; a.S = S; a.nh = nh; a.limit = seq->d_row_limit;
       a.out = att; a.out_stride = H; a.P = P; a.T_el = T;
+      a.part = part; a.part_bytes = kGemmPartBytes;   // free between the GEMMs
       LAUNCH(launch_attention(a, st), "attention");
     }
     {
@@ -547,8 +548,21 @@ dit_status dit_debug_attention(const dit_seq* seq, int n_heads, const void* q, i
   a.out = static_cast<act_t*>(out); a.out_stride = n_heads * 128;
   a.P = seq->P; a.T_el = seq->T;
   if (variant < 0 || variant > 16) return fail(DIT_ERR_ARG, "unknown attention variant %d", variant);
-  if (variant == 0) return hip_check(launch_attention(a, static_cast<hipStream_t>(stream)), "debug attention");
-  return hip_check(launch_attention_variant(a, variant, static_cast<hipStream_t>(stream)), "debug attention");
+  // key-split scratch: one buffer per device, allocated on first use and
+  // kept until the process ends (calls that overlap on one device race)
+  static float* part_of[64] = {nullptr};
+  int dev = 0;
+  dit_status rc2 = hip_check(hipGetDevice(&dev), "debug attention device");
+  if (rc2) return rc2;
+  if (dev < 0 || dev >= 64) return fail(DIT_ERR_UNSUPPORTED, "device index %d", dev);
+  if (!part_of[dev]) {
+    rc2 = hip_check(hipMalloc(&part_of[dev], kGemmPartBytes), "debug attention scratch");
+    if (rc2) return rc2;
+  }
+  a.part = part_of[dev]; a.part_bytes = kGemmPartBytes;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (variant == 0) return hip_check(launch_attention(a, st), "debug attention");
+  return hip_check(launch_attention_variant(a, variant, st), "debug attention");
 #endif
 }
 

@@ -55,7 +55,8 @@ struct GemmArgs {
   QkArgs qk;                        // EPI_QKV: norm weights, RoPE tables, cache, row mapping
 };
 // Bytes of split-K scratch the GEMM launcher can use: at most one round of
-// 256 tiles of 256 x 256 fp32 partial sums.
+// 256 tiles of 256 x 256 fp32 partial sums. The step lends the same buffer
+// to attention's key split (at most 512 x 128 x 129 floats).
 constexpr size_t kGemmPartBytes = (size_t)256 * 256 * 256 * 4;
 
 hipError_t launch_gemm(const GemmArgs& g, int epi, hipStream_t s);
@@ -76,6 +77,10 @@ struct AttnArgs {
   // row - e*T_el (layout tables and the mask describe one element). T_el = 0
   // or S - P: a single latent.
   int P, T_el;
+  // Key-split scratch (fp32; null: no split) and, filled in by the launcher,
+  // the first split unit and the pieces per split unit.
+  float* part; size_t part_bytes;
+  int split_base, split_s;
 };
 hipError_t launch_attention(const AttnArgs& a, hipStream_t s);
 hipError_t launch_attention_variant(const AttnArgs& a, int variant, hipStream_t s);

@@ -224,7 +224,11 @@ dit_status dit_debug_mask(const dit_seq* seq, uint8_t* mask, void* stream);
  *   q [N, q_stride] bf16 with head h at columns h*128.., kv_cache layer 0
  *   of a cache with capacity dit_kv_capacity(S) for n_heads heads,
  *   queries are global rows q_off..q_off+N-1, out [N, n_heads*128] bf16.
- *   variant 0 = the kernel the step uses; 1.. = alternative kernels. */
+ *   variant 0 = the kernel the step uses; 1.. = alternative kernels
+ *   (6, 7: 4, 5 with the last round of workgroups split over key ranges).
+ *   Split variants use a 64 MiB scratch per device, allocated on the
+ *   first call and kept until the process ends: calls that overlap on one
+ *   device race. */
 dit_status dit_debug_attention(const dit_seq* seq, int n_heads, const void* q, int q_stride,
                                int q_off, int N, const void* kv_cache, void* out,
                                int variant, void* stream);

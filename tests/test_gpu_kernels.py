@@ -110,7 +110,7 @@ def fill_cache(dev, S, nh, seed):
     return cache.to(dev), K.double().numpy(), V.double().numpy()
 
 
-@pytest.mark.parametrize("variant", [0, 1, 3, 4, 5])
+@pytest.mark.parametrize("variant", [0, 1, 3, 4, 5, 6, 7])
 @pytest.mark.parametrize("name,mode", [("c0w", "extract"), ("c0w", "cached"),
                                        ("ragged", "extract"), ("ragged", "cached"),
                                        ("many_ragged", "extract"), ("many_ragged", "cached"),
@@ -181,7 +181,7 @@ def test_attention_random_layouts(dev, seed):
         Qd = Q.reshape(N, nh * 128).contiguous().to(dev)
         allowed = O.block_causal_mask(ids, rows=np.arange(q_off, q_off + N))
         ref = O.masked_attention(Q.double().numpy(), K, V, allowed)
-        for variant in (0, 1, 3, 4, 5):
+        for variant in (0, 1, 3, 4, 5, 6, 7):
             out = torch.empty((N, nh * 128), dtype=torch.bfloat16, device=dev)
             L.dit_debug_attention(seq, nh, Qd, nh * 128, q_off, N, cache, out, variant)
             torch.cuda.synchronize()
