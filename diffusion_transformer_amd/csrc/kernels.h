@@ -81,6 +81,7 @@ struct AttnArgs {
   // the first split unit and the pieces per split unit.
   float* part; size_t part_bytes;
   int split_base, split_s;
+  int rev_q;                        // 1: a head's query blocks run last block first
 };
 hipError_t launch_attention(const AttnArgs& a, hipStream_t s);
 hipError_t launch_attention_variant(const AttnArgs& a, int variant, hipStream_t s);
