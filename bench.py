@@ -61,7 +61,7 @@ def summarize_profiles(trace_dir, fetch_dir, write_dir, command, out_md, out_jso
     import csv
     stats = list(csv.DictReader(open(os.path.join(trace_dir, "run_kernel_stats.csv"))))
     lines = [f"# rocprofv3 kernel stats: cached DiT step, c2 workload", "",
-             f"Command (from the repository root on the GPU box):", "", "```", command, "```", "",
+             f"Command (from the repository root on the MI355X machine):", "", "```", command, "```", "",
              "| kernel | calls | avg us | min us | max us | % time |", "|---|---|---|---|---|---|"]
     for r in stats[:16]:
         nm = r["Name"].replace("dit::(anonymous namespace)::", "").replace("|", "/")[:80]
@@ -150,7 +150,7 @@ def summarize_counters(counter_dir, fetch_dir, write_dir, command, out_md):
         if c and "ns" in e:
             groups[c].append(e)
     lines = ["# rocprofv3 counters per kernel: cached DiT step, c2 workload", "",
-             "Commands (from the repository root on the GPU box; R = repository root):", "", "```",
+             "Commands (from the repository root on the MI355X machine; R = repository root):", "", "```",
              command, "```", "",
              "MFMA: `SQ_INSTS_MFMA` x 32768 flop (every MFMA here is v_mfma_f32_32x32x16_bf16) over "
              "each dispatch's own duration, against the dense bf16 peak of 2.5 PFLOP/s. "
@@ -267,7 +267,7 @@ def main():
         import csv
         stats = list(csv.DictReader(open(os.path.join(sys.argv[2], "run_kernel_stats.csv"))))
         lines = [f"# rocprofv3 kernel stats: {sys.argv[3]}", "",
-                 "Command (from the repository root on the GPU box; R = repository root):", "",
+                 "Command (from the repository root on the MI355X machine; R = repository root):", "",
                  "```", sys.argv[4], "```", "",
                  "| kernel | calls | avg us | min us | max us | % time |", "|---|---|---|---|---|---|"]
         for r in stats[:14]:
@@ -305,7 +305,7 @@ def main():
     if args.only_timed:
         args.no_breakdown = True
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
               "(run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
 
