@@ -629,8 +629,9 @@ int device_cus() {
   return cus[dev];
 }
 
-// split = 0: never; 1: when it shortens the last round; the grid has
-// units = query blocks x heads workgroups, `per_cu` of them resident per CU.
+// The grid has units = query blocks x heads workgroups, `per_cu` of them
+// resident per CU. With `split`, the units of a last, partly filled round
+// are split over key ranges when that shortens the round (scratch allowing).
 template <int NWV, int QW, int NST>
 hipError_t run_attn2(const AttnArgs& a0, hipStream_t s, bool split) {
   constexpr int BQ2 = NWV * QW;
@@ -683,8 +684,8 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
   // leaves CUs idle, then 128-query workgroups two per CU. Target rows of a
   // cached step (q_off > 0) all stream the same keys, so a last, partly
   // filled round of workgroups is split over key ranges (measured on 32
-  // heads: 9216 queries x 22016 keys 3.11 -> 2.91 ms, x 50688 keys 7.42 ->
-  // 6.71 ms). The rows of an extract step differ in length; there the split
+  // heads: 9216 queries x 22016 keys 3.11 -> 2.86 ms, x 50688 keys 7.42 ->
+  // 6.47 ms). The rows of an extract step differ in length; there the split
   // measured slower and is not used. Instead each head's query blocks are
   // dealt last block first: target rows (all keys) start first and the short
   // text / reference blocks fill the tail (22016 rows: 4.96 -> 4.57 ms).
