@@ -140,6 +140,35 @@ def test_attention_matches_oracle(dev, name, mode, variant):
     assert err < 1e-2
 
 
+@pytest.mark.parametrize("name", ["many_ragged", "c1", "c3"])
+def test_attention_launch_choices_are_bitwise_neutral(dev, name):
+    """The step's launcher only reorders work: in extract mode it deals query
+    blocks last first (same output, bit for bit, as the unordered kernel), and
+    in cached mode its key split of the last round is the forced-split
+    variant's, bit for bit. With 2 heads every layout here runs the 4-wave
+    kernel (variants 5 and 7)."""
+    nh = 2
+    lay = layout_for(LAYOUTS[name])
+    P, T = lay["P"], lay["T"]
+    S = P + T
+    say(f"launcher order / split {name} S={S}")
+    cache, _, _ = fill_cache(dev, S, nh, seed=S + 7)
+    lim = torch.from_numpy(lay["row_limit"]).to(dev)
+    seq = L.make_seq(P, T, lim, lim, lim)
+    g = torch.Generator().manual_seed(13)
+    for mode, other in (("extract", 5), ("cached", 7)):
+        q_off, N = (0, S) if mode == "extract" else (P, T)
+        Qd = torch.randn((N, nh * 128), generator=g).to(torch.bfloat16).to(dev)
+        outs = []
+        for variant in (0, other):
+            out = torch.full((N, nh * 128), float("nan"), dtype=torch.bfloat16, device=dev)
+            L.dit_debug_attention(seq, nh, Qd, nh * 128, q_off, N, cache, out, variant)
+            outs.append(out)
+        torch.cuda.synchronize()
+        assert not torch.isnan(outs[0].float()).any(), mode
+        assert torch.equal(outs[0].view(torch.int16), outs[1].view(torch.int16)), mode
+
+
 def random_layout(seed):
     """Seeded random token layout: 1-10 text runs / reference images of
     mixed sizes in random order, then a target image (about 300-2500 tokens)."""
