@@ -11,6 +11,7 @@ torch would then load a second one next to it."""
 from __future__ import annotations
 
 import ctypes as C
+import ctypes as C_  # for wrappers whose arguments shadow C
 import os
 
 import numpy as np
@@ -60,6 +61,19 @@ class dit_seq(C.Structure):
                 ("d_rope_cos", C.c_void_p), ("d_rope_sin", C.c_void_p), ("B", C.c_int)]
 
 
+class dit_gemm_desc(C.Structure):
+    _fields_ = [("epilogue", C.c_int), ("M", C.c_int), ("N", C.c_int), ("K", C.c_int),
+                ("A", C.c_void_p), ("B", C.c_void_p), ("B2", C.c_void_p), ("C", C.c_void_p),
+                ("h", C.c_void_p), ("gate_t", C.c_void_p), ("gate_0", C.c_void_p),
+                ("n_pre", C.c_int), ("q_norm", C.c_void_p), ("k_norm", C.c_void_p),
+                ("rope_cos", C.c_void_p), ("rope_sin", C.c_void_p), ("kv_cache", C.c_void_p),
+                ("n_heads", C.c_int), ("S", C.c_int), ("q_row0", C.c_int), ("eps", C.c_float),
+                ("splits", C.c_int), ("scratch", C.c_void_p), ("scratch_bytes", C.c_size_t)]
+
+
+DIT_GEMM = {"bf16": 0, "f32": 1, "resid": 2, "swiglu": 3, "qkv": 5}
+
+
 def _load(path=None):
     path = path or LIB_PATH
     if not os.path.exists(path):
@@ -81,8 +95,8 @@ def _load(path=None):
         "dit_img_in": (i, [vp, vp, i, vp, vp]),
         "dit_latent_standardize": (i, [vp, vp, vp, ll, i, i, vp]),
         "dit_debug_mask": (i, [P(dit_seq), vp, vp]),
-        "dit_debug_attention": (i, [P(dit_seq), i, vp, i, i, i, vp, vp, i, vp]),
-        "dit_debug_gemm": (i, [vp, vp, vp, i, i, i, i, vp]),
+        "dit_debug_attention": (i, [P(dit_seq), i, vp, i, i, i, vp, vp, i, vp, sz, vp]),
+        "dit_debug_gemm": (i, [P(dit_gemm_desc), vp]),
         "dit_profile_enable": (i, [vp, i]),
         "dit_profile_read": (i, [vp, P(C.c_double), P(ll)]),
         "dit_last_error": (C.c_char_p, []),
@@ -179,9 +193,11 @@ def _make_api(_lib):
                            ("qkv", "q_norm", "k_norm", "o", "gate", "up", "down")])
         h = C.c_void_p()
         _check(_lib.dit_load_weights(C.byref(cfg), C.byref(ws), C.byref(h)))
+        _dims[h.value] = (cfg.hidden, cfg.latent)
         return h.value
 
     def dit_free(model):
+        _dims.pop(model, None)
         _lib.dit_free(model)
 
     def dit_workspace_bytes(model, n_tokens: int) -> int:
@@ -200,19 +216,51 @@ def _make_api(_lib):
     def _nbytes(t):
         return t.numel() * t.element_size()
 
+    _dims = {}   # model handle -> (hidden, latent), for the host-side tensor checks
+
+    def _need(t, what, numel, dtype=None):
+        """The C ABI cannot see tensor sizes: check on the host that a tensor
+        handed to a step is a contiguous float32 device tensor of the size
+        the call will read or write."""
+        dtype = torch.float32 if dtype is None else dtype
+        ok = (isinstance(t, torch.Tensor) and t.is_cuda and t.dtype == dtype and t.is_contiguous()
+              and t.numel() == numel)
+        if not ok:
+            desc = (f"{tuple(t.shape)} {t.dtype} on {t.device}, contiguous={t.is_contiguous()}"
+                    if isinstance(t, torch.Tensor) else type(t).__name__)
+            raise DitError(DIT_ERR_ARG, f"{what}: need a contiguous {dtype} device tensor of "
+                                        f"{numel} elements, got {desc}")
+
+    def _step_tensors(model, seq, x, v_out, prefix_hidden=None):
+        if model not in _dims:
+            raise DitError(DIT_ERR_ARG, "model handle is not loaded")
+        H, Cl = _dims[model]
+        rows = max(int(seq.B), 1) * int(seq.T)
+        _need(x, "x", rows * Cl)
+        _need(v_out, "v_out", rows * Cl)
+        if prefix_hidden is not None or seq.P > 0:
+            _need(prefix_hidden, "prefix_hidden", int(seq.P) * H)
+
     def dit_step_extract(model, seq: dit_seq, prefix_hidden, x, sigma, kv_cache, v_out, workspace,
                          flags=0, stream=None):
+        _step_tensors(model, seq, x, v_out, prefix_hidden)
         _check(_lib.dit_step_extract(model, C.byref(seq), _ptr(prefix_hidden), _ptr(x), float(sigma),
                                      _ptr(kv_cache), _nbytes(kv_cache), _ptr(v_out), _ptr(workspace),
                                      _nbytes(workspace), int(flags), _stream(stream)))
 
     def dit_step_cached(model, seq: dit_seq, x, sigma, kv_cache, v_out, workspace, stream=None):
+        _step_tensors(model, seq, x, v_out)
         _check(_lib.dit_step_cached(model, C.byref(seq), _ptr(x), float(sigma), _ptr(kv_cache),
                                     _nbytes(kv_cache), _ptr(v_out), _ptr(workspace),
                                     _nbytes(workspace), _stream(stream)))
 
     def euler_update(x, v, sigma_k, sigma_k1, n=None, stream=None):
-        n = x.numel() if n is None else n
+        n = x.numel() if n is None else int(n)
+        for t, what in ((x, "x"), (v, "v")):
+            if not (isinstance(t, torch.Tensor) and t.is_cuda and t.dtype == torch.float32
+                    and t.is_contiguous() and t.numel() >= n):
+                raise DitError(DIT_ERR_ARG, f"euler_update: {what} must be a contiguous float32 "
+                                            f"device tensor of at least {n} elements")
         _check(_lib.euler_update(_ptr(x), _ptr(v), float(sigma_k), float(sigma_k1), int(n),
                                  _stream(stream)))
 
@@ -229,13 +277,30 @@ def _make_api(_lib):
         _check(_lib.dit_debug_mask(C.byref(seq), _ptr(mask), _stream(stream)))
 
     def dit_debug_attention(seq: dit_seq, n_heads, q, q_stride, q_off, N, kv_cache, out, variant=0,
-                            stream=None):
+                            scratch=None, stream=None):
         _check(_lib.dit_debug_attention(C.byref(seq), int(n_heads), _ptr(q), int(q_stride), int(q_off),
-                                        int(N), _ptr(kv_cache), _ptr(out), int(variant), _stream(stream)))
+                                        int(N), _ptr(kv_cache), _ptr(out), int(variant), _ptr(scratch),
+                                        _nbytes(scratch) if scratch is not None else 0,
+                                        _stream(stream)))
 
-    def dit_debug_gemm(A, B, Cmat, M, N, K, variant=0, stream=None):
-        _check(_lib.dit_debug_gemm(_ptr(A), _ptr(B), _ptr(Cmat), int(M), int(N), int(K), int(variant),
-                                   _stream(stream)))
+    def dit_debug_gemm(epilogue, M, N, K, A, B, C=None, B2=None, h=None, gate_t=None, gate_0=None,
+                       n_pre=0, q_norm=None, k_norm=None, rope_cos=None, rope_sin=None,
+                       kv_cache=None, n_heads=0, S=0, q_row0=0, eps=1e-6, splits=0, scratch=None,
+                       stream=None):
+        """``epilogue``: one of DIT_GEMM's names or values (see dit_gemm_desc)."""
+        d = dit_gemm_desc()
+        d.epilogue = DIT_GEMM.get(epilogue, epilogue) if isinstance(epilogue, str) else int(epilogue)
+        d.M, d.N, d.K = int(M), int(N), int(K)
+        d.A, d.B, d.B2, d.C = _ptr(A), _ptr(B), _ptr(B2), _ptr(C)
+        d.h, d.gate_t, d.gate_0, d.n_pre = _ptr(h), _ptr(gate_t), _ptr(gate_0), int(n_pre)
+        d.q_norm, d.k_norm, d.rope_cos, d.rope_sin = _ptr(q_norm), _ptr(k_norm), _ptr(rope_cos), \
+            _ptr(rope_sin)
+        d.kv_cache, d.n_heads, d.S, d.q_row0, d.eps = _ptr(kv_cache), int(n_heads), int(S), \
+            int(q_row0), float(eps)
+        d.splits = int(splits)
+        d.scratch = _ptr(scratch)
+        d.scratch_bytes = _nbytes(scratch) if scratch is not None else 0
+        _check(_lib.dit_debug_gemm(C_.byref(d), _stream(stream)))
 
     def dit_profile_enable(model, kernel_class):
         if isinstance(kernel_class, str):
@@ -259,7 +324,7 @@ def _bind(path):
     ns.DitError = DitError
     for k in ("DIT_OK", "DIT_ERR_ARG", "DIT_ERR_SHAPE", "DIT_ERR_LAYOUT", "DIT_ERR_STATE",
               "DIT_ERR_WORKSPACE", "DIT_ERR_HIP", "DIT_ERR_UNSUPPORTED", "DIT_FLAG_NO_CAUSAL_CONDITION",
-              "PROF", "dit_seq", "dit_config", "dit_weights"):
+              "PROF", "DIT_GEMM", "dit_seq", "dit_config", "dit_weights", "dit_gemm_desc"):
         setattr(ns, k, globals()[k])
     return ns
 

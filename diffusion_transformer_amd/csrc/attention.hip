@@ -2,18 +2,13 @@
 // block-causal mask in row-limit form (key j visible to query i iff
 // j <= limit[i]); masked keys get exactly zero weight.
 //
-// Both kernels compute scores transposed, Sᵀ = K·Qᵀ (32 keys × 32 queries
+// Scores are computed transposed, Sᵀ = K·Qᵀ (32 keys × 32 queries
 // per MFMA block), so each lane holds keys of ONE query and the row max/sum
 // need in-lane work plus one exchange between the wave halves; the output is
 // accumulated transposed as well, Oᵀ = Vᵀ·Pᵀ, which lets the probabilities
 // feed the MFMA B operand straight from registers. V is kept transposed
 // (dim-major) in the cache. Waves whose queries see none of a key tile skip
 // its arithmetic; tiles past the workgroup's largest limit are never loaded.
-//
-// attn_kernel: first version (4 waves × 32 queries, K/Vᵀ tiles staged
-// through registers), kept as a reference variant.
-// attn2_kernel: the step's kernel; its own comment below lists the
-// differences.
 #include "common.h"
 #include "kernels.h"
 
@@ -22,192 +17,10 @@ namespace dit {
 namespace {
 
 constexpr int D = 128;
-constexpr int BQ = 128;
 constexpr int BKV = 64;
-constexpr int NT = 256;
-
-__global__ __launch_bounds__(NT) void attn_kernel(AttnArgs a) {
-  __shared__ u32x4 ks[2][BKV * 16];        // [key][16 chunks of 8 dims], chunk ^= key%16
-  __shared__ u32x2 vs[2][D * 16];          // [dim][16 chunks of 4 keys], chunk ^= (dim/2)%16
-  __shared__ int red[8];
-
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int h = blockIdx.y;
-  const int q_blk = blockIdx.x * BQ;
-  const int lq = lane & 31, half = lane >> 5;
-  const int qi = min(q_blk + wave * 32 + lq, a.N - 1);   // local query row (clamped)
-  const bool q_valid = q_blk + wave * 32 + lq < a.N;
-  const int lim = a.limit[a.q_off + qi];
-
-  const int wlim_min = wave_min_i(lim), wlim_max = wave_max_i(lim);
-  if (lane == 0) red[wave] = wlim_max;
-  __syncthreads();
-  const int blim_max = max(max(red[0], red[1]), max(red[2], red[3]));
-  const int kv_end = min(a.S, blim_max + 1);
-  const int ntiles = (kv_end + BKV - 1) / BKV;
-
-  // Q fragment as MFMA B operand: lane holds Q[query lq][16s + 8*half .. +7]
-  bf16x8 qf[8];
-  {
-    const u32x4* qp = reinterpret_cast<const u32x4*>(a.q + (size_t)qi * a.q_stride + h * D);
-#pragma unroll
-    for (int s = 0; s < 8; ++s) qf[s] = __builtin_bit_cast(bf16x8, qp[2 * s + half]);
-  }
-
-  const uint16_t* kbase = a.k + (size_t)h * a.cap * D;
-  const uint16_t* vbase = a.vt + (size_t)h * D * a.cap;
-
-  // per-thread load slots: K 4 chunks of 16 B, Vᵀ 4 chunks of 16 B
-  int k_row[4], k_c[4], v_row[4], v_c[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    int q = tid + i * NT;
-    k_row[i] = q >> 4; k_c[i] = q & 15;
-    v_row[i] = q >> 3; v_c[i] = q & 7;
-  }
-  u32x4 rk[4], rv[4];
-  auto gload = [&](int kv0) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      rk[i] = *reinterpret_cast<const u32x4*>(kbase + (size_t)(kv0 + k_row[i]) * D + k_c[i] * 8);
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      rv[i] = *reinterpret_cast<const u32x4*>(vbase + (size_t)v_row[i] * a.cap + kv0 + v_c[i] * 8);
-  };
-  auto lstore = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) ks[buf][k_row[i] * 16 + (k_c[i] ^ (k_row[i] & 15))] = rk[i];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int e = v_row[i];
-      const int c0 = 2 * v_c[i], c1 = c0 + 1;
-      u32x2 lo, hi;
-      lo.x = rv[i].x; lo.y = rv[i].y; hi.x = rv[i].z; hi.y = rv[i].w;
-      vs[buf][e * 16 + (c0 ^ ((e >> 1) & 15))] = lo;
-      vs[buf][e * 16 + (c1 ^ ((e >> 1) & 15))] = hi;
-    }
-  };
-
-  f32x16 oacc[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) oacc[j][r] = 0.f;
-  float m_run = -INFINITY, l_run = 0.f;
-  const float sl2 = 1.4426950408889634f * 0.08838834764831845f;   // log2(e)/sqrt(128)
-
-  if (ntiles > 0) {
-    gload(0);
-    lstore(0);
-  }
-  __syncthreads();
-
-  for (int t = 0; t < ntiles; ++t) {
-    const int cur = t & 1;
-    const int kv0 = t * BKV;
-    const bool more = t + 1 < ntiles;
-    if (more) gload(kv0 + BKV);
-
-    const int cls = tile_class<BKV>(kv0, wlim_min, wlim_max, a.S);
-    if (cls != 0) {
-      // ---- Sᵀ = K·Qᵀ for 64 keys ----
-      f32x16 sacc[2];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.f;
-#pragma unroll
-      for (int s = 0; s < 8; ++s) {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          const int row = kb * 32 + lq;
-          bf16x8 kf = __builtin_bit_cast(bf16x8, ks[cur][row * 16 + ((2 * s + half) ^ (row & 15))]);
-          sacc[kb] = mfma32(kf, qf[s], sacc[kb]);
-        }
-      }
-      // ---- scale, mask, online softmax (lane = one query, 32 of its keys) ----
-      float mt = -INFINITY;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float v = sacc[kb][r] * sl2;
-          if (cls == 2) {
-            const int j = kv0 + kb * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-            if (!key_visible(j, lim, a.S)) v = -INFINITY;
-          }
-          sacc[kb][r] = v;
-          mt = fmaxf(mt, v);
-        }
-      mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
-      const float m_new = fmaxf(m_run, mt);
-      // m_new is finite: key 0 is visible to every query and tile 0 is
-      // processed first; later all-masked rows keep m_run.
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-      m_run = m_new;
-      float ls = 0.f;
-      uint32_t pk[2][8];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; r += 2) {
-          const float p0 = __builtin_amdgcn_exp2f(sacc[kb][r] - m_new);
-          const float p1 = __builtin_amdgcn_exp2f(sacc[kb][r + 1] - m_new);
-          ls += p0 + p1;
-          pk[kb][r >> 1] = pack2bf(p0, p1);
-        }
-      l_run = l_run * alpha + ls;
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[j][r] *= alpha;
-      // ---- Oᵀ += Vᵀ·Pᵀ over 4 chunks of 16 keys ----
-      // chunk c = registers 8(c%2)..+7 of key block c/2: this lane's keys
-      // 16c + 4*half + {0..3} and 16c + 8 + 4*half + {0..3}.
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        u32x4 pb;
-        pb.x = pk[c >> 1][4 * (c & 1) + 0];
-        pb.y = pk[c >> 1][4 * (c & 1) + 1];
-        pb.z = pk[c >> 1][4 * (c & 1) + 2];
-        pb.w = pk[c >> 1][4 * (c & 1) + 3];
-        const bf16x8 pf = __builtin_bit_cast(bf16x8, pb);
-        const int k8a = 4 * c + half, k8b = 4 * c + 2 + half;
-#pragma unroll
-        for (int db = 0; db < 4; ++db) {
-          const int e = db * 32 + lq;
-          const u32x2 va = vs[cur][e * 16 + (k8a ^ ((e >> 1) & 15))];
-          const u32x2 vb = vs[cur][e * 16 + (k8b ^ ((e >> 1) & 15))];
-          u32x4 vv;
-          vv.x = va.x; vv.y = va.y; vv.z = vb.x; vv.w = vb.y;
-          oacc[db] = mfma32(__builtin_bit_cast(bf16x8, vv), pf, oacc[db]);
-        }
-      }
-    }
-    if (more) lstore(cur ^ 1);
-    __syncthreads();
-  }
-
-  // ---- normalize and store O[query][dim] ----
-  const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
-  const float inv = 1.f / l_tot;
-  if (q_valid) {
-    uint16_t* op = a.out + (size_t)qi * a.out_stride + h * D;
-#pragma unroll
-    for (int db = 0; db < 4; ++db)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int d0 = db * 32 + 8 * g + 4 * half;
-        u32x2 w;
-        w.x = pack2bf(oacc[db][4 * g + 0] * inv, oacc[db][4 * g + 1] * inv);
-        w.y = pack2bf(oacc[db][4 * g + 2] * inv, oacc[db][4 * g + 3] * inv);
-        *reinterpret_cast<u32x2*>(op + d0) = w;
-      }
-  }
-}
 
 // ---------------------------------------------------------------------------
-// Second-generation kernel. Differences from attn_kernel:
+// attn2_kernel<NWV, QW, NST>: NWV waves, QW queries per wave, NST stages.
 //  - each wave owns QW queries (QW/32 sub-blocks of 32) that share every K
 //    and Vᵀ fragment read, halving LDS traffic per FLOP at QW = 64;
 //  - K rows enter the score MFMA in the order π(i) = i with bits 2 and 3
@@ -223,7 +36,6 @@ __global__ __launch_bounds__(NT) void attn_kernel(AttnArgs a) {
 //    O and log2-sum-exp in fp32 and attn_combine_kernel merges them. With
 //    every unit streaming the same keys (target rows of a cached step) this
 //    turns a last, partly filled round of workgroups into a shorter one.
-#define LDSP(p) ((__attribute__((address_space(3))) void*)(p))
 
 // max over the two 32-lane halves of the wave (v_permlane32_swap, no LDS)
 __device__ __forceinline__ float half_max(float x) {
@@ -665,16 +477,10 @@ hipError_t run_attn2(const AttnArgs& a0, hipStream_t s, bool split) {
 
 hipError_t launch_attention_variant(const AttnArgs& a, int variant, hipStream_t s) {
   switch (variant) {
-    case 1: {
-      dim3 grid((a.N + BQ - 1) / BQ, a.nh);
-      hipLaunchKernelGGL(attn_kernel, grid, dim3(NT), 0, s, a);
-      return hipGetLastError();
-    }
-    case 3: return run_attn2<4, 32, 3>(a, s, false);
-    case 4: return run_attn2<8, 32, 3>(a, s, false);
-    case 5: return run_attn2<4, 32, 2>(a, s, false);   // two workgroups per CU
-    case 6: return run_attn2<8, 32, 3>(a, s, true);    // 4 with the last round split
-    case 7: return run_attn2<4, 32, 2>(a, s, true);    // 5 with the last round split
+    case 1: return run_attn2<8, 32, 3>(a, s, false);
+    case 2: return run_attn2<4, 32, 2>(a, s, false);   // two workgroups per CU
+    case 3: return run_attn2<8, 32, 3>(a, s, true);    // 1 with the last round split
+    case 4: return run_attn2<4, 32, 2>(a, s, true);    // 2 with the last round split
   }
   return hipErrorInvalidValue;
 }

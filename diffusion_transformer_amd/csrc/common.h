@@ -108,6 +108,9 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
+// LDS destination pointer of a buffer_load ... lds (address space 3).
+#define LDSP(p) ((__attribute__((address_space(3))) void*)(p))
+
 // Raw buffer resource over [p, p + bytes): loads past the end return zero.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);

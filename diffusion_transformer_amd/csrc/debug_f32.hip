@@ -138,7 +138,7 @@ hipError_t launch_gemm(const GemmArgs& g, int epi, hipStream_t s) {
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_gemm_variant(const GemmArgs&, int, hipStream_t) { return hipErrorInvalidValue; }
+hipError_t launch_gemm_forced_split(const GemmArgs&, int, int, hipStream_t) { return hipErrorInvalidValue; }
 
 hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
   dim3 grid((a.N + 3) / 4, a.nh);

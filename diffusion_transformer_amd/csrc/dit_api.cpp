@@ -7,6 +7,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -53,6 +54,9 @@ struct dit_model {
   const void* t1; const void* t2; const void* mod; const void* so;
   const void* img_in; const void* proj_out;
   std::vector<const void*> qkv, qn, kn, o, gate, up, down;
+  // Mutable host state, guarded by `mu`: the registry of extracted caches
+  // and the timing events.
+  std::mutex mu;
   std::vector<ExtractRecord> extracted;
   int prof_class = 0;
   std::vector<hipEvent_t> ev_start, ev_stop;
@@ -461,6 +465,7 @@ dit_status dit_step_extract(dit_model* m, const dit_seq* seq, const float* prefi
   if (seq->P > 0 && !prefix_hidden) return fail(DIT_ERR_ARG, "prefix_hidden is NULL");
   if (flags & ~DIT_FLAG_NO_CAUSAL_CONDITION) return fail(DIT_ERR_ARG, "unknown flags 0x%x", flags);
   if (!std::isfinite(sigma)) return fail(DIT_ERR_ARG, "sigma is not finite");
+  std::lock_guard<std::mutex> lock(m->mu);
   // forget any previous extract of this cache before overwriting it
   for (size_t i = 0; i < m->extracted.size(); ++i)
     if (m->extracted[i].kv == kv_cache) { m->extracted.erase(m->extracted.begin() + i); break; }
@@ -478,6 +483,7 @@ dit_status dit_step_cached(dit_model* m, const dit_seq* seq, const float* x, flo
                                     seq ? s_all(seq) - seq->P : 0);
   if (rc) return rc;
   if (!std::isfinite(sigma)) return fail(DIT_ERR_ARG, "sigma is not finite");
+  std::lock_guard<std::mutex> lock(m->mu);
   bool ok = false;
   for (const auto& r : m->extracted)
     if (r.kv == kv_cache && r.P == seq->P && r.T == seq->T && r.B == n_elem(seq)) ok = true;
@@ -528,15 +534,18 @@ dit_status dit_debug_mask(const dit_seq* seq, uint8_t* mask, void* stream) {
 
 dit_status dit_debug_attention(const dit_seq* seq, int n_heads, const void* q, int q_stride,
                                int q_off, int N, const void* kv_cache, void* out, int variant,
-                               void* stream) {
+                               void* scratch, size_t scratch_bytes, void* stream) {
   dit_status rc = check_seq(nullptr, seq);
   if (rc) return rc;
   const int S = seq->P + seq->T;
   if (!q || !kv_cache || !out) return fail(DIT_ERR_ARG, "NULL argument");
   if (n_heads <= 0 || N <= 0 || q_off < 0 || q_off + N > S || q_stride < n_heads * 128 || q_stride % 8)
     return fail(DIT_ERR_ARG, "bad attention shape");
+  if (variant < 0 || variant > 4) return fail(DIT_ERR_ARG, "unknown attention variant %d", variant);
+  if (scratch && (reinterpret_cast<uintptr_t>(scratch) & 15))
+    return fail(DIT_ERR_ARG, "scratch must be 16-byte aligned");
 #ifdef DIT_F32
-  (void)variant; (void)stream;
+  (void)scratch_bytes; (void)stream;
   return fail(DIT_ERR_UNSUPPORTED, "dit_debug_attention is not part of the fp32 debug build");
 #else
   const int cap = dit_kv_capacity(S);
@@ -547,53 +556,76 @@ dit_status dit_debug_attention(const dit_seq* seq, int n_heads, const void* q, i
   a.cap = cap; a.S = S; a.nh = n_heads; a.limit = seq->d_row_limit;
   a.out = static_cast<act_t*>(out); a.out_stride = n_heads * 128;
   a.P = seq->P; a.T_el = seq->T;
-  if (variant < 0 || variant > 16) return fail(DIT_ERR_ARG, "unknown attention variant %d", variant);
-  // key-split scratch: one buffer per device, allocated on first use and
-  // kept until the process ends (calls that overlap on one device race)
-  static float* part_of[64] = {nullptr};
-  int dev = 0;
-  dit_status rc2 = hip_check(hipGetDevice(&dev), "debug attention device");
-  if (rc2) return rc2;
-  if (dev < 0 || dev >= 64) return fail(DIT_ERR_UNSUPPORTED, "device index %d", dev);
-  if (!part_of[dev]) {
-    rc2 = hip_check(hipMalloc(&part_of[dev], kGemmPartBytes), "debug attention scratch");
-    if (rc2) return rc2;
-  }
-  a.part = part_of[dev]; a.part_bytes = kGemmPartBytes;
+  a.part = scratch ? static_cast<float*>(scratch) : nullptr;
+  a.part_bytes = scratch ? scratch_bytes : 0;
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (variant == 0) return hip_check(launch_attention(a, st), "debug attention");
   return hip_check(launch_attention_variant(a, variant, st), "debug attention");
 #endif
 }
 
-dit_status dit_debug_gemm(const void* A, const void* B, void* C, int M, int N, int K, int variant,
-                          void* stream) {
-  if (!A || !B || !C) return fail(DIT_ERR_ARG, "NULL argument");
+dit_status dit_debug_gemm(const dit_gemm_desc* d, void* stream) {
+  if (!d) return fail(DIT_ERR_ARG, "descriptor is NULL");
+  const int epi = d->epilogue;
+  if (epi != DIT_GEMM_BF16 && epi != DIT_GEMM_F32 && epi != DIT_GEMM_RESID && epi != DIT_GEMM_SWIGLU &&
+      epi != DIT_GEMM_QKV)
+    return fail(DIT_ERR_ARG, "unknown epilogue %d", epi);
+  if (!d->A || !d->B) return fail(DIT_ERR_ARG, "A or B is NULL");
+  if (epi == DIT_GEMM_RESID ? (!d->h || !d->gate_t || !d->gate_0) : !d->C)
+    return fail(DIT_ERR_ARG, "output or gate pointer is NULL");
+  if (epi == DIT_GEMM_SWIGLU && !d->B2) return fail(DIT_ERR_ARG, "SwiGLU needs B2 (up)");
+  if (d->splits != 0 && d->splits != 2 && d->splits != 4) return fail(DIT_ERR_ARG, "splits must be 0, 2 or 4");
+  const int N = epi == DIT_GEMM_SWIGLU ? 2 * d->N : d->N;   // packed gate/up width
+  if (!gemm_shape_ok(d->M, N, d->K, epi == DIT_GEMM_F32 ? EPI_F32 : EPI_BF16))
+    return fail(DIT_ERR_SHAPE, "GEMM needs M > 0, N %% %d == 0 and K %% 64 == 0",
+                epi == DIT_GEMM_F32 ? 64 : 256);
+  if (d->scratch && (reinterpret_cast<uintptr_t>(d->scratch) & 15))
+    return fail(DIT_ERR_ARG, "scratch must be 16-byte aligned");
+  if (epi == DIT_GEMM_F32 && d->splits) return fail(DIT_ERR_ARG, "the fp32-output GEMM is never split");
+  const int tail = d->M - (d->M - 1) / 256 * 256;   // rows of the last 256-row block
+  if (d->splits > 1) {
+    if ((d->K / 64) % d->splits) return fail(DIT_ERR_ARG, "K / 64 must be divisible by splits");
+    if (!d->scratch || d->scratch_bytes < (size_t)d->splits * tail * N * 4)
+      return fail(DIT_ERR_ARG, "scratch below splits * rows * N * 4 bytes");
+  }
 #ifdef DIT_F32
-  (void)M; (void)N; (void)K; (void)variant; (void)stream;
+  (void)stream; (void)tail;
   return fail(DIT_ERR_UNSUPPORTED, "dit_debug_gemm is not part of the fp32 debug build");
 #else
-  if (!gemm_shape_ok(M, N, K, EPI_BF16)) return fail(DIT_ERR_SHAPE, "GEMM needs M>0, N%%256==0, K%%64==0");
   GemmArgs g{};
-  g.A = static_cast<const act_t*>(A); g.lda = K;
-  g.B = static_cast<const uint16_t*>(B); g.ldb = K;
-  g.M = M; g.N = N; g.K = K; g.C = C; g.ldc = N;
-  if (variant < 0 || variant > 16) return fail(DIT_ERR_ARG, "unknown GEMM variant %d", variant);
-  if (variant == 0) return hip_check(launch_gemm(g, EPI_BF16, static_cast<hipStream_t>(stream)), "debug gemm");
-  if (variant == 6) {
-    // split-K path: scratch for up to 4 splits of the last 256-row block,
-    // allocated here and released after the launch completes
-    const size_t bytes = (size_t)4 * 256 * N * 4;
-    float* part = nullptr;
-    dit_status rc = hip_check(hipMalloc(&part, bytes), "debug gemm scratch");
-    if (rc) return rc;
-    g.part = part; g.part_bytes = bytes;
-    rc = hip_check(launch_gemm_variant(g, variant, static_cast<hipStream_t>(stream)), "debug gemm");
-    const dit_status rs = hip_check(hipStreamSynchronize(static_cast<hipStream_t>(stream)), "debug gemm sync");
-    hipFree(part);
-    return rc ? rc : rs;
+  g.A = static_cast<const act_t*>(d->A); g.lda = d->K;
+  g.B = U(d->B); g.B2 = U(d->B2); g.ldb = d->K;
+  g.M = d->M; g.N = N; g.K = d->K;
+  g.C = d->C; g.ldc = d->N;
+  g.Hres = d->h; g.ldh = d->N; g.gate_t = d->gate_t; g.gate_0 = d->gate_0; g.n_pre = d->n_pre;
+  g.part = static_cast<float*>(d->scratch); g.part_bytes = d->scratch ? d->scratch_bytes : 0;
+  int kepi = EPI_BF16;
+  if (epi == DIT_GEMM_F32) kepi = EPI_F32;
+  if (epi == DIT_GEMM_RESID) kepi = EPI_RESID;
+  if (epi == DIT_GEMM_SWIGLU) kepi = EPI_SWIGLU;
+  if (epi == DIT_GEMM_QKV) {
+    kepi = EPI_QKV;
+    const int nh = d->n_heads, H = nh * 128;
+    if (nh <= 0 || d->N != 3 * H) return fail(DIT_ERR_SHAPE, "QKV needs N = 3 * n_heads * 128");
+    if (!d->q_norm || !d->k_norm || !d->rope_cos || !d->rope_sin || !d->kv_cache)
+      return fail(DIT_ERR_ARG, "QKV needs norm weights, RoPE tables and a cache");
+    if (d->q_row0 < 0 || (long long)d->q_row0 + d->M > d->S || d->S > kMaxTokens)
+      return fail(DIT_ERR_ARG, "rows q_row0 .. q_row0 + M - 1 must lie inside S");
+    if (!(d->eps > 0.f)) return fail(DIT_ERR_ARG, "eps must be positive");
+    const int cap = dit_kv_capacity(d->S);
+    QkArgs& q = g.qk;
+    q.qkv = static_cast<act_t*>(d->C); q.ld = d->N; q.q_row0 = d->q_row0;
+    q.g_begin = d->q_row0; q.g_end = d->q_row0 + d->M;
+    q.S = d->S; q.cap = cap; q.nh = nh; q.H = H; q.P = 0; q.T_el = 0;
+    q.wq = U(d->q_norm); q.wk = U(d->k_norm);
+    q.cosv = d->rope_cos; q.sinv = d->rope_sin;
+    q.kc = static_cast<act_t*>(d->kv_cache);
+    q.vtc = q.kc + (size_t)nh * cap * 128;
+    q.eps = d->eps;
   }
-  return hip_check(launch_gemm_variant(g, variant, static_cast<hipStream_t>(stream)), "debug gemm");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (d->splits > 1) return hip_check(launch_gemm_forced_split(g, kepi, d->splits, st), "debug gemm");
+  return hip_check(launch_gemm(g, kepi, st), "debug gemm");
 #endif
 }
 
@@ -601,6 +633,7 @@ dit_status dit_profile_enable(dit_model* m, int kernel_class) {
   if (!m) return fail(DIT_ERR_ARG, "model is NULL");
   if (kernel_class < DIT_PROF_OFF || kernel_class > DIT_PROF_QKNORM_ROPE)
     return fail(DIT_ERR_ARG, "unknown kernel class %d", kernel_class);
+  std::lock_guard<std::mutex> lock(m->mu);
   m->prof_class = kernel_class;
   m->ev_used = 0;
   return DIT_OK;
@@ -608,6 +641,7 @@ dit_status dit_profile_enable(dit_model* m, int kernel_class) {
 
 dit_status dit_profile_read(dit_model* m, double* total_ms, long long* launches) {
   if (!m || !total_ms || !launches) return fail(DIT_ERR_ARG, "NULL argument");
+  std::lock_guard<std::mutex> lock(m->mu);
   double tot = 0;
   for (size_t i = 0; i < m->ev_used; ++i) {
     hipError_t e = hipEventSynchronize(m->ev_stop[i]);

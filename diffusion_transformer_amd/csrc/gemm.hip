@@ -1,13 +1,13 @@
 // bf16 MFMA GEMMs for gfx950: C = A·Bᵀ with A [M,K] and B [N,K] both
 // K-contiguous (activations × nn.Linear weights), fp32 accumulation, built
 // from v_mfma_f32_32x32x16_bf16 blocks, with fused epilogues (bf16 store,
-// fp32 store, gated fp32 residual update, SwiGLU).
+// gated fp32 residual update, SwiGLU, QK-RMSNorm + RoPE + KV-cache write).
 //
-// gemm_dma_kernel (the step's GEMMs): 256x256 block tile, 8 waves (2x4),
-// K in stages of 32 held in a ring of four 32 KB LDS stages that are filled
-// straight from global memory with buffer_load ... lds three stages ahead.
-// gemm_kernel: register-staged variant (global -> VGPR -> LDS, two stages),
-// used for the narrow proj_out GEMM (64x64 tiles) and kept as a reference.
+// gemm_w4_kernel (every GEMM of a layer): 256x256 block tile, 4 waves of
+// 128x128, K in stages of 64 held in two 64 KB LDS stages that are filled
+// straight from global memory with buffer_load ... lds one stage ahead.
+// gemm_kernel: register-staged (global -> VGPR -> LDS, two stages), used
+// for the narrow fp32-output proj_out GEMM with 64x64 tiles.
 //
 // Both use an XCD-aware tile order: the hardware deals workgroups
 // round-robin over the 8 XCDs, so block b is remapped to logical tile
@@ -231,295 +231,6 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_kernel(GemmArgs g) {
       }
     }
   }
-}
-
-// Epilogue shared by the direct-to-LDS kernels: wave (wm, wn) owns the
-// TM x TN patch at (m0 + wm*TM, n0 + wn*TN) in FM x FN blocks of 32x32.
-template <int FM, int FN, int TM, int TN, int EPI, bool SWAP>
-__device__ __forceinline__ void store_tile(const GemmArgs& g, f32x16 (&acc)[FM][FN], int m0, int n0,
-                                           int wm, int wn, int lrow, int lhalf) {
-  if (!SWAP) {
-    // accumulator register r of lane l holds C[8*(r/4) + 4*(l/32) + r%4][l%32]
-#pragma unroll
-    for (int i = 0; i < FM; ++i) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int m = m0 + wm * TM + i * 32 + 8 * (r >> 2) + 4 * lhalf + (r & 3);
-        if (m >= g.M) continue;
-        if (EPI == EPI_SWIGLU) {
-#pragma unroll
-          for (int j = 0; j < FN; j += 2) {
-            const int f = ((n0 + wn * TN + j * 32) >> 1) + lrow;
-            const float gv = acc[i][j][r], uv = acc[i][j + 1][r];
-            reinterpret_cast<bf16_t*>(g.C)[(size_t)m * g.ldc + f] = f2bf(gv / (1.f + __expf(-gv)) * uv);
-          }
-        } else {
-#pragma unroll
-          for (int j = 0; j < FN; ++j) {
-            const int n = n0 + wn * TN + j * 32 + lrow;
-            const float v = acc[i][j][r];
-            if (EPI == EPI_BF16) {
-              reinterpret_cast<bf16_t*>(g.C)[(size_t)m * g.ldc + n] = f2bf(v);
-            } else if (EPI == EPI_F32) {
-              reinterpret_cast<float*>(g.C)[(size_t)m * g.ldc + n] = v;
-            } else {
-              const float gt = (m < g.n_pre ? g.gate_0 : g.gate_t)[n];
-              float* hp = g.Hres + (size_t)m * g.ldh + n;
-              *hp = *hp + gt * v;
-            }
-          }
-        }
-      }
-    }
-    return;
-  }
-  // ---- epilogue: lane owns row m = .. + lrow, columns n0c + 8g + 4*lhalf + {0..3} ----
-#pragma unroll
-  for (int i = 0; i < FM; ++i) {
-    const int m = m0 + wm * TM + i * 32 + lrow;
-    if (m >= g.M) continue;
-    if (EPI == EPI_SWIGLU) {
-#pragma unroll
-      for (int j = 0; j < FN; j += 2) {
-        const int fbase = ((n0 + wn * TN + j * 32) >> 1);     // gate block j, up block j+1
-#pragma unroll
-        for (int gq = 0; gq < 4; ++gq) {
-          float o[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const float gv = acc[i][j][4 * gq + e], uv = acc[i][j + 1][4 * gq + e];
-            o[e] = gv / (1.f + __expf(-gv)) * uv;
-          }
-          u32x2 w;
-          w.x = pack2bf(o[0], o[1]);
-          w.y = pack2bf(o[2], o[3]);
-          *reinterpret_cast<u32x2*>(reinterpret_cast<bf16_t*>(g.C) + (size_t)m * g.ldc + fbase + 8 * gq + 4 * lhalf) = w;
-        }
-      }
-    } else {
-#pragma unroll
-      for (int j = 0; j < FN; ++j) {
-#pragma unroll
-        for (int gq = 0; gq < 4; ++gq) {
-          const int n = n0 + wn * TN + j * 32 + 8 * gq + 4 * lhalf;
-          float a4[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) a4[e] = acc[i][j][4 * gq + e];
-          if (EPI == EPI_BF16) {
-            u32x2 w;
-            w.x = pack2bf(a4[0], a4[1]);
-            w.y = pack2bf(a4[2], a4[3]);
-            *reinterpret_cast<u32x2*>(reinterpret_cast<bf16_t*>(g.C) + (size_t)m * g.ldc + n) = w;
-          } else if (EPI == EPI_F32) {
-            *reinterpret_cast<float4*>(reinterpret_cast<float*>(g.C) + (size_t)m * g.ldc + n) =
-                make_float4(a4[0], a4[1], a4[2], a4[3]);
-          } else {
-            const float4 gt = *reinterpret_cast<const float4*>((m < g.n_pre ? g.gate_0 : g.gate_t) + n);
-            float4* hp = reinterpret_cast<float4*>(g.Hres + (size_t)m * g.ldh + n);
-            float4 hv = *hp;
-            hv.x += gt.x * a4[0];
-            hv.y += gt.y * a4[1];
-            hv.z += gt.z * a4[2];
-            hv.w += gt.w * a4[3];
-            *hp = hv;
-          }
-        }
-      }
-    }
-  }
-}
-
-// ---------------------------------------------------------------------------
-// Direct-to-LDS variant: BM = BN = 256, BK = 32, a ring of 4 LDS stages of
-// 32 KB (separate arrays, so the compiler's LDS-DMA wait tracking can tell
-// them apart). Tiles are fetched with buffer_load ... lds three stages ahead
-// of their use, so no registers are spent on staging. Each LDS row holds 32
-// bf16 of K (64 bytes = 4 chunks); chunk c of row r sits at c ^ ((r/4)%4),
-// which spreads the 16 rows one ds_read_b128 phase touches over 16 distinct
-// bank groups. One barrier per stage, placed after the first 16-wide slice
-// so the next stage's first fragments are read while the second slice runs.
-#define LDSP(p) ((__attribute__((address_space(3))) void*)(p))
-
-template <int WM, int WN, int EPI, bool SWAP = true, int GM = GROUP_M>
-__global__ __launch_bounds__(WM* WN * 64) void gemm_dma_kernel(GemmArgs g) {
-  constexpr int BM = 256, BN = 256, DBK = 32;
-  constexpr int NT = WM * WN * 64;
-  constexpr int NW = WM * WN;
-  constexpr int TM = BM / WM, TN = BN / WN;
-  constexpr int FM = TM / 32, FN = TN / 32;
-  constexpr int BLK = (BM + BN) / 16;          // 1 KB blocks (16 rows) per stage
-  constexpr int CH = BLK / NW;                 // DMA instructions per wave per stage
-  static_assert(CH * NW == BLK, "blocks per wave");
-  static_assert(EPI != EPI_SWIGLU || (FN % 2 == 0 && TN % 64 == 0), "SwiGLU pairs 32-col blocks");
-  constexpr int SW = (BM + BN) * DBK / 8;      // u32x4 per stage (2048)
-  __shared__ u32x4 st0[SW], st1[SW], st2[SW], st3[SW];
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave / WN, wn = wave % WN;
-
-  const int ntm = (g.M + BM - 1) / BM;
-  const int ntn = g.N / BN;
-  const int nblk = ntm * ntn;
-  int b = blockIdx.x;
-  const int per = nblk >> 3;
-  if (b < per * 8) b = (b & 7) * per + (b >> 3);
-  const int in_group = GM * ntn;
-  const int gid = b / in_group;
-  const int first = gid * GM;
-  const int gsz = min(ntm - first, GM);
-  const int tm = first + (b % in_group) % gsz;
-  const int tn = (b % in_group) / gsz;
-  const int m0 = tm * BM, n0 = tn * BN;
-
-  // lane part of every DMA: row l/4 of the 16-row block, logical chunk
-  // (l%4) ^ ((l/16)%4) so the lane's 16 bytes land at physical slot l%4
-  const int lr = lane >> 2;
-  const int lc = (lane & 3) ^ ((lane >> 4) & 3);
-  const __amdgpu_buffer_rsrc_t rA = make_rsrc(
-      g.A + (size_t)m0 * g.lda, (uint32_t)min((size_t)(g.M - m0) * g.lda * 2, (size_t)0xFFFFFFF0u));
-  __amdgpu_buffer_rsrc_t rG, rU;
-  if (EPI == EPI_SWIGLU) {
-    const size_t bytes = min((size_t)(BN / 2) * g.ldb * 2, (size_t)0xFFFFFFF0u);
-    rG = make_rsrc(g.B + (size_t)(n0 >> 1) * g.ldb, (uint32_t)bytes);
-    rU = make_rsrc(g.B2 + (size_t)(n0 >> 1) * g.ldb, (uint32_t)bytes);
-  } else {
-    rG = rU = make_rsrc(g.B + (size_t)n0 * g.ldb, (uint32_t)min((size_t)BN * g.ldb * 2, (size_t)0xFFFFFFF0u));
-  }
-  const uint32_t aoff = (uint32_t)((lr * g.lda + lc * 8) * 2);
-  const uint32_t boff = (uint32_t)((lr * g.ldb + lc * 8) * 2);
-  const int nk = g.K / DBK;
-
-  // DMA blocks: instruction j < CH/2 of a wave loads A block j*NW + wave;
-  // instruction CH/2 + jj loads a 16-row B block whose gate/up choice is a
-  // compile-time function of jj (B block bb = 4*q + 2*mat + half holds
-  // features 32*q + 16*half + r of matrix mat).
-  static_assert(BM == BN && CH % 2 == 0, "A and B blocks split evenly");
-  constexpr int CHB = CH / 2;
-  static_assert(NW * CHB == BN / 16 && (NW == 4 || NW == 8), "B block mapping");
-  auto dma = [&](u32x4* stg, int kt) {
-    const uint32_t ko = (uint32_t)(kt * DBK * 2);
-#pragma unroll
-    for (int j = 0; j < CHB; ++j) {
-      const int blk = j * NW + wave;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rA, LDSP(stg + blk * 64), 16, aoff,
-                                               ko + (uint32_t)(blk * 16 * g.lda * 2), 0, 0);
-    }
-#pragma unroll
-    for (int jj = 0; jj < CHB; ++jj) {
-      int q, mat, hf;
-      if (NW == 4) { q = wave; mat = jj >> 1; hf = jj & 1; }
-      else { q = wave >> 1; mat = jj; hf = wave & 1; }
-      const int bb = 4 * q + 2 * mat + hf;
-      u32x4* dst = stg + (BM / 16 + bb) * 64;
-      if (EPI == EPI_SWIGLU) {
-        const uint32_t so = ko + (uint32_t)((32 * q + 16 * hf) * g.ldb * 2);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(mat ? rU : rG, LDSP(dst), 16, boff, so, 0, 0);
-      } else {
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rG, LDSP(dst), 16, boff,
-                                                 ko + (uint32_t)(bb * 16 * g.ldb * 2), 0, 0);
-      }
-    }
-  };
-
-  f32x16 acc[FM][FN];
-#pragma unroll
-  for (int i = 0; i < FM; ++i)
-#pragma unroll
-    for (int j = 0; j < FN; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-
-  const int lrow = lane & 31, lhalf = lane >> 5;
-  const int swz = (lrow >> 2) & 3;
-  bf16x8 fa[2][FM], fb[2][FN];
-  auto lread = [&](int fs, const u32x4* stg, int s) {
-    const int ph = (2 * s + lhalf) ^ swz;
-#pragma unroll
-    for (int i = 0; i < FM; ++i) fa[fs][i] = __builtin_bit_cast(bf16x8, stg[(wm * TM + i * 32 + lrow) * 4 + ph]);
-#pragma unroll
-    for (int j = 0; j < FN; ++j) fb[fs][j] = __builtin_bit_cast(bf16x8, stg[(BM + wn * TN + j * 32 + lrow) * 4 + ph]);
-  };
-  // Operands swapped (B fragment first): each 32x32 block is accumulated as
-  // Cᵀ, so lane l holds row l%32 of the block and, in registers 4g..4g+3,
-  // the four consecutive columns 8g + 4*(l/32) + {0..3} -> vector stores.
-  auto mma = [&](int fs) {
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-      for (int j = 0; j < FN; ++j)
-        acc[i][j] = SWAP ? mfma32(fb[fs][j], fa[fs][i], acc[i][j]) : mfma32(fa[fs][i], fb[fs][j], acc[i][j]);
-  };
-  // wait until this wave's DMA of the stage needed next has landed (the two
-  // younger stages may stay in flight) and its LDS reads are done, then sync
-  static_assert(2 * CH <= 63, "vmcnt range");
-  auto stage_barrier = [&]() {
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * CH));
-    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
-    __builtin_amdgcn_s_barrier();
-  };
-
-  // prologue: stages 0..2 in flight; wait for stage 0
-  dma(st0, 0);
-  dma(st1, min(1, nk - 1));
-  dma(st2, min(2, nk - 1));
-  __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * CH));
-  __builtin_amdgcn_s_barrier();
-  lread(0, st0, 0);
-
-  // iteration on stage `cur`: DMA tile kt+3 into `fut` (freed at the last
-  // barrier), slice 0, barrier (tile kt+1 visible), slice 1 while the next
-  // stage's slice-0 fragments load.
-  // Instruction order is pinned with sched_group_barrier: the fragment
-  // reads for the next slice go out one per MFMA at the front of the
-  // current slice's MFMAs (so they have the rest of the slice to land), and
-  // the DMAs are spread over the remaining MFMAs.
-  constexpr int NMF = FM * FN, NRD = FM + FN;
-  // slice 0: reads paired with MFMAs first, then DMAs paired with the rest
-  constexpr int P0 = NRD < NMF ? NRD : NMF;
-  constexpr int P1 = (NMF - P0) < CH ? (NMF - P0) : CH;
-  auto iter = [&](u32x4* cur, u32x4* nxt, u32x4* fut, int kt) {
-    lread(1, cur, 1);
-    dma(fut, min(kt + 3, nk - 1));
-    mma(0);
-#pragma unroll
-    for (int k = 0; k < P0; ++k) {
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
-    }
-    if (NRD > P0) __builtin_amdgcn_sched_group_barrier(0x100, NRD - P0, 0);
-#pragma unroll
-    for (int k = 0; k < P1; ++k) {
-      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // VMEM read (LDS DMA)
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    }
-    if (CH > P1) __builtin_amdgcn_sched_group_barrier(0x020, CH - P1, 0);
-    if (NMF > P0 + P1) __builtin_amdgcn_sched_group_barrier(0x008, NMF - P0 - P1, 0);
-    stage_barrier();
-    lread(0, nxt, 0);
-    mma(1);
-#pragma unroll
-    for (int k = 0; k < P0; ++k) {
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
-    }
-    if (NRD > P0) __builtin_amdgcn_sched_group_barrier(0x100, NRD - P0, 1);
-    if (NMF > P0) __builtin_amdgcn_sched_group_barrier(0x008, NMF - P0, 1);
-  };
-  int kt = 0;
-  for (; kt + 3 < nk; kt += 4) {
-    iter(st0, st1, st3, kt);
-    iter(st1, st2, st0, kt + 1);
-    iter(st2, st3, st1, kt + 2);
-    iter(st3, st0, st2, kt + 3);
-  }
-  if (kt < nk) iter(st0, st1, st3, kt);
-  if (kt + 1 < nk) iter(st1, st2, st0, kt + 1);
-  if (kt + 2 < nk) iter(st2, st3, st1, kt + 2);
-  __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));   // drain outstanding DMA before exit
-
-  store_tile<FM, FN, TM, TN, EPI, SWAP>(g, acc, m0, n0, wm, wn, lrow, lhalf);
 }
 
 // Epilogue through LDS for the swapped layout (each 32x32 block accumulated
@@ -842,8 +553,9 @@ __device__ __forceinline__ void store_tile_lds_f32(const GemmArgs& g, f32x16 (&a
 // LDS rows hold 64 bf16 of K (8 chunks of 16 B); chunk c of row r sits at
 // c ^ ((r/2)%8), which puts the 16 rows one ds_read_b128 phase touches on
 // all 64 banks exactly once.
-template <int EPI, bool SWAP, bool PACKED = (EPI == EPI_SWIGLU)>
+template <int EPI, bool PACKED = (EPI == EPI_SWIGLU)>
 __global__ __launch_bounds__(256) void gemm_w4_kernel(GemmArgs g) {
+  static_assert(EPI != EPI_F32, "fp32 output goes through gemm_kernel");
   constexpr int BM = 256, BN = 256, SBK = 64;
   constexpr int WN = 2, TM = 128, TN = 128, FM = 4, FN = 4;
   constexpr int SW = (BM + BN) * SBK / 8;      // u32x4 per stage (64 KB)
@@ -944,7 +656,7 @@ __global__ __launch_bounds__(256) void gemm_w4_kernel(GemmArgs g) {
     for (int i = i0; i < i1; ++i)
 #pragma unroll
       for (int j = 0; j < FN; ++j)
-        acc[i][j] = SWAP ? mfma32(fb[fs][j], fa[fs][i], acc[i][j]) : mfma32(fa[fs][i], fb[fs][j], acc[i][j]);
+        acc[i][j] = mfma32(fb[fs][j], fa[fs][i], acc[i][j]);   // operands swapped: Cᵀ blocks
   };
 
   dma(st0, 0);
@@ -1000,22 +712,18 @@ __global__ __launch_bounds__(256) void gemm_w4_kernel(GemmArgs g) {
   if (kt < nk) iter(st0, st1, kt);
   __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));   // drain the final (redundant) DMA before exit
 
-  if (SWAP && EPI != EPI_F32) {
-    lds_barrier();   // every wave is done with the stage buffers
-    char* reg = reinterpret_cast<char*>((wave < 2 ? st0 : st1)) + (wave & 1) * 32768;
-    if (EPI == EPI_RESID) store_tile_lds_f32<false>(g, acc, m0, n0, wm, wn, lane, reg, 0);
-    else if (EPI == EPI_PART) store_tile_lds_f32<true>(g, acc, m0, n0, wm, wn, lane, reg, split);
-    else if (EPI == EPI_QKV) store_tile_qkv(g, acc, m0, n0, wm, wn, lane, reg);
-    else store_tile_lds<(EPI == EPI_SWIGLU ? EPI_SWIGLU : EPI_BF16)>(g, acc, m0, n0, wm, wn, lane, reg);
-  } else {
-    store_tile<FM, FN, TM, TN, EPI, SWAP>(g, acc, m0, n0, wm, wn, lrow, lhalf);
-  }
+  lds_barrier();   // every wave is done with the stage buffers
+  char* reg = reinterpret_cast<char*>((wave < 2 ? st0 : st1)) + (wave & 1) * 32768;
+  if (EPI == EPI_RESID) store_tile_lds_f32<false>(g, acc, m0, n0, wm, wn, lane, reg, 0);
+  else if (EPI == EPI_PART) store_tile_lds_f32<true>(g, acc, m0, n0, wm, wn, lane, reg, split);
+  else if (EPI == EPI_QKV) store_tile_qkv(g, acc, m0, n0, wm, wn, lane, reg);
+  else store_tile_lds<(EPI == EPI_SWIGLU ? EPI_SWIGLU : EPI_BF16)>(g, acc, m0, n0, wm, wn, lane, reg);
 }
 
-template <int EPI, bool SWAP, bool PACKED = (EPI == EPI_SWIGLU)>
+template <int EPI, bool PACKED = (EPI == EPI_SWIGLU)>
 hipError_t run_w4(const GemmArgs& g, hipStream_t s) {
   const int nblk = ((g.M + 255) / 256) * (g.N / 256) * (EPI == EPI_PART ? g.splits : 1);
-  hipLaunchKernelGGL((gemm_w4_kernel<EPI, SWAP, PACKED>), dim3(nblk), dim3(256), 0, s, g);
+  hipLaunchKernelGGL((gemm_w4_kernel<EPI, PACKED>), dim3(nblk), dim3(256), 0, s, g);
   return hipGetLastError();
 }
 
@@ -1075,7 +783,7 @@ hipError_t run_reduce(const GemmArgs& g, hipStream_t s) {
 }
 
 template <int EPI>
-hipError_t run_main(const GemmArgs& g, hipStream_t s) { return run_w4<EPI, true>(g, s); }
+hipError_t run_main(const GemmArgs& g, hipStream_t s) { return run_w4<EPI>(g, s); }
 
 hipError_t run_epi(const GemmArgs& g, int epi, hipStream_t s) {
   switch (epi) {
@@ -1106,7 +814,7 @@ hipError_t launch_gemm_split(const GemmArgs& g, int epi, int r, int splits, hipS
   gt.n_pre = g.n_pre - gm.M;
   gt.splits = splits;
   // the partial sums of a SwiGLU GEMM keep its packed gate/up columns
-  hipError_t e = epi == EPI_SWIGLU ? run_w4<EPI_PART, true, true>(gt, s) : run_w4<EPI_PART, true, false>(gt, s);
+  hipError_t e = epi == EPI_SWIGLU ? run_w4<EPI_PART, true>(gt, s) : run_w4<EPI_PART, false>(gt, s);
   if (e != hipSuccess) return e;
   switch (epi) {
     case EPI_BF16: return run_reduce<EPI_BF16>(gt, s);
@@ -1126,13 +834,6 @@ hipError_t launch_gemm_split(const GemmArgs& g, int epi, int r, int splits, hipS
   return hipErrorInvalidValue;
 }
 
-template <int WM, int WN, int EPI, bool SWAP = true, int GM = GROUP_M>
-hipError_t run_dma(const GemmArgs& g, hipStream_t s) {
-  const int nblk = ((g.M + 255) / 256) * (g.N / 256);
-  hipLaunchKernelGGL((gemm_dma_kernel<WM, WN, EPI, SWAP, GM>), dim3(nblk), dim3(WM * WN * 64), 0, s, g);
-  return hipGetLastError();
-}
-
 template <int BM, int BN, int WM, int WN, int EPI>
 hipError_t run(const GemmArgs& g, hipStream_t s) {
   const int nblk = ((g.M + BM - 1) / BM) * (g.N / BN);
@@ -1148,20 +849,8 @@ bool gemm_shape_ok(int M, int N, int K, int epi) {
   return N % 256 == 0;
 }
 
-hipError_t launch_gemm_variant(const GemmArgs& g, int variant, hipStream_t s) {
-  switch (variant) {
-    case 1: return run<256, 256, 2, 4, EPI_BF16>(g, s);        // register-staged, 2-stage LDS
-    case 2: return run_dma<2, 4, EPI_BF16, true>(g, s);        // direct-to-LDS, swapped operands
-    case 3: return run_dma<2, 2, EPI_BF16, false>(g, s);       // direct-to-LDS, 4 waves of 128x128
-    case 4: return run_w4<EPI_BF16, false>(g, s);              // 4 waves of 128x128, K stages of 64
-    case 5: return run_dma<2, 4, EPI_BF16, false>(g, s);       // 8 waves of 128x64
-    case 6: {                                                  // split-K path for the last row block
-      int sp = 1;
-      while (sp < 4 && (g.K / 64) % (2 * sp) == 0) sp *= 2;
-      return launch_gemm_split(g, EPI_BF16, 1, sp, s);
-    }
-  }
-  return hipErrorInvalidValue;
+hipError_t launch_gemm_forced_split(const GemmArgs& g, int epi, int splits, hipStream_t s) {
+  return launch_gemm_split(g, epi, 1, splits, s);
 }
 
 hipError_t launch_gemm(const GemmArgs& g, int epi, hipStream_t s) {

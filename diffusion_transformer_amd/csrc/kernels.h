@@ -56,11 +56,14 @@ struct GemmArgs {
 };
 // Bytes of split-K scratch the GEMM launcher can use: at most one round of
 // 256 tiles of 256 x 256 fp32 partial sums. The step lends the same buffer
-// to attention's key split (at most 512 x 128 x 129 floats).
+// to attention's key split (256 x 129 floats per piece).
 constexpr size_t kGemmPartBytes = (size_t)256 * 256 * 256 * 4;
 
 hipError_t launch_gemm(const GemmArgs& g, int epi, hipStream_t s);
-hipError_t launch_gemm_variant(const GemmArgs& g, int variant, hipStream_t s);
+// The last 256-row block (or the whole GEMM, if smaller) as `splits` K
+// splits into g.part, reduced with the epilogue; the rows before it in one
+// ordinary launch. The caller checks K / 64 % splits == 0 and the scratch.
+hipError_t launch_gemm_forced_split(const GemmArgs& g, int epi, int splits, hipStream_t s);
 bool gemm_shape_ok(int M, int N, int K, int epi);
 
 struct AttnArgs {

@@ -100,9 +100,20 @@ def _rng(seed: int, name: str) -> np.random.Generator:
 
 def round_bf16(x: np.ndarray) -> np.ndarray:
     """float32 -> nearest bfloat16 (ties to even), returned as float32."""
-    b = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
-    b = (b + (np.uint32(0x7FFF) + ((b >> np.uint32(16)) & np.uint32(1)))) & np.uint32(0xFFFF0000)
-    return b.view(np.float32)
+    return _round_bf16_inplace(np.array(x, dtype=np.float32, copy=True))
+
+
+def _round_bf16_inplace(a: np.ndarray) -> np.ndarray:
+    """Round an owned, contiguous float32 array to bfloat16 in place (ties to
+    even): add 0x7FFF plus the kept part's lowest bit, then clear the low 16
+    bits."""
+    b = a.view(np.uint32)
+    keep_lsb = b >> np.uint32(16)
+    keep_lsb &= np.uint32(1)
+    keep_lsb += np.uint32(0x7FFF)
+    b += keep_lsb
+    b &= np.uint32(0xFFFF0000)
+    return a
 
 
 def bf16_bits(x: np.ndarray) -> np.ndarray:
@@ -115,39 +126,82 @@ def _normal(seed, name, shape, fan_in):
     g = _rng(seed, name)
     a = g.standard_normal(size=shape, dtype=np.float32)
     a *= np.float32(1.0 / np.sqrt(fan_in))
-    return round_bf16(a)
+    return _round_bf16_inplace(a)
 
 
-def make_weights(cfg: dict, seed: int = 21, n_layers: int | None = None) -> dict:
+def _global_specs(cfg: dict):
+    H, C, Dt = cfg["hidden"], cfg["latent"], cfg["time_dim"]
+    return [("t1", "t1", (H, Dt), Dt), ("t2", "t2", (H, H), H), ("mod", "mod", (4 * H, H), H),
+            ("so", "so", (H, H), H), ("img_in", "img_in", (H, C), C),
+            ("proj_out", "proj_out", (C, H), H)]
+
+
+def _layer_specs(cfg: dict, l: int):
+    H, d, F = cfg["hidden"], cfg["head_dim"], cfg["ffn"]
+    return [("qkv", f"l{l}.qkv", (3 * H, H), H), ("q_norm", f"l{l}.q_norm", (d,), d),
+            ("k_norm", f"l{l}.k_norm", (d,), d), ("o", f"l{l}.o", (H, H), H),
+            ("gate", f"l{l}.gate", (F, H), H), ("up", f"l{l}.up", (F, H), H),
+            ("down", f"l{l}.down", (H, F), F)]
+
+
+def global_weights(cfg: dict, seed: int = 21) -> dict:
+    """The weights shared by all layers (see ``make_weights``)."""
+    return {key: _normal(seed, name, shape, fan) for key, name, shape, fan in _global_specs(cfg)}
+
+
+def layer_weights(cfg: dict, l: int, seed: int = 21, workers: int = 1) -> dict:
+    """Layer ``l``'s weights (see ``make_weights``); each tensor has its own
+    named stream, so the values do not depend on ``workers`` or on which
+    other layers are drawn."""
+    return layers_weights(cfg, [l], seed, workers)[0]
+
+
+def layers_weights(cfg: dict, layers, seed: int = 21, workers: int = 1) -> list:
+    """Weights of the given layers, drawn by up to ``workers`` threads (one
+    tensor per task; NumPy's generators release the GIL while filling)."""
+    jobs = [(i, key, name, shape, fan) for i, l in enumerate(layers)
+            for key, name, shape, fan in _layer_specs(cfg, l)]
+    out = [dict() for _ in layers]
+    if workers <= 1:
+        for i, key, name, shape, fan in jobs:
+            out[i][key] = _normal(seed, name, shape, fan)
+        return out
+    from concurrent.futures import ThreadPoolExecutor
+    with ThreadPoolExecutor(max_workers=workers) as ex:
+        futs = [(i, key, ex.submit(_normal, seed, name, shape, fan))
+                for i, key, name, shape, fan in jobs]
+        for i, key, f in futs:
+            out[i][key] = f.result()
+    return out
+
+
+def make_weights(cfg: dict, seed: int = 21, n_layers: int | None = None,
+                 workers: int = 1) -> dict:
     """All weights in nn.Linear layout [out, in], bf16-exact float32.
 
     Global: t1 [H, D_t], t2 [H, H], mod [4H, H], so [H, H], img_in [H, C],
     proj_out [C, H]. Per layer: qkv [3H, H] (q rows, then k, then v),
     q_norm [d], k_norm [d], o [H, H], gate [F, H], up [F, H], down [H, F].
     """
-    H, d, F = cfg["hidden"], cfg["head_dim"], cfg["ffn"]
-    C, Dt = cfg["latent"], cfg["time_dim"]
     L = cfg["n_layers"] if n_layers is None else n_layers
-    W = {
-        "t1": _normal(seed, "t1", (H, Dt), Dt),
-        "t2": _normal(seed, "t2", (H, H), H),
-        "mod": _normal(seed, "mod", (4 * H, H), H),
-        "so": _normal(seed, "so", (H, H), H),
-        "img_in": _normal(seed, "img_in", (H, C), C),
-        "proj_out": _normal(seed, "proj_out", (C, H), H),
-        "layers": [],
-    }
-    for l in range(L):
-        W["layers"].append({
-            "qkv": _normal(seed, f"l{l}.qkv", (3 * H, H), H),
-            "q_norm": _normal(seed, f"l{l}.q_norm", (d,), d),
-            "k_norm": _normal(seed, f"l{l}.k_norm", (d,), d),
-            "o": _normal(seed, f"l{l}.o", (H, H), H),
-            "gate": _normal(seed, f"l{l}.gate", (F, H), H),
-            "up": _normal(seed, f"l{l}.up", (F, H), H),
-            "down": _normal(seed, f"l{l}.down", (H, F), F),
-        })
+    W = global_weights(cfg, seed)
+    W["layers"] = layers_weights(cfg, range(L), seed, workers)
     return W
+
+
+def bits_crc(bits: dict) -> int:
+    """CRC-32 of a dict of bf16 bit-pattern arrays, in key order (a
+    fingerprint to tell whether stored expected values were made from the
+    same weights)."""
+    c = 0
+    for k in sorted(bits):
+        c = zlib.crc32(np.ascontiguousarray(bits[k]).tobytes(), c)
+    return c
+
+
+def weights_crc(tensors: dict) -> int:
+    """``bits_crc`` of bf16-exact float32 weights."""
+    return bits_crc({k: bf16_bits(v) for k, v in tensors.items()})
 
 
 def make_inputs(cfg: dict, seed: int = 21) -> dict:

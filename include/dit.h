@@ -11,10 +11,20 @@
  *
  * Conventions shared by every entry point:
  *  - Ownership: the caller allocates ALL device memory (weights, prefix
- *    hidden states, latents, velocity, KV cache, workspace, layout tables).
- *    Except for the small host-side model handle, the library allocates
- *    nothing. Weight pointers are borrowed from dit_load_weights until
- *    dit_free; the caller keeps them alive and unchanged.
+ *    hidden states, latents, velocity, KV cache, workspace, layout tables,
+ *    and the scratch of the test hooks). Except for the small host-side
+ *    model handle (and, while per-kernel timing is on, its HIP events), the
+ *    library allocates nothing. Weight pointers are borrowed from
+ *    dit_load_weights until dit_free; the caller keeps them alive and
+ *    unchanged.
+ *  - Threads: the weights are never written. A model handle's mutable
+ *    host state is its registry of extracted caches (behind DIT_ERR_STATE)
+ *    and its timing events; every call that reads or writes them takes a
+ *    lock held by the handle, so calls on one handle from several threads
+ *    are serialized on the host (the GPU work they enqueue is ordered only
+ *    by the streams given). Steps that may run on the GPU at the same time
+ *    need distinct workspaces and distinct caches. dit_free must not race
+ *    with other calls on the handle.
  *  - Device pointers must be 16-byte aligned. bf16 tensors are raw
  *    bfloat16 bit patterns (uint16), row-major. Linear weights use the
  *    [out_features, in_features] layout: y = W x.
@@ -25,9 +35,10 @@
  *    is returned and dit_last_error() (thread-local) holds a message.
  *    A failed kernel launch returns DIT_ERR_HIP. No C++ exception crosses
  *    the ABI.
- *  - Supported shapes on the GPU: head_dim 128, hidden = n_heads*128 and a
- *    multiple of 256, ffn a multiple of 128, latent 64, time_dim even and
- *    <= 1024, rope_dims even and summing to 128.
+ *  - Supported shapes on the GPU: head_dim 128, hidden = n_heads*128, a
+ *    multiple of 256 and at most 4096, ffn a multiple of 128, latent 64,
+ *    time_dim a multiple of 8 and at most 1024, rope_dims even and summing
+ *    to 128.
  */
 #ifndef DIT_H_
 #define DIT_H_
@@ -224,23 +235,75 @@ dit_status dit_debug_mask(const dit_seq* seq, uint8_t* mask, void* stream);
  *   q [N, q_stride] bf16 with head h at columns h*128.., kv_cache layer 0
  *   of a cache with capacity dit_kv_capacity(S) for n_heads heads,
  *   queries are global rows q_off..q_off+N-1, out [N, n_heads*128] bf16.
- *   variant 0 = the kernel the step uses; 1.. = alternative kernels
- *   (6, 7: 4, 5 with the last round of workgroups split over key ranges).
- *   Split variants use a 64 MiB scratch per device, allocated on the
- *   first call and kept until the process ends: calls that overlap on one
- *   device race. */
+ *   variant 0 = the launch the step makes (kernel shape, key split of a
+ *   cached step's last round, longest-first order of an extract step);
+ *   1 = 256-query workgroups (8 waves), 2 = 128-query workgroups (4 waves,
+ *   two per CU), both in index order and unsplit; 3, 4 = 1, 2 with the last
+ *   round of workgroups split over key ranges.
+ *   scratch (device, caller-owned, may be NULL = no split) holds the split
+ *   pieces: 256 * 129 * 4 bytes per piece at most; a launch whose pieces do
+ *   not fit runs unsplit. Calls that overlap on one scratch race. */
 dit_status dit_debug_attention(const dit_seq* seq, int n_heads, const void* q, int q_stride,
                                int q_off, int N, const void* kv_cache, void* out,
-                               int variant, void* stream);
+                               int variant, void* scratch, size_t scratch_bytes, void* stream);
 
-/* Test hook: C[M,N] = A[M,K] · B[N,K]ᵀ with the step's bf16 MFMA GEMM
- * (A, B bf16, C bf16). N must be a multiple of 256 and K of 64.
- * variant 0 = the tile configuration the step uses for its bf16-output
- * GEMMs; 1.. = alternative tile configurations (DIT_ERR_ARG if unknown);
- * 6 = the split-K path for the last 256-row block (the library allocates
- * and frees its partial-sum scratch and waits for the stream). */
-dit_status dit_debug_gemm(const void* A, const void* B, void* C, int M, int N, int K,
-                          int variant, void* stream);
+/* Test hook: one GEMM of the step, with its fused epilogue, on explicit
+ * device buffers: y = A · Bᵀ with A [M, K] and B [N, K] bf16 (K-contiguous,
+ * the weights' nn.Linear layout), fp32 accumulation. Epilogues (the step's
+ * use in brackets; mapping rows 4A and 5A of the lab index page):
+ *   DIT_GEMM_BF16   C bf16 [M, N] = y.
+ *   DIT_GEMM_F32    C fp32 [M, N] = y (the proj_out kernel; N % 64 == 0).
+ *   DIT_GEMM_RESID  h fp32 [M, N] += g[n] * y, g = gate_0 for rows < n_pre
+ *                   and gate_t for the others, fp32 [N] each [O and down
+ *                   projections: h += tanh(gate) * out].
+ *   DIT_GEMM_SWIGLU C bf16 [M, N] = SiLU(A · Bᵀ) * (A · B2ᵀ) with B the gate
+ *                   and B2 the up weights, both [N, K] [the SwiGLU MLP].
+ *   DIT_GEMM_QKV    N = 3 * n_heads * 128 columns q | k | v, each head's
+ *                   128 columns rounded to bf16, then q and k per head
+ *                   RMSNorm (1 + w) with q_norm / k_norm (bf16 [128]) and
+ *                   eps, and RoPE with the tables of token q_row0 + m
+ *                   (rope_cos / rope_sin [S, 64]); q is written to C's q
+ *                   columns (C bf16 [M, N]; its k and v columns are left
+ *                   unspecified), k to K cache row q_row0 + m and v to
+ *                   Vᵀ cache column q_row0 + m of layer 0 of kv_cache
+ *                   (capacity dit_kv_capacity(S), dit_kv_capacity layout).
+ * M > 0, N % 256 == 0 (DIT_GEMM_F32: % 64), K % 64 == 0, else DIT_ERR_SHAPE.
+ * splits: 0 = the step's rule (the last row blocks are split over K when
+ * the tile count leaves a partly idle round and the partial sums fit the
+ * scratch; none without scratch); 2 or 4 = always compute the last 256-row
+ * block as that many K splits (needs K / 64 divisible by splits and
+ * scratch_bytes >= splits * 256 * N * 4, doubled for DIT_GEMM_SWIGLU;
+ * DIT_ERR_ARG otherwise). The scratch is caller-owned device memory. */
+enum {
+  DIT_GEMM_BF16 = 0,
+  DIT_GEMM_F32 = 1,
+  DIT_GEMM_RESID = 2,
+  DIT_GEMM_SWIGLU = 3,
+  DIT_GEMM_QKV = 5
+};
+typedef struct dit_gemm_desc {
+  int epilogue;
+  int M, N, K;
+  const void* A;
+  const void* B;
+  const void* B2;           /* SWIGLU: up weights */
+  void* C;
+  float* h;                 /* RESID */
+  const float* gate_t;      /* RESID */
+  const float* gate_0;      /* RESID */
+  int n_pre;                /* RESID */
+  const void* q_norm;       /* QKV */
+  const void* k_norm;       /* QKV */
+  const float* rope_cos;    /* QKV */
+  const float* rope_sin;    /* QKV */
+  void* kv_cache;           /* QKV */
+  int n_heads, S, q_row0;   /* QKV */
+  float eps;                /* QKV */
+  int splits;
+  void* scratch;
+  size_t scratch_bytes;
+} dit_gemm_desc;
+dit_status dit_debug_gemm(const dit_gemm_desc* d, void* stream);
 
 /* Per-kernel timing over HIP events recorded on the step's stream around
  * every launch of one kernel class (0 = off). Enabling it adds an event

@@ -325,10 +325,24 @@ def _output(h_tgt, cond, W, dims):
     return (layernorm(h_tgt, dims.eps) * (1.0 + cond["scale_out"])) @ W["proj_out"].T
 
 
+class _F64Layers:
+    """The per-layer weights of ``W["layers"]`` read one layer at a time and
+    converted to float64 when a layer is used. ``W["layers"]`` may be a list
+    of per-layer dicts or a callable ``l -> dict`` that supplies layer l on
+    demand, so a deep model's weights need not all be held in float64 at
+    once; the arithmetic is the same either way."""
+
+    def __init__(self, layers):
+        self._src = layers
+
+    def __getitem__(self, l):
+        L = self._src(l) if callable(self._src) else self._src[l]
+        return {k: np.asarray(v, dtype=np.float64) for k, v in L.items()}
+
+
 def _f64(W):
     out = {k: np.asarray(v, dtype=np.float64) for k, v in W.items() if k != "layers"}
-    out["layers"] = [{k: np.asarray(v, dtype=np.float64) for k, v in L.items()}
-                     for L in W["layers"]]
+    out["layers"] = _F64Layers(W["layers"])
     return out
 
 

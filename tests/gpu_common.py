@@ -33,3 +33,39 @@ def i16_to_f32(t):
     """bf16 bits held in an int16 tensor -> float32 numpy."""
     a = t.cpu().numpy().astype(np.int16).view(np.uint16).astype(np.uint32) << 16
     return a.view(np.float32)
+
+
+def synth_weights_on_device(cfg, dev, seed=21, workers=16, n_layers=None):
+    """The seeded host weights of ``synth`` (the ones the oracle and the
+    stored expected values use), drawn layer by layer on ``workers`` threads
+    and uploaded as bf16 without keeping the host copies. Returns
+    (device weight dict for ``DitRuntime(on_device=True)``, per-layer CRC-32
+    of the bf16 bits, CRC-32 of the shared weights)."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    import torch
+    from diffusion_transformer_amd.runtime import GLOBAL_KEYS, LAYER_KEYS
+
+    def up(bits):
+        return torch.from_numpy(bits.view(np.int16)).to(dev).view(torch.bfloat16)
+
+    Lc = cfg["n_layers"] if n_layers is None else n_layers
+    G = synth.global_weights(cfg, seed)
+    gbits = {k: synth.bf16_bits(v) for k, v in G.items()}
+    out = {k: up(gbits[k]) for k in GLOBAL_KEYS}
+    for k in LAYER_KEYS:
+        out[k] = []
+
+    def one(l):
+        bits = {k: synth.bf16_bits(v) for k, v in synth.layer_weights(cfg, l, seed).items()}
+        return bits, synth.bits_crc(bits)
+
+    crcs = []
+    with ThreadPoolExecutor(max_workers=workers) as ex:
+        for l0 in range(0, Lc, workers):
+            for bits, crc in ex.map(one, range(l0, min(Lc, l0 + workers))):
+                crcs.append(crc)
+                for k in LAYER_KEYS:
+                    out[k].append(up(bits[k]))
+            say(f"  weights of layers < {min(Lc, l0 + workers)} drawn and uploaded")
+    return out, crcs, synth.bits_crc(gbits)

@@ -157,7 +157,8 @@ def test_step_state_and_workspace_errors():
                                     wsb, 0, None)
         assert r == L.DIT_ERR_ARG            # misaligned
         assert L._lib.euler_update(None, FAKE, 1.0, 0.5, 4, None) == L.DIT_ERR_ARG
-        assert L._lib.dit_debug_gemm(FAKE, FAKE, FAKE, 10, 100, 64, 0, None) == L.DIT_ERR_SHAPE
+        d = L.dit_gemm_desc(epilogue=0, M=10, N=100, K=64, A=FAKE, B=FAKE, C=FAKE)
+        assert L._lib.dit_debug_gemm(C.byref(d), None) == L.DIT_ERR_SHAPE
         assert L._lib.dit_profile_enable(m, 99) == L.DIT_ERR_ARG
     finally:
         L.dit_free(m)
@@ -266,3 +267,104 @@ if given is not None:
         ang = O.rope_angles(ol.coords, dims)
         assert np.abs(lay["rope_cos"] - np.cos(ang)).max() < 1e-7
         assert np.abs(lay["rope_sin"] - np.sin(ang)).max() < 1e-7
+
+
+def test_debug_gemm_descriptor_validation():
+    """The GEMM test hook rejects on the host: unknown epilogues, missing
+    operands, unsupported shapes, a forced split without enough scratch or
+    with K not divisible into the splits, and a QKV width that is not three
+    heads' worth."""
+    def st(**kw):
+        base = dict(epilogue=0, M=300, N=512, K=256, A=FAKE, B=FAKE, C=FAKE)
+        base.update(kw)
+        return L._lib.dit_debug_gemm(C.byref(L.dit_gemm_desc(**base)), None)
+
+    assert st(epilogue=4) == L.DIT_ERR_ARG            # the internal partial-sum epilogue
+    assert st(epilogue=9) == L.DIT_ERR_ARG
+    assert st(A=None) == L.DIT_ERR_ARG
+    assert st(epilogue=2, C=None) == L.DIT_ERR_ARG    # residual needs h and both gates
+    assert st(epilogue=3) == L.DIT_ERR_ARG            # SwiGLU needs the up weights
+    assert st(K=100) == L.DIT_ERR_SHAPE
+    assert st(epilogue=1, N=96) == L.DIT_ERR_SHAPE    # fp32 output: N % 64
+    assert st(splits=3) == L.DIT_ERR_ARG
+    assert st(splits=2) == L.DIT_ERR_ARG              # no scratch
+    need = 2 * (300 - 256) * 512 * 4
+    assert st(splits=2, scratch=FAKE, scratch_bytes=need - 1) == L.DIT_ERR_ARG
+    assert st(splits=4, K=192, scratch=FAKE, scratch_bytes=1 << 30) == L.DIT_ERR_ARG
+    assert st(epilogue=1, splits=2, scratch=FAKE, scratch_bytes=1 << 30) == L.DIT_ERR_ARG
+    assert st(epilogue=5, N=768, n_heads=1, q_norm=FAKE, k_norm=FAKE, rope_cos=FAKE,
+              rope_sin=FAKE, kv_cache=FAKE, S=300, eps=1e-6) == L.DIT_ERR_SHAPE
+    assert st(epilogue=5, N=768, n_heads=2, q_norm=FAKE, k_norm=FAKE, rope_cos=FAKE,
+              rope_sin=FAKE, kv_cache=FAKE, S=299, eps=1e-6) == L.DIT_ERR_ARG   # rows past S
+    assert st(epilogue=5, N=768, n_heads=2, S=300, eps=1e-6) == L.DIT_ERR_ARG  # no tables
+
+
+def test_debug_attention_validation():
+    seq = L.dit_seq(7, 4, FAKE, FAKE, FAKE)
+
+    def st(variant=0, scratch=None, N=4, q_off=7):
+        return L._lib.dit_debug_attention(C.byref(seq), 2, FAKE, 256, q_off, N, FAKE, FAKE,
+                                          variant, scratch, 1 << 20, None)
+
+    assert st(variant=5) == L.DIT_ERR_ARG
+    assert st(scratch=FAKE + 4) == L.DIT_ERR_ARG
+    assert st(N=5) == L.DIT_ERR_ARG                   # rows past S
+
+
+def test_host_tensor_checks_in_the_binding():
+    """The binding checks on the host what the C ABI cannot see: the step's
+    x / v / prefix tensors must be contiguous float32 device tensors of the
+    sizes the call reads and writes (here CPU tensors are refused)."""
+    import torch
+    cfg, c = cfg_c("c0w")
+    W = {k: FAKE for k in ("t1", "t2", "mod", "so", "img_in", "proj_out")}
+    for k in ("qkv", "q_norm", "k_norm", "o", "gate", "up", "down"):
+        W[k] = [FAKE] * cfg["n_layers"]
+    m = L.dit_load_weights(c, W)
+    try:
+        seq = L.dit_seq(7, 4, FAKE, FAKE, FAKE)
+        x = torch.zeros((4, 64))
+        with pytest.raises(L.DitError) as e:
+            L.dit_step_cached(m, seq, x, 0.5, FAKE, x, FAKE)
+        assert e.value.status == L.DIT_ERR_ARG and "x" in str(e.value)
+        with pytest.raises(L.DitError):
+            L.dit_step_extract(m, seq, torch.zeros((7, 256)), x, 1.0, FAKE, x, FAKE)
+        with pytest.raises(L.DitError):
+            L.euler_update(x, x, 1.0, 0.5)
+    finally:
+        L.dit_free(m)
+
+
+def test_model_handle_calls_from_many_threads():
+    """Calls on one handle from several threads are serialized by the
+    handle's lock: concurrent cached-step requests (refused: nothing was
+    extracted) and timing-state calls neither crash nor change each other's
+    answers."""
+    import threading
+    cfg, c = cfg_c("c0w")
+    st, m = load(c)
+    assert st == L.DIT_OK
+    seq = L.dit_seq(7, 4, FAKE, FAKE, FAKE)
+    kvb, wsb = L.dit_kv_cache_bytes(m, 11), L.dit_workspace_bytes(m, 4)
+    bad = []
+
+    def work(i):
+        for _ in range(300):
+            r = L._lib.dit_step_cached(m, C.byref(seq), FAKE, 0.85, FAKE, kvb, FAKE, FAKE, wsb, None)
+            if r != L.DIT_ERR_STATE:
+                bad.append(("cached", r))
+            if L._lib.dit_profile_enable(m, 1 + i % 7) != L.DIT_OK:
+                bad.append("enable")
+            ms, n = C.c_double(), C.c_longlong()
+            if L._lib.dit_profile_read(m, C.byref(ms), C.byref(n)) != L.DIT_OK or n.value != 0:
+                bad.append("read")
+
+    try:
+        th = [threading.Thread(target=work, args=(i,)) for i in range(8)]
+        for t in th:
+            t.start()
+        for t in th:
+            t.join()
+        assert not bad, bad[:5]
+    finally:
+        L.dit_free(m)

@@ -21,21 +21,25 @@ def dev():
     return torch.device("cuda:0")
 
 
-@pytest.mark.parametrize("variant", [0, 1, 2, 3, 4, 5, 6])
+@pytest.mark.parametrize("splits", [0, 2, 4])
 @pytest.mark.parametrize("M,N,K", [(32, 256, 64), (300, 512, 128), (257, 768, 256), (600, 1024, 512)])
-def test_gemm_exact_small_integers(dev, M, N, K, variant):
+def test_gemm_exact_small_integers(dev, M, N, K, splits):
     """Entries in {-1, 0, 1}: every partial sum is an integer of magnitude
-    <= K <= 256, exact in fp32 and in the bf16 output, so the MFMA GEMM must
+    <= K <= 512, exact in fp32 and in the bf16 output, so the MFMA GEMM must
     match integer matrix multiplication bit for bit (checks the MFMA lane
-    layout, the LDS swizzle, the tile order and the ragged M tail)."""
-    say(f"gemm exact M={M} N={N} K={K} variant={variant}")
+    layout, the LDS swizzle, the tile order, the ragged M tail and, with
+    ``splits``, the split-K partial sums and their reduction)."""
+    if splits and (K // 64) % splits:
+        pytest.skip("K / 64 not divisible by splits")
+    say(f"gemm exact M={M} N={N} K={K} splits={splits}")
     g = torch.Generator().manual_seed(M * 7 + N + K)
     A = torch.randint(-1, 2, (M, K), generator=g).to(torch.float32)
     B = torch.randint(-1, 2, (N, K), generator=g).to(torch.float32)
     want = (A.to(torch.int64) @ B.to(torch.int64).T).to(torch.float32)
     Ad, Bd = A.to(dev, torch.bfloat16), B.to(dev, torch.bfloat16)
     Cd = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
-    L.dit_debug_gemm(Ad, Bd, Cd, M, N, K, variant)
+    scratch = torch.empty(4 * 256 * N, dtype=torch.float32, device=dev) if splits else None
+    L.dit_debug_gemm("bf16", M, N, K, Ad, Bd, Cd, splits=splits, scratch=scratch)
     torch.cuda.synchronize()
     assert torch.equal(Cd.float().cpu(), want)
 
@@ -49,7 +53,7 @@ def test_gemm_random_full_shape_sampled(dev):
     A = torch.randn((M, K), generator=g, device=dev).to(torch.bfloat16)
     B = torch.randn((N, K), generator=g, device=dev).to(torch.bfloat16)
     Cd = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
-    L.dit_debug_gemm(A, B, Cd, M, N, K)
+    L.dit_debug_gemm("bf16", M, N, K, A, B, Cd)
     torch.cuda.synchronize()
     rs = np.random.default_rng(0)
     rows = rs.choice(M, 64, replace=False)
@@ -110,7 +114,16 @@ def fill_cache(dev, S, nh, seed):
     return cache.to(dev), K.double().numpy(), V.double().numpy()
 
 
-@pytest.mark.parametrize("variant", [0, 1, 3, 4, 5, 6, 7])
+ATTN_VARIANTS = [0, 1, 2, 3, 4]
+
+
+def attn_scratch(dev):
+    """Caller-owned key-split scratch of the attention test hook (64 MiB,
+    the size the step lends it)."""
+    return torch.empty(1 << 24, dtype=torch.float32, device=dev)
+
+
+@pytest.mark.parametrize("variant", ATTN_VARIANTS)
 @pytest.mark.parametrize("name,mode", [("c0w", "extract"), ("c0w", "cached"),
                                        ("ragged", "extract"), ("ragged", "cached"),
                                        ("many_ragged", "extract"), ("many_ragged", "cached"),
@@ -130,7 +143,7 @@ def test_attention_matches_oracle(dev, name, mode, variant):
     seq = L.make_seq(P, T, lim, lim, lim)
     out = torch.empty((N, nh * 128), dtype=torch.bfloat16, device=dev)
     Qd = Q.reshape(N, nh * 128).contiguous().to(dev)
-    L.dit_debug_attention(seq, nh, Qd, nh * 128, q_off, N, cache, out, variant)
+    L.dit_debug_attention(seq, nh, Qd, nh * 128, q_off, N, cache, out, variant, attn_scratch(dev))
     torch.cuda.synchronize()
     ids = O.build_layout(LAYOUTS[name]).image_ids
     allowed = O.block_causal_mask(ids, rows=np.arange(q_off, q_off + N))
@@ -146,7 +159,7 @@ def test_attention_launch_choices_are_bitwise_neutral(dev, name):
     blocks last first (same output, bit for bit, as the unordered kernel), and
     in cached mode its key split of the last round is the forced-split
     variant's, bit for bit. With 2 heads every layout here runs the 4-wave
-    kernel (variants 5 and 7)."""
+    kernel (variants 2 and 4)."""
     nh = 2
     lay = layout_for(LAYOUTS[name])
     P, T = lay["P"], lay["T"]
@@ -156,13 +169,14 @@ def test_attention_launch_choices_are_bitwise_neutral(dev, name):
     lim = torch.from_numpy(lay["row_limit"]).to(dev)
     seq = L.make_seq(P, T, lim, lim, lim)
     g = torch.Generator().manual_seed(13)
-    for mode, other in (("extract", 5), ("cached", 7)):
+    scratch = attn_scratch(dev)
+    for mode, other in (("extract", 2), ("cached", 4)):
         q_off, N = (0, S) if mode == "extract" else (P, T)
         Qd = torch.randn((N, nh * 128), generator=g).to(torch.bfloat16).to(dev)
         outs = []
         for variant in (0, other):
             out = torch.full((N, nh * 128), float("nan"), dtype=torch.bfloat16, device=dev)
-            L.dit_debug_attention(seq, nh, Qd, nh * 128, q_off, N, cache, out, variant)
+            L.dit_debug_attention(seq, nh, Qd, nh * 128, q_off, N, cache, out, variant, scratch)
             outs.append(out)
         torch.cuda.synchronize()
         assert not torch.isnan(outs[0].float()).any(), mode
@@ -210,9 +224,10 @@ def test_attention_random_layouts(dev, seed):
         Qd = Q.reshape(N, nh * 128).contiguous().to(dev)
         allowed = O.block_causal_mask(ids, rows=np.arange(q_off, q_off + N))
         ref = O.masked_attention(Q.double().numpy(), K, V, allowed)
-        for variant in (0, 1, 3, 4, 5, 6, 7):
+        for variant in ATTN_VARIANTS:
             out = torch.empty((N, nh * 128), dtype=torch.bfloat16, device=dev)
-            L.dit_debug_attention(seq, nh, Qd, nh * 128, q_off, N, cache, out, variant)
+            L.dit_debug_attention(seq, nh, Qd, nh * 128, q_off, N, cache, out, variant,
+                                  attn_scratch(dev))
             torch.cuda.synchronize()
             err = rel_err(out.float().cpu().numpy(), ref)
             assert err < 1e-2, (mode, variant, err)
@@ -235,3 +250,90 @@ def test_latent_standardize_matches_oracle(dev, C):
     L.dit_latent_standardize(zd, md, sd, inverse=True)
     torch.cuda.synchronize()
     assert rel_err(zd.cpu().numpy(), O.unstandardize(ref, mean, std)) < 1e-6
+
+
+def rising_qk(kind, S, N, nh, seed):
+    """Queries and keys whose scores drive the softmax's running max.
+    "rising": every key is c*j*u + noise and every query 10*u + noise (u a
+    unit direction per head), so scores climb about ten log2 units per 64-key
+    tile and the running max must be raised on most tiles; "creeping": half
+    that slope, so between raises the unnormalized weights reach up to 2^8;
+    "q8" / "q32": N(0,1) keys with queries scaled 8x / 32x (peaked, random)."""
+    g = np.random.default_rng(seed)
+    u = g.standard_normal((nh, 128))
+    u /= np.linalg.norm(u, axis=1, keepdims=True)
+    if kind in ("rising", "creeping"):
+        c = 0.12 if kind == "rising" else 0.06
+        K = c * np.arange(S)[:, None, None] * u[None] + g.standard_normal((S, nh, 128))
+        Q = 10.0 * u[None] + g.standard_normal((N, nh, 128))
+    else:
+        K = g.standard_normal((S, nh, 128))
+        Q = (8.0 if kind == "q8" else 32.0) * g.standard_normal((N, nh, 128))
+    return Q, K, g.standard_normal((S, nh, 128))
+
+
+def running_max_events(Q, K, allowed, tile=64, jump=8.0):
+    """Host-side count, in the kernel's exp2 domain (score * log2(e)/sqrt(d))
+    and its key-tile order, of the tiles whose max exceeds the query's
+    running max by more than ``jump`` (the kernel must raise its max and
+    rescale O and l) and of those that exceed it by at most ``jump`` (the
+    kernel keeps its max and the weights exceed 1)."""
+    scale = np.log2(np.e) / np.sqrt(Q.shape[2])
+    n_raise = n_over1 = 0
+    for h in range(Q.shape[1]):
+        s = (Q[:, h] @ K[:, h].T) * scale
+        s = np.where(allowed, s, -np.inf)
+        m = np.full(s.shape[0], -np.inf)
+        for t0 in range(0, s.shape[1], tile):
+            tm = s[:, t0:t0 + tile].max(axis=1)
+            seen = np.isfinite(m) & np.isfinite(tm)
+            n_raise += int((seen & (tm > m + jump)).sum())
+            n_over1 += int((seen & (tm > m) & (tm <= m + jump)).sum())
+            m = np.maximum(m, tm)
+    return n_raise, n_over1
+
+
+@pytest.mark.parametrize("kind", ["rising", "creeping", "q8", "q32"])
+@pytest.mark.parametrize("name,mode", [("c1", "extract"), ("c1", "cached"),
+                                       ("many_ragged", "extract"), ("many_ragged", "cached")])
+def test_attention_running_max_raised_mid_stream(dev, name, mode, kind):
+    """Scores that rise along the key sequence or are strongly peaked: the
+    kernel's lazy running max is raised in the middle of the key stream (O and
+    l rescaled) on many tiles, and on others the unnormalized weights exceed 1
+    -- both counted on the host from the same inputs -- and every variant
+    (split ones included) still matches the fp64 oracle."""
+    nh = 2
+    lay = layout_for(LAYOUTS[name])
+    P, T = lay["P"], lay["T"]
+    S = P + T
+    q_off, N = (0, S) if mode == "extract" else (P, T)
+    Q, K, V = rising_qk(kind, S, N, nh, seed=S + len(kind))
+    Qb = torch.from_numpy(Q).to(torch.bfloat16)
+    Kb = torch.from_numpy(K).to(torch.bfloat16)
+    Vb = torch.from_numpy(V).to(torch.bfloat16)
+    cap = L.dit_kv_capacity(S)
+    cache = torch.zeros(2 * nh * cap * 128, dtype=torch.int16)
+    kv, vt = cache_views(cache, 1, nh, cap)
+    kv[0, :, :S, :] = Kb.transpose(0, 1).view(torch.int16)
+    vt[0, :, :, :S] = Vb.permute(1, 2, 0).view(torch.int16)
+    cache = cache.to(dev)
+    ids = O.build_layout(LAYOUTS[name]).image_ids
+    allowed = O.block_causal_mask(ids, rows=np.arange(q_off, q_off + N))
+    Qh, Kh, Vh = Qb.double().numpy(), Kb.double().numpy(), Vb.double().numpy()
+    n_raise, n_over1 = running_max_events(Qh, Kh, allowed)
+    say(f"running max {kind} {name} {mode}: {n_raise} raises, {n_over1} tiles with weights > 1")
+    if kind != "q32":
+        assert n_over1 > 0
+    assert n_raise > (N * nh if kind == "rising" else 0)
+    ref = O.masked_attention(Qh, Kh, Vh, allowed)
+    lim = torch.from_numpy(lay["row_limit"]).to(dev)
+    seq = L.make_seq(P, T, lim, lim, lim)
+    Qd = Qb.reshape(N, nh * 128).contiguous().to(dev)
+    scratch = attn_scratch(dev)
+    for variant in ATTN_VARIANTS:
+        out = torch.empty((N, nh * 128), dtype=torch.bfloat16, device=dev)
+        L.dit_debug_attention(seq, nh, Qd, nh * 128, q_off, N, cache, out, variant, scratch)
+        torch.cuda.synchronize()
+        err = rel_err(out.float().cpu().numpy(), ref)
+        assert err < 1e-2, (variant, err)
+    say(f"  last variant rel err {err:.2e}")

@@ -1,13 +1,15 @@
 """GPU parity of the whole step (extract, cached, Euler) through the C ABI
 against the fp64 oracle on the same seeded inputs, plus the cache
 invariants the pages state, checked on the GPU path itself."""
+import os
+
 import numpy as np
 import pytest
 import torch
 
 import oracle as O
 from diffusion_transformer_amd import synth
-from gpu_common import cache_views, i16_to_f32, rel_err, say
+from gpu_common import cache_views, i16_to_f32, rel_err, say, synth_weights_on_device
 from oracle_inputs import dims_of, oracle_prefix
 
 pytestmark = pytest.mark.gpu
@@ -30,7 +32,7 @@ def build(name, dev, n_layers=None, seed=21):
     cfg = synth.config(name)
     if n_layers is not None:
         cfg["n_layers"] = n_layers
-    W = synth.make_weights(cfg, seed=seed)
+    W = synth.make_weights(cfg, seed=seed, workers=16)
     I = synth.make_inputs(cfg, seed=seed)
     rt = DitRuntime(cfg, W, device=dev)
     seq = rt.sequence(cfg["segments"])
@@ -122,26 +124,96 @@ def test_cache_rows_land_at_their_token_index(dev):
     assert int(vt[0, :, :, seq.S:].abs().sum()) == 0
 
 
-@pytest.fixture(scope="module")
-def c2_full(dev):
-    """32-layer, 4096-wide text-to-image workload (256 text + 64x64 target)
-    with seeded weights drawn on the GPU."""
-    from diffusion_transformer_amd.runtime import random_weights_device
-    cfg = synth.config("c2")
-    Wd = random_weights_device(cfg, 21, dev)
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def depth_golden(name, n_layers):
+    """Stored oracle values of the 8-step Turbo loop of a deep model (written
+    by ``tests/golden/make_depth_goldens.py``, which calls only the oracle and
+    the seeded generators)."""
+    path = os.path.join(GOLDEN, f"depth_{name}_L{n_layers}.npz")
+    assert os.path.exists(path), f"missing {path}: run tests/golden/make_depth_goldens.py"
+    g = np.load(path)
+    return {k: g[k] for k in g.files}
+
+
+def deep_runtime(name, n_layers, dev):
+    """A runtime holding the seeded host weights of ``synth`` (the oracle's),
+    drawn and uploaded layer by layer."""
+    cfg = synth.config(name)
+    cfg["n_layers"] = n_layers
+    Wd, crcs, gcrc = synth_weights_on_device(cfg, dev)
     rt = DitRuntime(cfg, Wd, device=dev, on_device=True)
     I = synth.make_inputs(cfg)
     seq = rt.sequence(cfg["segments"])
     pre = rt.prefix_hidden(I)
     x0 = torch.from_numpy(I["x0"]).to(dev)
-    yield cfg, rt, seq, pre, x0
+    return cfg, rt, seq, pre, x0, Wd, (crcs, gcrc)
+
+
+@pytest.fixture(scope="module")
+def c2_full(dev):
+    """32-layer, 4096-wide text-to-image workload (256 text + 64x64 target)
+    with the seeded host weights the oracle's stored values were made from."""
+    say("c2 full depth: drawing 32 layers of seeded weights")
+    cfg, rt, seq, pre, x0, Wd, crcs = deep_runtime("c2", 32, dev)
+    yield cfg, rt, seq, pre, x0, crcs
+    rt.close()
+    del Wd
+    torch.cuda.empty_cache()
+
+
+def check_turbo_loop_against_golden(name, rt, seq, pre, x0, cfg, crcs):
+    g = depth_golden(name, cfg["n_layers"])
+    assert list(g["layer_crc"]) == list(crcs[0]) and int(g["global_crc"]) == crcs[1], \
+        "the stored oracle values were made from other weights"
+    sig = cfg["sigmas"]
+    rows = g["rows"]
+    vs, xs = rt.run_loop(seq, pre, x0, sig, use_cache=True)
+    torch.cuda.synchronize()
+    worst = 0.0
+    for k in range(len(sig) - 1):
+        v = vs[k].cpu().numpy()
+        e_v = rel_err(v[rows], g["v"][k])
+        e_max = abs(float(np.abs(v).max()) - g["v_absmax"][k]) / g["v_absmax"][k]
+        e_xm = abs(float(xs[k].abs().max()) - g["x_absmax"][k]) / g["x_absmax"][k]
+        say(f"  step {k} {'extract' if k == 0 else 'cached'}: v rel {e_v:.3e} on {len(rows)} rows, "
+            f"max|v| rel {e_max:.1e}, max|x| rel {e_xm:.1e}")
+        assert e_v < TOL_BF16 and e_max < TOL_BF16 and e_xm < TOL_BF16
+        worst = max(worst, e_v)
+    e_x = rel_err(xs[-1].cpu().numpy(), g["x_final"])
+    say(f"  final latent (all {seq.T} rows) rel {e_x:.3e}; worst v step {worst:.3e}")
+    assert e_x < TOL_BF16
+
+
+@pytest.mark.timeout(900)
+def test_full_depth_turbo_loop_matches_oracle(dev, c2_full):
+    """The target configuration: the 32-layer, 4096-wide model over the whole
+    8-step Turbo loop (extract, then seven cached steps) against the fp64
+    oracle's stored values -- v_θ of every step on a seeded eighth of the
+    target rows, max |v_θ| and max |x| over all rows, and the final latent
+    on every row."""
+    cfg, rt, seq, pre, x0, crcs = c2_full
+    say("c2 full depth: 8-step Turbo loop vs the oracle")
+    check_turbo_loop_against_golden("c2", rt, seq, pre, x0, cfg, crcs)
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("name", ["c3", "c4"])
+def test_two_layer_turbo_loop_matches_oracle(dev, name):
+    """The editing (4352-row prefix) and multi-reference (12800-row prefix,
+    96x96 target) workloads at full width with two layers, over all eight
+    Turbo steps, against the oracle's stored values."""
+    say(f"{name} two layers: 8-step Turbo loop vs the oracle")
+    cfg, rt, seq, pre, x0, Wd, crcs = deep_runtime(name, 2, dev)
+    check_turbo_loop_against_golden(name, rt, seq, pre, x0, cfg, crcs)
     rt.close()
     del Wd
     torch.cuda.empty_cache()
 
 
 def test_full_depth_cached_matches_recompute(dev, c2_full):
-    cfg, rt, seq, pre, x0 = c2_full
+    cfg, rt, seq, pre, x0, _ = c2_full
     say("c2 full depth: 8-step cached loop vs recompute")
     vs_c, xs_c = rt.run_loop(seq, pre, x0, cfg["sigmas"], use_cache=True)
     vs_r, xs_r = rt.run_loop(seq, pre, x0, cfg["sigmas"], use_cache=False)
@@ -158,7 +230,7 @@ def test_full_depth_cache_invariants(dev, c2_full):
     """Prefix K/V independent of σ and x; cached steps never write rows < P;
     the same cached step twice gives identical bits; without t = 0
     conditioning the prefix K/V change."""
-    cfg, rt, seq, pre, x0 = c2_full
+    cfg, rt, seq, pre, x0, _ = c2_full
     say("c2 full depth: cache invariants")
     P, S = seq.P, seq.S
     cap = L.dit_kv_capacity(S)
@@ -204,9 +276,9 @@ def test_full_depth_cache_invariants(dev, c2_full):
 def test_full_depth_largest_workloads_cached_matches_recompute(dev, name):
     """The editing (4352-row prefix), multi-reference (12800-row prefix, 96x96
     target, 22016 keys, 11.6 GB of KV cache) and ten-reference (41472-row
-    prefix, 50688 keys, 26.6 GB of KV cache) workloads at full depth: the
-    first three Turbo steps, cached against full recompute, finite and within
-    the cached-path bound."""
+    prefix, 50688 keys, 26.6 GB of KV cache) workloads at full depth: all
+    eight Turbo steps, cached against full recompute, finite and within the
+    cached-path bound."""
     from diffusion_transformer_amd.runtime import random_weights_device
     cfg = synth.config(name)
     Wd = random_weights_device(cfg, 21, dev)
@@ -215,8 +287,8 @@ def test_full_depth_largest_workloads_cached_matches_recompute(dev, name):
     seq = rt.sequence(cfg["segments"])
     pre = rt.prefix_hidden(I)
     x0 = torch.from_numpy(I["x0"]).to(dev)
-    sig = cfg["sigmas"][:4]
-    say(f"{name} full depth P={seq.P} T={seq.T}: 3-step cached loop vs recompute")
+    sig = cfg["sigmas"]
+    say(f"{name} full depth P={seq.P} T={seq.T}: 8-step cached loop vs recompute")
     vs_c, xs_c = rt.run_loop(seq, pre, x0, sig, use_cache=True)
     vs_r, xs_r = rt.run_loop(seq, pre, x0, sig, use_cache=False)
     torch.cuda.synchronize()
@@ -404,6 +476,37 @@ def test_degenerate_layouts(dev, segs):
     torch.cuda.synchronize()
     ref = O.run_loop(W, dims_of(cfg), O.build_layout(cfg["segments"]), oracle_prefix(cfg, W, I),
                      I["x0"], sig, use_cache=True)
+    for k, r in enumerate(ref):
+        e_v = rel_err(vs[k].cpu().numpy(), r["v"])
+        e_x = rel_err(xs[k].cpu().numpy(), r["x_next"])
+        say(f"  step {k} {r['mode']}: v rel {e_v:.3e}  x rel {e_x:.3e}")
+        assert e_v < TOL_BF16 and e_x < TOL_BF16
+    rt.close()
+
+
+def test_peaked_attention_loop_matches_oracle(dev):
+    """Peaked attention inside the step: QK-RMSNorm weights near 1.5 (so
+    1 + w is about 2.5 and every score is about six times larger) on a
+    344-token layout with six key tiles, through the 3-step loop against the
+    oracle on the same weights."""
+    segs = [("text", 100), ("ref", 10, 10), ("target", 12, 12)]
+    cfg = synth.config("c0w", segments=segs)
+    W = synth.make_weights(cfg)
+    g = np.random.default_rng(31)
+    for layer in W["layers"]:
+        for k in ("q_norm", "k_norm"):
+            layer[k] = synth.round_bf16((1.5 + 0.1 * g.standard_normal(128)).astype(np.float32))
+    I = synth.make_inputs(cfg)
+    rt = DitRuntime(cfg, W, device=dev)
+    seq = rt.sequence(cfg["segments"])
+    pre = rt.prefix_hidden(I)
+    x0 = torch.from_numpy(I["x0"]).to(dev)
+    sig = cfg["sigmas"]
+    say(f"peaked attention: P={seq.P} T={seq.T}")
+    vs, xs = rt.run_loop(seq, pre, x0, sig, use_cache=True)
+    torch.cuda.synchronize()
+    ref = O.run_loop(W, dims_of(cfg), O.build_layout(segs), oracle_prefix(cfg, W, I), I["x0"], sig,
+                     use_cache=True)
     for k, r in enumerate(ref):
         e_v = rel_err(vs[k].cpu().numpy(), r["v"])
         e_x = rel_err(xs[k].cpu().numpy(), r["x_next"])
