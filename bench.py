@@ -27,7 +27,7 @@ PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 GEMM_SRC = os.path.join(ROOT, "diffusion_transformer_amd", "csrc", "gemm.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gemm_gateup_c2_cached.json")
 # the dominant kernel of the cached step: the fused gate/up GEMM + SwiGLU
-GATEUP_KERNEL = "gemm_w4_kernel<3, true, true>"
+GATEUP_KERNEL = "gemm_w4_kernel<3, true>"
 GATEUP_LABEL = "gemm_w4_kernel<SwiGLU> (gate/up, 256x256 tiles, 4 waves of 128x128)"
 
 
@@ -95,10 +95,63 @@ def summarize_profiles(trace_dir, fetch_dir, write_dir, command, out_md, out_jso
     lines += ["", f"Total {fb + wb:.4g} bytes per launch vs {alg:.4g} algorithmic "
                   f"(A 32 MiB + B 256 MiB read, 128 MiB written): x{(fb + wb) / alg:.2f}."]
     open(out_md, "w").write("\n".join(lines) + "\n")
+    hbm_kernels_summary(trace_dir, fetch_dir, write_dir, command, res,
+                        os.path.join(ROOT, "profiles", "hbm_kernels_c2_cached.md"))
     json.dump({"kernel": GATEUP_LABEL + ", cached c2 (M=4096)",
                "source_sha256": source_sha(GEMM_SRC), "fetch": res["FETCH_SIZE"],
                "write": res["WRITE_SIZE"], "bytes_per_launch": fb + wb,
                "algorithmic_bytes": alg}, open(out_json, "w"), indent=1)
+
+
+# Bandwidth-bound kernels of the c2 cached step (T = 4096 target rows,
+# H = 4096): kernel-name match, grid size, algorithmic bytes per launch.
+HBM_KERNELS = [
+    ("LayerNorm + modulation (ln_mod_kernel)", "ln_mod_kernel", 2048 * 256,
+     4096 * 4096 * (4 + 2) + 2 * 4096 * 4),
+    ("final AdaLN + proj_out (final_out_kernel)", "final_out_kernel", 256 * 256,
+     4096 * 4096 * 4 + 4096 * 64 * 4 + 4096 * 4 + 64 * 4096 * 2),
+    ("img_in (img_in_kernel)", "img_in_kernel", 16 * 64 * 256,
+     4096 * 4096 * 4 + 4096 * 64 * 4 + 4096 * 64 * 2),
+    ("modulation GEMV [16384 x 4096] (gemv_kernel)", "gemv_kernel", 1024 * 256,
+     16384 * 4096 * 2 + 4096 * 4 + 16384 * 4),
+]
+
+
+def hbm_kernels_summary(trace_dir, fetch_dir, write_dir, command, calib, out_md):
+    """Calibrated FETCH_SIZE / WRITE_SIZE bytes per launch of the
+    bandwidth-bound kernels, against their algorithmic bytes and the kernel
+    trace's average duration (same command as the gate/up summary)."""
+    import csv
+    trace = list(csv.DictReader(open(os.path.join(trace_dir, "run_kernel_trace.csv"))))
+
+    def grid(r):
+        return int(r.get("Grid_Size") or r.get("Grid_Size_X") or 0)
+    lines = ["# rocprofv3 HBM bytes of the bandwidth-bound kernels: cached DiT step, c2 workload", "",
+             "Commands (from the repository root on the MI355X machine; R = repository root):", "", "```",
+             command, "```", "",
+             f"FETCH_SIZE x{calib['FETCH_SIZE']['factor']:.4f}, WRITE_SIZE x{calib['WRITE_SIZE']['factor']:.4f} "
+             "(the fp32->bf16 copy of 2^28 elements reads 1 GiB and writes 512 MiB). Durations: kernel "
+             "trace of the timed run. HBM peak 8 TB/s.", "",
+             "| kernel | launches | avg us | fetched MB | written MB | algorithmic MB | measured / alg "
+             "| GB/s (alg bytes) | % of 8 TB/s |", "|---|---|---|---|---|---|---|---|---|"]
+    for label, match, g, alg in HBM_KERNELS:
+        ns = [int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) for r in trace
+              if match in r["Kernel_Name"] and grid(r) == g]
+        by = {}
+        for name, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+            rows = [r for r in csv.DictReader(open(os.path.join(d, "run_counter_collection.csv")))
+                    if match in r["Kernel_Name"] and int(r["Grid_Size"]) == g]
+            by[name] = (sum(float(r["Counter_Value"]) for r in rows) / len(rows) * calib[name]["factor"] * 1024
+                        if rows else float("nan"))
+        if not ns:
+            continue
+        avg = sum(ns) / len(ns)
+        gbs = alg / avg
+        lines.append(f"| {label} | {len(ns)} | {avg / 1e3:.1f} | {by['FETCH_SIZE'] / 1e6:.1f} | "
+                     f"{by['WRITE_SIZE'] / 1e6:.1f} | {alg / 1e6:.1f} | "
+                     f"{(by['FETCH_SIZE'] + by['WRITE_SIZE']) / alg:.2f} | {gbs:.0f} | "
+                     f"{gbs / PEAK_HBM_GBS * 100:.1f} |")
+    open(out_md, "w").write("\n".join(lines) + "\n")
 
 
 def summarize_counters(counter_dir, fetch_dir, write_dir, command, out_md):
@@ -261,6 +314,119 @@ def cpu_baseline(cfg, seconds_hint=True):
                        f"scaled x{cfg['n_layers']}")}
 
 
+def measured_peaks(L, dev):
+    """The ceilings this GPU actually reaches, next to the spec peaks: a
+    register-only bf16 MFMA loop on N(0,1) operands (the library's own
+    32x32x16 instruction, one workgroup of 4 waves per CU, ~0.5 s per
+    launch, best of 3) and a 1 GiB fp32 device-to-device copy (bytes read +
+    written, median of 10)."""
+    import torch
+    g = torch.Generator(device=dev).manual_seed(7)
+    ops = torch.randn(1 << 19, generator=g, device=dev).to(torch.bfloat16)   # 1 MiB
+    blocks, iters = 256, 400
+    out = torch.empty(blocks * 256, dtype=torch.float32, device=dev)
+    flop = blocks * 4 * iters * 64 * 32768
+    best = 0.0
+    for _ in range(3):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        L.dit_debug_mfma_loop(ops, out, blocks, iters)
+        b.record()
+        torch.cuda.synchronize()
+        best = max(best, flop / (a.elapsed_time(b) / 1e3) / 1e12)
+    src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    L.dit_debug_stream_copy(src, dst)
+    ts = []
+    for _ in range(10):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        L.dit_debug_stream_copy(src, dst)
+        b.record()
+        torch.cuda.synchronize()
+        ts.append(a.elapsed_time(b))
+    gbs = 2 * src.numel() * 4 / (float(np.median(ts)) / 1e3) / 1e9
+    del src, dst
+    return {"mfma_bf16_tflops": round(best, 1), "hbm_copy_gbs": round(gbs, 1),
+            "method": "register-only v_mfma_f32_32x32x16_bf16 loop on N(0,1) bf16 operands "
+                      "(256 workgroups x 4 waves, 8 chains per wave, best of 3); "
+                      "1 GiB device copy with 16-byte accesses (the library's copy kernel), "
+                      "read + written bytes (median of 10)"}
+
+
+def visible_pairs(row_limit, rows):
+    """Visible (query, key) pairs of the given query rows under the
+    row-limit form of the block-causal mask."""
+    return int(np.sum(row_limit[rows].astype(np.int64) + 1))
+
+
+def time_workload(rt, L, name, steps=5):
+    """Cached and extract step times of another workload with the same
+    model (same layer shapes): the editing and multi-reference layouts."""
+    import torch
+    from diffusion_transformer_amd import synth
+    cfg = synth.config(name)
+    H, F, nh, d, Lc = cfg["hidden"], cfg["ffn"], cfg["n_heads"], cfg["head_dim"], cfg["n_layers"]
+    I = synth.make_inputs(cfg, seed=21)
+    seq = rt.sequence(cfg["segments"])
+    P, T, S = seq.P, seq.T, seq.S
+    pre = rt.prefix_hidden(I)
+    x = torch.from_numpy(I["x0"]).to(rt.device)
+    sig = cfg["sigmas"]
+    cache = rt.alloc_cache(seq)
+    ws = rt.alloc_workspace(S)
+    v = torch.empty_like(x)
+    stream = torch.cuda.current_stream()
+
+    def ev():
+        return torch.cuda.Event(enable_timing=True)
+    rt.step_extract(seq, pre, x.clone(), sig[0], cache, v, ws)
+    ex = []
+    for _ in range(2):
+        a, b = ev(), ev()
+        a.record(stream)
+        rt.step_extract(seq, pre, x.clone(), sig[0], cache, v, ws)
+        b.record(stream)
+        torch.cuda.synchronize()
+        ex.append(a.elapsed_time(b))
+    xc = x.clone()
+    rt.step_cached(seq, xc, sig[1], cache, v, ws)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(steps):
+        j = 1 + (k % (len(sig) - 2))
+        rt.step_cached(seq, xc, sig[j], cache, v, ws)
+        L.euler_update(xc, v, sig[j], sig[j + 1])
+    torch.cuda.synchronize()
+    cached_ms = (time.perf_counter() - t0) * 1000.0 / steps
+    L.dit_profile_enable(rt.model, "attention")
+    for k in range(2):
+        rt.step_cached(seq, xc, sig[1 + k], cache, v, ws)
+    torch.cuda.synchronize()
+    att_ms, att_n = L.dit_profile_read(rt.model)
+    L.dit_profile_enable(rt.model, "off")
+    att_avg = att_ms / max(att_n, 1)
+    lim = seq.host["row_limit"]
+    gemm = lambda n: 2 * n * H * (3 * H + H + 2 * F) + 2 * n * F * H
+    fl_cached = Lc * (gemm(T) + 4 * d * nh * visible_pairs(lim, np.arange(P, S)))
+    fl_extract = Lc * (gemm(S) + 4 * d * nh * visible_pairs(lim, np.arange(S)))
+    att_tf = 4 * d * nh * T * S / (att_avg / 1e3) / 1e12
+    extract_ms = float(np.median(ex))
+    out = {"workload": f"{name}: {describe(cfg)}", "prefix_tokens": P, "target_tokens": T,
+           "ms_per_cached_step": round(cached_ms, 3), "target_tok_s": round(T / (cached_ms / 1e3), 1),
+           "step_frac_bf16_peak": round(fl_cached / (cached_ms / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+           "extract_ms": round(extract_ms, 3), "extract_over_cached": round(extract_ms / cached_ms, 3),
+           "flop_ratio_extract_over_cached": round(fl_extract / fl_cached, 3),
+           "token_ratio_S_over_T": round(S / T, 3),
+           "attention_ms_per_layer": round(att_avg, 4),
+           "attention_frac_bf16_peak": round(att_tf / PEAK_BF16_TFLOPS, 4)}
+    del cache, ws
+    torch.cuda.empty_cache()
+    return out
+
+
 def main():
     if len(sys.argv) > 1 and sys.argv[1] == "--summarize-trace":
         # bench.py --summarize-trace TRACE_DIR TITLE "COMMAND" OUT_MD
@@ -298,12 +464,18 @@ def main():
     ap.add_argument("--no-breakdown", action="store_true")
     ap.add_argument("--only-timed", action="store_true",
                     help="run only cache build + warmup + timed cached steps (for profilers)")
+    ap.add_argument("--workloads", default="c3,c4",
+                    help="other workloads with the same layer shapes timed in the same run "
+                         "(reusing the loaded weights), reported under 'workloads'")
+    ap.add_argument("--no-peaks", action="store_true", help="skip the measured MFMA / copy ceilings")
     ap.add_argument("--calib-copy", action="store_true",
                     help="after timing, run one fp32->bf16 conversion of 2^28 elements "
                          "(1 GiB read, 512 MiB written) to calibrate byte counters")
     args = ap.parse_args()
     if args.only_timed:
         args.no_breakdown = True
+        args.no_peaks = True
+        args.workloads = ""
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the library has no multi-GPU path "
               "(run with --gpus 1)", file=sys.stderr)
@@ -412,7 +584,14 @@ def main():
     # ---- per-kernel breakdown of the cached step (separate passes) ----
     breakdown = {}
     if not args.no_breakdown:
-        for name in ("gemm_qkv", "gemm_o", "gemm_gateup", "gemm_down", "attention", "ln"):
+        hbm_bytes = {   # algorithmic bytes per launch of the bandwidth-bound kernels
+            "ln": T * H * (4 + 2) + 2 * H * 4,
+            "final": T * H * 4 + T * cfg["latent"] * 4 + H * 4 + cfg["latent"] * H * 2,
+            "img_in": T * H * 4 + T * cfg["latent"] * 4 + H * cfg["latent"] * 2,
+            "gemv_mod": 4 * H * H * 2 + H * 4 + 4 * H * 4,
+        }
+        for name in ("gemm_qkv", "gemm_o", "gemm_gateup", "gemm_down", "attention", "ln", "final",
+                     "img_in", "gemv_mod"):
             L.dit_profile_enable(rt.model, name)
             xb = x.clone()
             for k in range(3):
@@ -424,12 +603,29 @@ def main():
             if name in fl:
                 tf = fl[name] / (avg / 1e3) / 1e12
                 entry.update({"tflops": round(tf, 1), "frac_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4)})
-            elif name == "ln":
-                by = T * H * (4 + 2) + 2 * H * 4
+            elif name in hbm_bytes:
+                by = hbm_bytes[name]
                 gbs = by / (avg / 1e3) / 1e9
                 entry.update({"gbs": round(gbs, 1), "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4)})
             breakdown[name] = entry
         L.dit_profile_enable(rt.model, "off")
+
+    # ---- the same model on the other workloads (same layer shapes) ----
+    others = {}
+    for name in [w for w in args.workloads.split(",") if w and w != args.config and B == 1]:
+        print(f"[bench] workload {name} with the same weights", file=sys.stderr, flush=True)
+        others[name] = time_workload(rt, L, name)
+
+    peaks = None
+    if not args.no_peaks:
+        print("[bench] measured MFMA / copy ceilings", file=sys.stderr, flush=True)
+        peaks = measured_peaks(L, dev)
+        roofline["frac_measured_peak"] = round(gu_tflops / peaks["mfma_bf16_tflops"], 4)
+        for name, e in breakdown.items():
+            if "tflops" in e:
+                e["frac_measured_mfma_peak"] = round(e["tflops"] / peaks["mfma_bf16_tflops"], 4)
+            if "gbs" in e:
+                e["frac_measured_copy_peak"] = round(e["gbs"] / peaks["hbm_copy_gbs"], 4)
 
     step_flops = Lc * sum(fl.values())
     out = {
@@ -461,6 +657,8 @@ def main():
         "loop_8step_ms": None if loop_ms != loop_ms else round(loop_ms, 3),
         "roofline": roofline,
         "kernels": breakdown,
+        "measured_peaks": peaks,
+        "workloads": others,
     }
     if not args.no_cpu_baseline:
         print("[bench] timing the fp64 oracle on the host (cpu_baseline)", file=sys.stderr, flush=True)

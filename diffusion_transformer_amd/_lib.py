@@ -24,13 +24,16 @@ DIT_OK, DIT_ERR_ARG, DIT_ERR_SHAPE, DIT_ERR_LAYOUT, DIT_ERR_STATE, DIT_ERR_WORKS
     DIT_ERR_HIP, DIT_ERR_UNSUPPORTED = range(8)
 DIT_FLAG_NO_CAUSAL_CONDITION = 1
 PROF = {"off": 0, "gemm_qkv": 1, "gemm_o": 2, "gemm_gateup": 3, "gemm_down": 4,
-        "attention": 5, "ln": 6, "qknorm_rope": 7}
+        "attention": 5, "ln": 6, "qknorm_rope": 7, "final": 8, "img_in": 9, "gemv": 10,
+        "gemv_mod": 11}
 SEG_TEXT, SEG_REF, SEG_TARGET = 0, 1, 2
 
 EXPORTS = ["dit_build_layout", "dit_load_weights", "dit_free", "dit_workspace_bytes",
            "dit_kv_capacity", "dit_kv_cache_bytes", "dit_step_extract", "dit_step_cached",
            "euler_update", "dit_img_in", "dit_latent_standardize", "dit_debug_mask", "dit_debug_attention",
-           "dit_debug_gemm", "dit_profile_enable", "dit_profile_read", "dit_last_error",
+           "dit_debug_gemm", "dit_debug_final_out", "dit_debug_stream_copy", "dit_debug_mfma_loop",
+           "dit_profile_enable", "dit_profile_read",
+           "dit_last_error",
            "dit_version"]
 
 
@@ -71,7 +74,7 @@ class dit_gemm_desc(C.Structure):
                 ("splits", C.c_int), ("scratch", C.c_void_p), ("scratch_bytes", C.c_size_t)]
 
 
-DIT_GEMM = {"bf16": 0, "f32": 1, "resid": 2, "swiglu": 3, "qkv": 5}
+DIT_GEMM = {"bf16": 0, "resid": 2, "swiglu": 3, "qkv": 5}
 
 
 def _load(path=None):
@@ -97,6 +100,9 @@ def _load(path=None):
         "dit_debug_mask": (i, [P(dit_seq), vp, vp]),
         "dit_debug_attention": (i, [P(dit_seq), i, vp, i, i, i, vp, vp, i, vp, sz, vp]),
         "dit_debug_gemm": (i, [P(dit_gemm_desc), vp]),
+        "dit_debug_mfma_loop": (i, [vp, vp, i, i, vp]),
+        "dit_debug_final_out": (i, [vp, i, i, i, vp, f, vp, vp, vp]),
+        "dit_debug_stream_copy": (i, [vp, vp, sz, vp]),
         "dit_profile_enable": (i, [vp, i]),
         "dit_profile_read": (i, [vp, P(C.c_double), P(ll)]),
         "dit_last_error": (C.c_char_p, []),
@@ -231,19 +237,19 @@ def _make_api(_lib):
             raise DitError(DIT_ERR_ARG, f"{what}: need a contiguous {dtype} device tensor of "
                                         f"{numel} elements, got {desc}")
 
-    def _step_tensors(model, seq, x, v_out, prefix_hidden=None):
+    def _step_tensors(model, seq, x, v_out, prefix_hidden=None, extract=False):
         if model not in _dims:
             raise DitError(DIT_ERR_ARG, "model handle is not loaded")
         H, Cl = _dims[model]
         rows = max(int(seq.B), 1) * int(seq.T)
         _need(x, "x", rows * Cl)
         _need(v_out, "v_out", rows * Cl)
-        if prefix_hidden is not None or seq.P > 0:
+        if extract and (prefix_hidden is not None or seq.P > 0):
             _need(prefix_hidden, "prefix_hidden", int(seq.P) * H)
 
     def dit_step_extract(model, seq: dit_seq, prefix_hidden, x, sigma, kv_cache, v_out, workspace,
                          flags=0, stream=None):
-        _step_tensors(model, seq, x, v_out, prefix_hidden)
+        _step_tensors(model, seq, x, v_out, prefix_hidden, extract=True)
         _check(_lib.dit_step_extract(model, C.byref(seq), _ptr(prefix_hidden), _ptr(x), float(sigma),
                                      _ptr(kv_cache), _nbytes(kv_cache), _ptr(v_out), _ptr(workspace),
                                      _nbytes(workspace), int(flags), _stream(stream)))
@@ -301,6 +307,19 @@ def _make_api(_lib):
         d.scratch = _ptr(scratch)
         d.scratch_bytes = _nbytes(scratch) if scratch is not None else 0
         _check(_lib.dit_debug_gemm(C_.byref(d), _stream(stream)))
+
+    def dit_debug_final_out(h, scale_out, w_out, v_out, eps=1e-6, stream=None):
+        """h [rows, H] f32, scale_out [H] f32, w_out [64, H] bf16, v_out [rows, 64] f32."""
+        _check(_lib.dit_debug_final_out(_ptr(h), int(h.shape[1]), int(h.shape[0]), int(h.shape[1]),
+                                        _ptr(scale_out), float(eps), _ptr(w_out), _ptr(v_out),
+                                        _stream(stream)))
+
+    def dit_debug_stream_copy(src, dst, stream=None):
+        _check(_lib.dit_debug_stream_copy(_ptr(src), _ptr(dst), _nbytes(src), _stream(stream)))
+
+    def dit_debug_mfma_loop(ops, out, blocks, iters, stream=None):
+        _check(_lib.dit_debug_mfma_loop(_ptr(ops), _ptr(out), int(blocks), int(iters),
+                                        _stream(stream)))
 
     def dit_profile_enable(model, kernel_class):
         if isinstance(kernel_class, str):

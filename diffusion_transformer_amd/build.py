@@ -15,9 +15,10 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OUT = os.path.join(PKG, "libdit.so")
 OUT_F32 = os.path.join(PKG, "libdit_f32.so")
-SOURCES = ["gemm.hip", "attention.hip", "mask.hip", "elementwise.hip", "dit_api.cpp"]
+SOURCES = ["gemm.hip", "attention.hip", "mask.hip", "elementwise.hip", "head.hip", "peak.hip",
+           "dit_api.cpp"]
 # fp32 debug build: fp32 activations / cache / attention, plain FMA GEMMs
-SOURCES_F32 = ["debug_f32.hip", "mask.hip", "elementwise.hip", "dit_api.cpp"]
+SOURCES_F32 = ["debug_f32.hip", "mask.hip", "elementwise.hip", "head.hip", "dit_api.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

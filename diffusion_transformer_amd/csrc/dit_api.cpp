@@ -170,7 +170,8 @@ inline const uint16_t* U(const void* p) { return static_cast<const uint16_t*>(p)
 // cached: the T target tokens (global rows P..S-1).
 dit_status run_step(dit_model* m, const dit_seq* seq, bool extract, const float* prefix,
                     const float* x, float sigma, void* kv, float* v_out, void* ws, int flags,
-                    hipStream_t st) {
+                    hipStream_t st, bool timing = true) {
+  dit_model* const tmm = timing ? m : nullptr;   // per-kernel events only when timing
   const dit_config& c = m->cfg;
   const int H = c.hidden, F = c.ffn, nh = c.n_heads, L = c.n_layers;
   // S: one element's sequence (layout tables, mask); SA: all rows/keys with
@@ -208,24 +209,39 @@ dit_status run_step(dit_model* m, const dit_seq* seq, bool extract, const float*
   const int nv = extract ? 2 : 1;
   const float t_pre = (flags & DIT_FLAG_NO_CAUSAL_CONDITION) ? t : 0.f;
   LAUNCH(launch_temb(t, t_pre, c.time_dim, c.rope_base, te, st), "temb");
-  LAUNCH(launch_gemv(U(m->t1), H, c.time_dim, te, c.time_dim, nv, a1, H, a1s, st), "gemv t1");
-  LAUNCH(launch_gemv(U(m->t2), H, H, a1s, H, nv, tb, H, tbs, st), "gemv t2");
-  LAUNCH(launch_gemv(U(m->mod), 4 * H, H, tbs, H, nv, mod, 4 * H, nullptr, st), "gemv mod");
+  {
+    Timed tm(tmm, DIT_PROF_GEMV, st);
+    LAUNCH(launch_gemv(U(m->t1), H, c.time_dim, te, c.time_dim, nv, a1, H, a1s, st), "gemv t1");
+  }
+  {
+    Timed tm(tmm, DIT_PROF_GEMV, st);
+    LAUNCH(launch_gemv(U(m->t2), H, H, a1s, H, nv, tb, H, tbs, st), "gemv t2");
+  }
+  {
+    Timed tm(tmm, DIT_PROF_GEMV_MOD, st);
+    LAUNCH(launch_gemv(U(m->mod), 4 * H, H, tbs, H, nv, mod, 4 * H, nullptr, st), "gemv mod");
+  }
   LAUNCH(launch_gate_tanh(mod, H, nv, st), "gate tanh");
-  LAUNCH(launch_gemv(U(m->so), H, H, tbs, H, 1, scale_out, H, nullptr, st), "gemv so");
+  {
+    Timed tm(tmm, DIT_PROF_GEMV, st);
+    LAUNCH(launch_gemv(U(m->so), H, H, tbs, H, 1, scale_out, H, nullptr, st), "gemv so");
+  }
   const float* row_t = mod;
   const float* row_0 = extract ? mod + 4 * H : mod;
 
   // ---- residual stream init ----
   if (extract && P > 0)
     LAUNCH(hipMemcpyAsync(hbuf, prefix, (size_t)P * H * 4, hipMemcpyDeviceToDevice, st), "prefix copy");
-  LAUNCH(launch_img_in(U(m->img_in), x, TB, H, hbuf + (size_t)n_pre * H, H, st), "img_in");
+  {
+    Timed tm(tmm, DIT_PROF_IMG_IN, st);
+    LAUNCH(launch_img_in(U(m->img_in), x, TB, H, hbuf + (size_t)n_pre * H, H, st), "img_in");
+  }
 
   for (int l = 0; l < L; ++l) {
     act_t* kl = kbase + (size_t)l * nh * cap * 128;
     act_t* vl = vbase + (size_t)l * nh * 128 * cap;
     {
-      Timed tm(m, DIT_PROF_LN, st);
+      Timed tm(tmm, DIT_PROF_LN, st);
       LAUNCH(launch_ln_mod(hbuf, H, N, H, row_t, row_0, n_pre, c.eps, xb, H, st), "ln1");
     }
     // QKV projection with the per-head QK-RMSNorm, RoPE and K / Vᵀ cache
@@ -238,7 +254,7 @@ dit_status run_step(dit_model* m, const dit_seq* seq, bool extract, const float*
     q.cosv = seq->d_rope_cos; q.sinv = seq->d_rope_sin;
     q.kc = kl; q.vtc = vl; q.eps = c.eps;
     {
-      Timed tm(m, DIT_PROF_GEMM_QKV, st);
+      Timed tm(tmm, DIT_PROF_GEMM_QKV, st);
       GemmArgs g{};
       g.A = xb; g.lda = H; g.B = U(m->qkv[l]); g.ldb = H; g.M = N; g.N = 3 * H; g.K = H;
       g.C = qkv; g.ldc = 3 * H;
@@ -248,13 +264,13 @@ dit_status run_step(dit_model* m, const dit_seq* seq, bool extract, const float*
     }
     if (extract && cap > SA) {
       // cache keys SA .. cap-1 (capacity padding) are zero-filled
-      Timed tm(m, DIT_PROF_QKNORM_ROPE, st);
+      Timed tm(tmm, DIT_PROF_QKNORM_ROPE, st);
       QkArgs z = q;
       z.g_begin = SA; z.g_end = cap;
       LAUNCH(launch_qknorm_rope(z, st), "cache padding");
     }
     {
-      Timed tm(m, DIT_PROF_ATTENTION, st);
+      Timed tm(tmm, DIT_PROF_ATTENTION, st);
       AttnArgs a{};
       a.q = qkv; a.q_stride = 3 * H; a.q_off = q_row0; a.N = N;
       a.k = kl; a.vt = vl; a.cap = cap; a.S = S; a.nh = nh; a.limit = seq->d_row_limit;
@@ -263,7 +279,7 @@ dit_status run_step(dit_model* m, const dit_seq* seq, bool extract, const float*
       LAUNCH(launch_attention(a, st), "attention");
     }
     {
-      Timed tm(m, DIT_PROF_GEMM_O, st);
+      Timed tm(tmm, DIT_PROF_GEMM_O, st);
       GemmArgs g{};
       g.A = att; g.lda = H; g.B = U(m->o[l]); g.ldb = H; g.M = N; g.N = H; g.K = H;
       g.Hres = hbuf; g.ldh = H; g.gate_t = row_t + H; g.gate_0 = row_0 + H; g.n_pre = n_pre;
@@ -271,11 +287,11 @@ dit_status run_step(dit_model* m, const dit_seq* seq, bool extract, const float*
       LAUNCH(launch_gemm(g, EPI_RESID, st), "gemm o");
     }
     {
-      Timed tm(m, DIT_PROF_LN, st);
+      Timed tm(tmm, DIT_PROF_LN, st);
       LAUNCH(launch_ln_mod(hbuf, H, N, H, row_t + 2 * H, row_0 + 2 * H, n_pre, c.eps, xb, H, st), "ln2");
     }
     {
-      Timed tm(m, DIT_PROF_GEMM_GATEUP, st);
+      Timed tm(tmm, DIT_PROF_GEMM_GATEUP, st);
       GemmArgs g{};
       g.A = xb; g.lda = H; g.B = U(m->gate[l]); g.B2 = U(m->up[l]); g.ldb = H;
       g.M = N; g.N = 2 * F; g.K = H; g.C = ffn; g.ldc = F;
@@ -283,7 +299,7 @@ dit_status run_step(dit_model* m, const dit_seq* seq, bool extract, const float*
       LAUNCH(launch_gemm(g, EPI_SWIGLU, st), "gemm gate/up");
     }
     {
-      Timed tm(m, DIT_PROF_GEMM_DOWN, st);
+      Timed tm(tmm, DIT_PROF_GEMM_DOWN, st);
       GemmArgs g{};
       g.A = ffn; g.lda = F; g.B = U(m->down[l]); g.ldb = F; g.M = N; g.N = H; g.K = F;
       g.Hres = hbuf; g.ldh = H; g.gate_t = row_t + 3 * H; g.gate_0 = row_0 + 3 * H; g.n_pre = n_pre;
@@ -293,6 +309,7 @@ dit_status run_step(dit_model* m, const dit_seq* seq, bool extract, const float*
   }
 
   // ---- scale-only final AdaLN on target rows, proj_out -> v ----
+#ifdef DIT_F32
   LAUNCH(launch_ln_mod(hbuf + (size_t)n_pre * H, H, TB, H, scale_out, scale_out, 0, c.eps, xb, H, st),
          "final ln");
   {
@@ -301,6 +318,13 @@ dit_status run_step(dit_model* m, const dit_seq* seq, bool extract, const float*
     g.C = v_out; g.ldc = c.latent;
     LAUNCH(launch_gemm(g, EPI_F32, st), "gemm proj_out");
   }
+#else
+  {
+    Timed tm(tmm, DIT_PROF_FINAL, st);
+    LAUNCH(launch_final_out(hbuf + (size_t)n_pre * H, H, TB, H, scale_out, c.eps, U(m->proj_out), v_out, st),
+           "final adaln + proj_out");
+  }
+#endif
 #undef LAUNCH
   return DIT_OK;
 }
@@ -567,8 +591,7 @@ dit_status dit_debug_attention(const dit_seq* seq, int n_heads, const void* q, i
 dit_status dit_debug_gemm(const dit_gemm_desc* d, void* stream) {
   if (!d) return fail(DIT_ERR_ARG, "descriptor is NULL");
   const int epi = d->epilogue;
-  if (epi != DIT_GEMM_BF16 && epi != DIT_GEMM_F32 && epi != DIT_GEMM_RESID && epi != DIT_GEMM_SWIGLU &&
-      epi != DIT_GEMM_QKV)
+  if (epi != DIT_GEMM_BF16 && epi != DIT_GEMM_RESID && epi != DIT_GEMM_SWIGLU && epi != DIT_GEMM_QKV)
     return fail(DIT_ERR_ARG, "unknown epilogue %d", epi);
   if (!d->A || !d->B) return fail(DIT_ERR_ARG, "A or B is NULL");
   if (epi == DIT_GEMM_RESID ? (!d->h || !d->gate_t || !d->gate_0) : !d->C)
@@ -576,12 +599,10 @@ dit_status dit_debug_gemm(const dit_gemm_desc* d, void* stream) {
   if (epi == DIT_GEMM_SWIGLU && !d->B2) return fail(DIT_ERR_ARG, "SwiGLU needs B2 (up)");
   if (d->splits != 0 && d->splits != 2 && d->splits != 4) return fail(DIT_ERR_ARG, "splits must be 0, 2 or 4");
   const int N = epi == DIT_GEMM_SWIGLU ? 2 * d->N : d->N;   // packed gate/up width
-  if (!gemm_shape_ok(d->M, N, d->K, epi == DIT_GEMM_F32 ? EPI_F32 : EPI_BF16))
-    return fail(DIT_ERR_SHAPE, "GEMM needs M > 0, N %% %d == 0 and K %% 64 == 0",
-                epi == DIT_GEMM_F32 ? 64 : 256);
+  if (!gemm_shape_ok(d->M, N, d->K, EPI_BF16))
+    return fail(DIT_ERR_SHAPE, "GEMM needs M > 0, N %% 256 == 0 and K %% 64 == 0");
   if (d->scratch && (reinterpret_cast<uintptr_t>(d->scratch) & 15))
     return fail(DIT_ERR_ARG, "scratch must be 16-byte aligned");
-  if (epi == DIT_GEMM_F32 && d->splits) return fail(DIT_ERR_ARG, "the fp32-output GEMM is never split");
   const int tail = d->M - (d->M - 1) / 256 * 256;   // rows of the last 256-row block
   if (d->splits > 1) {
     if ((d->K / 64) % d->splits) return fail(DIT_ERR_ARG, "K / 64 must be divisible by splits");
@@ -600,7 +621,6 @@ dit_status dit_debug_gemm(const dit_gemm_desc* d, void* stream) {
   g.Hres = d->h; g.ldh = d->N; g.gate_t = d->gate_t; g.gate_0 = d->gate_0; g.n_pre = d->n_pre;
   g.part = static_cast<float*>(d->scratch); g.part_bytes = d->scratch ? d->scratch_bytes : 0;
   int kepi = EPI_BF16;
-  if (epi == DIT_GEMM_F32) kepi = EPI_F32;
   if (epi == DIT_GEMM_RESID) kepi = EPI_RESID;
   if (epi == DIT_GEMM_SWIGLU) kepi = EPI_SWIGLU;
   if (epi == DIT_GEMM_QKV) {
@@ -629,9 +649,50 @@ dit_status dit_debug_gemm(const dit_gemm_desc* d, void* stream) {
 #endif
 }
 
+dit_status dit_debug_final_out(const float* h, int ldh, int rows, int H, const float* scale_out,
+                               float eps, const void* w_out, float* v_out, void* stream) {
+  if (!h || !scale_out || !w_out || !v_out) return fail(DIT_ERR_ARG, "NULL argument");
+  if (rows < 0 || H <= 0 || H % 256 || H > 4096 || ldh < H || ldh % 4)
+    return fail(DIT_ERR_SHAPE, "need H a multiple of 256, at most 4096, ldh >= H and a multiple of 4");
+  if (!(eps > 0.f)) return fail(DIT_ERR_ARG, "eps must be positive");
+  if ((reinterpret_cast<uintptr_t>(h) | reinterpret_cast<uintptr_t>(scale_out) |
+       reinterpret_cast<uintptr_t>(w_out) | reinterpret_cast<uintptr_t>(v_out)) & 15)
+    return fail(DIT_ERR_ARG, "buffers must be 16-byte aligned");
+#ifdef DIT_F32
+  (void)stream;
+  return fail(DIT_ERR_UNSUPPORTED, "dit_debug_final_out is not part of the fp32 debug build");
+#else
+  return hip_check(launch_final_out(h, ldh, rows, H, scale_out, eps, U(w_out), v_out,
+                                    static_cast<hipStream_t>(stream)),
+                   "final out");
+#endif
+}
+
+dit_status dit_debug_stream_copy(const void* src, void* dst, size_t bytes, void* stream) {
+  if (!src || !dst) return fail(DIT_ERR_ARG, "NULL argument");
+  if (bytes % 16 || ((reinterpret_cast<uintptr_t>(src) | reinterpret_cast<uintptr_t>(dst)) & 15))
+    return fail(DIT_ERR_ARG, "bytes and pointers must be multiples of 16");
+  return hip_check(launch_stream_copy(src, dst, bytes, static_cast<hipStream_t>(stream)), "copy");
+}
+
+dit_status dit_debug_mfma_loop(const void* ops, float* out, int blocks, int iters, void* stream) {
+  if (!ops || !out) return fail(DIT_ERR_ARG, "NULL argument");
+  if (blocks <= 0 || iters <= 0) return fail(DIT_ERR_ARG, "blocks and iters must be positive");
+  if ((reinterpret_cast<uintptr_t>(ops) | reinterpret_cast<uintptr_t>(out)) & 15)
+    return fail(DIT_ERR_ARG, "buffers must be 16-byte aligned");
+#ifdef DIT_F32
+  (void)stream;
+  return fail(DIT_ERR_UNSUPPORTED, "dit_debug_mfma_loop is not part of the fp32 debug build");
+#else
+  return hip_check(launch_mfma_loop(static_cast<const uint16_t*>(ops), out, blocks, iters,
+                                    static_cast<hipStream_t>(stream)),
+                   "mfma loop");
+#endif
+}
+
 dit_status dit_profile_enable(dit_model* m, int kernel_class) {
   if (!m) return fail(DIT_ERR_ARG, "model is NULL");
-  if (kernel_class < DIT_PROF_OFF || kernel_class > DIT_PROF_QKNORM_ROPE)
+  if (kernel_class < DIT_PROF_OFF || kernel_class > DIT_PROF_GEMV_MOD)
     return fail(DIT_ERR_ARG, "unknown kernel class %d", kernel_class);
   std::lock_guard<std::mutex> lock(m->mu);
   m->prof_class = kernel_class;

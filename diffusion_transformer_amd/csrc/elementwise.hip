@@ -1,6 +1,6 @@
 // Bandwidth-bound kernels of the step: modulated LayerNorm, QK-RMSNorm +
-// 3D RoPE + KV-cache write, timestep-MLP / modulation GEMVs, img_in and the
-// Euler update. Each streams its operands once with 8–16-byte accesses and
+// 3D RoPE + KV-cache write, timestep-MLP / modulation GEMVs and the Euler
+// update. Each streams its operands once with 8–16-byte accesses and
 // reduces within a wavefront (64 lanes) or a 256-thread workgroup.
 #include "common.h"
 #include "kernels.h"
@@ -189,39 +189,73 @@ __global__ __launch_bounds__(256) void qknorm_rope_kernel(QkArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// GEMV: one wave per output row, 16-byte weight loads, wave reduction.
+// GEMV, Y[v][o] = W[o] · X[v] for v < nv <= 2 (the timestep MLP, the shared
+// modulation and the final scale; the modulation weight alone is 134 MB at
+// H = 4096). X is staged in LDS once per workgroup; each wave owns GV_ROWS
+// consecutive rows and issues all of their 16-byte weight loads (up to
+// GV_ROWS x 8 per lane) before the first multiply, so every wave keeps up to
+// 32 KB of weights in flight.
+constexpr int GV_ROWS = 4;
+constexpr int GV_MAXC = 8;   // 16-byte chunks per lane per row: I <= 4096
+
 __global__ __launch_bounds__(256) void gemv_kernel(const uint16_t* __restrict__ W, int O, int I,
                                                    const float* __restrict__ X, int ldx, int nv,
                                                    float* __restrict__ Y, int ldy, float* Ys) {
-  const int lane = threadIdx.x & 63;
-  const int o = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (o >= O) return;
-  const uint16_t* wr = W + (size_t)o * I;
-  float acc0 = 0.f, acc1 = 0.f;
-  for (int k = lane * 8; k < I; k += 512) {
-    const u32x4 w = *reinterpret_cast<const u32x4*>(wr + k);
-    float wf[8];
-    wf[0] = __uint_as_float(w.x << 16); wf[1] = __uint_as_float(w.x & 0xffff0000u);
-    wf[2] = __uint_as_float(w.y << 16); wf[3] = __uint_as_float(w.y & 0xffff0000u);
-    wf[4] = __uint_as_float(w.z << 16); wf[5] = __uint_as_float(w.z & 0xffff0000u);
-    wf[6] = __uint_as_float(w.w << 16); wf[7] = __uint_as_float(w.w & 0xffff0000u);
-    const float* x0 = X + k;
+  __shared__ __align__(16) float xs[2][GV_MAXC * 512];
+  for (int q = threadIdx.x; q < nv * I; q += 256) {
+    const int v = q >= I, i = q - v * I;
+    xs[v][i] = X[(size_t)v * ldx + i];
+  }
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int o0 = (blockIdx.x * 4 + wave) * GV_ROWS;
+  const int nch = I >> 3;                     // 16-byte chunks per row
+  u32x4 w[GV_ROWS][GV_MAXC];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) acc0 += wf[j] * x0[j];
-    if (nv > 1) {
-      const float* x1 = X + ldx + k;
+  for (int r = 0; r < GV_ROWS; ++r)
 #pragma unroll
-      for (int j = 0; j < 8; ++j) acc1 += wf[j] * x1[j];
+    for (int c = 0; c < GV_MAXC; ++c) {
+      const int ch = lane + 64 * c;
+      w[r][c] = (o0 + r < O && ch < nch) ? *reinterpret_cast<const u32x4*>(W + (size_t)(o0 + r) * I + 8 * ch)
+                                         : (u32x4){0u, 0u, 0u, 0u};
+    }
+  __syncthreads();
+  float acc[GV_ROWS][2];
+#pragma unroll
+  for (int r = 0; r < GV_ROWS; ++r) acc[r][0] = acc[r][1] = 0.f;
+#pragma unroll
+  for (int c = 0; c < GV_MAXC; ++c) {
+    const int ch = lane + 64 * c;
+    if (ch < nch) {
+#pragma unroll
+      for (int v = 0; v < 2; ++v) {
+        if (v < nv) {
+          const float4 xa = *reinterpret_cast<const float4*>(&xs[v][8 * ch]);
+          const float4 xb = *reinterpret_cast<const float4*>(&xs[v][8 * ch + 4]);
+          const float xv[8] = {xa.x, xa.y, xa.z, xa.w, xb.x, xb.y, xb.z, xb.w};
+#pragma unroll
+          for (int r = 0; r < GV_ROWS; ++r) {
+            const uint32_t u[4] = {w[r][c].x, w[r][c].y, w[r][c].z, w[r][c].w};
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+              acc[r][v] += __uint_as_float(u[k] << 16) * xv[2 * k];
+              acc[r][v] += __uint_as_float(u[k] & 0xffff0000u) * xv[2 * k + 1];
+            }
+          }
+        }
+      }
     }
   }
-  acc0 = wave_sum(acc0);
-  if (nv > 1) acc1 = wave_sum(acc1);
-  if (lane == 0) {
-    Y[o] = acc0;
-    if (Ys) Ys[o] = acc0 / (1.f + __expf(-acc0));
-    if (nv > 1) {
-      Y[ldy + o] = acc1;
-      if (Ys) Ys[ldy + o] = acc1 / (1.f + __expf(-acc1));
+#pragma unroll
+  for (int r = 0; r < GV_ROWS; ++r) {
+#pragma unroll
+    for (int v = 0; v < 2; ++v) {
+      if (v < nv) {
+        const float y = wave_sum(acc[r][v]);
+        if (lane == 0 && o0 + r < O) {
+          Y[(size_t)v * ldy + o0 + r] = y;
+          if (Ys) Ys[(size_t)v * ldy + o0 + r] = y / (1.f + __expf(-y));
+        }
+      }
     }
   }
 }
@@ -235,39 +269,6 @@ __global__ void temb_kernel(double t0, double t1, int D, double base, float* out
   out[half + i] = (float)sin(t0 * f);
   out[D + i] = (float)cos(t1 * f);
   out[D + half + i] = (float)sin(t1 * f);
-}
-
-// ---------------------------------------------------------------------------
-// img_in: each thread owns one output column n (its 64 weights in
-// registers); the workgroup walks 64 tokens whose latents sit in LDS.
-__global__ __launch_bounds__(256) void img_in_kernel(const uint16_t* __restrict__ W,
-                                                     const float* __restrict__ x, int n, int H,
-                                                     float* __restrict__ out, int ldo) {
-  __shared__ float xs[64][64];
-  const int col = blockIdx.x * 256 + threadIdx.x;
-  const int t0 = blockIdx.y * 64;
-  for (int q = threadIdx.x; q < 64 * 64; q += 256) {
-    const int t = q >> 6, c = q & 63;
-    xs[t][c] = (t0 + t < n) ? x[(size_t)(t0 + t) * 64 + c] : 0.f;
-  }
-  float w[64];
-  const u32x4* wp = reinterpret_cast<const u32x4*>(W + (size_t)col * 64);
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const u32x4 v = wp[j];
-    w[8 * j + 0] = __uint_as_float(v.x << 16); w[8 * j + 1] = __uint_as_float(v.x & 0xffff0000u);
-    w[8 * j + 2] = __uint_as_float(v.y << 16); w[8 * j + 3] = __uint_as_float(v.y & 0xffff0000u);
-    w[8 * j + 4] = __uint_as_float(v.z << 16); w[8 * j + 5] = __uint_as_float(v.z & 0xffff0000u);
-    w[8 * j + 6] = __uint_as_float(v.w << 16); w[8 * j + 7] = __uint_as_float(v.w & 0xffff0000u);
-  }
-  __syncthreads();
-  const int tend = min(64, n - t0);
-  for (int t = 0; t < tend; ++t) {
-    float acc = 0.f;
-#pragma unroll
-    for (int c = 0; c < 64; ++c) acc += w[c] * xs[t][c];
-    out[(size_t)(t0 + t) * ldo + col] = acc;
-  }
 }
 
 __global__ void euler_kernel(float* __restrict__ x, const float* __restrict__ v, float dsig,
@@ -298,7 +299,9 @@ hipError_t launch_qknorm_rope(const QkArgs& a, hipStream_t s) {
 
 hipError_t launch_gemv(const uint16_t* W, int O, int I, const float* X, int ldx, int nv, float* Y,
                        int ldy, float* Ys, hipStream_t s) {
-  hipLaunchKernelGGL(gemv_kernel, dim3((O + 3) / 4), dim3(256), 0, s, W, O, I, X, ldx, nv, Y, ldy, Ys);
+  if (I > GV_MAXC * 512 || I % 8 || nv < 1 || nv > 2) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(gemv_kernel, dim3((O + 4 * GV_ROWS - 1) / (4 * GV_ROWS)), dim3(256), 0, s, W, O, I, X,
+                     ldx, nv, Y, ldy, Ys);
   return hipGetLastError();
 }
 
@@ -359,11 +362,29 @@ hipError_t launch_temb(float t0, float t1, int D, float base, float* out, hipStr
   return hipGetLastError();
 }
 
-hipError_t launch_img_in(const uint16_t* W, const float* x, int n, int H, float* out, int ldo,
-                         hipStream_t s) {
+// Device copy: each thread moves 4 chunks of 16 bytes per grid step, all
+// four loads issued before the stores.
+__global__ __launch_bounds__(256) void stream_copy_kernel(const u32x4* __restrict__ src,
+                                                          u32x4* __restrict__ dst, long long n) {
+  const long long stride = (long long)gridDim.x * 256 * 4;
+  for (long long i = (long long)blockIdx.x * 1024 + threadIdx.x; i < n; i += stride) {
+    u32x4 v[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (i + 256 * j < n) v[j] = src[i + 256 * j];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (i + 256 * j < n) dst[i + 256 * j] = v[j];
+  }
+}
+
+hipError_t launch_stream_copy(const void* src, void* dst, size_t bytes, hipStream_t s) {
+  const long long n = (long long)(bytes / 16);
   if (n <= 0) return hipSuccess;
-  dim3 grid(H / 256, (n + 63) / 64);
-  hipLaunchKernelGGL(img_in_kernel, grid, dim3(256), 0, s, W, x, n, H, out, ldo);
+  long long blocks = (n + 1023) / 1024;
+  if (blocks > 256 * 16) blocks = 256 * 16;
+  hipLaunchKernelGGL(stream_copy_kernel, dim3((unsigned)blocks), dim3(256), 0, s,
+                     static_cast<const u32x4*>(src), static_cast<u32x4*>(dst), n);
   return hipGetLastError();
 }
 

@@ -6,10 +6,8 @@
 // gemm_w4_kernel (every GEMM of a layer): 256x256 block tile, 4 waves of
 // 128x128, K in stages of 64 held in two 64 KB LDS stages that are filled
 // straight from global memory with buffer_load ... lds one stage ahead.
-// gemm_kernel: register-staged (global -> VGPR -> LDS, two stages), used
-// for the narrow fp32-output proj_out GEMM with 64x64 tiles.
 //
-// Both use an XCD-aware tile order: the hardware deals workgroups
+// It uses an XCD-aware tile order: the hardware deals workgroups
 // round-robin over the 8 XCDs, so block b is remapped to logical tile
 // (b%8)*(n/8) + b/8, giving each XCD a contiguous run of logical tiles;
 // logical tiles are then grouped GROUP_M tile-rows at a time so a run
@@ -23,215 +21,6 @@ namespace {
 
 constexpr int BK = 64;
 constexpr int GROUP_M = 4;
-
-template <int BM, int BN, int WM, int WN, int EPI>
-__global__ __launch_bounds__(WM* WN * 64) void gemm_kernel(GemmArgs g) {
-  constexpr int NT = WM * WN * 64;
-  constexpr int TM = BM / WM, TN = BN / WN;
-  constexpr int FM = TM / 32, FN = TN / 32;
-  constexpr int ACH = BM * BK / 8 / NT;   // 16-byte A chunks per thread per stage
-  constexpr int BCH = BN * BK / 8 / NT;
-  static_assert(ACH * NT * 8 == BM * BK && BCH * NT * 8 == BN * BK, "tile/thread mismatch");
-  static_assert(EPI != EPI_SWIGLU || (FN % 2 == 0 && TN % 64 == 0), "SwiGLU pairs 32-col blocks");
-
-  __shared__ u32x4 smem[2][(BM + BN) * BK / 8];
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int wm = wave / WN, wn = wave % WN;
-
-  // ---- tile coordinates (XCD-aware, grouped) ----
-  const int ntm = (g.M + BM - 1) / BM;
-  const int ntn = g.N / BN;
-  const int nblk = ntm * ntn;
-  int b = blockIdx.x;
-  const int per = nblk >> 3;
-  if (b < per * 8) b = (b & 7) * per + (b >> 3);
-  const int in_group = GROUP_M * ntn;
-  const int gid = b / in_group;
-  const int first = gid * GROUP_M;
-  const int gsz = min(ntm - first, GROUP_M);
-  const int tm = first + (b % in_group) % gsz;
-  const int tn = (b % in_group) / gsz;
-  const int m0 = tm * BM, n0 = tn * BN;
-
-  // ---- buffer resources (base at this tile's first row / feature) ----
-  // Rows past M fall outside the A resource and read as zero. Thread t
-  // loads 16-byte chunk c = t%8 of rows r0 + i*RPI (r0 = t/8, RPI = NT/8);
-  // its lane offset is fixed, the row step i and the K position go into
-  // the scalar offset, and the LDS slot of chunk i is a constant offset
-  // (RPI is a multiple of 16, so the swizzle (row/2)%8 is the same for all i).
-  constexpr int RPI = NT / 8;
-  static_assert(RPI % 16 == 0, "swizzle must repeat across chunk passes");
-  const int r0 = tid >> 3, c0 = tid & 7;
-  const int sw0 = (r0 >> 1) & 7;
-  const __amdgpu_buffer_rsrc_t rA = make_rsrc(
-      g.A + (size_t)m0 * g.lda, (uint32_t)min((size_t)(g.M - m0) * g.lda * 2, (size_t)0xFFFFFFF0u));
-  const uint32_t aoff = (uint32_t)((r0 * g.lda + c0 * 8) * 2);
-  const uint32_t astep = (uint32_t)(RPI * g.lda * 2);
-  const int adst = r0 * 8 + (c0 ^ sw0);
-  // B: for SwiGLU the packed column p maps to feature 32*(p/64) + p%32 of
-  // the gate matrix if (p/32) is even, else of the up matrix.
-  __amdgpu_buffer_rsrc_t rB0, rB1;
-  uint32_t boff, bstep;
-  if (EPI == EPI_SWIGLU) {
-    const size_t bytes = min((size_t)(BN / 2) * g.ldb * 2, (size_t)0xFFFFFFF0u);
-    rB0 = make_rsrc(g.B + (size_t)(n0 >> 1) * g.ldb, (uint32_t)bytes);
-    rB1 = make_rsrc(g.B2 + (size_t)(n0 >> 1) * g.ldb, (uint32_t)bytes);
-    if (RPI >= 64) {
-      // every chunk of this thread is in the same 32-row half: pick the
-      // matrix once per wave (8 rows per wave never cross a 32-row block)
-      const int sel = __builtin_amdgcn_readfirstlane((r0 >> 5) & 1);
-      if (sel) rB0 = rB1;
-      boff = (uint32_t)(((32 * (r0 >> 6) + (r0 & 31)) * g.ldb + c0 * 8) * 2);
-      bstep = (uint32_t)((RPI / 2) * g.ldb * 2);
-    } else {
-      // RPI == 32: chunk i is gate for even i, up for odd i, row 32*(i/2) + r0
-      boff = (uint32_t)((r0 * g.ldb + c0 * 8) * 2);
-      bstep = (uint32_t)(32 * g.ldb * 2);
-    }
-  } else {
-    rB0 = rB1 = make_rsrc(g.B + (size_t)n0 * g.ldb, (uint32_t)min((size_t)BN * g.ldb * 2, (size_t)0xFFFFFFF0u));
-    boff = (uint32_t)((r0 * g.ldb + c0 * 8) * 2);
-    bstep = (uint32_t)(RPI * g.ldb * 2);
-  }
-  const int bdst = BM * 8 + r0 * 8 + (c0 ^ sw0);
-
-  f32x16 acc[FM][FN];
-#pragma unroll
-  for (int i = 0; i < FM; ++i)
-#pragma unroll
-    for (int j = 0; j < FN; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-
-  const int nk = g.K / BK;
-  const int lrow = lane & 31;
-  const int lhalf = lane >> 5;
-  const int sw = (lane >> 1) & 7;   // (row/2) % 8 of every row this lane reads
-
-  // Two register staging sets: tile kt+1 sits in set (kt+1)&1 while the
-  // loads of tile kt+2 go to set kt&1, so every global load has two K steps
-  // of MFMA work to arrive before its ds_write.
-  u32x4 ra[2][ACH], rb[2][BCH];
-  auto gload = [&](int set, int kt) {
-    const uint32_t ko = (uint32_t)(kt * BK * 2);   // bytes
-#pragma unroll
-    for (int i = 0; i < ACH; ++i)
-      ra[set][i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rA, aoff, ko + i * astep, 0));
-#pragma unroll
-    for (int i = 0; i < BCH; ++i) {
-      if (EPI == EPI_SWIGLU && RPI < 64)
-        rb[set][i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-            (i & 1) ? rB1 : rB0, boff, ko + (i >> 1) * bstep, 0));
-      else
-        rb[set][i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rB0, boff, ko + i * bstep, 0));
-    }
-  };
-  auto lstore = [&](int set, int buf) {
-#pragma unroll
-    for (int i = 0; i < ACH; ++i) smem[buf][adst + i * RPI * 8] = ra[set][i];
-#pragma unroll
-    for (int i = 0; i < BCH; ++i) smem[buf][bdst + i * RPI * 8] = rb[set][i];
-  };
-  // fragments of one 16-wide K slice, double-buffered in registers
-  bf16x8 fa[2][FM], fb[2][FN];
-  auto lread = [&](int fset, int buf, int s) {
-    const u32x4* As = smem[buf];
-    const u32x4* Bs = smem[buf] + BM * 8;
-    const int ch = (2 * s + lhalf) ^ sw;
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
-      fa[fset][i] = __builtin_bit_cast(bf16x8, As[(wm * TM + i * 32 + lrow) * 8 + ch]);
-#pragma unroll
-    for (int j = 0; j < FN; ++j)
-      fb[fset][j] = __builtin_bit_cast(bf16x8, Bs[(wn * TN + j * 32 + lrow) * 8 + ch]);
-  };
-  auto mma = [&](int fset) {
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-      for (int j = 0; j < FN; ++j) acc[i][j] = mfma32(fa[fset][i], fb[fset][j], acc[i][j]);
-  };
-
-  // prologue: tile 0 -> LDS buffer 0; tile 1 in flight in set 1
-  gload(0, 0);
-  gload(1, min(1, nk - 1));
-  lstore(0, 0);
-  lds_barrier();
-  lread(0, 0, 0);
-
-  // One K step of 64 = four 16-wide slices s = 0..3 on LDS buffer par:
-  //  - tile kt+2 is requested into register set par (freed when tile kt
-  //    was stored);
-  //  - slice s+1 is read from LDS while the MFMAs of slice s run;
-  //  - tile kt+1 (register set par^1, requested one step earlier) is
-  //    stored to the other LDS buffer during slice 1;
-  //  - the only barrier sits before slice 3, so the first slice of the next
-  //    tile is read while slice 3 computes. Every read of a buffer is issued
-  //    before the barrier that precedes the next store into it.
-  // All memory operations in the loop are unconditional: past the end the
-  // loads re-read the last tile and the store fills the idle LDS buffer,
-  // which nothing reads again. This keeps the waitcnt analysis exact (the
-  // LDS stores wait only for the older register set).
-  auto step = [&](int kt, int par) {
-    gload(par, min(kt + 2, nk - 1));
-    __builtin_amdgcn_sched_barrier(0);   // keep the prefetch at the top
-    lread(1, par, 1);
-    mma(0);
-    lread(0, par, 2);
-    lstore(par ^ 1, par ^ 1);
-    __builtin_amdgcn_sched_barrier(0);
-    mma(1);
-    lread(1, par, 3);
-    mma(0);
-    lds_barrier();
-    lread(0, par ^ 1, 0);
-    mma(1);
-  };
-  int kt = 0;
-  for (; kt + 1 < nk; kt += 2) {
-    step(kt, 0);
-    step(kt + 1, 1);
-  }
-  if (kt < nk) step(kt, 0);
-
-  // ---- epilogue ----
-#pragma unroll
-  for (int i = 0; i < FM; ++i) {
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int m = m0 + wm * TM + i * 32 + 8 * (r >> 2) + 4 * lhalf + (r & 3);
-      if (m >= g.M) continue;
-      if (EPI == EPI_SWIGLU) {
-#pragma unroll
-        for (int j = 0; j < FN; j += 2) {
-          const int n = n0 + wn * TN + j * 32;            // multiple of 64
-          const int f = (n >> 1) + lrow;
-          const float gv = acc[i][j][r], uv = acc[i][j + 1][r];
-          const float sv = gv / (1.f + __expf(-gv));
-          reinterpret_cast<bf16_t*>(g.C)[(size_t)m * g.ldc + f] = f2bf(sv * uv);
-        }
-      } else {
-#pragma unroll
-        for (int j = 0; j < FN; ++j) {
-          const int n = n0 + wn * TN + j * 32 + lrow;
-          const float v = acc[i][j][r];
-          if (EPI == EPI_BF16) {
-            reinterpret_cast<bf16_t*>(g.C)[(size_t)m * g.ldc + n] = f2bf(v);
-          } else if (EPI == EPI_F32) {
-            reinterpret_cast<float*>(g.C)[(size_t)m * g.ldc + n] = v;
-          } else {
-            const float gt = (m < g.n_pre ? g.gate_0 : g.gate_t)[n];
-            float* hp = g.Hres + (size_t)m * g.ldh + n;
-            *hp = *hp + gt * v;
-          }
-        }
-      }
-    }
-  }
-}
 
 // Epilogue through LDS for the swapped layout (each 32x32 block accumulated
 // as Cᵀ: lane l holds row l%32 and, in registers 4q..4q+3, the four
@@ -555,7 +344,7 @@ __device__ __forceinline__ void store_tile_lds_f32(const GemmArgs& g, f32x16 (&a
 // all 64 banks exactly once.
 template <int EPI, bool PACKED = (EPI == EPI_SWIGLU)>
 __global__ __launch_bounds__(256) void gemm_w4_kernel(GemmArgs g) {
-  static_assert(EPI != EPI_F32, "fp32 output goes through gemm_kernel");
+  static_assert(EPI != EPI_F32, "no fp32-output GEMM in this library (proj_out is fused into the final AdaLN)");
   constexpr int BM = 256, BN = 256, SBK = 64;
   constexpr int WN = 2, TM = 128, TN = 128, FM = 4, FN = 4;
   constexpr int SW = (BM + BN) * SBK / 8;      // u32x4 per stage (64 KB)
@@ -834,18 +623,10 @@ hipError_t launch_gemm_split(const GemmArgs& g, int epi, int r, int splits, hipS
   return hipErrorInvalidValue;
 }
 
-template <int BM, int BN, int WM, int WN, int EPI>
-hipError_t run(const GemmArgs& g, hipStream_t s) {
-  const int nblk = ((g.M + BM - 1) / BM) * (g.N / BN);
-  hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, EPI>), dim3(nblk), dim3(WM * WN * 64), 0, s, g);
-  return hipGetLastError();
-}
-
 }  // namespace
 
 bool gemm_shape_ok(int M, int N, int K, int epi) {
-  if (M <= 0 || N <= 0 || K <= 0 || K % BK) return false;
-  if (epi == EPI_F32) return N % 64 == 0;
+  if (M <= 0 || N <= 0 || K <= 0 || K % BK || epi == EPI_F32) return false;
   return N % 256 == 0;
 }
 
@@ -854,7 +635,7 @@ hipError_t launch_gemm_forced_split(const GemmArgs& g, int epi, int splits, hipS
 }
 
 hipError_t launch_gemm(const GemmArgs& g, int epi, hipStream_t s) {
-  if (epi == EPI_F32) return run<64, 64, 2, 2, EPI_F32>(g, s);
+  if (epi == EPI_F32) return hipErrorInvalidValue;
   // One block tile per CU per round: when the tiles leave the last round
   // mostly idle and dropping the last r row blocks makes the rest whole
   // rounds, those r row blocks are spread over the idle CUs by splitting K.

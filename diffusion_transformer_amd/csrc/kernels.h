@@ -107,9 +107,19 @@ hipError_t launch_standardize(float* z, const float* mean, const float* std, lon
                               int channels, int inverse, hipStream_t s);
 // tanh of the gate sections of nv modulation rows [scale1 | gate1 | scale2 | gate2].
 hipError_t launch_gate_tanh(float* mod, int H, int nv, hipStream_t s);
-// hidden[i][n] = Σ_c W[n][c] x[i][c]; W bf16 [H, 64], x f32 [n, 64].
+// hidden[i][n] = Σ_c W[n][c] x[i][c]; W bf16 [H, 64], x f32 [n, 64], fp32 out.
 hipError_t launch_img_in(const uint16_t* W, const float* x, int n, int H, float* out, int ldo,
                          hipStream_t s);
+// v[i] = W_out · (LN(h[i]) · (1 + scale)) for rows < rows: LN non-affine
+// over H (<= 4096, % 256 == 0), the scaled row rounded to bf16, W_out bf16
+// [64, H], v fp32 [rows, 64].
+hipError_t launch_final_out(const float* h, int ldh, int rows, int H, const float* scale, float eps,
+                            const uint16_t* W, float* v, hipStream_t s);
 hipError_t launch_euler(float* x, const float* v, float dsig, long long n, hipStream_t s);
+// dst = src, bytes % 16 == 0, 16-byte accesses.
+hipError_t launch_stream_copy(const void* src, void* dst, size_t bytes, hipStream_t s);
+// Register-only bf16 MFMA loop (measured ceiling): blocks x 4 waves x iters
+// x 64 MFMAs of 32x32x16; ops 1 MiB of bf16 operands, out [blocks * 256].
+hipError_t launch_mfma_loop(const uint16_t* ops, float* out, int blocks, int iters, hipStream_t s);
 
 }  // namespace dit

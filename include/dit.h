@@ -252,7 +252,6 @@ dit_status dit_debug_attention(const dit_seq* seq, int n_heads, const void* q, i
  * the weights' nn.Linear layout), fp32 accumulation. Epilogues (the step's
  * use in brackets; mapping rows 4A and 5A of the lab index page):
  *   DIT_GEMM_BF16   C bf16 [M, N] = y.
- *   DIT_GEMM_F32    C fp32 [M, N] = y (the proj_out kernel; N % 64 == 0).
  *   DIT_GEMM_RESID  h fp32 [M, N] += g[n] * y, g = gate_0 for rows < n_pre
  *                   and gate_t for the others, fp32 [N] each [O and down
  *                   projections: h += tanh(gate) * out].
@@ -267,7 +266,7 @@ dit_status dit_debug_attention(const dit_seq* seq, int n_heads, const void* q, i
  *                   unspecified), k to K cache row q_row0 + m and v to
  *                   Vᵀ cache column q_row0 + m of layer 0 of kv_cache
  *                   (capacity dit_kv_capacity(S), dit_kv_capacity layout).
- * M > 0, N % 256 == 0 (DIT_GEMM_F32: % 64), K % 64 == 0, else DIT_ERR_SHAPE.
+ * M > 0, N % 256 == 0, K % 64 == 0, else DIT_ERR_SHAPE.
  * splits: 0 = the step's rule (the last row blocks are split over K when
  * the tile count leaves a partly idle round and the partial sums fit the
  * scratch; none without scratch); 2 or 4 = always compute the last 256-row
@@ -276,7 +275,6 @@ dit_status dit_debug_attention(const dit_seq* seq, int n_heads, const void* q, i
  * DIT_ERR_ARG otherwise). The scratch is caller-owned device memory. */
 enum {
   DIT_GEMM_BF16 = 0,
-  DIT_GEMM_F32 = 1,
   DIT_GEMM_RESID = 2,
   DIT_GEMM_SWIGLU = 3,
   DIT_GEMM_QKV = 5
@@ -305,6 +303,31 @@ typedef struct dit_gemm_desc {
 } dit_gemm_desc;
 dit_status dit_debug_gemm(const dit_gemm_desc* d, void* stream);
 
+/* Test hook: the step's scale-only final AdaLN + proj_out kernel on
+ * explicit buffers (page 6B §1 and §3: v = W_out · (LN(h) · (1 + scale_out))
+ * per target token; LN non-affine with population variance, eps inside the
+ * root; the scaled row rounded to bf16 before the product, fp32 accumulation).
+ *   h [rows, H] f32 (row stride ldh), scale_out [H] f32, w_out [64, H] bf16,
+ *   v_out [rows, 64] f32 (all device). H must be the model widths the
+ *   library supports (a multiple of 256, at most 4096). */
+dit_status dit_debug_final_out(const float* h, int ldh, int rows, int H, const float* scale_out,
+                               float eps, const void* w_out, float* v_out, void* stream);
+
+/* Measurement hook: a device-to-device copy of `bytes` (a multiple of 16)
+ * with 16-byte accesses, the HBM ceiling the bandwidth-bound kernels are
+ * compared with. */
+dit_status dit_debug_stream_copy(const void* src, void* dst, size_t bytes, void* stream);
+
+/* Measurement hook: the bf16 MFMA ceiling the kernels run against. A
+ * register-only loop of v_mfma_f32_32x32x16_bf16 (blocks workgroups of 4
+ * waves, each wave iters x 64 MFMAs in 8 independent chains) on operands
+ * read once from ops (device, 1 MiB of bf16: pass real-looking data, since
+ * the operands' bit patterns set the power draw and with it the clock);
+ * out (device, blocks * 256 floats) receives a checksum per thread.
+ * Work per launch: blocks * 4 * iters * 64 * 32768 flop. blocks and iters
+ * must be positive; not part of the fp32 debug build. */
+dit_status dit_debug_mfma_loop(const void* ops, float* out, int blocks, int iters, void* stream);
+
 /* Per-kernel timing over HIP events recorded on the step's stream around
  * every launch of one kernel class (0 = off). Enabling it adds an event
  * pair per launch. dit_profile_read returns the summed milliseconds and
@@ -318,7 +341,11 @@ enum {
   DIT_PROF_GEMM_DOWN = 4,
   DIT_PROF_ATTENTION = 5,
   DIT_PROF_LN = 6,
-  DIT_PROF_QKNORM_ROPE = 7   /* the standalone kernel: cache padding of an extract step */
+  DIT_PROF_QKNORM_ROPE = 7,  /* the standalone kernel: cache padding of an extract step */
+  DIT_PROF_FINAL = 8,        /* scale-only final AdaLN + proj_out (one kernel) */
+  DIT_PROF_IMG_IN = 9,
+  DIT_PROF_GEMV = 10,        /* timestep MLP and final-scale GEMVs */
+  DIT_PROF_GEMV_MOD = 11     /* the shared modulation GEMV, [4H, H] */
 };
 dit_status dit_profile_enable(dit_model* m, int kernel_class);
 dit_status dit_profile_read(dit_model* m, double* total_ms, long long* launches);

@@ -18,6 +18,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 def header_functions():
     src = open(os.path.join(ROOT, "include", "dit.h")).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    src = re.sub(r"^\s*#.*$", "", src, flags=re.M)       # preprocessor lines
     return sorted(set(re.findall(r"\b(\w+)\s*\([^;{]*\)\s*;", src)) - {"if", "for", "while"})
 
 
@@ -285,13 +286,12 @@ def test_debug_gemm_descriptor_validation():
     assert st(epilogue=2, C=None) == L.DIT_ERR_ARG    # residual needs h and both gates
     assert st(epilogue=3) == L.DIT_ERR_ARG            # SwiGLU needs the up weights
     assert st(K=100) == L.DIT_ERR_SHAPE
-    assert st(epilogue=1, N=96) == L.DIT_ERR_SHAPE    # fp32 output: N % 64
+    assert st(epilogue=1) == L.DIT_ERR_ARG            # no fp32-output GEMM (proj_out is fused)
     assert st(splits=3) == L.DIT_ERR_ARG
     assert st(splits=2) == L.DIT_ERR_ARG              # no scratch
     need = 2 * (300 - 256) * 512 * 4
     assert st(splits=2, scratch=FAKE, scratch_bytes=need - 1) == L.DIT_ERR_ARG
     assert st(splits=4, K=192, scratch=FAKE, scratch_bytes=1 << 30) == L.DIT_ERR_ARG
-    assert st(epilogue=1, splits=2, scratch=FAKE, scratch_bytes=1 << 30) == L.DIT_ERR_ARG
     assert st(epilogue=5, N=768, n_heads=1, q_norm=FAKE, k_norm=FAKE, rope_cos=FAKE,
               rope_sin=FAKE, kv_cache=FAKE, S=300, eps=1e-6) == L.DIT_ERR_SHAPE
     assert st(epilogue=5, N=768, n_heads=2, q_norm=FAKE, k_norm=FAKE, rope_cos=FAKE,
@@ -368,3 +368,14 @@ def test_model_handle_calls_from_many_threads():
         assert not bad, bad[:5]
     finally:
         L.dit_free(m)
+
+
+def test_measurement_and_final_hooks_validation():
+    f = L._lib.dit_debug_final_out
+    assert f(None, 4096, 10, 4096, FAKE, 1e-6, FAKE, FAKE, None) == L.DIT_ERR_ARG
+    assert f(FAKE, 4096, 10, 4000, FAKE, 1e-6, FAKE, FAKE, None) == L.DIT_ERR_SHAPE
+    assert f(FAKE, 4096, 10, 8192, FAKE, 1e-6, FAKE, FAKE, None) == L.DIT_ERR_SHAPE
+    assert f(FAKE, 100, 10, 256, FAKE, 1e-6, FAKE, FAKE, None) == L.DIT_ERR_SHAPE      # ldh < H
+    assert f(FAKE, 4096, 10, 4096, FAKE, 0.0, FAKE, FAKE, None) == L.DIT_ERR_ARG
+    assert L._lib.dit_debug_stream_copy(FAKE, FAKE, 24, None) == L.DIT_ERR_ARG
+    assert L._lib.dit_debug_mfma_loop(FAKE, FAKE, 0, 10, None) == L.DIT_ERR_ARG

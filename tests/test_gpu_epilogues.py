@@ -77,6 +77,8 @@ SHAPES = [(700, 512, 512), (256, 256, 64), (37, 768, 1024)]
 @pytest.mark.parametrize("splits", [0, 2, 4])
 @pytest.mark.parametrize("M,N,K", SHAPES)
 def test_bf16_epilogue(dev, M, N, K, splits):
+    if splits and (K // 64) % splits:
+        pytest.skip("K / 64 not divisible by splits")
     A, (B,) = operands(M, N, K, seed=M + N + K)
     C = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
     say(f"bf16 epilogue M={M} N={N} K={K} splits={splits}")
@@ -87,18 +89,61 @@ def test_bf16_epilogue(dev, M, N, K, splits):
     check_bf16(host(C.cpu()), a @ b.T, ACC * (np.abs(a) @ np.abs(b).T), "C")
 
 
-@pytest.mark.parametrize("M,N,K", [(700, 64, 512), (4096, 64, 4096), (5, 128, 64)])
-def test_f32_epilogue(dev, M, N, K):
-    """The proj_out GEMM (fp32 output, 64x64 tiles)."""
-    A, (B,) = operands(M, N, K, seed=3 * M + N)
-    C = torch.empty((M, N), dtype=torch.float32, device=dev)
-    say(f"f32 epilogue M={M} N={N} K={K}")
-    L.dit_debug_gemm("f32", M, N, K, A.to(dev), B.to(dev), C)
+@pytest.mark.parametrize("rows,H", [(4096, 4096), (700, 4096), (37, 256), (1, 512), (16, 4096)])
+def test_final_adaln_proj_out(dev, rows, H):
+    """The step's last kernel: v = W_out (LN(h) (1 + scale_out)), LN
+    non-affine with population variance and eps 1e-6, the scaled row rounded
+    to bf16, fp32 accumulation over H. Against fp64; the bound allows the
+    fp32 accumulation and, for the few elements whose fp32 normalized value
+    lies within fp32 error of a bf16 rounding boundary, the other neighbour."""
+    g = torch.Generator().manual_seed(rows + H)
+    h = 3.0 * torch.randn((rows, H), generator=g) + 0.5
+    sc = 0.3 * torch.randn(H, generator=g)
+    W = (torch.randn((64, H), generator=g) / np.sqrt(H)).to(torch.bfloat16)
+    v = torch.full((rows, 64), float("nan"), device=dev)
+    say(f"final AdaLN + proj_out rows={rows} H={H}")
+    L.dit_debug_final_out(h.to(dev), sc.to(dev), W.to(dev), v)
     torch.cuda.synchronize()
-    a, b = host(A), host(B)
-    ref = a @ b.T
-    err = np.abs(C.cpu().double().numpy() - ref)
-    assert np.all(err <= ACC * (np.abs(a) @ np.abs(b).T) + 2.0 ** -24 * np.abs(ref))
+    hh = h.double().numpy()
+    y = (hh - hh.mean(1, keepdims=True)) / np.sqrt(hh.var(1, keepdims=True) + 1e-6)
+    y = y * (1.0 + sc.double().numpy())
+    yb = bf16_np(y)
+    w = host(W)
+    ref = yb @ w.T
+    near = ulp_bf16(y) / 2 - np.abs(y - yb) <= 4e-6 * np.abs(y) + 1e-7
+    bound = ACC * (np.abs(yb) @ np.abs(w).T) + (near * ulp_bf16(y)) @ np.abs(w).T
+    err = np.abs(v.cpu().double().numpy() - ref)
+    say(f"  max err / bound {float((err / bound).max()):.3f}; {int(near.sum())} near-boundary inputs")
+    assert np.all(err <= bound)
+
+
+@pytest.mark.parametrize("n", [4096, 700, 1])
+def test_img_in_is_fp32_exact(dev, n):
+    """img_in (fp32 latents, bf16 weights) through three bf16 MFMAs per block
+    on an exact three-way split of each latent: every output within fp32
+    accumulation error of the fp64 product."""
+    H = 4096
+    g = torch.Generator().manual_seed(n)
+    x = torch.randn((n, 64), generator=g) * 2.0
+    W = (torch.randn((H, 64), generator=g) / 8.0).to(torch.bfloat16)
+    say(f"img_in n={n}")
+    c = L.make_config(hidden=H, n_heads=32, head_dim=128, ffn=16384, n_layers=1)
+    wd = {k: torch.zeros(8, dtype=torch.bfloat16, device=dev) for k in ("t1", "t2", "mod", "so", "proj_out")}
+    wd["img_in"] = W.to(dev)
+    for k in ("qkv", "q_norm", "k_norm", "o", "gate", "up", "down"):
+        wd[k] = [torch.zeros(8, dtype=torch.bfloat16, device=dev)]
+    m = L.dit_load_weights(c, wd)
+    out = torch.full((n, H), float("nan"), device=dev)
+    try:
+        L.dit_img_in(m, x.to(dev).contiguous(), out)
+        torch.cuda.synchronize()
+    finally:
+        L.dit_free(m)
+    xx, w = x.double().numpy(), host(W)
+    ref = xx @ w.T
+    bound = ACC * (np.abs(xx) @ np.abs(w).T)
+    err = np.abs(out.cpu().double().numpy() - ref)
+    assert np.all(err <= bound), float((err / bound).max())
 
 
 @pytest.mark.parametrize("splits", [0, 2, 4])
@@ -107,6 +152,8 @@ def test_f32_epilogue(dev, M, N, K):
 def test_residual_epilogue(dev, M, N, K, n_pre, splits):
     """h += g * (A Bᵀ), with g = gate_0 on rows < n_pre and gate_t after:
     the O and down projections' gated residual update, in fp32."""
+    if splits and (K // 64) % splits:
+        pytest.skip("K / 64 not divisible by splits")
     A, (B,) = operands(M, N, K, seed=5 * M + K)
     g = torch.Generator().manual_seed(M)
     h0 = torch.randn((M, N), generator=g)
