@@ -30,6 +30,7 @@ SEG_TEXT, SEG_REF, SEG_TARGET = 0, 1, 2
 
 EXPORTS = ["dit_build_layout", "dit_load_weights", "dit_free", "dit_workspace_bytes",
            "dit_kv_capacity", "dit_kv_cache_bytes", "dit_step_extract", "dit_step_cached",
+           "dit_step_cached_noalloc",
            "euler_update", "dit_img_in", "dit_latent_standardize", "dit_debug_mask", "dit_debug_attention",
            "dit_debug_gemm", "dit_debug_final_out", "dit_debug_stream_copy", "dit_debug_mfma_loop",
            "dit_profile_enable", "dit_profile_read",
@@ -94,6 +95,7 @@ def _load(path=None):
         "dit_kv_cache_bytes": (sz, [vp, i]),
         "dit_step_extract": (i, [vp, P(dit_seq), vp, vp, f, vp, sz, vp, vp, sz, i, vp]),
         "dit_step_cached": (i, [vp, P(dit_seq), vp, f, vp, sz, vp, vp, sz, vp]),
+        "dit_step_cached_noalloc": (i, [vp, P(dit_seq), vp, f, vp, sz, vp, vp]),
         "euler_update": (i, [vp, vp, f, f, ll, vp]),
         "dit_img_in": (i, [vp, vp, i, vp, vp]),
         "dit_latent_standardize": (i, [vp, vp, vp, ll, i, i, vp]),
@@ -259,6 +261,11 @@ def _make_api(_lib):
         _check(_lib.dit_step_cached(model, C.byref(seq), _ptr(x), float(sigma), _ptr(kv_cache),
                                     _nbytes(kv_cache), _ptr(v_out), _ptr(workspace),
                                     _nbytes(workspace), _stream(stream)))
+
+    def dit_step_cached_noalloc(model, seq: dit_seq, x, sigma, kv_cache, v_out, stream=None):
+        _step_tensors(model, seq, x, v_out)
+        _check(_lib.dit_step_cached_noalloc(model, C.byref(seq), _ptr(x), float(sigma), _ptr(kv_cache),
+                                            _nbytes(kv_cache), _ptr(v_out), _stream(stream)))
 
     def euler_update(x, v, sigma_k, sigma_k1, n=None, stream=None):
         n = x.numel() if n is None else int(n)

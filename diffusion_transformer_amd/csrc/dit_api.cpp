@@ -47,6 +47,14 @@ struct ExtractRecord {
   int P, T, B;
 };
 
+// Workspace of dit_step_cached_noalloc: one array per GPU, in the code
+// object's own device memory (held by each GPU the library runs on until the
+// process ends). Host code never uses this name as an address: the device
+// address comes from hipGetSymbolAddress, once per device.
+#ifndef DIT_F32
+static __device__ __align__(256) unsigned char g_step_scratch[DIT_NOALLOC_SCRATCH_BYTES];
+#endif
+
 }  // namespace
 
 struct dit_model {
@@ -517,6 +525,58 @@ dit_status dit_step_cached(dit_model* m, const dit_seq* seq, const float* x, flo
                 seq->P, seq->T, n_elem(seq));
   return run_step(m, seq, false, nullptr, x, sigma, kv_cache, v_out, workspace, 0,
                   static_cast<hipStream_t>(stream));
+}
+
+dit_status dit_step_cached_noalloc(dit_model* m, const dit_seq* seq, const float* x, float sigma,
+                                   void* kv_cache, size_t kv_bytes, float* v_out, void* stream) {
+  if (!m) return fail(DIT_ERR_ARG, "model is NULL");
+  dit_status rc = check_seq(m, seq);
+  if (rc) return rc;
+  const int n = s_all(seq) - seq->P;
+  const size_t need = dit_workspace_bytes(m, n);
+  if (need > DIT_NOALLOC_SCRATCH_BYTES)
+    return fail(DIT_ERR_WORKSPACE,
+                "dit_step_cached_noalloc: %d target rows need %zu bytes of workspace, above the "
+                "library's fixed %zu-byte device scratch (use dit_step_cached with a workspace)",
+                n, need, (size_t)DIT_NOALLOC_SCRATCH_BYTES);
+#ifdef DIT_F32
+  (void)x; (void)sigma; (void)kv_cache; (void)kv_bytes; (void)v_out; (void)stream;
+  return fail(DIT_ERR_UNSUPPORTED, "dit_step_cached_noalloc is not part of the fp32 debug build");
+#else
+  // device address of this GPU's scratch array, looked up once per device
+  static std::mutex mu;
+  static void* addr[64] = {nullptr};
+  int dev = 0;
+  rc = hip_check(hipGetDevice(&dev), "noalloc: device");
+  if (rc) return rc;
+  if (dev < 0 || dev >= 64) return fail(DIT_ERR_UNSUPPORTED, "device index %d", dev);
+  void* ws = nullptr;
+  {
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[dev]) {
+      void* p = nullptr;
+      rc = hip_check(hipGetSymbolAddress(&p, HIP_SYMBOL(g_step_scratch)), "noalloc: scratch address");
+      if (rc) return rc;
+      addr[dev] = p;
+    }
+    ws = addr[dev];
+  }
+  rc = check_step_common(m, seq, x, kv_cache, kv_bytes, v_out, ws, DIT_NOALLOC_SCRATCH_BYTES, n);
+  if (rc) return rc;
+  if (!std::isfinite(sigma)) return fail(DIT_ERR_ARG, "sigma is not finite");
+  std::lock_guard<std::mutex> lock(m->mu);
+  bool ok = false;
+  for (const auto& r : m->extracted)
+    if (r.kv == kv_cache && r.P == seq->P && r.T == seq->T && r.B == n_elem(seq)) ok = true;
+  if (!ok)
+    return fail(DIT_ERR_STATE,
+                "no dit_step_extract with t=0 conditioning ran on this cache for P=%d T=%d B=%d",
+                seq->P, seq->T, n_elem(seq));
+  // nothing in the workspace has to start at zero: every region a step
+  // reads is written earlier in the same step
+  return run_step(m, seq, false, nullptr, x, sigma, kv_cache, v_out, ws, 0,
+                  static_cast<hipStream_t>(stream), false);
+#endif
 }
 
 dit_status euler_update(float* x, const float* v, float sigma_k, float sigma_k1, long long n,

@@ -204,6 +204,20 @@ dit_status dit_step_cached(dit_model* m, const dit_seq* seq, const float* x, flo
                            void* kv_cache, size_t kv_bytes, float* v_out, void* workspace,
                            size_t ws_bytes, void* stream);
 
+/* For callers that cannot allocate device memory (code recorded into a HIP
+ * graph, tight serving loops, hosts that forbid allocation): dit_step_cached
+ * with its workspace taken from a fixed device array the library holds, one
+ * per GPU (DIT_NOALLOC_SCRATCH_BYTES, reserved on every GPU the library runs
+ * on until the process ends). No allocation and no per-kernel timing happen
+ * in this call. The array is shared by every call on that GPU and keeps the
+ * last call's contents (nothing in it needs to start at zero); calls that
+ * overlap on one GPU race. Workspace needs above the array's size (about
+ * 2200 target rows at H = 4096, F = 16384) return DIT_ERR_WORKSPACE before
+ * any device work; other arguments and errors as dit_step_cached. */
+#define DIT_NOALLOC_SCRATCH_BYTES ((size_t)256 << 20)
+dit_status dit_step_cached_noalloc(dit_model* m, const dit_seq* seq, const float* x, float sigma,
+                                   void* kv_cache, size_t kv_bytes, float* v_out, void* stream);
+
 /* Flow-matching Euler update (page 6B §1/§6):
  * x[i] += (sigma_k1 - sigma_k) * v[i] for i < n, in float32, in place. */
 dit_status euler_update(float* x, const float* v, float sigma_k, float sigma_k1, long long n,

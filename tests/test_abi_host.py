@@ -370,6 +370,26 @@ def test_model_handle_calls_from_many_threads():
         L.dit_free(m)
 
 
+def test_noalloc_step_refuses_sizes_above_its_array():
+    """The allocation-free cached step refuses, on the host and before any
+    device work, a target row count whose workspace exceeds the library's
+    fixed device array (c1's dimensions: 4096 target rows need about 360 MB);
+    null arguments are refused too."""
+    cfg, c = cfg_c("c1")
+    st, m = load(c)
+    assert st == L.DIT_OK
+    try:
+        big = L.dit_seq(16, 4096, FAKE, FAKE, FAKE)
+        assert L.dit_workspace_bytes(m, 4096) > 256 << 20
+        r = L._lib.dit_step_cached_noalloc(m, C.byref(big), FAKE, 0.5, FAKE, 1 << 40, FAKE, None)
+        assert r == L.DIT_ERR_WORKSPACE
+        assert "fixed" in L.dit_last_error()
+        assert L._lib.dit_step_cached_noalloc(None, C.byref(big), FAKE, 0.5, FAKE, 1 << 40, FAKE,
+                                              None) == L.DIT_ERR_ARG
+    finally:
+        L.dit_free(m)
+
+
 def test_measurement_and_final_hooks_validation():
     f = L._lib.dit_debug_final_out
     assert f(None, 4096, 10, 4096, FAKE, 1e-6, FAKE, FAKE, None) == L.DIT_ERR_ARG
