@@ -124,8 +124,10 @@ def hbm_kernels_summary(trace_dir, fetch_dir, write_dir, command, calib, out_md)
     import csv
     trace = list(csv.DictReader(open(os.path.join(trace_dir, "run_kernel_trace.csv"))))
 
-    def grid(r):
-        return int(r.get("Grid_Size") or r.get("Grid_Size_X") or 0)
+    def grid(r):   # total work-items (the trace lists the grid per axis)
+        if r.get("Grid_Size"):
+            return int(r["Grid_Size"])
+        return int(r["Grid_Size_X"]) * int(r.get("Grid_Size_Y") or 1) * int(r.get("Grid_Size_Z") or 1)
     lines = ["# rocprofv3 HBM bytes of the bandwidth-bound kernels: cached DiT step, c2 workload", "",
              "Commands (from the repository root on the MI355X machine; R = repository root):", "", "```",
              command, "```", "",

@@ -202,13 +202,10 @@ __global__ __launch_bounds__(256) void gemv_kernel(const uint16_t* __restrict__ 
                                                    const float* __restrict__ X, int ldx, int nv,
                                                    float* __restrict__ Y, int ldy, float* Ys) {
   __shared__ __align__(16) float xs[2][GV_MAXC * 512];
-  for (int q = threadIdx.x; q < nv * I; q += 256) {
-    const int v = q >= I, i = q - v * I;
-    xs[v][i] = X[(size_t)v * ldx + i];
-  }
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int o0 = (blockIdx.x * 4 + wave) * GV_ROWS;
   const int nch = I >> 3;                     // 16-byte chunks per row
+  // the weight loads go out first; X is staged while they are in flight
   u32x4 w[GV_ROWS][GV_MAXC];
 #pragma unroll
   for (int r = 0; r < GV_ROWS; ++r)
@@ -218,6 +215,10 @@ __global__ __launch_bounds__(256) void gemv_kernel(const uint16_t* __restrict__ 
       w[r][c] = (o0 + r < O && ch < nch) ? *reinterpret_cast<const u32x4*>(W + (size_t)(o0 + r) * I + 8 * ch)
                                          : (u32x4){0u, 0u, 0u, 0u};
     }
+  for (int q = threadIdx.x; q < nv * (I >> 2); q += 256) {   // float4 of X (I % 8 == 0)
+    const int v = q >= (I >> 2), i4 = q - v * (I >> 2);
+    *reinterpret_cast<float4*>(&xs[v][4 * i4]) = *reinterpret_cast<const float4*>(X + (size_t)v * ldx + 4 * i4);
+  }
   __syncthreads();
   float acc[GV_ROWS][2];
 #pragma unroll

@@ -22,7 +22,8 @@ namespace {
 // 64 x 64 patch at column 64w, as 2 x 2 blocks of 32 x 32, K = 64 in 4 steps
 // of 16. Operands come straight from global memory (the 16 KB of latents of
 // a workgroup and the 32 KB of weight rows are cache hits for all but the
-// first wave that touches them).
+// first wave that touches them); the result is written row by row through
+// LDS.
 __device__ __forceinline__ void split3(const float (&x)[8], bf16x8& hi, bf16x8& mid, bf16x8& lo) {
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
@@ -38,9 +39,12 @@ __device__ __forceinline__ void split3(const float (&x)[8], bf16x8& hi, bf16x8& 
   }
 }
 
+constexpr int IMG_LD = 68;   // floats per staged row (64 + 4 of padding)
+
 __global__ __launch_bounds__(256) void img_in_kernel(const uint16_t* __restrict__ W,
                                                      const float* __restrict__ x, int n,
                                                      float* __restrict__ out, int ldo) {
+  __shared__ __align__(16) float img_smem[4 * 64 * IMG_LD];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int l32 = lane & 31, lh = lane >> 5;
   const int t0 = blockIdx.y * 64;
@@ -86,24 +90,31 @@ __global__ __launch_bounds__(256) void img_in_kernel(const uint16_t* __restrict_
       }
     }
   }
-  // register r of lane l: row 8(r/4) + 4lh + r%4 of the block, column l32
+  // Register r of lane l holds row 8(r/4) + 4lh + r%4 of its block, column
+  // l32. The wave's 64 x 64 patch goes through LDS (rows padded to 272 bytes)
+  // so that every store instruction writes four whole 256-byte row segments.
+  float* pt = img_smem + wave * 64 * IMG_LD;
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int t = t0 + 32 * i + 8 * (r >> 2) + 4 * lh + (r & 3);
-      if (t < n) {
-        float* op = out + (size_t)t * ldo + c0 + l32;
-        op[0] = acc[i][0][r];
-        op[32] = acc[i][1][r];
-      }
-    }
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        pt[(32 * i + 8 * (r >> 2) + 4 * lh + (r & 3)) * IMG_LD + 32 * j + l32] = acc[i][j][r];
+  __builtin_amdgcn_s_waitcnt(kWaitLgkm0);   // the region is private to this wave
+#pragma unroll
+  for (int it = 0; it < 16; ++it) {
+    const int row = 4 * it + (lane >> 4);
+    const int t = t0 + row;
+    const float4 v4 = *reinterpret_cast<const float4*>(pt + row * IMG_LD + 4 * (lane & 15));
+    if (t < n) *reinterpret_cast<float4*>(out + (size_t)t * ldo + c0 + 4 * (lane & 15)) = v4;
+  }
 }
 
 // ---------------------------------------------------------------------------
 // Scale-only final AdaLN + proj_out. A workgroup of 4 waves owns 16 rows:
 //  1. wave w normalizes rows 4w..4w+3 (each row in registers between the
-//     mean and the variance pass, the next row's loads in flight), scales by
+//     mean and the variance pass, two rows' loads in flight), scales by
 //     (1 + scale_out) and stores it as bf16 in LDS (16 rows x H, 16-byte
 //     chunks XOR-swizzled by the row so the fragment reads are conflict
 //     free);
@@ -115,10 +126,14 @@ __global__ __launch_bounds__(256) void img_in_kernel(const uint16_t* __restrict_
 constexpr int FO_ROWS = 16;
 constexpr int FO_MAXV = 16;   // float4 per lane per row: H <= 4096
 
+// HC: the width when known at compile time (4096, the production width: all
+// the guards below fold away), 0 for any other supported width.
+template <int HC>
 __global__ __launch_bounds__(256) void final_out_kernel(const float* __restrict__ h, int ldh, int rows,
-                                                        int H, const float* __restrict__ scale,
+                                                        int H_, const float* __restrict__ scale,
                                                         float eps, const uint16_t* __restrict__ W,
                                                         float* __restrict__ v) {
+  const int H = HC ? HC : H_;
   __shared__ __align__(16) unsigned char fo_smem[FO_ROWS * FO_MAXV * 256 * 2 + 4 * FO_ROWS * 64 * 4];
   unsigned char* ys = fo_smem;                                   // [16][H] bf16, swizzled
   float* part = reinterpret_cast<float*>(fo_smem + FO_ROWS * FO_MAXV * 256 * 2);   // [4][16][64]
@@ -126,6 +141,35 @@ __global__ __launch_bounds__(256) void final_out_kernel(const float* __restrict_
   const int r0 = blockIdx.x * FO_ROWS;
   const int nv = H >> 2;            // float4 per row
   const int rowb = H * 2;           // LDS bytes per row
+  constexpr uint32_t kOut = 0x80000000u;   // an offset past every resource: loads return 0
+
+  // Every global load is a buffer load whose resource ends at the data's
+  // end, so rows past `rows`, columns past H and K past this wave's range
+  // read as zero without a branch.
+  const __amdgpu_buffer_rsrc_t rh =
+      make_rsrc(h + (size_t)r0 * ldh, (uint32_t)((size_t)min(rows - r0, FO_ROWS) * ldh * 4));
+  const __amdgpu_buffer_rsrc_t rw = make_rsrc(W, (uint32_t)(64u * (uint32_t)H * 2u));
+
+  // W_out fragments of this wave's quarter of H, 16 K-steps (256 columns of
+  // W) per chunk and two chunks in registers: the first is fetched before
+  // the LayerNorm so its latency hides behind it, each next one while the
+  // current one is multiplied.
+  const int kq = H >> 2;
+  const int kb = wave * kq, ke = kb + kq;
+  const int l32 = lane & 31, lh = lane >> 5;
+  const uint32_t wo0 = (uint32_t)(l32 * H + 8 * lh) * 2u, wo1 = (uint32_t)((32 + l32) * H + 8 * lh) * 2u;
+  u32x4 bw0[2][16], bw1[2][16];
+  auto fetch = [&](u32x4 (&b)[2][16], int k0) {
+#pragma unroll
+    for (int st = 0; st < 16; ++st) {
+      const int k = k0 + 16 * st;
+      const bool in = k < ke;
+      b[0][st] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rw, in ? wo0 + 2u * k : kOut, 0, 0));
+      b[1][st] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rw, in ? wo1 + 2u * k : kOut, 0, 0));
+    }
+  };
+  fetch(bw0, kb);
+  __builtin_amdgcn_sched_barrier(0);
 
   float4 sc[FO_MAXV];
 #pragma unroll
@@ -133,31 +177,26 @@ __global__ __launch_bounds__(256) void final_out_kernel(const float* __restrict_
     const int c = lane + 64 * i;
     sc[i] = c < nv ? reinterpret_cast<const float4*>(scale)[c] : make_float4(0.f, 0.f, 0.f, 0.f);
   }
-  float4 cur[FO_MAXV], nxt[FO_MAXV];
-  auto load = [&](float4 (&dst)[FO_MAXV], int row) {
-    const float4* hp = reinterpret_cast<const float4*>(h + (size_t)row * ldh);
+  float4 ra[FO_MAXV], rb[FO_MAXV];
+  auto load = [&](float4 (&dst)[FO_MAXV], int lr) {      // local row lr of this workgroup
 #pragma unroll
     for (int i = 0; i < FO_MAXV; ++i) {
       const int c = lane + 64 * i;
-      dst[i] = (row < rows && c < nv) ? hp[c] : make_float4(0.f, 0.f, 0.f, 0.f);
+      const uint32_t off = c < nv ? (uint32_t)(lr * ldh + 4 * c) * 4u : kOut;
+      dst[i] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(rh, off, 0, 0));
     }
   };
-  load(cur, r0 + 4 * wave);
-#pragma unroll 1
-  for (int rr = 0; rr < 4; ++rr) {
-    const int lr = 4 * wave + rr;                 // local row
-    if (rr < 3) load(nxt, r0 + lr + 1);
+  auto norm_store = [&](const float4 (&x)[FO_MAXV], int lr) {
     float s = 0.f;
 #pragma unroll
-    for (int i = 0; i < FO_MAXV; ++i) s += (cur[i].x + cur[i].y) + (cur[i].z + cur[i].w);
+    for (int i = 0; i < FO_MAXV; ++i) s += (x[i].x + x[i].y) + (x[i].z + x[i].w);
     const float mean = wave_sum(s) / (float)H;
     float q = 0.f;
 #pragma unroll
     for (int i = 0; i < FO_MAXV; ++i) {
-      if (lane + 64 * i < nv) {
-        const float a = cur[i].x - mean, b = cur[i].y - mean, c = cur[i].z - mean, d = cur[i].w - mean;
-        q += (a * a + b * b) + (c * c + d * d);
-      }
+      const float m = lane + 64 * i < nv ? 1.f : 0.f;     // columns past H add nothing
+      const float a = x[i].x - mean, b = x[i].y - mean, c = x[i].z - mean, d = x[i].w - mean;
+      q += m * ((a * a + b * b) + (c * c + d * d));
     }
     const float rstd = rsqrtf(wave_sum(q) / (float)H + eps);
 #pragma unroll
@@ -165,42 +204,69 @@ __global__ __launch_bounds__(256) void final_out_kernel(const float* __restrict_
       const int c4 = lane + 64 * i;                // columns 4c4 .. 4c4+3
       if (c4 < nv) {
         u32x2 w;
-        w.x = pack2bf((cur[i].x - mean) * rstd * (1.f + sc[i].x), (cur[i].y - mean) * rstd * (1.f + sc[i].y));
-        w.y = pack2bf((cur[i].z - mean) * rstd * (1.f + sc[i].z), (cur[i].w - mean) * rstd * (1.f + sc[i].w));
+        w.x = pack2bf((x[i].x - mean) * rstd * (1.f + sc[i].x), (x[i].y - mean) * rstd * (1.f + sc[i].y));
+        w.y = pack2bf((x[i].z - mean) * rstd * (1.f + sc[i].z), (x[i].w - mean) * rstd * (1.f + sc[i].w));
         const int chunk = (c4 >> 1) ^ (lr & 15);   // 16-byte chunk, swizzled by the row
         *reinterpret_cast<u32x2*>(ys + lr * rowb + chunk * 16 + (c4 & 1) * 8) = w;
       }
     }
-    if (rr < 3) {
-#pragma unroll
-      for (int i = 0; i < FO_MAXV; ++i) cur[i] = nxt[i];
-    }
-  }
+  };
+  // wave w: rows 4w .. 4w+3, two row buffers in turn. The scheduling
+  // barriers keep each batch of loads where it is issued (ahead of the
+  // arithmetic that hides it) instead of letting the compiler sink it.
+  load(ra, 4 * wave);
+  load(rb, 4 * wave + 1);
+  __builtin_amdgcn_sched_barrier(0);
+  norm_store(ra, 4 * wave);
+  __builtin_amdgcn_sched_barrier(0);
+  load(ra, 4 * wave + 2);
+  __builtin_amdgcn_sched_barrier(0);
+  norm_store(rb, 4 * wave + 1);
+  __builtin_amdgcn_sched_barrier(0);
+  load(rb, 4 * wave + 3);
+  __builtin_amdgcn_sched_barrier(0);
+  norm_store(ra, 4 * wave + 2);
+  norm_store(rb, 4 * wave + 3);
   __syncthreads();
 
-  // out[16 x 64] partial over k in [kq * wave, kq * (wave + 1))
-  const int kq = H >> 2;
-  const int l32 = lane & 31, lh = lane >> 5;
+  // out[16 x 64] partial over k in [kb, ke)
   f32x16 acc[2];
 #pragma unroll
   for (int j = 0; j < 2; ++j)
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[j][r] = 0.f;
-  const bf16x8 zero8 = {};
-  const uint16_t* w0 = W + (size_t)l32 * H + 8 * lh;
-  const uint16_t* w1 = W + (size_t)(32 + l32) * H + 8 * lh;
-#pragma unroll 4
-  for (int k = wave * kq; k < (wave + 1) * kq; k += 16) {
-    const bf16x8 b0 = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(w0 + k));
-    const bf16x8 b1 = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(w1 + k));
-    bf16x8 a = zero8;
-    if (l32 < FO_ROWS) {
-      const int chunk = ((k + 8 * lh) >> 3) ^ l32;
-      a = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(ys + l32 * rowb + chunk * 16));
+  const int arow = l32 & 15;                       // lanes 16..31 read a row and zero it
+  const bool areal = l32 < FO_ROWS;
+  const int nsteps = kq >> 4;                      // 16-wide K steps of this wave
+  auto compute = [&](const u32x4 (&b)[2][16], int c) {
+#pragma unroll
+    for (int st = 0; st < 16; ++st) {
+      if (16 * c + st < nsteps) {                  // wave-uniform
+        const int k = kb + 16 * (16 * c + st);
+        const int chunk = ((k + 8 * lh) >> 3) ^ arow;
+        u32x4 av = *reinterpret_cast<const u32x4*>(ys + arow * rowb + chunk * 16);
+        av = areal ? av : (u32x4){0u, 0u, 0u, 0u};
+        const bf16x8 a = __builtin_bit_cast(bf16x8, av);
+        acc[0] = mfma32(a, __builtin_bit_cast(bf16x8, b[0][st]), acc[0]);
+        acc[1] = mfma32(a, __builtin_bit_cast(bf16x8, b[1][st]), acc[1]);
+      }
     }
-    acc[0] = mfma32(a, b0, acc[0]);
-    acc[1] = mfma32(a, b1, acc[1]);
+  };
+  // kq <= 1024: at most 4 chunks of 16 steps
+  if (nsteps > 16) fetch(bw1, kb + 256);
+  __builtin_amdgcn_sched_barrier(0);
+  compute(bw0, 0);
+  if (nsteps > 16) {
+    if (nsteps > 32) fetch(bw0, kb + 512);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(bw1, 1);
   }
+  if (nsteps > 32) {
+    if (nsteps > 48) fetch(bw1, kb + 768);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(bw0, 2);
+  }
+  if (nsteps > 48) compute(bw1, 3);
   // rows 0..15 of a block sit in registers r < 8 (row 8(r/4) + 4lh + r%4)
 #pragma unroll
   for (int j = 0; j < 2; ++j)
@@ -235,8 +301,11 @@ hipError_t launch_img_in(const uint16_t* W, const float* x, int n, int H, float*
 hipError_t launch_final_out(const float* h, int ldh, int rows, int H, const float* scale, float eps,
                             const uint16_t* W, float* v, hipStream_t s) {
   if (rows <= 0) return hipSuccess;
-  hipLaunchKernelGGL(final_out_kernel, dim3((rows + FO_ROWS - 1) / FO_ROWS), dim3(256), 0, s, h, ldh,
-                     rows, H, scale, eps, W, v);
+  const dim3 grid((rows + FO_ROWS - 1) / FO_ROWS);
+  if (H == 4096)
+    hipLaunchKernelGGL(final_out_kernel<4096>, grid, dim3(256), 0, s, h, ldh, rows, H, scale, eps, W, v);
+  else
+    hipLaunchKernelGGL(final_out_kernel<0>, grid, dim3(256), 0, s, h, ldh, rows, H, scale, eps, W, v);
   return hipGetLastError();
 }
 
