@@ -57,9 +57,10 @@ __global__ __launch_bounds__(NWV * 64, (NWV == 4 && NST == 2) ? 2 : 1) void attn
   constexpr int VT = D * 8;             // u32x4 per Vᵀ tile (128 dims x 128 B)
   constexpr int DMA_PER_WAVE = 32 / NWV;   // 16 K + 16 Vᵀ 1-KB blocks per tile
   static_assert(32 % NWV == 0 && (DMA_PER_WAVE % 2) == 0, "DMA split");
-  static_assert(NST == 2 || NST == 3, "ring of 2 or 3 stages");
-  __shared__ u32x4 k0s[KT], k1s[KT], k2s[NST == 3 ? KT : 1];
-  __shared__ u32x4 v0s[VT], v1s[VT], v2s[NST == 3 ? VT : 1];
+  static_assert(NST >= 2 && NST <= 4, "ring of 2, 3 or 4 stages");
+  // NST == 4 addresses its stages as one ring (k0s .. k0s + 4*KT)
+  __shared__ u32x4 k0s[NST == 4 ? 4 * KT : KT], k1s[NST == 4 ? 1 : KT], k2s[NST == 3 ? KT : 1];
+  __shared__ u32x4 v0s[NST == 4 ? 4 * VT : VT], v1s[NST == 4 ? 1 : VT], v2s[NST == 3 ? VT : 1];
   __shared__ int red[NWV];
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -177,9 +178,11 @@ __global__ __launch_bounds__(NWV * 64, (NWV == 4 && NST == 2) ? 2 : 1) void attn
   for (int sb = 0; sb < NSB; ++sb) { m_run[sb] = -INFINITY; l_run[sb] = 0.f; }
   const float sl2 = 1.4426950408889634f * 0.08838834764831845f;   // log2(e)/sqrt(128)
 
-  auto tile = [&](const u32x4* ks, const u32x4* vs, int kv0) {
+  // Scores, mask and online softmax of one key tile (K in ks): the bf16
+  // probabilities go to pk; false when no query of the wave sees the tile.
+  auto scores = [&](const u32x4* ks, int kv0, uint32_t (&pk)[NSB][2][8]) -> bool {
     const int cls = tile_class<BKV>(kv0, wlim_min, wlim_max, a.S);
-    if (cls == 0) return;
+    if (cls == 0) return false;
     f32x16 sacc[NSB][2];
 #pragma unroll
     for (int sb = 0; sb < NSB; ++sb)
@@ -224,7 +227,6 @@ __global__ __launch_bounds__(NWV * 64, (NWV == 4 && NST == 2) ? 2 : 1) void attn
     }
     // Scores stay unscaled; the softmax scale log2(e)/sqrt(d) > 0 commutes
     // with the max and is folded into the exponent: p = 2^(s*c - m).
-    uint32_t pk[NSB][2][8];
 #pragma unroll
     for (int sb = 0; sb < NSB; ++sb) {
       float mt = -INFINITY;
@@ -262,8 +264,12 @@ __global__ __launch_bounds__(NWV * 64, (NWV == 4 && NST == 2) ? 2 : 1) void attn
         }
       l_run[sb] = ls;
     }
-    // Oᵀ += Vᵀ·Pᵀ: chunk c = registers 8(c%2).. of key block c/2, which
-    // (through π) are keys 16c + 8*half + {0..7} of this lane's query
+    return true;
+  };
+  // Oᵀ += Vᵀ·Pᵀ for one key tile (Vᵀ in vs): chunk c = registers 8(c%2).. of
+  // key block c/2, which (through π) are keys 16c + 8*half + {0..7} of this
+  // lane's query
+  auto pv = [&](const u32x4* vs, const uint32_t (&pk)[NSB][2][8]) {
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       bf16x8 pf[NSB];
@@ -306,7 +312,8 @@ __global__ __launch_bounds__(NWV * 64, (NWV == 4 && NST == 2) ? 2 : 1) void attn
     // barrier so tile t+1 (stage B) is visible.
     auto iter = [&](u32x4* kA, u32x4* vA, u32x4* kC, u32x4* vC, int t) {
       dma(kC, vC, kt0 + min(t + 2, last) * BKV);
-      tile(kA, vA, kt0 + t * BKV);
+      uint32_t pk[NSB][2][8];
+      if (scores(kA, kt0 + t * BKV, pk)) pv(vA, pk);
       wait_barrier();
     };
     int t = 0;
@@ -317,6 +324,50 @@ __global__ __launch_bounds__(NWV * 64, (NWV == 4 && NST == 2) ? 2 : 1) void attn
     }
     if (t < ntiles) iter(k0s, v0s, k2s, v2s, t);
     if (t + 1 < ntiles) iter(k1s, v1s, k0s, v0s, t + 1);
+  } else if constexpr (NST == 4) {
+    // Ring of 4 stages, tiles t+1 and t+2 in flight. The two waves that
+    // share a SIMD (w and w + NWV/2) work out of phase: the upper half of
+    // the waves multiplies P·V one tile late, so while one wave of a pair
+    // runs its softmax (VALU) the other issues MFMAs, and their LDS reads
+    // fall at different times. A late wave keeps the tile's probabilities
+    // in registers and its Vᵀ stays in its stage one tile longer (stage
+    // (t+2)%4, refilled during tile t, last held tile t-2, whose products
+    // every wave finished before the previous barrier). The arithmetic on
+    // O, m and l is the same sequence as in the in-phase ring, so the
+    // results are bitwise those of the 3-stage kernel.
+    constexpr int PER_TILE = DMA_PER_WAVE;
+    const bool late = wave >= NWV / 2;
+    bool pend = false;
+    uint32_t pkl[NSB][2][8];
+    auto wait_barrier = [&]() {
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm(PER_TILE));   // tile t+1 landed, t+2 may fly
+      __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+      __builtin_amdgcn_s_barrier();
+    };
+    if (ntiles > 0) {
+      dma(k0s, v0s, kt0);
+      dma(k0s + KT, v0s + VT, kt0 + min(1, last) * BKV);
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm(PER_TILE));
+      __builtin_amdgcn_s_barrier();
+    }
+    // tile t in stage t%4: A = t%4, P = (t-1)%4 (the late waves' Vᵀ), C = (t+2)%4
+    auto iter = [&](u32x4* kA, u32x4* vA, u32x4* vP, u32x4* kC, u32x4* vC, int t) {
+      dma(kC, vC, kt0 + min(t + 2, last) * BKV);
+      if (!late) {
+        uint32_t pk[NSB][2][8];
+        if (scores(kA, kt0 + t * BKV, pk)) pv(vA, pk);
+      } else {
+        if (pend) pv(vP, pkl);
+        pend = scores(kA, kt0 + t * BKV, pkl);
+      }
+      wait_barrier();
+    };
+    // the four stages are consecutive: stage i at k0s + i*KT, v0s + i*VT
+#pragma unroll 1
+    for (int t = 0; t < ntiles; ++t)
+      iter(k0s + (t & 3) * KT, v0s + (t & 3) * VT, v0s + ((t + 3) & 3) * VT, k0s + ((t + 2) & 3) * KT,
+           v0s + ((t + 2) & 3) * VT, t);
+    if (late && pend) pv(v0s + ((ntiles - 1) & 3) * VT, pkl);
   } else {
     // double buffer (64 KB, so two workgroups share a CU and their barriers
     // fall at different times): tile t+1 is fetched into the other stage,
@@ -328,7 +379,8 @@ __global__ __launch_bounds__(NWV * 64, (NWV == 4 && NST == 2) ? 2 : 1) void attn
     }
     auto iter = [&](u32x4* kA, u32x4* vA, u32x4* kB, u32x4* vB, int t) {
       dma(kB, vB, kt0 + min(t + 1, last) * BKV);
-      tile(kA, vA, kt0 + t * BKV);
+      uint32_t pk[NSB][2][8];
+      if (scores(kA, kt0 + t * BKV, pk)) pv(vA, pk);
       __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
       __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
       __builtin_amdgcn_s_barrier();
@@ -481,6 +533,8 @@ hipError_t launch_attention_variant(const AttnArgs& a, int variant, hipStream_t 
     case 2: return run_attn2<4, 32, 2>(a, s, false);   // two workgroups per CU
     case 3: return run_attn2<8, 32, 3>(a, s, true);    // 1 with the last round split
     case 4: return run_attn2<4, 32, 2>(a, s, true);    // 2 with the last round split
+    case 5: return run_attn2<8, 32, 4>(a, s, false);   // 1 with the wave pairs out of phase
+    case 6: return run_attn2<8, 32, 4>(a, s, true);    // 5 with the last round split
   }
   return hipErrorInvalidValue;
 }

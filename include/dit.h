@@ -253,7 +253,9 @@ dit_status dit_debug_mask(const dit_seq* seq, uint8_t* mask, void* stream);
  *   cached step's last round, longest-first order of an extract step);
  *   1 = 256-query workgroups (8 waves), 2 = 128-query workgroups (4 waves,
  *   two per CU), both in index order and unsplit; 3, 4 = 1, 2 with the last
- *   round of workgroups split over key ranges.
+ *   round of workgroups split over key ranges; 5 = 1 with a 4-stage ring and
+ *   the two waves of each SIMD a tile out of phase (same arithmetic as 1);
+ *   6 = 5 with the last round split.
  *   scratch (device, caller-owned, may be NULL = no split) holds the split
  *   pieces: 256 * 129 * 4 bytes per piece at most; a launch whose pieces do
  *   not fit runs unsplit. Calls that overlap on one scratch race. */

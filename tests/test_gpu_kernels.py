@@ -114,7 +114,7 @@ def fill_cache(dev, S, nh, seed):
     return cache.to(dev), K.double().numpy(), V.double().numpy()
 
 
-ATTN_VARIANTS = [0, 1, 2, 3, 4]
+ATTN_VARIANTS = [0, 1, 2, 3, 4, 5, 6]
 
 
 def attn_scratch(dev):
@@ -337,3 +337,33 @@ def test_attention_running_max_raised_mid_stream(dev, name, mode, kind):
         err = rel_err(out.float().cpu().numpy(), ref)
         assert err < 1e-2, (variant, err)
     say(f"  last variant rel err {err:.2e}")
+
+
+@pytest.mark.parametrize("name,mode", [("c1", "extract"), ("c1", "cached"), ("many_ragged", "extract"),
+                                       ("many_ragged", "cached"), ("c3", "cached")])
+def test_out_of_phase_attention_is_bitwise_the_in_phase_kernel(dev, name, mode):
+    """The 4-stage kernel whose wave pairs multiply P·V one tile apart
+    performs the same arithmetic on O, m and l as the 3-stage kernel:
+    bit-identical output, unsplit (variants 1 and 5) and with the last round
+    split over key ranges (variants 3 and 6)."""
+    nh = 2
+    lay = layout_for(LAYOUTS[name])
+    P, T = lay["P"], lay["T"]
+    S = P + T
+    cache, _, _ = fill_cache(dev, S, nh, seed=S + 11)
+    lim = torch.from_numpy(lay["row_limit"]).to(dev)
+    seq = L.make_seq(P, T, lim, lim, lim)
+    q_off, N = (0, S) if mode == "extract" else (P, T)
+    g = torch.Generator().manual_seed(17)
+    Qd = (3.0 * torch.randn((N, nh * 128), generator=g)).to(torch.bfloat16).to(dev)
+    say(f"out-of-phase attention {name} {mode} S={S}")
+    scratch = attn_scratch(dev)
+    for a, b in ((1, 5), (3, 6)):
+        outs = []
+        for variant in (a, b):
+            out = torch.full((N, nh * 128), float("nan"), dtype=torch.bfloat16, device=dev)
+            L.dit_debug_attention(seq, nh, Qd, nh * 128, q_off, N, cache, out, variant, scratch)
+            outs.append(out)
+        torch.cuda.synchronize()
+        assert not torch.isnan(outs[0].float()).any()
+        assert torch.equal(outs[0].view(torch.int16), outs[1].view(torch.int16)), (a, b)
