@@ -114,7 +114,13 @@ def fill_cache(dev, S, nh, seed):
     return cache.to(dev), K.double().numpy(), V.double().numpy()
 
 
-ATTN_VARIANTS = [0, 1, 2, 3, 4, 5, 6]
+ATTN_VARIANTS = [0, 1, 2, 3, 4, 5, 6, 7, 8]
+
+
+def variant_applies(variant, mode, S):
+    """Variants 7 and 8 (the pipelined kernel of cached steps) take the
+    target rows of a cached step with S a multiple of 64 only."""
+    return variant < 7 or (mode == "cached" and S % 64 == 0)
 
 
 def attn_scratch(dev):
@@ -134,6 +140,8 @@ def test_attention_matches_oracle(dev, name, mode, variant):
     lay = layout_for(LAYOUTS[name])
     P, T = lay["P"], lay["T"]
     S = P + T
+    if not variant_applies(variant, mode, S):
+        pytest.skip("variant takes cached rows with S % 64 == 0 only")
     say(f"attention {name} {mode} S={S} variant={variant}")
     cache, K, V = fill_cache(dev, S, nh, seed=S)
     q_off, N = (0, S) if mode == "extract" else (P, T)
@@ -225,6 +233,8 @@ def test_attention_random_layouts(dev, seed):
         allowed = O.block_causal_mask(ids, rows=np.arange(q_off, q_off + N))
         ref = O.masked_attention(Q.double().numpy(), K, V, allowed)
         for variant in ATTN_VARIANTS:
+            if not variant_applies(variant, mode, S):
+                continue
             out = torch.empty((N, nh * 128), dtype=torch.bfloat16, device=dev)
             L.dit_debug_attention(seq, nh, Qd, nh * 128, q_off, N, cache, out, variant,
                                   attn_scratch(dev))
@@ -331,6 +341,8 @@ def test_attention_running_max_raised_mid_stream(dev, name, mode, kind):
     Qd = Qb.reshape(N, nh * 128).contiguous().to(dev)
     scratch = attn_scratch(dev)
     for variant in ATTN_VARIANTS:
+        if not variant_applies(variant, mode, S):
+            continue
         out = torch.empty((N, nh * 128), dtype=torch.bfloat16, device=dev)
         L.dit_debug_attention(seq, nh, Qd, nh * 128, q_off, N, cache, out, variant, scratch)
         torch.cuda.synchronize()
@@ -367,3 +379,86 @@ def test_out_of_phase_attention_is_bitwise_the_in_phase_kernel(dev, name, mode):
         torch.cuda.synchronize()
         assert not torch.isnan(outs[0].float()).any()
         assert torch.equal(outs[0].view(torch.int16), outs[1].view(torch.int16)), (a, b)
+
+
+def cache_from(dev, K, V):
+    """Layer-0 cache holding the bf16 roundings of K, V [S, nh, 128]."""
+    S, nh = K.shape[0], K.shape[1]
+    cap = L.dit_kv_capacity(S)
+    cache = torch.zeros(2 * nh * cap * 128, dtype=torch.int16)
+    kv, vt = cache_views(cache, 1, nh, cap)
+    kv[0, :, :S, :] = torch.from_numpy(K).to(torch.bfloat16).transpose(0, 1).view(torch.int16)
+    vt[0, :, :, :S] = torch.from_numpy(V).to(torch.bfloat16).permute(1, 2, 0).view(torch.int16)
+    return cache.to(dev)
+
+
+@pytest.mark.parametrize("kind", ["randn3", "rising", "q32"])
+@pytest.mark.parametrize("name", ["c1", "c3"])
+def test_pipelined_attention_is_bitwise_the_staged_kernel(dev, name, kind):
+    """The cached-step kernel that overlaps the softmax of tile t with the
+    score MFMAs of tile t+1 and the P·V of tile t-1 performs the same
+    arithmetic per query as the staged 8-wave kernel, raised running maxima
+    included (rising / peaked scores): bit-identical output unsplit
+    (variants 1 and 7) and with the last round split over key ranges
+    (variants 3 and 8)."""
+    nh = 2
+    lay = layout_for(LAYOUTS[name])
+    P, T = lay["P"], lay["T"]
+    S = P + T
+    if kind == "randn3":
+        g = np.random.default_rng(S)
+        Q = 3.0 * g.standard_normal((T, nh, 128))
+        K, V = g.standard_normal((S, nh, 128)), g.standard_normal((S, nh, 128))
+    else:
+        Q, K, V = rising_qk(kind, S, T, nh, seed=S + 5)
+    cache = cache_from(dev, K, V)
+    lim = torch.from_numpy(lay["row_limit"]).to(dev)
+    seq = L.make_seq(P, T, lim, lim, lim)
+    Qd = torch.from_numpy(Q).to(torch.bfloat16).reshape(T, nh * 128).contiguous().to(dev)
+    say(f"pipelined attention {name} {kind} S={S}")
+    scratch = attn_scratch(dev)
+    for a, b in ((1, 7), (3, 8)):
+        outs = []
+        for variant in (a, b):
+            out = torch.full((T, nh * 128), float("nan"), dtype=torch.bfloat16, device=dev)
+            L.dit_debug_attention(seq, nh, Qd, nh * 128, P, T, cache, out, variant, scratch)
+            outs.append(out)
+        torch.cuda.synchronize()
+        assert not torch.isnan(outs[0].float()).any()
+        assert torch.equal(outs[0].view(torch.int16), outs[1].view(torch.int16)), (a, b)
+
+
+def test_cached_launcher_takes_the_pipelined_kernel(dev):
+    """At 16 heads the c3 target rows make 256 workgroups of 256 queries, so
+    the step's launcher runs the pipelined kernel with its last-round key
+    split: bit-identical to variant 8, and sampled rows match the fp64
+    oracle."""
+    nh = 16
+    lay = layout_for(LAYOUTS["c3"])
+    P, T = lay["P"], lay["T"]
+    S = P + T
+    g = np.random.default_rng(S + 16)
+    Q = 2.0 * g.standard_normal((T, nh, 128))
+    K, V = g.standard_normal((S, nh, 128)), g.standard_normal((S, nh, 128))
+    cache = cache_from(dev, K, V)
+    lim = torch.from_numpy(lay["row_limit"]).to(dev)
+    seq = L.make_seq(P, T, lim, lim, lim)
+    Qb = torch.from_numpy(Q).to(torch.bfloat16)
+    Qd = Qb.reshape(T, nh * 128).contiguous().to(dev)
+    say(f"cached launcher, c3 at {nh} heads")
+    scratch = attn_scratch(dev)
+    outs = []
+    for variant in (0, 8):
+        out = torch.full((T, nh * 128), float("nan"), dtype=torch.bfloat16, device=dev)
+        L.dit_debug_attention(seq, nh, Qd, nh * 128, P, T, cache, out, variant, scratch)
+        outs.append(out)
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0].view(torch.int16), outs[1].view(torch.int16))
+    rows = np.unique(np.concatenate([[0, T - 1], np.random.default_rng(3).choice(T, 30, replace=False)]))
+    ids = O.build_layout(LAYOUTS["c3"]).image_ids
+    allowed = O.block_causal_mask(ids, rows=P + rows)
+    Kb = torch.from_numpy(K).to(torch.bfloat16).double().numpy()
+    Vb = torch.from_numpy(V).to(torch.bfloat16).double().numpy()
+    ref = O.masked_attention(Qb[rows].double().numpy(), Kb, Vb, allowed)
+    got = outs[0].float().cpu().numpy()[rows]
+    assert rel_err(got, ref) < 1e-2
