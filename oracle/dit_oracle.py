@@ -193,11 +193,14 @@ def rope_rotate(x, angles):
 
 def timestep_embedding(t: float, time_dim: int, base: float = 10000.0):
     """[3B] §1/§6: the timestep 1000·σ becomes a sin-cos vector; the lab's
-    script block [3B] orders it cosine first with frequencies
-    base^(-2i/time_dim), i < time_dim/2."""
-    freqs = base ** (-2.0 * np.arange(time_dim // 2, dtype=np.float64) / time_dim)
-    ang = float(t) * freqs
-    return np.concatenate([np.cos(ang), np.sin(ang)])
+    [3B] block orders it cosine first. With K = time_dim/2 angular
+    frequencies ω_i = base^(-i/K), i < K, the vector is
+    [cos(t ω_0) .. cos(t ω_{K-1}), sin(t ω_0) .. sin(t ω_{K-1})],
+    taken here as the real and imaginary parts of exp(i t ω)."""
+    half = time_dim // 2
+    omega = np.exp(-np.log(base) * np.arange(half, dtype=np.float64) / half)
+    rot = np.exp(1j * (float(t) * omega))
+    return np.hstack((rot.real, rot.imag))
 
 
 def silu(x):
@@ -206,18 +209,20 @@ def silu(x):
 
 
 def layernorm(x, eps: float = 1e-6):
-    """Non-affine LayerNorm with population variance, eps inside the root
-    ([INDEX] script, math helpers)."""
-    mu = x.mean(axis=-1, keepdims=True)
-    var = ((x - mu) ** 2).mean(axis=-1, keepdims=True)
-    return (x - mu) / np.sqrt(var + eps)
+    """Non-affine LayerNorm over the last axis: (x - E[x]) · (Var[x] + ε)^(-1/2)
+    with the population (1/n) variance ([INDEX] script, math helpers)."""
+    centred = x - np.mean(x, axis=-1, keepdims=True)
+    inv_sd = 1.0 / np.sqrt(np.var(x, axis=-1, keepdims=True) + eps)
+    return centred * inv_sd
 
 
 def rmsnorm(x, w, eps: float = 1e-6):
-    """Zero-centred RMSNorm x·rsqrt(mean(x²)+eps)·(1+w) ([INDEX] script,
-    math helpers; used per head as QK-RMSNorm, mapping row 4A)."""
-    ms = np.mean(x * x, axis=-1, keepdims=True)
-    return x / np.sqrt(ms + eps) * (1.0 + w)
+    """Zero-centred RMSNorm over the last axis (length d):
+    x · (‖x‖²/d + ε)^(-1/2) · (1 + w) ([INDEX] script, math helpers; used per
+    head as QK-RMSNorm, mapping row 4A)."""
+    d = x.shape[-1]
+    sq = np.linalg.norm(x, axis=-1, keepdims=True) ** 2
+    return (x * (1.0 / np.sqrt(sq / d + eps))) * (1.0 + w)
 
 
 def conditioning(W, dims: DitDims, sigma: float, causal_condition: bool = True):
