@@ -57,10 +57,9 @@ __global__ __launch_bounds__(NWV * 64, (NWV == 4 && NST == 2) ? 2 : 1) void attn
   constexpr int VT = D * 8;             // u32x4 per Vᵀ tile (128 dims x 128 B)
   constexpr int DMA_PER_WAVE = 32 / NWV;   // 16 K + 16 Vᵀ 1-KB blocks per tile
   static_assert(32 % NWV == 0 && (DMA_PER_WAVE % 2) == 0, "DMA split");
-  static_assert(NST >= 2 && NST <= 4, "ring of 2, 3 or 4 stages");
-  // NST == 4 addresses its stages as one ring (k0s .. k0s + 4*KT)
-  __shared__ u32x4 k0s[NST == 4 ? 4 * KT : KT], k1s[NST == 4 ? 1 : KT], k2s[NST == 3 ? KT : 1];
-  __shared__ u32x4 v0s[NST == 4 ? 4 * VT : VT], v1s[NST == 4 ? 1 : VT], v2s[NST == 3 ? VT : 1];
+  static_assert(NST == 2 || NST == 3, "ring of 2 or 3 stages");
+  __shared__ u32x4 k0s[KT], k1s[KT], k2s[NST == 3 ? KT : 1];
+  __shared__ u32x4 v0s[VT], v1s[VT], v2s[NST == 3 ? VT : 1];
   __shared__ int red[NWV];
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -324,50 +323,6 @@ __global__ __launch_bounds__(NWV * 64, (NWV == 4 && NST == 2) ? 2 : 1) void attn
     }
     if (t < ntiles) iter(k0s, v0s, k2s, v2s, t);
     if (t + 1 < ntiles) iter(k1s, v1s, k0s, v0s, t + 1);
-  } else if constexpr (NST == 4) {
-    // Ring of 4 stages, tiles t+1 and t+2 in flight. The two waves that
-    // share a SIMD (w and w + NWV/2) work out of phase: the upper half of
-    // the waves multiplies P·V one tile late, so while one wave of a pair
-    // runs its softmax (VALU) the other issues MFMAs, and their LDS reads
-    // fall at different times. A late wave keeps the tile's probabilities
-    // in registers and its Vᵀ stays in its stage one tile longer (stage
-    // (t+2)%4, refilled during tile t, last held tile t-2, whose products
-    // every wave finished before the previous barrier). The arithmetic on
-    // O, m and l is the same sequence as in the in-phase ring, so the
-    // results are bitwise those of the 3-stage kernel.
-    constexpr int PER_TILE = DMA_PER_WAVE;
-    const bool late = wave >= NWV / 2;
-    bool pend = false;
-    uint32_t pkl[NSB][2][8];
-    auto wait_barrier = [&]() {
-      __builtin_amdgcn_s_waitcnt(waitcnt_vm(PER_TILE));   // tile t+1 landed, t+2 may fly
-      __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
-      __builtin_amdgcn_s_barrier();
-    };
-    if (ntiles > 0) {
-      dma(k0s, v0s, kt0);
-      dma(k0s + KT, v0s + VT, kt0 + min(1, last) * BKV);
-      __builtin_amdgcn_s_waitcnt(waitcnt_vm(PER_TILE));
-      __builtin_amdgcn_s_barrier();
-    }
-    // tile t in stage t%4: A = t%4, P = (t-1)%4 (the late waves' Vᵀ), C = (t+2)%4
-    auto iter = [&](u32x4* kA, u32x4* vA, u32x4* vP, u32x4* kC, u32x4* vC, int t) {
-      dma(kC, vC, kt0 + min(t + 2, last) * BKV);
-      if (!late) {
-        uint32_t pk[NSB][2][8];
-        if (scores(kA, kt0 + t * BKV, pk)) pv(vA, pk);
-      } else {
-        if (pend) pv(vP, pkl);
-        pend = scores(kA, kt0 + t * BKV, pkl);
-      }
-      wait_barrier();
-    };
-    // the four stages are consecutive: stage i at k0s + i*KT, v0s + i*VT
-#pragma unroll 1
-    for (int t = 0; t < ntiles; ++t)
-      iter(k0s + (t & 3) * KT, v0s + (t & 3) * VT, v0s + ((t + 3) & 3) * VT, k0s + ((t + 2) & 3) * KT,
-           v0s + ((t + 2) & 3) * VT, t);
-    if (late && pend) pv(v0s + ((ntiles - 1) & 3) * VT, pkl);
   } else {
     // double buffer (64 KB, so two workgroups share a CU and their barriers
     // fall at different times): tile t+1 is fetched into the other stage,
@@ -888,16 +843,14 @@ hipError_t run_attn3(const AttnArgs& a0, hipStream_t s, bool split) {
 
 hipError_t launch_attention_variant(const AttnArgs& a, int variant, hipStream_t s) {
   // the pipelined kernel serves cached rows (every key visible) over whole 64-key tiles only
-  if ((variant == 7 || variant == 8) && (a.q_off != a.P || a.S % BKV)) return hipErrorInvalidValue;
+  if ((variant == 5 || variant == 6) && (a.q_off != a.P || a.S % BKV)) return hipErrorInvalidValue;
   switch (variant) {
     case 1: return run_attn2<8, 32, 3>(a, s, false);
     case 2: return run_attn2<4, 32, 2>(a, s, false);   // two workgroups per CU
     case 3: return run_attn2<8, 32, 3>(a, s, true);    // 1 with the last round split
     case 4: return run_attn2<4, 32, 2>(a, s, true);    // 2 with the last round split
-    case 5: return run_attn2<8, 32, 4>(a, s, false);   // 1 with the wave pairs out of phase
-    case 6: return run_attn2<8, 32, 4>(a, s, true);    // 5 with the last round split
-    case 7: return run_attn3(a, s, false);              // pipelined, cached rows only
-    case 8: return run_attn3(a, s, true);               // 7 with the last round split
+    case 5: return run_attn3(a, s, false);              // pipelined, cached rows only
+    case 6: return run_attn3(a, s, true);               // 5 with the last round split
   }
   return hipErrorInvalidValue;
 }

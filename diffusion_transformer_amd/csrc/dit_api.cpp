@@ -625,9 +625,9 @@ dit_status dit_debug_attention(const dit_seq* seq, int n_heads, const void* q, i
   if (!q || !kv_cache || !out) return fail(DIT_ERR_ARG, "NULL argument");
   if (n_heads <= 0 || N <= 0 || q_off < 0 || q_off + N > S || q_stride < n_heads * 128 || q_stride % 8)
     return fail(DIT_ERR_ARG, "bad attention shape");
-  if (variant < 0 || variant > 8) return fail(DIT_ERR_ARG, "unknown attention variant %d", variant);
-  if ((variant == 7 || variant == 8) && (q_off != seq->P || S % 64))
-    return fail(DIT_ERR_ARG, "variants 7 and 8 take target rows (q_off = P) and S a multiple of 64");
+  if (variant < 0 || variant > 6) return fail(DIT_ERR_ARG, "unknown attention variant %d", variant);
+  if ((variant == 5 || variant == 6) && (q_off != seq->P || S % 64))
+    return fail(DIT_ERR_ARG, "variants 5 and 6 take target rows (q_off = P) and S a multiple of 64");
   if (scratch && (reinterpret_cast<uintptr_t>(scratch) & 15))
     return fail(DIT_ERR_ARG, "scratch must be 16-byte aligned");
 #ifdef DIT_F32

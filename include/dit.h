@@ -253,12 +253,11 @@ dit_status dit_debug_mask(const dit_seq* seq, uint8_t* mask, void* stream);
  *   cached step's last round, longest-first order of an extract step);
  *   1 = 256-query workgroups (8 waves), 2 = 128-query workgroups (4 waves,
  *   two per CU), both in index order and unsplit; 3, 4 = 1, 2 with the last
- *   round of workgroups split over key ranges; 5 = 1 with a 4-stage ring and
- *   the two waves of each SIMD a tile out of phase (same arithmetic as 1);
- *   6 = 5 with the last round split; 7 = the cached-step kernel (4 waves of
- *   64 queries, the scores of tile t+1 computed under the softmax of tile t;
- *   target rows only: q_off = P and S a multiple of 64, DIT_ERR_ARG
- *   otherwise), 8 = 7 with the last round split.
+ *   round of workgroups split over key ranges; 5 = the pipelined kernel of
+ *   cached steps (8 waves of 32 queries; the softmax of key tile t runs
+ *   under the score MFMAs of tile t+1 and the P·V of tile t-1; same
+ *   arithmetic per query as 1; target rows only: q_off = P and S a multiple
+ *   of 64, DIT_ERR_ARG otherwise), 6 = 5 with the last round split.
  *   scratch (device, caller-owned, may be NULL = no split) holds the split
  *   pieces: 256 * 129 * 4 bytes per piece at most; a launch whose pieces do
  *   not fit runs unsplit. Calls that overlap on one scratch race. */

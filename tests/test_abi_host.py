@@ -306,9 +306,9 @@ def test_debug_attention_validation():
         return L._lib.dit_debug_attention(C.byref(seq), 2, FAKE, 256, q_off, N, FAKE, FAKE,
                                           variant, scratch, 1 << 20, None)
 
-    assert st(variant=9) == L.DIT_ERR_ARG             # no such variant
-    assert st(variant=7) == L.DIT_ERR_ARG             # pipelined kernel: S = 11 not a multiple of 64
-    assert st(variant=8, N=11, q_off=0) == L.DIT_ERR_ARG   # ... and target rows only
+    assert st(variant=7) == L.DIT_ERR_ARG             # no such variant
+    assert st(variant=5) == L.DIT_ERR_ARG             # pipelined kernel: S = 11 not a multiple of 64
+    assert st(variant=6, N=11, q_off=0) == L.DIT_ERR_ARG   # ... and target rows only
     assert st(scratch=FAKE + 4) == L.DIT_ERR_ARG
     assert st(N=5) == L.DIT_ERR_ARG                   # rows past S
 

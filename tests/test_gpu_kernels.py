@@ -114,13 +114,13 @@ def fill_cache(dev, S, nh, seed):
     return cache.to(dev), K.double().numpy(), V.double().numpy()
 
 
-ATTN_VARIANTS = [0, 1, 2, 3, 4, 5, 6, 7, 8]
+ATTN_VARIANTS = [0, 1, 2, 3, 4, 5, 6]
 
 
 def variant_applies(variant, mode, S):
-    """Variants 7 and 8 (the pipelined kernel of cached steps) take the
+    """Variants 5 and 6 (the pipelined kernel of cached steps) take the
     target rows of a cached step with S a multiple of 64 only."""
-    return variant < 7 or (mode == "cached" and S % 64 == 0)
+    return variant < 5 or (mode == "cached" and S % 64 == 0)
 
 
 def attn_scratch(dev):
@@ -351,36 +351,6 @@ def test_attention_running_max_raised_mid_stream(dev, name, mode, kind):
     say(f"  last variant rel err {err:.2e}")
 
 
-@pytest.mark.parametrize("name,mode", [("c1", "extract"), ("c1", "cached"), ("many_ragged", "extract"),
-                                       ("many_ragged", "cached"), ("c3", "cached")])
-def test_out_of_phase_attention_is_bitwise_the_in_phase_kernel(dev, name, mode):
-    """The 4-stage kernel whose wave pairs multiply P·V one tile apart
-    performs the same arithmetic on O, m and l as the 3-stage kernel:
-    bit-identical output, unsplit (variants 1 and 5) and with the last round
-    split over key ranges (variants 3 and 6)."""
-    nh = 2
-    lay = layout_for(LAYOUTS[name])
-    P, T = lay["P"], lay["T"]
-    S = P + T
-    cache, _, _ = fill_cache(dev, S, nh, seed=S + 11)
-    lim = torch.from_numpy(lay["row_limit"]).to(dev)
-    seq = L.make_seq(P, T, lim, lim, lim)
-    q_off, N = (0, S) if mode == "extract" else (P, T)
-    g = torch.Generator().manual_seed(17)
-    Qd = (3.0 * torch.randn((N, nh * 128), generator=g)).to(torch.bfloat16).to(dev)
-    say(f"out-of-phase attention {name} {mode} S={S}")
-    scratch = attn_scratch(dev)
-    for a, b in ((1, 5), (3, 6)):
-        outs = []
-        for variant in (a, b):
-            out = torch.full((N, nh * 128), float("nan"), dtype=torch.bfloat16, device=dev)
-            L.dit_debug_attention(seq, nh, Qd, nh * 128, q_off, N, cache, out, variant, scratch)
-            outs.append(out)
-        torch.cuda.synchronize()
-        assert not torch.isnan(outs[0].float()).any()
-        assert torch.equal(outs[0].view(torch.int16), outs[1].view(torch.int16)), (a, b)
-
-
 def cache_from(dev, K, V):
     """Layer-0 cache holding the bf16 roundings of K, V [S, nh, 128]."""
     S, nh = K.shape[0], K.shape[1]
@@ -399,8 +369,8 @@ def test_pipelined_attention_is_bitwise_the_staged_kernel(dev, name, kind):
     score MFMAs of tile t+1 and the P·V of tile t-1 performs the same
     arithmetic per query as the staged 8-wave kernel, raised running maxima
     included (rising / peaked scores): bit-identical output unsplit
-    (variants 1 and 7) and with the last round split over key ranges
-    (variants 3 and 8)."""
+    (variants 1 and 5) and with the last round split over key ranges
+    (variants 3 and 6)."""
     nh = 2
     lay = layout_for(LAYOUTS[name])
     P, T = lay["P"], lay["T"]
@@ -417,7 +387,7 @@ def test_pipelined_attention_is_bitwise_the_staged_kernel(dev, name, kind):
     Qd = torch.from_numpy(Q).to(torch.bfloat16).reshape(T, nh * 128).contiguous().to(dev)
     say(f"pipelined attention {name} {kind} S={S}")
     scratch = attn_scratch(dev)
-    for a, b in ((1, 7), (3, 8)):
+    for a, b in ((1, 5), (3, 6)):
         outs = []
         for variant in (a, b):
             out = torch.full((T, nh * 128), float("nan"), dtype=torch.bfloat16, device=dev)
@@ -431,7 +401,7 @@ def test_pipelined_attention_is_bitwise_the_staged_kernel(dev, name, kind):
 def test_cached_launcher_takes_the_pipelined_kernel(dev):
     """At 16 heads the c3 target rows make 256 workgroups of 256 queries, so
     the step's launcher runs the pipelined kernel with its last-round key
-    split: bit-identical to variant 8, and sampled rows match the fp64
+    split: bit-identical to variant 6, and sampled rows match the fp64
     oracle."""
     nh = 16
     lay = layout_for(LAYOUTS["c3"])
@@ -448,7 +418,7 @@ def test_cached_launcher_takes_the_pipelined_kernel(dev):
     say(f"cached launcher, c3 at {nh} heads")
     scratch = attn_scratch(dev)
     outs = []
-    for variant in (0, 8):
+    for variant in (0, 6):
         out = torch.full((T, nh * 128), float("nan"), dtype=torch.bfloat16, device=dev)
         L.dit_debug_attention(seq, nh, Qd, nh * 128, P, T, cache, out, variant, scratch)
         outs.append(out)
