@@ -195,8 +195,10 @@ def summarize_counters(counter_dir, fetch_dir, write_dir, command, out_md):
         if "gemm_w4_kernel<2" in n:
             return "O GEMM (residual epilogue)" if e["counters"]["SQ_INSTS_MFMA"] < split else \
                 "down GEMM (residual epilogue)"
+        if "attn3_kernel" in n:
+            return "attention, cached steps (pipelined kernel)"
         if "attn2_kernel" in n:
-            return "attention"
+            return "attention, extract step (cache build)"
         return None
 
     groups = defaultdict(list)
@@ -215,7 +217,8 @@ def summarize_counters(counter_dir, fetch_dir, write_dir, command, out_md):
              "| clock GHz | LDS instr | LDS bank conflicts |",
              "|---|---|---|---|---|---|---|---|---|---|"]
     for c in ("QKV GEMM + norm/RoPE/cache epilogue", "O GEMM (residual epilogue)",
-              "gate/up GEMM (SwiGLU epilogue)", "down GEMM (residual epilogue)", "attention"):
+              "gate/up GEMM (SwiGLU epilogue)", "down GEMM (residual epilogue)",
+              "attention, cached steps (pipelined kernel)", "attention, extract step (cache build)"):
         es = groups.get(c)
         if not es:
             continue
