@@ -114,6 +114,8 @@ HBM_KERNELS = [
      4096 * 4096 * 4 + 4096 * 64 * 4 + 4096 * 64 * 2),
     ("modulation GEMV [16384 x 4096] (gemv_kernel)", "gemv_kernel", 1024 * 256,
      16384 * 4096 * 2 + 4096 * 4 + 16384 * 4),
+    ("Euler update x += dsigma * v, 4096 x 64 (euler_kernel)", "euler_kernel", 1024 * 256,
+     4096 * 64 * 12),
 ]
 
 
