@@ -398,28 +398,13 @@ __global__ __launch_bounds__(NWV * 64, (NWV == 4 && NST == 2) ? 2 : 1) void attn
   }
 }
 
-// Interleave of a scheduling region: PRE LDS reads, then NM MFMAs, each
-// followed by one more LDS read (while ND last) and NV vector instructions,
-// so every fragment is read PRE MFMAs before its use.
-template <int NM, int ND, int NV, int PRE = 3>
-__device__ __forceinline__ void weave() {
-#pragma unroll
-  for (int i = 0; i < PRE && i < ND; ++i) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-#pragma unroll
-  for (int i = 0; i < NM; ++i) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                       // MFMA
-    if (i + PRE < ND) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);     // DS read
-    __builtin_amdgcn_sched_group_barrier(0x002, NV, 0);                      // VALU
-  }
-}
-
 // ---------------------------------------------------------------------------
 // attn3_kernel: the cached step's attention, software-pipelined inside each
 // wave. Target rows of a cached step see every key, so no tile needs a mask
 // (the launcher uses this kernel only when S is a multiple of 64).
-// 8 waves of 32 queries (two per SIMD). For tile t a wave issues, in one
-// scheduling region, the score MFMAs of tile t+1 and the P·V MFMAs of tile
-// t-1 on the matrix core, and the softmax of tile t (row max, lazy rescale
+// 8 waves of 32 queries (two per SIMD). For tile t a wave issues, in 32
+// fixed slots, the score MFMAs of tile t+1 and the P·V MFMAs of tile t-1 on
+// the matrix core, and the softmax of tile t (row max, lazy rescale
 // decision, exponentials, bf16 packing, row sums) on the vector ALU; the
 // three are independent, so the two units work at the same time. A raised
 // running max rescales O after the P·V of tile t-1 has landed in it, which
