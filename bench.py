@@ -321,6 +321,24 @@ def cpu_baseline(cfg, seconds_hint=True):
                        f"scaled x{cfg['n_layers']}")}
 
 
+def run_conditions(dev, batch, peaks):
+    """What every number above was measured under: batch, prefix cache,
+    guidance scale, software versions, device and, from the register-only
+    MFMA loop, the clock the matrix cores effectively ran at (each of the
+    1024 SIMDs retires 1024 bf16 flop per clock at full rate)."""
+    import torch
+    props = torch.cuda.get_device_properties(dev)
+    cond = {"batch": batch,
+            "prefix_cache": "on: value and latency are cached steps; extract_ms is the cache build",
+            "cfg_scale": 1.0,
+            "hip": torch.version.hip, "torch": torch.__version__,
+            "device": f"{props.name} ({getattr(props, 'gcnArchName', '?')}), "
+                      f"{props.multi_processor_count} CUs, {props.total_memory / 2**30:.0f} GiB"}
+    if peaks:
+        cond["mfma_loop_clock_ghz"] = round(peaks["mfma_bf16_tflops"] * 1e12 / (1024 * 1024) / 1e9, 3)
+    return cond
+
+
 def measured_peaks(L, dev):
     """The ceilings this GPU actually reaches, next to the spec peaks: a
     register-only bf16 MFMA loop on N(0,1) operands (the library's own
@@ -666,6 +684,7 @@ def main():
         "kernels": breakdown,
         "measured_peaks": peaks,
         "workloads": others,
+        "run_conditions": run_conditions(dev, B, peaks),
     }
     if not args.no_cpu_baseline:
         print("[bench] timing the fp64 oracle on the host (cpu_baseline)", file=sys.stderr, flush=True)
