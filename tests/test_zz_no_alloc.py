@@ -1,8 +1,9 @@
 """The allocation-free cached step (dit_step_cached_noalloc, workspace in the
 library's fixed device array) against dit_step_cached with a caller
-workspace: two calls in a row, the second with a smaller layout, both bit
-for bit equal to the ordinary entry point; sizes above the array are
-refused before any device work."""
+workspace: three calls in a row, each with a smaller layout than the one
+before (the first large enough, 256 workgroups of 256 target queries, for
+the pipelined attention kernel), all bit for bit equal to the ordinary entry
+point; sizes above the array are refused before any device work."""
 import numpy as np
 import pytest
 import torch
@@ -27,7 +28,8 @@ def test_noalloc_cached_step_matches_cached_step(dev):
     cfg = synth.config("c1")                      # one layer, hidden 4096, 32 heads, ffn 16384
     W = synth.make_weights(cfg, workers=16)
     rt = DitRuntime(cfg, W, device=dev)
-    layouts = [cfg["segments"], [("text", 128), ("ref", 8, 8), ("target", 16, 16)]]
+    layouts = [[("text", 512), ("target", 32, 64)], cfg["segments"],
+               [("text", 128), ("ref", 8, 8), ("target", 16, 16)]]
     prev_T = None
     for call, segs in enumerate(layouts):
         c = synth.config("c1", segments=segs)
