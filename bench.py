@@ -158,7 +158,8 @@ def hbm_kernels_summary(trace_dir, fetch_dir, write_dir, command, calib, out_md)
     open(out_md, "w").write("\n".join(lines) + "\n")
 
 
-def summarize_counters(counter_dir, fetch_dir, write_dir, command, out_md):
+def summarize_counters(counter_dir, fetch_dir, write_dir, command, out_md,
+                       title="cached DiT step, c2 workload", ln_section=True):
     """Per-kernel rocprofv3 counter evidence for the cached step: MFMA
     instructions (all v_mfma_f32_32x32x16_bf16, 32768 flop each) over the
     dispatch's own duration against the dense bf16 peak, the matrix-core
@@ -185,7 +186,12 @@ def summarize_counters(counter_dir, fetch_dir, write_dir, command, out_md):
         return out
 
     disp = per_dispatch(counter_dir)
-    mf = [e["counters"]["SQ_INSTS_MFMA"] for e in disp.values() if "gemm_w4_kernel<2" in e["name"]]
+    # O (K = hidden) and down (K = ffn) share the residual epilogue; per
+    # workgroup the down projection issues ffn/hidden times the MFMAs
+    def per_wg(e):
+        return e["counters"]["SQ_INSTS_MFMA"] / max(e["grid"] // 256, 1)
+
+    mf = [per_wg(e) for e in disp.values() if "gemm_w4_kernel<2" in e["name"]]
     split = (min(mf) + max(mf)) / 2 if mf else 0
 
     def cls(e):
@@ -195,8 +201,7 @@ def summarize_counters(counter_dir, fetch_dir, write_dir, command, out_md):
         if GATEUP_KERNEL in n:
             return "gate/up GEMM (SwiGLU epilogue)"
         if "gemm_w4_kernel<2" in n:
-            return "O GEMM (residual epilogue)" if e["counters"]["SQ_INSTS_MFMA"] < split else \
-                "down GEMM (residual epilogue)"
+            return "O GEMM (residual epilogue)" if per_wg(e) < split else "down GEMM (residual epilogue)"
         if "attn3_kernel" in n:
             return "attention, cached steps (pipelined kernel)"
         if "attn2_kernel" in n:
@@ -208,7 +213,7 @@ def summarize_counters(counter_dir, fetch_dir, write_dir, command, out_md):
         c = cls(e)
         if c and "ns" in e:
             groups[c].append(e)
-    lines = ["# rocprofv3 counters per kernel: cached DiT step, c2 workload", "",
+    lines = [f"# rocprofv3 counters per kernel: {title}", "",
              "Commands (from the repository root on the MI355X machine; R = repository root):", "", "```",
              command, "```", "",
              "MFMA: `SQ_INSTS_MFMA` x 32768 flop (every MFMA here is v_mfma_f32_32x32x16_bf16) over "
@@ -244,7 +249,7 @@ def summarize_counters(counter_dir, fetch_dir, write_dir, command, out_md):
         res[name] = (known_kib / calib, ln)
     ff, lnf = res["FETCH_SIZE"]
     wf, lnw = res["WRITE_SIZE"]
-    if lnf and lnw:
+    if ln_section and lnf and lnw:
         fb = sum(e["counters"]["FETCH_SIZE"] for e in lnf) / len(lnf) * ff * 1024
         wb = sum(e["counters"]["WRITE_SIZE"] for e in lnw) / len(lnw) * wf * 1024
         ns = (sum(e["ns"] for e in lnf) + sum(e["ns"] for e in lnw)) / (len(lnf) + len(lnw))
@@ -469,9 +474,13 @@ def main():
         open(sys.argv[5], "w").write("\n".join(lines) + "\n")
         return
     if len(sys.argv) > 1 and sys.argv[1] == "--summarize-counters":
-        # bench.py --summarize-counters COUNTER_DIR FETCH_DIR WRITE_DIR "COMMAND"
-        summarize_counters(sys.argv[2], sys.argv[3], sys.argv[4], sys.argv[5],
-                           os.path.join(ROOT, "profiles", "counters_c2_cached.md"))
+        # bench.py --summarize-counters COUNTER_DIR FETCH_DIR WRITE_DIR "COMMAND" [OUT_MD "TITLE"]
+        if len(sys.argv) > 7:
+            summarize_counters(sys.argv[2], sys.argv[3], sys.argv[4], sys.argv[5], sys.argv[6], sys.argv[7],
+                               ln_section=False)
+        else:
+            summarize_counters(sys.argv[2], sys.argv[3], sys.argv[4], sys.argv[5],
+                               os.path.join(ROOT, "profiles", "counters_c2_cached.md"))
         return
     if len(sys.argv) > 1 and sys.argv[1] == "--summarize-prof":
         # bench.py --summarize-prof TRACE_DIR FETCH_DIR WRITE_DIR "COMMAND"
