@@ -89,6 +89,64 @@ def test_one_layer_full_token_counts_sampled(dev, name):
     assert e0 < TOL_BF16 and e1 < TOL_BF16
 
 
+def random_full_width_layout(seed):
+    """Seeded random layout at the real width: 1-4 text runs and 0-3
+    reference images of mixed sizes in random order, then a target of
+    46..64 x 46..64 tokens (enough 256-row blocks, with 32 heads, for the
+    cached step's pipelined attention). Even seeds pad the first text run so S
+    is a multiple of 64; odd seeds make it not one (staged kernel)."""
+    r = np.random.default_rng(500 + seed)
+    segs = [("text", int(r.integers(16, 300))) for _ in range(int(r.integers(1, 5)))]
+    segs += [("ref", int(r.integers(8, 49)), int(r.integers(8, 49))) for _ in range(int(r.integers(0, 4)))]
+    order = r.permutation(len(segs))
+    segs = [segs[i] for i in order]
+    segs.append(("target", int(r.integers(46, 65)), int(r.integers(46, 65))))
+    S = sum(s[1] if s[0] == "text" else s[1] * s[2] for s in segs)
+    i = next(k for k, s in enumerate(segs) if s[0] == "text")
+    if seed % 2 == 0 and S % 64:
+        segs[i] = ("text", segs[i][1] + 64 - S % 64)
+    elif seed % 2 == 1 and S % 64 == 0:
+        segs[i] = ("text", segs[i][1] + 1)
+    return segs
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_random_layouts_one_layer_sampled(dev, seed):
+    """Random full-width layouts (one layer, hidden 4096, 32 heads): v_θ of
+    48 sampled target rows from extract and from a cached step against the
+    oracle's row-wise evaluation, with S a multiple of 64 or not (the two
+    attention kernels of cached steps)."""
+    segs = random_full_width_layout(seed)
+    cfg = synth.config("c1", segments=segs)
+    W = synth.make_weights(cfg, seed=21, workers=16)
+    I = synth.make_inputs(cfg, seed=21 + seed)
+    rt = DitRuntime(cfg, W, device=dev)
+    seq = rt.sequence(cfg["segments"])
+    pre = rt.prefix_hidden(I)
+    x0 = torch.from_numpy(I["x0"]).to(dev)
+    say(f"random layout {seed}: {len(segs)} segments, P={seq.P} T={seq.T} S%64={seq.S % 64}")
+    cache = rt.alloc_cache(seq)
+    ws = rt.alloc_workspace(seq.S)
+    v = torch.empty_like(x0)
+    rt.step_extract(seq, pre, x0, 1.0, cache, v, ws)
+    x1 = synth._rng(98 + seed, "x_alt").standard_normal((seq.T, 64), dtype=np.float32)
+    v1 = torch.empty_like(x0)
+    rt.step_cached(seq, torch.from_numpy(x1).to(dev), 0.978453, cache, v1, ws)
+    torch.cuda.synchronize()
+    rows = np.sort(np.random.default_rng(8 + seed).choice(seq.T, 48, replace=False))
+    rows = np.unique(np.concatenate([[0, seq.T - 1], rows]))
+    dims = dims_of(cfg)
+    lay = O.build_layout(cfg["segments"])
+    opre = oracle_prefix(cfg, W, I)
+    r0 = O.cached_rows_one_layer(W, dims, lay, opre, I["x0"], 1.0, rows)
+    r1 = O.cached_rows_one_layer(W, dims, lay, opre, x1, 0.978453, rows)
+    e0 = rel_err(v.cpu().numpy()[rows], r0)
+    e1 = rel_err(v1.cpu().numpy()[rows], r1)
+    say(f"  extract rows rel {e0:.3e}  cached rows rel {e1:.3e}")
+    assert e0 < TOL_BF16 and e1 < TOL_BF16
+    rt.close()
+
+
 def nearest_rows(got, ref):
     """Index of the nearest ref row (squared distance) for every got row."""
     g = got.astype(np.float64)
