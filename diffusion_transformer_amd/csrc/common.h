@@ -13,6 +13,14 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));           // 32x32 MF
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));          // 16-byte move
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));          // 8-byte move
 
+// SiLU x·sigmoid(x) = x / (1 + e^-x), with the hardware reciprocal (within
+// 1 ulp) instead of the IEEE division sequence: the result is rounded to bf16
+// next, which this error changes only when it straddles a rounding boundary.
+// Saturates to -0 for very negative x (e^-x = inf, reciprocal 0).
+__device__ __forceinline__ float silu_f(float x) {
+  return x * __builtin_amdgcn_rcpf(1.f + __expf(-x));
+}
+
 __device__ __forceinline__ float bf2f(bf16_t b) { return __uint_as_float(((uint32_t)b) << 16); }
 // float -> bf16, round to nearest even (lowers to v_cvt_pk_bf16_f32 on gfx950).
 __device__ __forceinline__ bf16_t f2bf(float f) { return __builtin_bit_cast(bf16_t, (__bf16)f); }

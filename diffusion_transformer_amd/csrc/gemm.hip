@@ -55,7 +55,7 @@ __device__ __forceinline__ void store_tile_lds(const GemmArgs& g, f32x16 (&acc)[
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const float gv = acc[i][j][4 * q + e], uv = acc[i][j + 1][4 * q + e];
-            o[e] = gv / (1.f + __expf(-gv)) * uv;
+            o[e] = silu_f(gv) * uv;
           }
           const int slot = (2 * ((j >> 1) * 4 + q) + lhalf) ^ (row & (SLOTS - 1));
           u32x2 w;
@@ -544,8 +544,8 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(GemmArgs g) {
     // output feature c is packed column 64*(c/32) + c%32 (gate); up is 32 later
     const int pg = 64 * (c >> 5) + (c & 31);
     const float4 gv = sum4(pg), uv = sum4(pg + 32);
-    const float o0 = gv.x / (1.f + __expf(-gv.x)) * uv.x, o1 = gv.y / (1.f + __expf(-gv.y)) * uv.y;
-    const float o2 = gv.z / (1.f + __expf(-gv.z)) * uv.z, o3 = gv.w / (1.f + __expf(-gv.w)) * uv.w;
+    const float o0 = silu_f(gv.x) * uv.x, o1 = silu_f(gv.y) * uv.y;
+    const float o2 = silu_f(gv.z) * uv.z, o3 = silu_f(gv.w) * uv.w;
     u32x2 w;
     w.x = pack2bf(o0, o1);
     w.y = pack2bf(o2, o3);
