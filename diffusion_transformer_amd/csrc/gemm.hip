@@ -428,12 +428,6 @@ __global__ __launch_bounds__(256) void gemm_w4_kernel(GemmArgs g) {
   };
 
   f32x16 acc[FM][FN];
-#pragma unroll
-  for (int i = 0; i < FM; ++i)
-#pragma unroll
-    for (int j = 0; j < FN; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
   const int lrow = lane & 31, lhalf = lane >> 5;
   const int swz = (lrow >> 1) & 7;
@@ -454,6 +448,17 @@ __global__ __launch_bounds__(256) void gemm_w4_kernel(GemmArgs g) {
   };
 
   dma(st0, 0);
+  // the 256 accumulator registers are cleared while the first stage is in
+  // flight: the empty asm takes each cleared block as an accumulator-register
+  // operand here, so the clearing cannot sink below the wait
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+      asm volatile("" : "+a"(acc[i][j]));
+    }
   __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
   __builtin_amdgcn_s_barrier();
   lread(0, st0, 0);
