@@ -119,6 +119,16 @@ __device__ __forceinline__ void lds_barrier() {
 // LDS destination pointer of a buffer_load ... lds (address space 3).
 #define LDSP(p) ((__attribute__((address_space(3))) void*)(p))
 
+// A pointer the caller knows to be the same in every lane, moved to scalar
+// registers (so a buffer resource built from it needs no per-lane loop).
+template <class T>
+__device__ __forceinline__ T* uniform_ptr(T* p) {
+  const uint64_t v = (uint64_t)p;
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)v);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(v >> 32));
+  return (T*)(((uint64_t)hi << 32) | lo);
+}
+
 // Raw buffer resource over [p, p + bytes): loads past the end return zero.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);

@@ -153,6 +153,16 @@ __device__ __forceinline__ void store_tile_qkv(const GemmArgs& g, f32x16 (&acc)[
 #pragma unroll
     for (int j = 0; j < 8; ++j) w[j] = 1.f + bf2f(wv[8 * cc + j]);
     bf16_t* C = reinterpret_cast<bf16_t*>(g.C);
+    // q rows go to C (row stride ldc), k rows to the head's cache rows
+    // (stride 128). The buffer resource ends after the last row below M, so
+    // stores of rows past M are dropped by the bounds check and the loop has
+    // no per-row branch (the rows interleave freely).
+    const bf16_t* dbase = sec == 0 ? C + (size_t)rbase * g.ldc + c0
+                                   : a.kc + ((size_t)hh * a.cap + a.q_row0 + rbase) * 128;
+    const uint32_t dstride = sec == 0 ? (uint32_t)g.ldc * 2u : 256u;
+    const __amdgpu_buffer_rsrc_t rdst =
+        make_rsrc(uniform_ptr(dbase), (uint32_t)__builtin_amdgcn_readfirstlane(
+                                          (int)((uint32_t)max(0, min(128, g.M - rbase)) * dstride)));
     // RoPE tables of the lane's 32 rows (R = 4 it + lane/16), loaded up
     // front. Table row of token gq: gq itself before the prefix end P, else
     // P + (gq - P) % T_el (the latent's own layout row); it advances by 4
@@ -183,7 +193,6 @@ __device__ __forceinline__ void store_tile_qkv(const GemmArgs& g, f32x16 (&acc)[
 #pragma unroll
     for (int it = 0; it < 32; ++it) {
       const int R = it * 4 + (lane >> 4);
-      const int m = rbase + R;
       // chunk cc of row R (see store_tile_lds)
       const int pc = cc ^ ((R & (SLOTS - 1)) >> 1);
       u32x4 v = *reinterpret_cast<const u32x4*>(reg + R * ROWB + pc * 16);
@@ -208,10 +217,7 @@ __device__ __forceinline__ void store_tile_qkv(const GemmArgs& g, f32x16 (&acc)[
         o[k] = pack2bf(x0 * c4[k] - x1 * s4[k], x0 * s4[k] + x1 * c4[k]);
       }
       const u32x4 ov = {o[0], o[1], o[2], o[3]};
-      if (m < g.M) {
-        if (sec == 0) *reinterpret_cast<u32x4*>(C + (size_t)m * g.ldc + c0 + 8 * cc) = ov;
-        else *reinterpret_cast<u32x4*>(a.kc + ((size_t)hh * a.cap + a.q_row0 + m) * 128 + 8 * cc) = ov;
-      }
+      __builtin_amdgcn_raw_buffer_store_b128(ov, rdst, (int)((uint32_t)R * dstride + 16u * cc), 0, 0);
     }
   } else {
     // transposed staging: dim row d (128 tokens, 256 bytes), 16-byte token
@@ -220,6 +226,10 @@ __device__ __forceinline__ void store_tile_qkv(const GemmArgs& g, f32x16 (&acc)[
     // lane writes 2 dims x 2 tokens as two 4-byte words (the even-token lane
     // dims +0, +1, the odd-token lane dims +2, +3).
     const bool odd = lrow & 1;
+    // byte selectors of v_perm over {nb, mine}: the even lane keeps its own
+    // low halves in the low half of each word, the odd lane in the high half
+    const uint32_t sel_lo = odd ? 0x01000504u : 0x05040100u;
+    const uint32_t sel_hi = odd ? 0x03020706u : 0x07060302u;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int te = i * 32 + (lrow & ~1);     // even token of the pair
@@ -234,8 +244,8 @@ __device__ __forceinline__ void store_tile_qkv(const GemmArgs& g, f32x16 (&acc)[
                                                                     true);
           const uint32_t mine = odd ? p23 : p01;
           // words (token te, token te+1) for the lane's two dims
-          const uint32_t lo = odd ? ((nb & 0xFFFFu) | (mine << 16)) : ((mine & 0xFFFFu) | (nb << 16));
-          const uint32_t hi = odd ? ((nb >> 16) | (mine & 0xFFFF0000u)) : ((mine >> 16) | (nb & 0xFFFF0000u));
+          const uint32_t lo = __builtin_amdgcn_perm(nb, mine, sel_lo);
+          const uint32_t hi = __builtin_amdgcn_perm(nb, mine, sel_hi);
           const int d = j * 32 + 8 * q + 4 * lhalf + (odd ? 2 : 0);
           const int off = (((te >> 3) ^ (d & 15)) << 4) + (te & 7) * 2;
           *reinterpret_cast<uint32_t*>(reg + d * ROWB + off) = lo;
