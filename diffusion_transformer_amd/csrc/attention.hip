@@ -769,7 +769,7 @@ int device_cus() {
 // resident per CU. With `split`, the units of a last, partly filled round
 // are split over key ranges when that shortens the round (scratch allowing).
 template <int NWV, int QW, int NST>
-hipError_t run_attn2(const AttnArgs& a0, hipStream_t s, bool split) {
+hipError_t run_attn2(const AttnArgs& a0, hipStream_t s, bool split, const LaunchEvents& ev = {}) {
   constexpr int BQ2 = NWV * QW;
   constexpr int per_cu = (NWV == 4 && NST == 2) ? 2 : 1;
   AttnArgs a = a0;
@@ -787,18 +787,19 @@ hipError_t run_attn2(const AttnArgs& a0, hipStream_t s, bool split) {
     }
   }
   const int nblk = a.split_s > 1 ? a.split_base + (units - a.split_base) * a.split_s : units;
-  hipLaunchKernelGGL((attn2_kernel<NWV, QW, NST>), dim3(nblk), dim3(NWV * 64), 0, s, a);
-  if (a.split_s > 1) {
+  const bool comb = a.split_s > 1;
+  launch_k((attn2_kernel<NWV, QW, NST>), dim3(nblk), dim3(NWV * 64), s, ev.start, comb ? nullptr : ev.stop, a);
+  if (comb) {
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(attn_combine_kernel, dim3((units - a.split_base) * (BQ2 / 8)), dim3(256), 0, s,
-                       a, BQ2);
+    launch_k(attn_combine_kernel, dim3((units - a.split_base) * (BQ2 / 8)), dim3(256), s, nullptr, ev.stop,
+             a, BQ2);
   }
   return hipGetLastError();
 }
 
 // The cached-step kernel: same grid and key split as attn2_kernel<8, 32, 3>.
-hipError_t run_attn3(const AttnArgs& a0, hipStream_t s, bool split) {
+hipError_t run_attn3(const AttnArgs& a0, hipStream_t s, bool split, const LaunchEvents& ev = {}) {
   constexpr int BQ2 = 256;
   AttnArgs a = a0;
   const int units = ((a.N + BQ2 - 1) / BQ2) * a.nh;
@@ -814,12 +815,13 @@ hipError_t run_attn3(const AttnArgs& a0, hipStream_t s, bool split) {
     }
   }
   const int nblk = a.split_s > 1 ? a.split_base + (units - a.split_base) * a.split_s : units;
-  hipLaunchKernelGGL(attn3_kernel, dim3(nblk), dim3(512), 0, s, a);
-  if (a.split_s > 1) {
+  const bool comb = a.split_s > 1;
+  launch_k(attn3_kernel, dim3(nblk), dim3(512), s, ev.start, comb ? nullptr : ev.stop, a);
+  if (comb) {
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(attn_combine_kernel, dim3((units - a.split_base) * (BQ2 / 8)), dim3(256), 0, s,
-                       a, BQ2);
+    launch_k(attn_combine_kernel, dim3((units - a.split_base) * (BQ2 / 8)), dim3(256), s, nullptr, ev.stop,
+             a, BQ2);
   }
   return hipGetLastError();
 }
@@ -840,7 +842,7 @@ hipError_t launch_attention_variant(const AttnArgs& a, int variant, hipStream_t 
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
+hipError_t launch_attention(const AttnArgs& a, hipStream_t s, const LaunchEvents& ev) {
   // 256 queries per workgroup (8 waves, one workgroup per CU) unless that
   // leaves CUs idle, then 128-query workgroups two per CU. Target rows of a
   // cached step (q_off > 0) all stream the same keys, so a last, partly
@@ -858,9 +860,9 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
   const bool split = a.q_off > 0;
   AttnArgs b = a;
   b.rev_q = a.q_off == 0;
-  if (blocks256 < 256) return run_attn2<4, 32, 2>(b, s, split);
-  if (a.q_off > 0 && a.q_off == a.P && a.S % BKV == 0) return run_attn3(b, s, split);
-  return run_attn2<8, 32, 3>(b, s, split);
+  if (blocks256 < 256) return run_attn2<4, 32, 2>(b, s, split, ev);
+  if (a.q_off > 0 && a.q_off == a.P && a.S % BKV == 0) return run_attn3(b, s, split, ev);
+  return run_attn2<8, 32, 3>(b, s, split, ev);
 }
 
 

@@ -1,5 +1,6 @@
 // Shared device-side types and helpers for the gfx950 kernels.
 #pragma once
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -118,6 +119,25 @@ __device__ __forceinline__ void lds_barrier() {
 
 // LDS destination pointer of a buffer_load ... lds (address space 3).
 #define LDSP(p) ((__attribute__((address_space(3))) void*)(p))
+
+// One kernel launch; the events, when given, are taken by the kernel's own
+// dispatch packet (start as it starts, stop as it ends), so timing puts no
+// extra packet between kernels.
+template <typename F, typename... Args>
+inline void launch_k(F kernel, dim3 grid, dim3 block, hipStream_t s, hipEvent_t start, hipEvent_t stop,
+                     Args... args) {
+  if (start || stop)
+    hipExtLaunchKernelGGL(kernel, grid, block, 0u, s, start, stop, 0u, args...);
+  else
+    hipLaunchKernelGGL(kernel, grid, block, 0, s, args...);
+}
+
+// The events of a launch with nothing to run (empty input), so that a
+// timed launch always records both.
+inline void mark_empty(const LaunchEvents& ev, hipStream_t s) {
+  if (ev.start) hipEventRecord(ev.start, s);
+  if (ev.stop) hipEventRecord(ev.stop, s);
+}
 
 // A pointer the caller knows to be the same in every lane, moved to scalar
 // registers (so a buffer resource built from it needs no per-lane loop).

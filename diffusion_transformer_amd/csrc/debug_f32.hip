@@ -120,7 +120,7 @@ bool gemm_shape_ok(int M, int N, int K, int epi) {
   return N % 64 == 0;
 }
 
-hipError_t launch_gemm(const GemmArgs& g, int epi, hipStream_t s) {
+static hipError_t gemm_sequence(const GemmArgs& g, int epi, hipStream_t s) {
   switch (epi) {
     case EPI_BF16: return run_f32<EPI_BF16>(g, s);
     case EPI_RESID: return run_f32<EPI_RESID>(g, s);
@@ -138,11 +138,18 @@ hipError_t launch_gemm(const GemmArgs& g, int epi, hipStream_t s) {
   return hipErrorInvalidValue;
 }
 
+hipError_t launch_gemm(const GemmArgs& g, int epi, hipStream_t s, const LaunchEvents& ev) {
+  if (ev.start) hipEventRecord(ev.start, s);
+  const hipError_t e = gemm_sequence(g, epi, s);
+  if (ev.stop) hipEventRecord(ev.stop, s);
+  return e;
+}
+
 hipError_t launch_gemm_forced_split(const GemmArgs&, int, int, hipStream_t) { return hipErrorInvalidValue; }
 
-hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
+hipError_t launch_attention(const AttnArgs& a, hipStream_t s, const LaunchEvents& ev) {
   dim3 grid((a.N + 3) / 4, a.nh);
-  hipLaunchKernelGGL(attn_f32_kernel, grid, dim3(256), 0, s, a);
+  launch_k(attn_f32_kernel, grid, dim3(256), s, ev.start, ev.stop, a);
   return hipGetLastError();
 }
 

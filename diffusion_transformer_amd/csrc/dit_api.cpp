@@ -150,12 +150,17 @@ Plan plan(const dit_config& c, int n) {
   return p;
 }
 
+// Timing of one launch of a profiled kernel class: a pair of events that
+// the launcher records on its kernels' dispatch packets (ev()), or, for the
+// launchers that take no events, that are recorded into the stream around
+// the launch (by_launch = false).
 struct Timed {
   dit_model* m;
   int cls;
   hipStream_t s;
-  bool on;
-  Timed(dit_model* m_, int cls_, hipStream_t s_) : m(m_), cls(cls_), s(s_), on(m_ && m_->prof_class == cls_) {
+  bool on, by_launch;
+  Timed(dit_model* m_, int cls_, hipStream_t s_, bool by_launch_ = true)
+      : m(m_), cls(cls_), s(s_), on(m_ && m_->prof_class == cls_), by_launch(by_launch_) {
     if (!on) return;
     if (m->ev_used == m->ev_start.size()) {
       hipEvent_t a, b;
@@ -163,11 +168,19 @@ struct Timed {
       m->ev_start.push_back(a);
       m->ev_stop.push_back(b);
     }
-    hipEventRecord(m->ev_start[m->ev_used], s);
+    if (!by_launch) hipEventRecord(m->ev_start[m->ev_used], s);
+  }
+  LaunchEvents ev() const {
+    LaunchEvents e;
+    if (on && by_launch) {
+      e.start = m->ev_start[m->ev_used];
+      e.stop = m->ev_stop[m->ev_used];
+    }
+    return e;
   }
   ~Timed() {
     if (!on) return;
-    hipEventRecord(m->ev_stop[m->ev_used], s);
+    if (!by_launch) hipEventRecord(m->ev_stop[m->ev_used], s);
     m->ev_used++;
   }
 };
@@ -219,20 +232,20 @@ dit_status run_step(dit_model* m, const dit_seq* seq, bool extract, const float*
   LAUNCH(launch_temb(t, t_pre, c.time_dim, c.rope_base, te, st), "temb");
   {
     Timed tm(tmm, DIT_PROF_GEMV, st);
-    LAUNCH(launch_gemv(U(m->t1), H, c.time_dim, te, c.time_dim, nv, a1, H, a1s, st), "gemv t1");
+    LAUNCH(launch_gemv(U(m->t1), H, c.time_dim, te, c.time_dim, nv, a1, H, a1s, st, tm.ev()), "gemv t1");
   }
   {
     Timed tm(tmm, DIT_PROF_GEMV, st);
-    LAUNCH(launch_gemv(U(m->t2), H, H, a1s, H, nv, tb, H, tbs, st), "gemv t2");
+    LAUNCH(launch_gemv(U(m->t2), H, H, a1s, H, nv, tb, H, tbs, st, tm.ev()), "gemv t2");
   }
   {
     Timed tm(tmm, DIT_PROF_GEMV_MOD, st);
-    LAUNCH(launch_gemv(U(m->mod), 4 * H, H, tbs, H, nv, mod, 4 * H, nullptr, st), "gemv mod");
+    LAUNCH(launch_gemv(U(m->mod), 4 * H, H, tbs, H, nv, mod, 4 * H, nullptr, st, tm.ev()), "gemv mod");
   }
   LAUNCH(launch_gate_tanh(mod, H, nv, st), "gate tanh");
   {
     Timed tm(tmm, DIT_PROF_GEMV, st);
-    LAUNCH(launch_gemv(U(m->so), H, H, tbs, H, 1, scale_out, H, nullptr, st), "gemv so");
+    LAUNCH(launch_gemv(U(m->so), H, H, tbs, H, 1, scale_out, H, nullptr, st, tm.ev()), "gemv so");
   }
   const float* row_t = mod;
   const float* row_0 = extract ? mod + 4 * H : mod;
@@ -242,7 +255,7 @@ dit_status run_step(dit_model* m, const dit_seq* seq, bool extract, const float*
     LAUNCH(hipMemcpyAsync(hbuf, prefix, (size_t)P * H * 4, hipMemcpyDeviceToDevice, st), "prefix copy");
   {
     Timed tm(tmm, DIT_PROF_IMG_IN, st);
-    LAUNCH(launch_img_in(U(m->img_in), x, TB, H, hbuf + (size_t)n_pre * H, H, st), "img_in");
+    LAUNCH(launch_img_in(U(m->img_in), x, TB, H, hbuf + (size_t)n_pre * H, H, st, tm.ev()), "img_in");
   }
 
   for (int l = 0; l < L; ++l) {
@@ -250,7 +263,7 @@ dit_status run_step(dit_model* m, const dit_seq* seq, bool extract, const float*
     act_t* vl = vbase + (size_t)l * nh * 128 * cap;
     {
       Timed tm(tmm, DIT_PROF_LN, st);
-      LAUNCH(launch_ln_mod(hbuf, H, N, H, row_t, row_0, n_pre, c.eps, xb, H, st), "ln1");
+      LAUNCH(launch_ln_mod(hbuf, H, N, H, row_t, row_0, n_pre, c.eps, xb, H, st, tm.ev()), "ln1");
     }
     // QKV projection with the per-head QK-RMSNorm, RoPE and K / Vᵀ cache
     // writes of tokens q_row0 .. q_row0+N-1 fused into its epilogue
@@ -268,11 +281,11 @@ dit_status run_step(dit_model* m, const dit_seq* seq, bool extract, const float*
       g.C = qkv; g.ldc = 3 * H;
       g.part = part; g.part_bytes = kGemmPartBytes;
       g.qk = q;
-      LAUNCH(launch_gemm(g, EPI_QKV, st), "gemm qkv");
+      LAUNCH(launch_gemm(g, EPI_QKV, st, tm.ev()), "gemm qkv");
     }
     if (extract && cap > SA) {
       // cache keys SA .. cap-1 (capacity padding) are zero-filled
-      Timed tm(tmm, DIT_PROF_QKNORM_ROPE, st);
+      Timed tm(tmm, DIT_PROF_QKNORM_ROPE, st, false);
       QkArgs z = q;
       z.g_begin = SA; z.g_end = cap;
       LAUNCH(launch_qknorm_rope(z, st), "cache padding");
@@ -284,7 +297,7 @@ dit_status run_step(dit_model* m, const dit_seq* seq, bool extract, const float*
       a.k = kl; a.vt = vl; a.cap = cap; a.S = S; a.nh = nh; a.limit = seq->d_row_limit;
       a.out = att; a.out_stride = H; a.P = P; a.T_el = T;
       a.part = part; a.part_bytes = kGemmPartBytes;   // free between the GEMMs
-      LAUNCH(launch_attention(a, st), "attention");
+      LAUNCH(launch_attention(a, st, tm.ev()), "attention");
     }
     {
       Timed tm(tmm, DIT_PROF_GEMM_O, st);
@@ -292,11 +305,11 @@ dit_status run_step(dit_model* m, const dit_seq* seq, bool extract, const float*
       g.A = att; g.lda = H; g.B = U(m->o[l]); g.ldb = H; g.M = N; g.N = H; g.K = H;
       g.Hres = hbuf; g.ldh = H; g.gate_t = row_t + H; g.gate_0 = row_0 + H; g.n_pre = n_pre;
       g.part = part; g.part_bytes = kGemmPartBytes;
-      LAUNCH(launch_gemm(g, EPI_RESID, st), "gemm o");
+      LAUNCH(launch_gemm(g, EPI_RESID, st, tm.ev()), "gemm o");
     }
     {
       Timed tm(tmm, DIT_PROF_LN, st);
-      LAUNCH(launch_ln_mod(hbuf, H, N, H, row_t + 2 * H, row_0 + 2 * H, n_pre, c.eps, xb, H, st), "ln2");
+      LAUNCH(launch_ln_mod(hbuf, H, N, H, row_t + 2 * H, row_0 + 2 * H, n_pre, c.eps, xb, H, st, tm.ev()), "ln2");
     }
     {
       Timed tm(tmm, DIT_PROF_GEMM_GATEUP, st);
@@ -304,7 +317,7 @@ dit_status run_step(dit_model* m, const dit_seq* seq, bool extract, const float*
       g.A = xb; g.lda = H; g.B = U(m->gate[l]); g.B2 = U(m->up[l]); g.ldb = H;
       g.M = N; g.N = 2 * F; g.K = H; g.C = ffn; g.ldc = F;
       g.part = part; g.part_bytes = kGemmPartBytes;
-      LAUNCH(launch_gemm(g, EPI_SWIGLU, st), "gemm gate/up");
+      LAUNCH(launch_gemm(g, EPI_SWIGLU, st, tm.ev()), "gemm gate/up");
     }
     {
       Timed tm(tmm, DIT_PROF_GEMM_DOWN, st);
@@ -312,7 +325,7 @@ dit_status run_step(dit_model* m, const dit_seq* seq, bool extract, const float*
       g.A = ffn; g.lda = F; g.B = U(m->down[l]); g.ldb = F; g.M = N; g.N = H; g.K = F;
       g.Hres = hbuf; g.ldh = H; g.gate_t = row_t + 3 * H; g.gate_0 = row_0 + 3 * H; g.n_pre = n_pre;
       g.part = part; g.part_bytes = kGemmPartBytes;
-      LAUNCH(launch_gemm(g, EPI_RESID, st), "gemm down");
+      LAUNCH(launch_gemm(g, EPI_RESID, st, tm.ev()), "gemm down");
     }
   }
 
@@ -329,7 +342,8 @@ dit_status run_step(dit_model* m, const dit_seq* seq, bool extract, const float*
 #else
   {
     Timed tm(tmm, DIT_PROF_FINAL, st);
-    LAUNCH(launch_final_out(hbuf + (size_t)n_pre * H, H, TB, H, scale_out, c.eps, U(m->proj_out), v_out, st),
+    LAUNCH(launch_final_out(hbuf + (size_t)n_pre * H, H, TB, H, scale_out, c.eps, U(m->proj_out), v_out, st,
+                            tm.ev()),
            "final adaln + proj_out");
   }
 #endif

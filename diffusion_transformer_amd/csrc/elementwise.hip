@@ -283,10 +283,13 @@ __global__ void euler_kernel(float* __restrict__ x, const float* __restrict__ v,
 
 hipError_t launch_ln_mod(const float* h, int ldh, int rows, int H, const float* scale_t,
                          const float* scale_0, int n_pre, float eps, act_t* out, int ldo,
-                         hipStream_t s) {
-  if (rows <= 0) return hipSuccess;
-  hipLaunchKernelGGL(ln_mod_kernel, dim3((rows + LN_ROWS - 1) / LN_ROWS), dim3(LN_NT), 0, s, h, ldh, rows,
-                     H, scale_t, scale_0, n_pre, eps, out, ldo);
+                         hipStream_t s, const LaunchEvents& ev) {
+  if (rows <= 0) {
+    mark_empty(ev, s);
+    return hipSuccess;
+  }
+  launch_k(ln_mod_kernel, dim3((rows + LN_ROWS - 1) / LN_ROWS), dim3(LN_NT), s, ev.start, ev.stop, h, ldh,
+           rows, H, scale_t, scale_0, n_pre, eps, out, ldo);
   return hipGetLastError();
 }
 
@@ -299,10 +302,10 @@ hipError_t launch_qknorm_rope(const QkArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_gemv(const uint16_t* W, int O, int I, const float* X, int ldx, int nv, float* Y,
-                       int ldy, float* Ys, hipStream_t s) {
+                       int ldy, float* Ys, hipStream_t s, const LaunchEvents& ev) {
   if (I > GV_MAXC * 512 || I % 8 || nv < 1 || nv > 2) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(gemv_kernel, dim3((O + 4 * GV_ROWS - 1) / (4 * GV_ROWS)), dim3(256), 0, s, W, O, I, X,
-                     ldx, nv, Y, ldy, Ys);
+  launch_k(gemv_kernel, dim3((O + 4 * GV_ROWS - 1) / (4 * GV_ROWS)), dim3(256), s, ev.start, ev.stop, W, O,
+           I, X, ldx, nv, Y, ldy, Ys);
   return hipGetLastError();
 }
 

@@ -530,9 +530,9 @@ __global__ __launch_bounds__(256) void gemm_w4_kernel(GemmArgs g) {
 }
 
 template <int EPI, bool PACKED = (EPI == EPI_SWIGLU)>
-hipError_t run_w4(const GemmArgs& g, hipStream_t s) {
+hipError_t run_w4(const GemmArgs& g, hipStream_t s, const LaunchEvents& ev = {}) {
   const int nblk = ((g.M + 255) / 256) * (g.N / 256) * (EPI == EPI_PART ? g.splits : 1);
-  hipLaunchKernelGGL((gemm_w4_kernel<EPI, PACKED>), dim3(nblk), dim3(256), 0, s, g);
+  launch_k((gemm_w4_kernel<EPI, PACKED>), dim3(nblk), dim3(256), s, ev.start, ev.stop, g);
   return hipGetLastError();
 }
 
@@ -591,15 +591,12 @@ hipError_t run_reduce(const GemmArgs& g, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <int EPI>
-hipError_t run_main(const GemmArgs& g, hipStream_t s) { return run_w4<EPI>(g, s); }
-
-hipError_t run_epi(const GemmArgs& g, int epi, hipStream_t s) {
+hipError_t run_epi(const GemmArgs& g, int epi, hipStream_t s, const LaunchEvents& ev = {}) {
   switch (epi) {
-    case EPI_BF16: return run_main<EPI_BF16>(g, s);
-    case EPI_RESID: return run_main<EPI_RESID>(g, s);
-    case EPI_SWIGLU: return run_main<EPI_SWIGLU>(g, s);
-    case EPI_QKV: return run_main<EPI_QKV>(g, s);
+    case EPI_BF16: return run_w4<EPI_BF16>(g, s, ev);
+    case EPI_RESID: return run_w4<EPI_RESID>(g, s, ev);
+    case EPI_SWIGLU: return run_w4<EPI_SWIGLU>(g, s, ev);
+    case EPI_QKV: return run_w4<EPI_QKV>(g, s, ev);
   }
   return hipErrorInvalidValue;
 }
@@ -654,7 +651,7 @@ hipError_t launch_gemm_forced_split(const GemmArgs& g, int epi, int splits, hipS
   return launch_gemm_split(g, epi, 1, splits, s);
 }
 
-hipError_t launch_gemm(const GemmArgs& g, int epi, hipStream_t s) {
+hipError_t launch_gemm(const GemmArgs& g, int epi, hipStream_t s, const LaunchEvents& ev) {
   if (epi == EPI_F32) return hipErrorInvalidValue;
   // One block tile per CU per round: when the tiles leave the last round
   // mostly idle and dropping the last r row blocks makes the rest whole
@@ -670,9 +667,14 @@ hipError_t launch_gemm(const GemmArgs& g, int epi, hipStream_t s) {
     while (r && 2 * splits * r * ntn <= kRound && (g.K / 64) % (2 * splits) == 0 &&
            (size_t)(2 * splits) * g.N * (size_t)(g.M - (ntm - r) * 256) * 4 <= g.part_bytes)
       splits *= 2;
-    if (r && splits > 1) return launch_gemm_split(g, epi, r, splits, s);
+    if (r && splits > 1) {
+      if (ev.start) hipEventRecord(ev.start, s);
+      const hipError_t e = launch_gemm_split(g, epi, r, splits, s);
+      if (ev.stop) hipEventRecord(ev.stop, s);
+      return e;
+    }
   }
-  return run_epi(g, epi, s);
+  return run_epi(g, epi, s, ev);
 }
 
 }  // namespace dit

@@ -291,21 +291,27 @@ __global__ __launch_bounds__(256) void final_out_kernel(const float* __restrict_
 }  // namespace
 
 hipError_t launch_img_in(const uint16_t* W, const float* x, int n, int H, float* out, int ldo,
-                         hipStream_t s) {
-  if (n <= 0) return hipSuccess;
+                         hipStream_t s, const LaunchEvents& ev) {
+  if (n <= 0) {
+    mark_empty(ev, s);
+    return hipSuccess;
+  }
   dim3 grid(H / 256, (n + 63) / 64);
-  hipLaunchKernelGGL(img_in_kernel, grid, dim3(256), 0, s, W, x, n, out, ldo);
+  launch_k(img_in_kernel, grid, dim3(256), s, ev.start, ev.stop, W, x, n, out, ldo);
   return hipGetLastError();
 }
 
 hipError_t launch_final_out(const float* h, int ldh, int rows, int H, const float* scale, float eps,
-                            const uint16_t* W, float* v, hipStream_t s) {
-  if (rows <= 0) return hipSuccess;
+                            const uint16_t* W, float* v, hipStream_t s, const LaunchEvents& ev) {
+  if (rows <= 0) {
+    mark_empty(ev, s);
+    return hipSuccess;
+  }
   const dim3 grid((rows + FO_ROWS - 1) / FO_ROWS);
   if (H == 4096)
-    hipLaunchKernelGGL(final_out_kernel<4096>, grid, dim3(256), 0, s, h, ldh, rows, H, scale, eps, W, v);
+    launch_k(final_out_kernel<4096>, grid, dim3(256), s, ev.start, ev.stop, h, ldh, rows, H, scale, eps, W, v);
   else
-    hipLaunchKernelGGL(final_out_kernel<0>, grid, dim3(256), 0, s, h, ldh, rows, H, scale, eps, W, v);
+    launch_k(final_out_kernel<0>, grid, dim3(256), s, ev.start, ev.stop, h, ldh, rows, H, scale, eps, W, v);
   return hipGetLastError();
 }
 

@@ -59,7 +59,14 @@ struct GemmArgs {
 // to attention's key split (256 x 129 floats per piece).
 constexpr size_t kGemmPartBytes = (size_t)256 * 256 * 256 * 4;
 
-hipError_t launch_gemm(const GemmArgs& g, int epi, hipStream_t s);
+// Timing events of one launch sequence: `start` is taken when its first
+// kernel starts and `stop` when its last one ends, by those kernels' own
+// dispatch packets (a multi-kernel GEMM split records them into the stream
+// around its kernels instead). Null events are not recorded.
+struct LaunchEvents {
+  hipEvent_t start = nullptr, stop = nullptr;
+};
+hipError_t launch_gemm(const GemmArgs& g, int epi, hipStream_t s, const LaunchEvents& ev = {});
 // The last 256-row block (or the whole GEMM, if smaller) as `splits` K
 // splits into g.part, reduced with the epilogue; the rows before it in one
 // ordinary launch. The caller checks K / 64 % splits == 0 and the scratch.
@@ -86,20 +93,20 @@ struct AttnArgs {
   int split_base, split_s;
   int rev_q;                        // 1: a head's query blocks run last block first
 };
-hipError_t launch_attention(const AttnArgs& a, hipStream_t s);
+hipError_t launch_attention(const AttnArgs& a, hipStream_t s, const LaunchEvents& ev = {});
 hipError_t launch_attention_variant(const AttnArgs& a, int variant, hipStream_t s);
 hipError_t launch_debug_mask(const int32_t* limit, int S, uint8_t* mask, hipStream_t s);
 
 // LN(h)·(1 + scale[row]) -> act_t. rows < n_pre use scale_0, others scale_t.
 hipError_t launch_ln_mod(const float* h, int ldh, int rows, int H, const float* scale_t,
                          const float* scale_0, int n_pre, float eps, act_t* out, int ldo,
-                         hipStream_t s);
+                         hipStream_t s, const LaunchEvents& ev = {});
 
 
 // Y[v][o] = W[o]·X[v] for v < nv (W bf16 [O, I]); optionally also writes
 // silu(Y) to Ys.
 hipError_t launch_gemv(const uint16_t* W, int O, int I, const float* X, int ldx, int nv,
-                       float* Y, int ldy, float* Ys, hipStream_t s);
+                       float* Y, int ldy, float* Ys, hipStream_t s, const LaunchEvents& ev = {});
 // [cos(t_v f_i), sin(t_v f_i)], f_i = base^(-2i/D), computed in double.
 hipError_t launch_temb(float t0, float t1, int D, float base, float* out, hipStream_t s);
 // z[r][c] = (z - mean[c]) / std[c] (inverse: z * std[c] + mean[c]), in place.
@@ -109,12 +116,12 @@ hipError_t launch_standardize(float* z, const float* mean, const float* std, lon
 hipError_t launch_gate_tanh(float* mod, int H, int nv, hipStream_t s);
 // hidden[i][n] = Σ_c W[n][c] x[i][c]; W bf16 [H, 64], x f32 [n, 64], fp32 out.
 hipError_t launch_img_in(const uint16_t* W, const float* x, int n, int H, float* out, int ldo,
-                         hipStream_t s);
+                         hipStream_t s, const LaunchEvents& ev = {});
 // v[i] = W_out · (LN(h[i]) · (1 + scale)) for rows < rows: LN non-affine
 // over H (<= 4096, % 256 == 0), the scaled row rounded to bf16, W_out bf16
 // [64, H], v fp32 [rows, 64].
 hipError_t launch_final_out(const float* h, int ldh, int rows, int H, const float* scale, float eps,
-                            const uint16_t* W, float* v, hipStream_t s);
+                            const uint16_t* W, float* v, hipStream_t s, const LaunchEvents& ev = {});
 hipError_t launch_euler(float* x, const float* v, float dsig, long long n, hipStream_t s);
 // dst = src, bytes % 16 == 0, 16-byte accesses.
 hipError_t launch_stream_copy(const void* src, void* dst, size_t bytes, hipStream_t s);
