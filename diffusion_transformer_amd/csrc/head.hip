@@ -23,7 +23,7 @@ namespace {
 // of 16. Operands come straight from global memory (the 16 KB of latents of
 // a workgroup and the 32 KB of weight rows are cache hits for all but the
 // first wave that touches them); the result is written row by row through
-// LDS.
+// LDS, one 32-token half at a time.
 __device__ __forceinline__ void split3(const float (&x)[8], bf16x8& hi, bf16x8& mid, bf16x8& lo) {
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
@@ -44,18 +44,11 @@ constexpr int IMG_LD = 68;   // floats per staged row (64 + 4 of padding)
 __global__ __launch_bounds__(256) void img_in_kernel(const uint16_t* __restrict__ W,
                                                      const float* __restrict__ x, int n,
                                                      float* __restrict__ out, int ldo) {
-  __shared__ __align__(16) float img_smem[4 * 64 * IMG_LD];
+  __shared__ __align__(16) float img_smem[4 * 32 * IMG_LD];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int l32 = lane & 31, lh = lane >> 5;
   const int t0 = blockIdx.y * 64;
   const int c0 = blockIdx.x * 256 + wave * 64;
-  f32x16 acc[2][2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
   // B fragments: lane supplies W[c0 + 32j + l32][16s + 8lh .. +7]
   bf16x8 wb[2][4];
 #pragma unroll
@@ -64,8 +57,16 @@ __global__ __launch_bounds__(256) void img_in_kernel(const uint16_t* __restrict_
     for (int s = 0; s < 4; ++s)
       wb[j][s] = __builtin_bit_cast(
           bf16x8, *reinterpret_cast<const u32x4*>(W + (size_t)(c0 + 32 * j + l32) * 64 + 16 * s + 8 * lh));
+  float* pt = img_smem + wave * 32 * IMG_LD;
+  // the two 32-token halves one after the other: half the accumulators and
+  // half the staging space, so four workgroups fit on a CU
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
+    f32x16 acc[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[j][r] = 0.f;
     const int t = t0 + 32 * i + l32;
     const bool ok = t < n;
 #pragma unroll
@@ -78,36 +79,35 @@ __global__ __launch_bounds__(256) void img_in_kernel(const uint16_t* __restrict_
         xv[4] = b.x; xv[5] = b.y; xv[6] = b.z; xv[7] = b.w;
       } else {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) xv[j] = 0.f;
+        for (int k = 0; k < 8; ++k) xv[k] = 0.f;
       }
       bf16x8 hi, mid, lo;
       split3(xv, hi, mid, lo);
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
-        acc[i][j] = mfma32(lo, wb[j][s], acc[i][j]);
-        acc[i][j] = mfma32(mid, wb[j][s], acc[i][j]);
-        acc[i][j] = mfma32(hi, wb[j][s], acc[i][j]);
+        acc[j] = mfma32(lo, wb[j][s], acc[j]);
+        acc[j] = mfma32(mid, wb[j][s], acc[j]);
+        acc[j] = mfma32(hi, wb[j][s], acc[j]);
       }
     }
-  }
-  // Register r of lane l holds row 8(r/4) + 4lh + r%4 of its block, column
-  // l32. The wave's 64 x 64 patch goes through LDS (rows padded to 272 bytes)
-  // so that every store instruction writes four whole 256-byte row segments.
-  float* pt = img_smem + wave * 64 * IMG_LD;
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
+    // Register r of lane l holds row 8(r/4) + 4lh + r%4 of its block,
+    // column l32. The wave's 32 x 64 half goes through LDS (rows padded to
+    // 272 bytes) so that every store instruction writes four whole 256-byte
+    // row segments.
+    if (i) __builtin_amdgcn_s_waitcnt(kWaitLgkm0);   // the first half's reads are done
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r)
-        pt[(32 * i + 8 * (r >> 2) + 4 * lh + (r & 3)) * IMG_LD + 32 * j + l32] = acc[i][j][r];
-  __builtin_amdgcn_s_waitcnt(kWaitLgkm0);   // the region is private to this wave
+        pt[(8 * (r >> 2) + 4 * lh + (r & 3)) * IMG_LD + 32 * j + l32] = acc[j][r];
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);   // the region is private to this wave
 #pragma unroll
-  for (int it = 0; it < 16; ++it) {
-    const int row = 4 * it + (lane >> 4);
-    const int t = t0 + row;
-    const float4 v4 = *reinterpret_cast<const float4*>(pt + row * IMG_LD + 4 * (lane & 15));
-    if (t < n) *reinterpret_cast<float4*>(out + (size_t)t * ldo + c0 + 4 * (lane & 15)) = v4;
+    for (int it = 0; it < 8; ++it) {
+      const int row = 4 * it + (lane >> 4);
+      const int tr = t0 + 32 * i + row;
+      const float4 v4 = *reinterpret_cast<const float4*>(pt + row * IMG_LD + 4 * (lane & 15));
+      if (tr < n) *reinterpret_cast<float4*>(out + (size_t)tr * ldo + c0 + 4 * (lane & 15)) = v4;
+    }
   }
 }
 
