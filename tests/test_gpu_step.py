@@ -571,3 +571,46 @@ def test_peaked_attention_loop_matches_oracle(dev):
         say(f"  step {k} {r['mode']}: v rel {e_v:.3e}  x rel {e_x:.3e}")
         assert e_v < TOL_BF16 and e_x < TOL_BF16
     rt.close()
+
+
+@pytest.mark.parametrize("name", ["c0w", "c1"])
+def test_per_kernel_timing_hooks(dev, name):
+    """dit_profile_enable / dit_profile_read for every kernel class: one
+    extract plus one cached step record one event pair per launch of that
+    class (on the kernel's own dispatch packet, or around a multi-kernel
+    split-K sequence), each with a positive duration that fits in the two
+    steps, and the outputs are bitwise those of an untimed run."""
+    cfg, W, I, rt, seq, pre, x0 = build(name, dev)
+    nl = cfg["n_layers"]
+    sig = cfg["sigmas"]
+    cache = rt.alloc_cache(seq)
+    ws = rt.alloc_workspace(seq.S_all)
+    pad = L.dit_kv_capacity(seq.S_all) > seq.S_all
+    per_step = {"gemm_qkv": nl, "gemm_o": nl, "gemm_gateup": nl, "gemm_down": nl, "attention": nl,
+                "ln": 2 * nl, "final": 1, "img_in": 1, "gemv": 3, "gemv_mod": 1}
+
+    def two_steps(cls):
+        L.dit_profile_enable(rt.model, cls)
+        x = x0.clone()
+        v0, v1 = torch.empty_like(x), torch.empty_like(x)
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        rt.step_extract(seq, pre, x, sig[0], cache, v0, ws)
+        rt.step_cached(seq, x, sig[1], cache, v1, ws)
+        b.record()
+        torch.cuda.synchronize()
+        ms, n = L.dit_profile_read(rt.model)
+        L.dit_profile_enable(rt.model, "off")
+        return v0, v1, ms, n, a.elapsed_time(b)
+
+    ref0, ref1, ms, n, _ = two_steps("off")
+    assert n == 0 and ms == 0.0
+    for cls in list(L.PROF)[1:]:
+        v0, v1, ms, n, wall = two_steps(cls)
+        want = 2 * per_step.get(cls, 0) + (nl if cls == "qknorm_rope" and pad else 0)
+        say(f"{name} {cls}: {n} launches, {ms:.4f} ms of {wall:.3f} ms")
+        assert n == want, (cls, n, want)
+        if n:
+            assert 0.0 < ms < wall, (cls, ms, wall)
+        assert torch.equal(v0, ref0) and torch.equal(v1, ref1), cls
