@@ -82,16 +82,24 @@ __device__ __forceinline__ void store_tile_lds(const GemmArgs& g, f32x16 (&acc)[
   constexpr int CPR = ROWB / 16;           // chunks per row
   constexpr int RPI = 64 / CPR;            // rows per instruction
   const int cc = lane % CPR;
-  bf16_t* C = reinterpret_cast<bf16_t*>(g.C);
-  const int col0 = (EPI == EPI_SWIGLU ? (n0 >> 1) + wn * 64 : n0 + wn * 128) + 8 * cc;
-#pragma unroll 4
+  // The patch's rows through a buffer resource that ends after the last row
+  // below M: stores of rows past M are dropped by the bounds check (the row
+  // is in the checked per-lane offset), so no store sits behind a branch and
+  // the LDS reads of several rows can be in flight at once.
+  const int mrow0 = m0 + wm * 128;
+  const bf16_t* cbase = reinterpret_cast<const bf16_t*>(g.C) + (size_t)mrow0 * g.ldc +
+                        (EPI == EPI_SWIGLU ? (n0 >> 1) + wn * 64 : n0 + wn * 128);
+  const uint32_t rowb = (uint32_t)g.ldc * 2u;
+  const __amdgpu_buffer_rsrc_t rC = make_rsrc(
+      uniform_ptr(cbase),
+      (uint32_t)__builtin_amdgcn_readfirstlane((int)((uint32_t)max(0, min(128, g.M - mrow0)) * rowb)));
+#pragma unroll
   for (int q = 0; q < 128 / RPI; ++q) {
     const int R = q * RPI + lane / CPR;
     const int pc = cc ^ ((R & (SLOTS - 1)) >> 1);
     u32x4 v = *reinterpret_cast<const u32x4*>(reg + R * ROWB + pc * 16);
     if (R & 1) v = (u32x4){v.z, v.w, v.x, v.y};
-    const int m = m0 + wm * 128 + R;
-    if (m < g.M) *reinterpret_cast<u32x4*>(C + (size_t)m * g.ldc + col0) = v;
+    __builtin_amdgcn_raw_buffer_store_b128(v, rC, (int)((uint32_t)R * rowb + 16u * cc), 0, 0);
   }
 }
 
@@ -297,15 +305,24 @@ __device__ __forceinline__ void store_tile_lds_f32(const GemmArgs& g, f32x16 (&a
   }
   float* out = PART ? g.part + (size_t)split * g.M * g.N : g.Hres;
   const int ldo = PART ? g.N : g.ldh;
+  // The patch's rows (residual or partial sums) through a buffer resource
+  // that ends after the last row below M: rows past M read as zero and their
+  // stores are dropped by the bounds check (the row is in the checked
+  // per-lane offset), so no load or store sits behind a branch.
+  const int mrow0 = m0 + wm * 128;
+  const uint32_t rowb = (uint32_t)ldo * 4u;
+  const __amdgpu_buffer_rsrc_t rO = make_rsrc(
+      uniform_ptr(out + (size_t)mrow0 * ldo + n0 + wn * 128),
+      (uint32_t)__builtin_amdgcn_readfirstlane((int)((uint32_t)max(0, min(128, g.M - mrow0)) * rowb)));
 #pragma unroll
   for (int hf = 0; hf < 2; ++hf) {
     const int mb = m0 + wm * 128 + hf * 64 + (lane >> 5);
     float4 hv[32];
 #pragma unroll
     for (int t = 0; t < 32; ++t) {
-      const int m = mb + 2 * t;
-      hv[t] = (!PART && m < g.M) ? *reinterpret_cast<const float4*>(g.Hres + (size_t)m * g.ldh + n)
-                                 : make_float4(0.f, 0.f, 0.f, 0.f);
+      const uint32_t off = (uint32_t)(hf * 64 + 2 * t + (lane >> 5)) * rowb + 16u * cc;
+      hv[t] = PART ? make_float4(0.f, 0.f, 0.f, 0.f)
+                   : __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(rO, (int)off, 0, 0));
     }
 #pragma unroll
     for (int ii = 0; ii < 2; ++ii) {
@@ -336,7 +353,8 @@ __device__ __forceinline__ void store_tile_lds_f32(const GemmArgs& g, f32x16 (&a
         h.z += gt.z * a.z;
         h.w += gt.w * a.w;
       }
-      if (m < g.M) *reinterpret_cast<float4*>(out + (size_t)m * ldo + n) = h;
+      const uint32_t off = (uint32_t)(hf * 64 + R) * rowb + 16u * cc;
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, h), rO, (int)off, 0, 0);
     }
     __builtin_amdgcn_s_waitcnt(kWaitLgkm0);   // reads done before the next half overwrites
   }
