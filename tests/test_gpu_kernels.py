@@ -44,6 +44,26 @@ def test_gemm_exact_small_integers(dev, M, N, K, splits):
     assert torch.equal(Cd.float().cpu(), want)
 
 
+@pytest.mark.parametrize("M,N,K", [(600, 512, 16384), (4096, 4096, 16384)])
+def test_long_k_gemm_exact_small_integers(dev, M, N, K):
+    """The down projection's K (16384, 256 K stages): with entries in
+    {-1, 0, 1} every partial sum is an integer below 2^24, exact in fp32, so
+    the output is the integer product rounded once to bf16 (round to nearest
+    even), bit for bit; at 4096 x 4096 a sample of rows is checked."""
+    say(f"long-K gemm exact M={M} N={N} K={K}")
+    g = torch.Generator().manual_seed(M + N + K)
+    A = torch.randint(-1, 2, (M, K), generator=g).to(torch.float32)
+    B = torch.randint(-1, 2, (N, K), generator=g).to(torch.float32)
+    Ad, Bd = A.to(dev, torch.bfloat16), B.to(dev, torch.bfloat16)
+    Cd = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    L.dit_debug_gemm("bf16", M, N, K, Ad, Bd, Cd)
+    torch.cuda.synchronize()
+    rows = torch.arange(M) if M <= 1024 else torch.from_numpy(
+        np.sort(np.random.default_rng(3).choice(M, 96, replace=False)))
+    want = (A[rows].to(torch.int64) @ B.to(torch.int64).T).to(torch.float32).to(torch.bfloat16)
+    assert torch.equal(Cd.cpu()[rows].view(torch.int16), want.view(torch.int16))
+
+
 def test_gemm_random_full_shape_sampled(dev):
     """QKV-shaped GEMM (4096 x 12288 x 4096) with N(0,1) bf16 inputs; sampled
     outputs against fp64 dot products of the same bf16 values."""
