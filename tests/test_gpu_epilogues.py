@@ -148,7 +148,7 @@ def test_img_in_is_fp32_exact(dev, n):
 
 @pytest.mark.parametrize("splits", [0, 2, 4])
 @pytest.mark.parametrize("M,N,K,n_pre", [(700, 512, 512, 300), (256, 256, 64, 0),
-                                         (37, 768, 1024, 37), (300, 512, 16384, 100)])
+                                         (37, 768, 1024, 37), (256, 512, 16384, 100)])
 def test_residual_epilogue(dev, M, N, K, n_pre, splits):
     """h += g * (A Bᵀ), with g = gate_0 on rows < n_pre and gate_t after:
     the O and down projections' gated residual update, in fp32."""
