@@ -433,13 +433,16 @@ __global__ __launch_bounds__(256) void gemm_w4_kernel(GemmArgs g) {
   // B block bb = 4j + w holds packed columns 8bb .. 8bb+7. For SwiGLU the
   // packed column p is feature 32*(p/64) + p%32 of gate (p/32 even) or up
   // (p/32 odd): block 4j + w is rows 32*(j/2) + 8w .. +7 of matrix j%2.
+  // A's block row goes into the per-lane offset, which the bounds check
+  // covers, so rows past M read as zero without touching memory past A; B's
+  // rows are always inside B (N is a multiple of the tile width).
   auto dma = [&](u32x4* stg, int kt) {
     const uint32_t ko = (uint32_t)((kbeg + kt * SBK) * 2);
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const int blk = 4 * j + wave;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rA, LDSP(stg + blk * 64), 16, aoff,
-                                               ko + (uint32_t)(blk * 8 * g.lda * 2), 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rA, LDSP(stg + blk * 64), 16,
+                                               aoff + (uint32_t)(blk * 8 * g.lda * 2), ko, 0, 0);
     }
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
