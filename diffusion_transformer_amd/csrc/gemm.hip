@@ -433,9 +433,9 @@ __global__ __launch_bounds__(256) void gemm_w4_kernel(GemmArgs g) {
   // B block bb = 4j + w holds packed columns 8bb .. 8bb+7. For SwiGLU the
   // packed column p is feature 32*(p/64) + p%32 of gate (p/32 even) or up
   // (p/32 odd): block 4j + w is rows 32*(j/2) + 8w .. +7 of matrix j%2.
-  // A's block row goes into the per-lane offset, which the bounds check
-  // covers, so rows past M read as zero without touching memory past A; B's
-  // rows are always inside B (N is a multiple of the tile width).
+  // The block row goes into the per-lane offset, which the bounds check
+  // covers (rows of A past M read as zero without touching memory past A),
+  // and the stage's K offset into the scalar one, the same for every DMA.
   auto dma = [&](u32x4* stg, int kt) {
     const uint32_t ko = (uint32_t)((kbeg + kt * SBK) * 2);
 #pragma unroll
@@ -449,11 +449,11 @@ __global__ __launch_bounds__(256) void gemm_w4_kernel(GemmArgs g) {
       const int bb = 4 * j + wave;
       u32x4* dst = stg + (BM / 8 + bb) * 64;
       if (PACKED) {
-        const uint32_t so = ko + (uint32_t)((32 * (j >> 1) + 8 * wave) * g.ldb * 2);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds((j & 1) ? rU : rG, LDSP(dst), 16, boff, so, 0, 0);
+        const uint32_t ro = (uint32_t)((32 * (j >> 1) + 8 * wave) * g.ldb * 2);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds((j & 1) ? rU : rG, LDSP(dst), 16, boff + ro, ko, 0, 0);
       } else {
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rG, LDSP(dst), 16, boff,
-                                                 ko + (uint32_t)(bb * 8 * g.ldb * 2), 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rG, LDSP(dst), 16, boff + (uint32_t)(bb * 8 * g.ldb * 2), ko,
+                                                 0, 0);
       }
     }
   };
