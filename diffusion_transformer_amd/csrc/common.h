@@ -135,8 +135,8 @@ inline void launch_k(F kernel, dim3 grid, dim3 block, hipStream_t s, hipEvent_t 
 // The events of a launch with nothing to run (empty input), so that a
 // timed launch always records both.
 inline void mark_empty(const LaunchEvents& ev, hipStream_t s) {
-  if (ev.start) hipEventRecord(ev.start, s);
-  if (ev.stop) hipEventRecord(ev.stop, s);
+  if (ev.start) (void)hipEventRecord(ev.start, s);
+  if (ev.stop) (void)hipEventRecord(ev.stop, s);
 }
 
 // A pointer the caller knows to be the same in every lane, moved to scalar

@@ -139,9 +139,9 @@ static hipError_t gemm_sequence(const GemmArgs& g, int epi, hipStream_t s) {
 }
 
 hipError_t launch_gemm(const GemmArgs& g, int epi, hipStream_t s, const LaunchEvents& ev) {
-  if (ev.start) hipEventRecord(ev.start, s);
+  if (ev.start) (void)hipEventRecord(ev.start, s);
   const hipError_t e = gemm_sequence(g, epi, s);
-  if (ev.stop) hipEventRecord(ev.stop, s);
+  if (ev.stop) (void)hipEventRecord(ev.stop, s);
   return e;
 }
 

@@ -168,7 +168,7 @@ struct Timed {
       m->ev_start.push_back(a);
       m->ev_stop.push_back(b);
     }
-    if (!by_launch) hipEventRecord(m->ev_start[m->ev_used], s);
+    if (!by_launch) (void)hipEventRecord(m->ev_start[m->ev_used], s);
   }
   LaunchEvents ev() const {
     LaunchEvents e;
@@ -180,7 +180,7 @@ struct Timed {
   }
   ~Timed() {
     if (!on) return;
-    if (!by_launch) hipEventRecord(m->ev_stop[m->ev_used], s);
+    if (!by_launch) (void)hipEventRecord(m->ev_stop[m->ev_used], s);
     m->ev_used++;
   }
 };
@@ -496,8 +496,8 @@ dit_status dit_load_weights(const dit_config* cfg, const dit_weights* w, dit_mod
 
 void dit_free(dit_model* m) {
   if (!m) return;
-  for (auto e : m->ev_start) hipEventDestroy(e);
-  for (auto e : m->ev_stop) hipEventDestroy(e);
+  for (auto e : m->ev_start) (void)hipEventDestroy(e);
+  for (auto e : m->ev_stop) (void)hipEventDestroy(e);
   delete m;
 }
 

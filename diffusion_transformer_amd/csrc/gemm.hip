@@ -689,9 +689,9 @@ hipError_t launch_gemm(const GemmArgs& g, int epi, hipStream_t s, const LaunchEv
            (size_t)(2 * splits) * g.N * (size_t)(g.M - (ntm - r) * 256) * 4 <= g.part_bytes)
       splits *= 2;
     if (r && splits > 1) {
-      if (ev.start) hipEventRecord(ev.start, s);
+      if (ev.start) (void)hipEventRecord(ev.start, s);
       const hipError_t e = launch_gemm_split(g, epi, r, splits, s);
-      if (ev.stop) hipEventRecord(ev.stop, s);
+      if (ev.stop) (void)hipEventRecord(ev.stop, s);
       return e;
     }
   }
