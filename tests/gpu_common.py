@@ -69,3 +69,15 @@ def synth_weights_on_device(cfg, dev, seed=21, workers=16, n_layers=None):
                     out[k].append(up(bits[k]))
             say(f"  weights of layers < {min(Lc, l0 + workers)} drawn and uploaded")
     return out, crcs, synth.bits_crc(gbits)
+
+
+def split_cases(shapes, splits=(0, 2, 4)):
+    """(shape..., splits) cases the split-K path takes: no split, or a split
+    count that divides the K / 64 stages (K is each shape's third entry)."""
+    return [(*s, k) for s in shapes for k in splits if k == 0 or (s[2] // 64) % k == 0]
+
+
+def seq_len(segments):
+    """Tokens of a layout: ("text", n) counts n, ("ref" | "target", h, w)
+    counts h * w."""
+    return sum(s[1] if s[0] == "text" else s[1] * s[2] for s in segments)

@@ -16,7 +16,7 @@ import pytest
 import torch
 
 from diffusion_transformer_amd import synth
-from gpu_common import cache_views, i16_to_f32, say
+from gpu_common import cache_views, i16_to_f32, say, split_cases
 
 pytestmark = pytest.mark.gpu
 
@@ -74,11 +74,8 @@ def scratch_for(splits, N, dev):
 SHAPES = [(700, 512, 512), (256, 256, 64), (37, 768, 1024)]
 
 
-@pytest.mark.parametrize("splits", [0, 2, 4])
-@pytest.mark.parametrize("M,N,K", SHAPES)
+@pytest.mark.parametrize("M,N,K,splits", split_cases(SHAPES))
 def test_bf16_epilogue(dev, M, N, K, splits):
-    if splits and (K // 64) % splits:
-        pytest.skip("K / 64 not divisible by splits")
     A, (B,) = operands(M, N, K, seed=M + N + K)
     C = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
     say(f"bf16 epilogue M={M} N={N} K={K} splits={splits}")
@@ -146,14 +143,11 @@ def test_img_in_is_fp32_exact(dev, n):
     assert np.all(err <= bound), float((err / bound).max())
 
 
-@pytest.mark.parametrize("splits", [0, 2, 4])
-@pytest.mark.parametrize("M,N,K,n_pre", [(700, 512, 512, 300), (256, 256, 64, 0),
-                                         (37, 768, 1024, 37), (256, 512, 16384, 100)])
+@pytest.mark.parametrize("M,N,K,n_pre,splits", split_cases([(700, 512, 512, 300), (256, 256, 64, 0),
+                                                            (37, 768, 1024, 37), (256, 512, 16384, 100)]))
 def test_residual_epilogue(dev, M, N, K, n_pre, splits):
     """h += g * (A Bᵀ), with g = gate_0 on rows < n_pre and gate_t after:
     the O and down projections' gated residual update, in fp32."""
-    if splits and (K // 64) % splits:
-        pytest.skip("K / 64 not divisible by splits")
     A, (B,) = operands(M, N, K, seed=5 * M + K)
     g = torch.Generator().manual_seed(M)
     h0 = torch.randn((M, N), generator=g)
@@ -174,13 +168,10 @@ def test_residual_epilogue(dev, M, N, K, n_pre, splits):
     assert np.all(err <= bound), (err / np.maximum(bound, 1e-30)).max()
 
 
-@pytest.mark.parametrize("splits", [0, 2, 4])
-@pytest.mark.parametrize("M,F,K", [(700, 256, 512), (256, 512, 64), (37, 384, 1024)])
+@pytest.mark.parametrize("M,F,K,splits", split_cases([(700, 256, 512), (256, 512, 64), (37, 384, 1024)]))
 def test_swiglu_epilogue(dev, M, F, K, splits):
     """SiLU(A Gᵀ) * (A Uᵀ) with gate and up weights interleaved by the
     kernel's loader: the SwiGLU MLP's first GEMM."""
-    if splits and (K // 64) % splits:
-        pytest.skip("K / 64 not divisible by splits")
     A, (G, U) = operands(M, F, K, seed=7 * M + F, n_b=2)
     C = torch.empty((M, F), dtype=torch.bfloat16, device=dev)
     say(f"swiglu epilogue M={M} F={F} K={K} splits={splits}")

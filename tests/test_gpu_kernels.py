@@ -7,7 +7,7 @@ import torch
 
 import oracle as O
 from diffusion_transformer_amd import synth
-from gpu_common import cache_views, rel_err, say
+from gpu_common import cache_views, rel_err, say, seq_len, split_cases
 
 pytestmark = pytest.mark.gpu
 
@@ -21,16 +21,14 @@ def dev():
     return torch.device("cuda:0")
 
 
-@pytest.mark.parametrize("splits", [0, 2, 4])
-@pytest.mark.parametrize("M,N,K", [(32, 256, 64), (300, 512, 128), (257, 768, 256), (600, 1024, 512)])
+@pytest.mark.parametrize("M,N,K,splits", split_cases([(32, 256, 64), (300, 512, 128), (257, 768, 256),
+                                                      (600, 1024, 512)]))
 def test_gemm_exact_small_integers(dev, M, N, K, splits):
     """Entries in {-1, 0, 1}: every partial sum is an integer of magnitude
     <= K <= 512, exact in fp32 and in the bf16 output, so the MFMA GEMM must
     match integer matrix multiplication bit for bit (checks the MFMA lane
     layout, the LDS swizzle, the tile order, the ragged M tail and, with
     ``splits``, the split-K partial sums and their reduction)."""
-    if splits and (K // 64) % splits:
-        pytest.skip("K / 64 not divisible by splits")
     say(f"gemm exact M={M} N={N} K={K} splits={splits}")
     g = torch.Generator().manual_seed(M * 7 + N + K)
     A = torch.randint(-1, 2, (M, K), generator=g).to(torch.float32)
@@ -149,19 +147,21 @@ def attn_scratch(dev):
     return torch.empty(1 << 24, dtype=torch.float32, device=dev)
 
 
-@pytest.mark.parametrize("variant", ATTN_VARIANTS)
-@pytest.mark.parametrize("name,mode", [("c0w", "extract"), ("c0w", "cached"),
-                                       ("ragged", "extract"), ("ragged", "cached"),
-                                       ("many_ragged", "extract"), ("many_ragged", "cached"),
-                                       ("c1", "extract"), ("c1", "cached"),
-                                       ("c3", "cached")])
+ATTN_CASES = [(name, mode, v)
+              for name, mode in [("c0w", "extract"), ("c0w", "cached"), ("ragged", "extract"),
+                                 ("ragged", "cached"), ("many_ragged", "extract"),
+                                 ("many_ragged", "cached"), ("c1", "extract"), ("c1", "cached"),
+                                 ("c3", "cached")]
+              for v in ATTN_VARIANTS if variant_applies(v, mode, seq_len(LAYOUTS[name]))]
+
+
+@pytest.mark.parametrize("name,mode,variant", ATTN_CASES)
 def test_attention_matches_oracle(dev, name, mode, variant):
     nh = 2
     lay = layout_for(LAYOUTS[name])
     P, T = lay["P"], lay["T"]
     S = P + T
-    if not variant_applies(variant, mode, S):
-        pytest.skip("variant takes cached rows with S % 64 == 0 only")
+    assert S == seq_len(LAYOUTS[name]) and variant_applies(variant, mode, S)
     say(f"attention {name} {mode} S={S} variant={variant}")
     cache, K, V = fill_cache(dev, S, nh, seed=S)
     q_off, N = (0, S) if mode == "extract" else (P, T)
