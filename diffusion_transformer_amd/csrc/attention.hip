@@ -752,19 +752,6 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a, int bq) {
   *reinterpret_cast<u32x2*>(a.out + (size_t)q * a.out_stride + h * D + d0) = w;
 }
 
-// Compute units of the current device (cached per device).
-int device_cus() {
-  static int cus[64] = {0};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
-  if (cus[dev] == 0) {
-    int n = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-    cus[dev] = n;
-  }
-  return cus[dev];
-}
-
 // The grid has units = query blocks x heads workgroups, `per_cu` of them
 // resident per CU. With `split`, the units of a last, partly filled round
 // are split over key ranges when that shortens the round (scratch allowing).

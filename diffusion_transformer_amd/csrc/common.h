@@ -120,6 +120,19 @@ __device__ __forceinline__ void lds_barrier() {
 // LDS destination pointer of a buffer_load ... lds (address space 3).
 #define LDSP(p) ((__attribute__((address_space(3))) void*)(p))
 
+// Compute units of the current device (cached per device; 0 if unknown).
+inline int device_cus() {
+  static int cus[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  if (cus[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    cus[dev] = n;
+  }
+  return cus[dev];
+}
+
 // One kernel launch; the events, when given, are taken by the kernel's own
 // dispatch packet (start as it starts, stop as it ends), so timing puts no
 // extra packet between kernels.

@@ -550,9 +550,193 @@ __global__ __launch_bounds__(256) void gemm_w4_kernel(GemmArgs g) {
   else store_tile_lds<(EPI == EPI_SWIGLU ? EPI_SWIGLU : EPI_BF16)>(g, acc, m0, n0, wm, wn, lane, reg);
 }
 
+// Persistent form of gemm_w4_kernel<EPI_SWIGLU> (the gate/up projection):
+// the same tiles, main loop and epilogue, for whole rounds of tiles and an
+// even number of K stages. The grid is one workgroup per CU, and each walks
+// the tiles launch order would have dealt to its slot: virtual block
+// b = blockIdx.x + r * gridDim.x for r = 0, 1, ..., so the same XCD works
+// on the same logical tiles. The last K stage of a tile fetches the first
+// stage of the next into st0 and the epilogue stages its 128 x 64 bf16
+// patch per wave in st1 only, so a tile starts without waiting on memory
+// and without a workgroup turnover.
+__global__ __launch_bounds__(256) void gemm_w4p_swiglu_kernel(GemmArgs g) {
+  constexpr int BM = 256, BN = 256, SBK = 64;
+  constexpr int WN = 2, TM = 128, TN = 128, FM = 4, FN = 4;
+  constexpr int SW = (BM + BN) * SBK / 8;      // u32x4 per stage (64 KB)
+  __shared__ u32x4 st0[SW], st1[SW];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / WN, wn = wave % WN;
+
+  const int ntm = (g.M + BM - 1) / BM;
+  const int ntn = g.N / BN;
+  const int nblk = ntm * ntn;                  // virtual blocks = tiles
+  const int per = nblk >> 3;
+  const int gm = g.K >= 8192 ? GROUP_M_LONG_K : GROUP_M;
+  const int in_group = gm * ntn;
+  auto tile_of = [&](int b, int& m0_, int& n0_) {
+    if (b < per * 8) b = (b & 7) * per + (b >> 3);
+    const int first = (b / in_group) * gm;
+    const int gsz = min(ntm - first, gm);
+    m0_ = (first + (b % in_group) % gsz) * BM;
+    n0_ = ((b % in_group) / gsz) * BN;
+  };
+  int vb = blockIdx.x;
+  int m0, n0;
+  tile_of(vb, m0, n0);
+  const int nk = g.K / SBK;
+
+  // DMA as in gemm_w4_kernel. `ln` is the lane id, made opaque again at the
+  // start of every tile, so the per-lane offsets are derived per tile rather
+  // than held in registers across the epilogue.
+  int ln = lane;
+  auto lane_off = [&](int ld) {
+    const int lr = ln >> 3;
+    const int lc = (ln & 7) ^ ((4 * (wave & 1) + (ln >> 4)) & 7);
+    return (uint32_t)((lr * ld + lc * 8) * 2);
+  };
+  const uint32_t bbytes = (uint32_t)min((size_t)(BN / 2) * g.ldb * 2, (size_t)0xFFFFFFF0u);
+  auto rsrc_a = [&](int m0_) {
+    return make_rsrc(g.A + (size_t)m0_ * g.lda, (uint32_t)min((size_t)(g.M - m0_) * g.lda * 2, (size_t)0xFFFFFFF0u));
+  };
+  __amdgpu_buffer_rsrc_t rA = rsrc_a(m0);
+  __amdgpu_buffer_rsrc_t rG = make_rsrc(g.B + (size_t)(n0 >> 1) * g.ldb, bbytes);
+  __amdgpu_buffer_rsrc_t rU = make_rsrc(g.B2 + (size_t)(n0 >> 1) * g.ldb, bbytes);
+  // ko: byte offset of the stage's first K column (the same for every DMA)
+  auto dma = [&](u32x4* stg, uint32_t ko) {
+    const uint32_t aoff = lane_off(g.lda), boff = lane_off(g.ldb);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int blk = 4 * j + wave;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rA, LDSP(stg + blk * 64), 16,
+                                               aoff + (uint32_t)(blk * 8 * g.lda * 2), ko, 0, 0);
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      u32x4* dst = stg + (BM / 8 + 4 * j + wave) * 64;
+      const uint32_t ro = (uint32_t)((32 * (j >> 1) + 8 * wave) * g.ldb * 2);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds((j & 1) ? rU : rG, LDSP(dst), 16, boff + ro, ko, 0, 0);
+    }
+  };
+
+  f32x16 acc[FM][FN];
+  bf16x8 fa[2][FM], fb[2][FN];
+  auto lread = [&](int fs, const u32x4* stg, int s) {
+    const int lrow = ln & 31, lhalf = ln >> 5;
+    const int ph = (2 * s + lhalf) ^ ((lrow >> 1) & 7);
+#pragma unroll
+    for (int i = 0; i < FM; ++i) fa[fs][i] = __builtin_bit_cast(bf16x8, stg[(wm * TM + i * 32 + lrow) * 8 + ph]);
+#pragma unroll
+    for (int j = 0; j < FN; ++j) fb[fs][j] = __builtin_bit_cast(bf16x8, stg[(BM + wn * TN + j * 32 + lrow) * 8 + ph]);
+  };
+  // init: the tile's first MFMA on each block starts from zero (no clearing)
+  auto mma = [&](int fs, int i0, int i1, bool init = false) {
+#pragma unroll
+    for (int i = i0; i < i1; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+        acc[i][j] = mfma32(fb[fs][j], fa[fs][i], init ? f32x16{} : acc[i][j]);   // swapped: Cᵀ blocks
+  };
+  auto pair = [&](int n_ds, int n_vm) {
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      if (k < n_ds) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                 // MFMA
+      if (k < n_vm) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // VMEM (LDS DMA)
+    }
+  };
+  // one K stage as in gemm_w4_kernel; its DMA fetches the stage at ko_dma.
+  // `first`: the tile's first stage, whose slice 0 initializes every block.
+  auto iter = [&](const u32x4* cur, u32x4* nxt, uint32_t ko_dma, bool first = false) {
+    lread(1, cur, 1);
+    dma(nxt, ko_dma);
+    mma(0, 0, FM, first);
+    pair(8, 16);
+    __builtin_amdgcn_sched_barrier(0);
+    lread(0, cur, 2);
+    mma(1, 0, FM);
+    pair(8, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    lread(1, cur, 3);
+    mma(0, 0, FM);
+    pair(8, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    mma(1, 0, FM / 2);
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+    lds_barrier();
+    lread(0, nxt, 0);
+    mma(1, FM / 2, FM);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  auto ko = [&](int kt) { return (uint32_t)(kt * SBK * 2); };
+
+  for (bool first_tile = true;; first_tile = false) {
+    asm volatile("" : "+v"(ln));
+    if (first_tile) dma(st0, 0);
+    if (first_tile) {
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+      __builtin_amdgcn_s_barrier();
+    } else {
+      // stage 0 landed before the previous tile's last barrier; this one
+      // orders the previous epilogue's LDS reads before the DMA into st1
+      lds_barrier();
+    }
+    lread(0, st0, 0);
+
+    // nk is even: stage 0 is read from st0, the last stage (odd) from st1,
+    // and the last stage's DMA fills st0 with the next tile's first stage
+    // (or, with no next tile, repeats the last stage, never read)
+    iter(st0, st1, ko(1), true);
+    for (int kt = 1; kt + 2 < nk; kt += 2) {
+      iter(st1, st0, ko(kt + 1));
+      iter(st0, st1, ko(kt + 2));
+    }
+    const int vn = vb + (int)gridDim.x;
+    const bool has_next = vn < nblk;
+    int m0n = m0, n0n = n0;
+    uint32_t ko_last = ko(nk - 1);
+    if (has_next) {
+      // the buffer resources switch to the next tile for the last DMA
+      tile_of(vn, m0n, n0n);
+      rA = rsrc_a(m0n);
+      rG = make_rsrc(g.B + (size_t)(n0n >> 1) * g.ldb, bbytes);
+      rU = make_rsrc(g.B2 + (size_t)(n0n >> 1) * g.ldb, bbytes);
+      ko_last = 0;
+    }
+    iter(st1, st0, ko_last);
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+
+    lds_barrier();   // every wave is done with the stage buffers
+    // st0 holds the next tile's first stage: the patch goes to st1 only
+    store_tile_lds<EPI_SWIGLU>(g, acc, m0, n0, wm, wn, lane, reinterpret_cast<char*>(st1) + wave * 16384);
+    if (!has_next) break;
+    vb = vn;
+    m0 = m0n;
+    n0 = n0n;
+  }
+}
+
 template <int EPI, bool PACKED = (EPI == EPI_SWIGLU)>
 hipError_t run_w4(const GemmArgs& g, hipStream_t s, const LaunchEvents& ev = {}) {
   const int nblk = ((g.M + 255) / 256) * (g.N / 256) * (EPI == EPI_PART ? g.splits : 1);
+  if (EPI == EPI_SWIGLU) {
+    // Persistent grid when the tiles are whole rounds of at least two (one
+    // workgroup per CU, 8 XCDs) and the K stages are even in number (the
+    // next tile's first stage then lands in st0).
+    const int cus = device_cus();
+    if (cus > 0 && cus % 8 == 0 && nblk % cus == 0 && nblk >= 2 * cus && (g.K / 64) % 2 == 0) {
+      launch_k(gemm_w4p_swiglu_kernel, dim3(cus), dim3(256), s, ev.start, ev.stop, g);
+      return hipGetLastError();
+    }
+  }
   launch_k((gemm_w4_kernel<EPI, PACKED>), dim3(nblk), dim3(256), s, ev.start, ev.stop, g);
   return hipGetLastError();
 }
