@@ -27,8 +27,11 @@ PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 GEMM_SRC = os.path.join(ROOT, "diffusion_transformer_amd", "csrc", "gemm.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gemm_gateup_c2_cached.json")
 # the dominant kernel of the cached step: the fused gate/up GEMM + SwiGLU
-GATEUP_KERNEL = "gemm_w4_kernel<3, true>"
-GATEUP_LABEL = "gemm_w4_kernel<SwiGLU> (gate/up, 256x256 tiles, 4 waves of 128x128)"
+GATEUP_KERNEL = "gemm_w4p_swiglu_kernel"
+# its grid: one 256-thread workgroup per CU (256 CUs), each walking 8 tiles
+GATEUP_GRID = 256 * 256
+GATEUP_LABEL = ("gemm_w4p_swiglu_kernel (gate/up + SwiGLU, persistent: one workgroup per CU, "
+                "256x256 tiles, 4 waves of 128x128)")
 
 
 def source_sha(path):
@@ -75,7 +78,7 @@ def summarize_profiles(trace_dir, fetch_dir, write_dir, command, out_md, out_jso
         known_kib = (1 << 28) * (4 if name == "FETCH_SIZE" else 2) / 1024.0
         factor = known_kib / float(calib["Counter_Value"])
         gu = [float(r["Counter_Value"]) for r in rows
-              if GATEUP_KERNEL in r["Kernel_Name"] and int(r["Grid_Size"]) == 2048 * 256]
+              if GATEUP_KERNEL in r["Kernel_Name"] and int(r["Grid_Size"]) == GATEUP_GRID]
         res[name] = {"calib_kib": float(calib["Counter_Value"]), "known_kib": known_kib,
                      "factor": factor, "gateup_kib_avg": sum(gu) / len(gu), "n": len(gu)}
     fb = res["FETCH_SIZE"]["gateup_kib_avg"] * res["FETCH_SIZE"]["factor"] * 1024
