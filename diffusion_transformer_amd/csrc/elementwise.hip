@@ -191,42 +191,47 @@ __global__ __launch_bounds__(256) void qknorm_rope_kernel(QkArgs a) {
 // ---------------------------------------------------------------------------
 // GEMV, Y[v][o] = W[o] · X[v] for v < nv <= 2 (the timestep MLP, the shared
 // modulation and the final scale; the modulation weight alone is 134 MB at
-// H = 4096). X is staged in LDS once per workgroup; each wave owns GV_ROWS
-// consecutive rows and issues all of their 16-byte weight loads (up to
-// GV_ROWS x 8 per lane) before the first multiply, so every wave keeps up to
-// 32 KB of weights in flight.
-constexpr int GV_ROWS = 4;
+// H = 4096), bound by streaming W. X is staged in LDS once per workgroup.
+// The grid is at most two workgroups per CU (all resident at once); each
+// wave walks row pairs in a grid stride and issues the 16-byte weight loads
+// of its next pair (16 KB) before it reduces the current one, so the weight
+// stream has no round boundary and each wave keeps 16-32 KB in flight.
 constexpr int GV_MAXC = 8;   // 16-byte chunks per lane per row: I <= 4096
+constexpr int GV_WG_PER_CU = 2;
 
 __global__ __launch_bounds__(256) void gemv_kernel(const uint16_t* __restrict__ W, int O, int I,
                                                    const float* __restrict__ X, int ldx, int nv,
                                                    float* __restrict__ Y, int ldy, float* Ys) {
   __shared__ __align__(16) float xs[2][GV_MAXC * 512];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int o0 = (blockIdx.x * 4 + wave) * GV_ROWS;
   const int nch = I >> 3;                     // 16-byte chunks per row
-  // the weight loads go out first; X is staged while they are in flight
-  u32x4 w[GV_ROWS][GV_MAXC];
+  const int npairs = (O + 1) >> 1;
+  const int stride = gridDim.x * 4;           // waves in the grid
+  int p = blockIdx.x * 4 + wave;              // this wave's first row pair
+  u32x4 w[2][2][GV_MAXC];                     // [buffer][row of the pair][chunk]
+  // Buffer loads through a resource that ends at W's end: rows past O and
+  // chunks past I take an offset past every record and read zero, so no
+  // load sits behind a branch (W is at most 2^31 bytes: checked on the host).
+  const __amdgpu_buffer_rsrc_t rw = make_rsrc(W, (uint32_t)((size_t)O * I * 2));
+  constexpr uint32_t kOut = 0x80000000u;
+  auto load = [&](u32x4 (&b)[2][GV_MAXC], int pp) {
 #pragma unroll
-  for (int r = 0; r < GV_ROWS; ++r)
+    for (int r = 0; r < 2; ++r)
+#pragma unroll
+      for (int c = 0; c < GV_MAXC; ++c) {
+        const int o = 2 * pp + r, ch = lane + 64 * c;
+        const uint32_t off = (o < O && ch < nch) ? (uint32_t)(((size_t)o * I + 8 * ch) * 2) : kOut;
+        b[r][c] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rw, off, 0, 0));
+      }
+  };
+  auto reduce_store = [&](const u32x4 (&b)[2][GV_MAXC], int pp) {
+    float acc[2][2];
+#pragma unroll
+    for (int r = 0; r < 2; ++r) acc[r][0] = acc[r][1] = 0.f;
+    // chunks past I hold zero weights and zero X (the staging pads X)
 #pragma unroll
     for (int c = 0; c < GV_MAXC; ++c) {
       const int ch = lane + 64 * c;
-      w[r][c] = (o0 + r < O && ch < nch) ? *reinterpret_cast<const u32x4*>(W + (size_t)(o0 + r) * I + 8 * ch)
-                                         : (u32x4){0u, 0u, 0u, 0u};
-    }
-  for (int q = threadIdx.x; q < nv * (I >> 2); q += 256) {   // float4 of X (I % 8 == 0)
-    const int v = q >= (I >> 2), i4 = q - v * (I >> 2);
-    *reinterpret_cast<float4*>(&xs[v][4 * i4]) = *reinterpret_cast<const float4*>(X + (size_t)v * ldx + 4 * i4);
-  }
-  __syncthreads();
-  float acc[GV_ROWS][2];
-#pragma unroll
-  for (int r = 0; r < GV_ROWS; ++r) acc[r][0] = acc[r][1] = 0.f;
-#pragma unroll
-  for (int c = 0; c < GV_MAXC; ++c) {
-    const int ch = lane + 64 * c;
-    if (ch < nch) {
 #pragma unroll
       for (int v = 0; v < 2; ++v) {
         if (v < nv) {
@@ -234,8 +239,8 @@ __global__ __launch_bounds__(256) void gemv_kernel(const uint16_t* __restrict__ 
           const float4 xb = *reinterpret_cast<const float4*>(&xs[v][8 * ch + 4]);
           const float xv[8] = {xa.x, xa.y, xa.z, xa.w, xb.x, xb.y, xb.z, xb.w};
 #pragma unroll
-          for (int r = 0; r < GV_ROWS; ++r) {
-            const uint32_t u[4] = {w[r][c].x, w[r][c].y, w[r][c].z, w[r][c].w};
+          for (int r = 0; r < 2; ++r) {
+            const uint32_t u[4] = {b[r][c].x, b[r][c].y, b[r][c].z, b[r][c].w};
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
               acc[r][v] += __uint_as_float(u[k] << 16) * xv[2 * k];
@@ -245,19 +250,38 @@ __global__ __launch_bounds__(256) void gemv_kernel(const uint16_t* __restrict__ 
         }
       }
     }
-  }
 #pragma unroll
-  for (int r = 0; r < GV_ROWS; ++r) {
+    for (int r = 0; r < 2; ++r) {
 #pragma unroll
-    for (int v = 0; v < 2; ++v) {
-      if (v < nv) {
-        const float y = wave_sum(acc[r][v]);
-        if (lane == 0 && o0 + r < O) {
-          Y[(size_t)v * ldy + o0 + r] = y;
-          if (Ys) Ys[(size_t)v * ldy + o0 + r] = y / (1.f + __expf(-y));
+      for (int v = 0; v < 2; ++v) {
+        if (v < nv) {
+          const float y = wave_sum(acc[r][v]);
+          const int o = 2 * pp + r;
+          if (lane == 0 && o < O) {
+            Y[(size_t)v * ldy + o] = y;
+            if (Ys) Ys[(size_t)v * ldy + o] = y / (1.f + __expf(-y));
+          }
         }
       }
     }
+  };
+  // the first pair's loads go out first; X is staged while they are in flight
+  load(w[0], p);
+  for (int q = threadIdx.x; q < nv * GV_MAXC * 128; q += 256) {   // float4 of X, zero past I
+    const int v = q / (GV_MAXC * 128), i4 = q - v * (GV_MAXC * 128);
+    *reinterpret_cast<float4*>(&xs[v][4 * i4]) =
+        4 * i4 < I ? *reinterpret_cast<const float4*>(X + (size_t)v * ldx + 4 * i4) : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+  __syncthreads();
+  // two buffers in turn (register arrays need compile-time indices)
+  while (p < npairs) {
+    load(w[1], p + stride);
+    reduce_store(w[0], p);
+    p += stride;
+    if (p >= npairs) break;
+    load(w[0], p + stride);
+    reduce_store(w[1], p);
+    p += stride;
   }
 }
 
@@ -303,9 +327,12 @@ hipError_t launch_qknorm_rope(const QkArgs& a, hipStream_t s) {
 
 hipError_t launch_gemv(const uint16_t* W, int O, int I, const float* X, int ldx, int nv, float* Y,
                        int ldy, float* Ys, hipStream_t s, const LaunchEvents& ev) {
-  if (I > GV_MAXC * 512 || I % 8 || nv < 1 || nv > 2) return hipErrorInvalidValue;
-  launch_k(gemv_kernel, dim3((O + 4 * GV_ROWS - 1) / (4 * GV_ROWS)), dim3(256), s, ev.start, ev.stop, W, O,
-           I, X, ldx, nv, Y, ldy, Ys);
+  if (I > GV_MAXC * 512 || I % 8 || nv < 1 || nv > 2 || (size_t)O * I * 2 >= 0x80000000u)
+    return hipErrorInvalidValue;
+  const int cus = device_cus();
+  const int need = ((O + 1) / 2 + 3) / 4;                 // workgroups of 4 waves, one row pair each
+  const int nblk = cus > 0 ? min(need, GV_WG_PER_CU * cus) : need;
+  launch_k(gemv_kernel, dim3(nblk), dim3(256), s, ev.start, ev.stop, W, O, I, X, ldx, nv, Y, ldy, Ys);
   return hipGetLastError();
 }
 
