@@ -18,12 +18,16 @@ namespace {
 // into three bf16 pieces by truncation, x = hi + mid + lo exactly (8
 // significant bits each), so three bf16 MFMAs per block give the fp32
 // product sum with fp32 accumulation (each bf16 x bf16 product is exact in
-// fp32). A workgroup of 4 waves computes 64 tokens x 256 columns; wave w the
-// 64 x 64 patch at column 64w, as 2 x 2 blocks of 32 x 32, K = 64 in 4 steps
-// of 16. Operands come straight from global memory (the 16 KB of latents of
-// a workgroup and the 32 KB of weight rows are cache hits for all but the
-// first wave that touches them); the result is written row by row through
-// LDS, one 32-token half at a time.
+// fp32). The kernel is bound by writing its fp32 output. A workgroup of 4
+// waves takes 64 tokens and IMG_CB blocks of 256 columns:
+//  1. its 256 threads split the 64 x 64 latents once into three bf16 tiles
+//     in LDS (128-byte token rows, 16-byte chunks XOR-swizzled by token%8);
+//  2. for each 256-column block, wave w computes the 64 x 64 patch at
+//     column 64w as two 32-token halves of 2 x 2 blocks of 32 x 32 (K = 64
+//     in 4 steps of 16; A fragments from LDS, W fragments from global memory
+//     (cache hits after the first wave), the next block's fetched while the
+//     current one is multiplied), and writes each half row by row through
+//     LDS; the stores of one half drain while the next half is computed.
 __device__ __forceinline__ void split3(const float (&x)[8], bf16x8& hi, bf16x8& mid, bf16x8& lo) {
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
@@ -35,78 +39,114 @@ __device__ __forceinline__ void split3(const float (&x)[8], bf16x8& hi, bf16x8& 
     hi[j] = __builtin_bit_cast(__bf16, (uint16_t)(b >> 16));
     mid[j] = __builtin_bit_cast(__bf16, (uint16_t)(__float_as_uint(r1) >> 16));
     lo[j] = __builtin_bit_cast(__bf16, (uint16_t)(__float_as_uint(r2) >> 16));
-    (void)m;
   }
 }
 
 constexpr int IMG_LD = 68;   // floats per staged row (64 + 4 of padding)
+constexpr int IMG_CB = 2;    // 256-column blocks per workgroup
 
 __global__ __launch_bounds__(256) void img_in_kernel(const uint16_t* __restrict__ W,
-                                                     const float* __restrict__ x, int n,
+                                                     const float* __restrict__ x, int n, int H,
                                                      float* __restrict__ out, int ldo) {
-  __shared__ __align__(16) float img_smem[4 * 32 * IMG_LD];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  __shared__ __align__(16) u32x4 img_split[3][64 * 8];       // [piece][token][chunk]: 24 KB
+  __shared__ __align__(16) float img_smem[4 * 32 * IMG_LD];  // per-wave output staging: 34 KB
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, lh = lane >> 5;
   const int t0 = blockIdx.y * 64;
-  const int c0 = blockIdx.x * 256 + wave * 64;
-  // B fragments: lane supplies W[c0 + 32j + l32][16s + 8lh .. +7]
-  bf16x8 wb[2][4];
-#pragma unroll
-  for (int j = 0; j < 2; ++j)
-#pragma unroll
-    for (int s = 0; s < 4; ++s)
-      wb[j][s] = __builtin_bit_cast(
-          bf16x8, *reinterpret_cast<const u32x4*>(W + (size_t)(c0 + 32 * j + l32) * 64 + 16 * s + 8 * lh));
-  float* pt = img_smem + wave * 32 * IMG_LD;
-  // the two 32-token halves one after the other: half the accumulators and
-  // half the staging space, so four workgroups fit on a CU
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    f32x16 acc[2];
+  const int ncb = H >> 8;
+  const int cb0 = blockIdx.x * IMG_CB;
+
+  // W fragments of a 256-column block: lane supplies W[c0 + 32j + l32][16s + 8lh .. +7]
+  auto fetch_w = [&](bf16x8 (&wb)[2][4], int cb) {
+    const int c0 = cb * 256 + wave * 64;
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc[j][r] = 0.f;
-    const int t = t0 + 32 * i + l32;
-    const bool ok = t < n;
+      for (int s = 0; s < 4; ++s)
+        wb[j][s] = __builtin_bit_cast(
+            bf16x8, *reinterpret_cast<const u32x4*>(W + (size_t)(c0 + 32 * j + l32) * 64 + 16 * s + 8 * lh));
+  };
+  bf16x8 wa[2][4], wbn[2][4];
+  fetch_w(wa, cb0);
+
+  // 1. split: thread tid takes token tid/4, channels 16(tid%4) .. +15
+  {
+    const int tk = tid >> 2, ch0 = 16 * (tid & 3);
+    const int t = t0 + tk;
+    float v[16];
+    if (t < n) {
+      const float4* xp = reinterpret_cast<const float4*>(x + (size_t)t * 64 + ch0);
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      float xv[8];
-      if (ok) {
-        const float4* xp = reinterpret_cast<const float4*>(x + (size_t)t * 64 + 16 * s + 8 * lh);
-        const float4 a = xp[0], b = xp[1];
-        xv[0] = a.x; xv[1] = a.y; xv[2] = a.z; xv[3] = a.w;
-        xv[4] = b.x; xv[5] = b.y; xv[6] = b.z; xv[7] = b.w;
-      } else {
-#pragma unroll
-        for (int k = 0; k < 8; ++k) xv[k] = 0.f;
+      for (int q = 0; q < 4; ++q) {
+        const float4 a = xp[q];
+        v[4 * q] = a.x; v[4 * q + 1] = a.y; v[4 * q + 2] = a.z; v[4 * q + 3] = a.w;
       }
+    } else {
+#pragma unroll
+      for (int k = 0; k < 16; ++k) v[k] = 0.f;
+    }
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+      float xv[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) xv[k] = v[8 * g + k];
       bf16x8 hi, mid, lo;
       split3(xv, hi, mid, lo);
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        acc[j] = mfma32(lo, wb[j][s], acc[j]);
-        acc[j] = mfma32(mid, wb[j][s], acc[j]);
-        acc[j] = mfma32(hi, wb[j][s], acc[j]);
-      }
+      const int slot = tk * 8 + (((ch0 >> 3) + g) ^ (tk & 7));
+      img_split[0][slot] = __builtin_bit_cast(u32x4, hi);
+      img_split[1][slot] = __builtin_bit_cast(u32x4, mid);
+      img_split[2][slot] = __builtin_bit_cast(u32x4, lo);
     }
-    // Register r of lane l holds row 8(r/4) + 4lh + r%4 of its block,
-    // column l32. The wave's 32 x 64 half goes through LDS (rows padded to
-    // 272 bytes) so that every store instruction writes four whole 256-byte
-    // row segments.
-    if (i) __builtin_amdgcn_s_waitcnt(kWaitLgkm0);   // the first half's reads are done
+  }
+  __syncthreads();
+
+  float* pt = img_smem + wave * 32 * IMG_LD;
+  for (int cbi = 0; cbi < IMG_CB; ++cbi) {
+    const int cb = cb0 + cbi;
+    if (cb >= ncb) break;                               // workgroup-uniform
+    const bool more = cbi + 1 < IMG_CB && cb + 1 < ncb;
+    if (more) fetch_w(cbi & 1 ? wa : wbn, cb + 1);
+    const bf16x8 (&wb)[2][4] = cbi & 1 ? wbn : wa;
+    const int c0 = cb * 256 + wave * 64;
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int i = 0; i < 2; ++i) {
+      f32x16 acc[2];
 #pragma unroll
-      for (int r = 0; r < 16; ++r)
-        pt[(8 * (r >> 2) + 4 * lh + (r & 3)) * IMG_LD + 32 * j + l32] = acc[j][r];
-    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);   // the region is private to this wave
+      for (int j = 0; j < 2; ++j)
 #pragma unroll
-    for (int it = 0; it < 8; ++it) {
-      const int row = 4 * it + (lane >> 4);
-      const int tr = t0 + 32 * i + row;
-      const float4 v4 = *reinterpret_cast<const float4*>(pt + row * IMG_LD + 4 * (lane & 15));
-      if (tr < n) *reinterpret_cast<float4*>(out + (size_t)tr * ldo + c0 + 4 * (lane & 15)) = v4;
+        for (int r = 0; r < 16; ++r) acc[j][r] = 0.f;
+      const int tk = 32 * i + l32;
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const int slot = tk * 8 + ((2 * s + lh) ^ (tk & 7));
+        const bf16x8 hi = __builtin_bit_cast(bf16x8, img_split[0][slot]);
+        const bf16x8 mid = __builtin_bit_cast(bf16x8, img_split[1][slot]);
+        const bf16x8 lo = __builtin_bit_cast(bf16x8, img_split[2][slot]);
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          acc[j] = mfma32(lo, wb[j][s], acc[j]);
+          acc[j] = mfma32(mid, wb[j][s], acc[j]);
+          acc[j] = mfma32(hi, wb[j][s], acc[j]);
+        }
+      }
+      // Register r of lane l holds row 8(r/4) + 4lh + r%4 of its block,
+      // column l32. The wave's 32 x 64 half goes through LDS (rows padded to
+      // 272 bytes) so that every store instruction writes four whole 256-byte
+      // row segments.
+      __builtin_amdgcn_s_waitcnt(kWaitLgkm0);   // the previous half's LDS reads are done
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          pt[(8 * (r >> 2) + 4 * lh + (r & 3)) * IMG_LD + 32 * j + l32] = acc[j][r];
+      __builtin_amdgcn_s_waitcnt(kWaitLgkm0);   // the region is private to this wave
+#pragma unroll
+      for (int it = 0; it < 8; ++it) {
+        const int row = 4 * it + (lane >> 4);
+        const int tr = t0 + 32 * i + row;
+        const float4 v4 = *reinterpret_cast<const float4*>(pt + row * IMG_LD + 4 * (lane & 15));
+        if (tr < n) *reinterpret_cast<float4*>(out + (size_t)tr * ldo + c0 + 4 * (lane & 15)) = v4;
+      }
     }
   }
 }
@@ -296,8 +336,8 @@ hipError_t launch_img_in(const uint16_t* W, const float* x, int n, int H, float*
     mark_empty(ev, s);
     return hipSuccess;
   }
-  dim3 grid(H / 256, (n + 63) / 64);
-  launch_k(img_in_kernel, grid, dim3(256), s, ev.start, ev.stop, W, x, n, out, ldo);
+  dim3 grid((H / 256 + IMG_CB - 1) / IMG_CB, (n + 63) / 64);
+  launch_k(img_in_kernel, grid, dim3(256), s, ev.start, ev.stop, W, x, n, H, out, ldo);
   return hipGetLastError();
 }
 
