@@ -107,17 +107,20 @@ def summarize_profiles(trace_dir, fetch_dir, write_dir, command, out_md, out_jso
 
 
 # Bandwidth-bound kernels of the c2 cached step (T = 4096 target rows,
-# H = 4096): kernel-name match, grid size, algorithmic bytes per launch.
+# H = 4096): kernel-name match, grid size (work-items), which of the matching
+# launches in dispatch order to take (index -> bool), algorithmic bytes per
+# launch. A step launches four GEMVs with the same grid (two workgroups per
+# CU), in the order timestep MLP 1, timestep MLP 2, modulation, final scale.
 HBM_KERNELS = [
-    ("LayerNorm + modulation (ln_mod_kernel)", "ln_mod_kernel", 2048 * 256,
+    ("LayerNorm + modulation (ln_mod_kernel)", "ln_mod_kernel", 2048 * 256, None,
      4096 * 4096 * (4 + 2) + 2 * 4096 * 4),
-    ("final AdaLN + proj_out (final_out_kernel)", "final_out_kernel", 256 * 256,
+    ("final AdaLN + proj_out (final_out_kernel)", "final_out_kernel", 256 * 256, None,
      4096 * 4096 * 4 + 4096 * 64 * 4 + 4096 * 4 + 64 * 4096 * 2),
-    ("img_in (img_in_kernel)", "img_in_kernel", 16 * 64 * 256,
+    ("img_in (img_in_kernel)", "img_in_kernel", 8 * 64 * 256, None,
      4096 * 4096 * 4 + 4096 * 64 * 4 + 4096 * 64 * 2),
-    ("modulation GEMV [16384 x 4096] (gemv_kernel)", "gemv_kernel", 1024 * 256,
+    ("modulation GEMV [16384 x 4096] (gemv_kernel)", "gemv_kernel", 512 * 256, lambda i: i % 4 == 2,
      16384 * 4096 * 2 + 4096 * 4 + 16384 * 4),
-    ("Euler update x += dsigma * v, 4096 x 64 (euler_kernel)", "euler_kernel", 1024 * 256,
+    ("Euler update x += dsigma * v, 4096 x 64 (euler_kernel)", "euler_kernel", 1024 * 256, None,
      4096 * 64 * 12),
 ]
 
@@ -141,13 +144,15 @@ def hbm_kernels_summary(trace_dir, fetch_dir, write_dir, command, calib, out_md)
              "trace of the timed run. HBM peak 8 TB/s.", "",
              "| kernel | launches | avg us | fetched MB | written MB | algorithmic MB | measured / alg "
              "| GB/s (alg bytes) | % of 8 TB/s |", "|---|---|---|---|---|---|---|---|---|"]
-    for label, match, g, alg in HBM_KERNELS:
-        ns = [int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) for r in trace
-              if match in r["Kernel_Name"] and grid(r) == g]
+    def pick(rows, match, g, sel):
+        rows = sorted((r for r in rows if match in r["Kernel_Name"] and grid(r) == g),
+                      key=lambda r: int(r["Dispatch_Id"]))
+        return [r for i, r in enumerate(rows) if sel is None or sel(i)]
+    for label, match, g, sel, alg in HBM_KERNELS:
+        ns = [int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) for r in pick(trace, match, g, sel)]
         by = {}
         for name, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
-            rows = [r for r in csv.DictReader(open(os.path.join(d, "run_counter_collection.csv")))
-                    if match in r["Kernel_Name"] and int(r["Grid_Size"]) == g]
+            rows = pick(csv.DictReader(open(os.path.join(d, "run_counter_collection.csv"))), match, g, sel)
             by[name] = (sum(float(r["Counter_Value"]) for r in rows) / len(rows) * calib[name]["factor"] * 1024
                         if rows else float("nan"))
         if not ns:
