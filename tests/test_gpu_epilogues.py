@@ -169,12 +169,14 @@ def test_residual_epilogue(dev, M, N, K, n_pre, splits):
 
 
 @pytest.mark.parametrize("M,F,K,splits", split_cases([(700, 256, 512), (256, 512, 64), (37, 384, 1024),
-                                                      (4096, 4096, 128)]))
+                                                      (4096, 4096, 128)]) + [(2500, 16384, 128, 0)])
 def test_swiglu_epilogue(dev, M, F, K, splits):
     """SiLU(A Gᵀ) * (A Uᵀ) with gate and up weights interleaved by the
-    kernel's loader: the SwiGLU MLP's first GEMM. 4096 x 4096 x 128 is 512
-    tiles with an even number of K stages, which takes the persistent grid
-    (one workgroup per CU, two tiles each)."""
+    kernel's loader: the SwiGLU MLP's first GEMM. 4096 x 4096 x 128 (512
+    tiles) and 2500 x 16384 x 128 (1280 tiles: ragged last row block, a last
+    tile-row group two rows high) are whole rounds with an even number of K
+    stages, which take the persistent grid (one workgroup per CU walking two
+    or five tiles)."""
     A, (G, U) = operands(M, F, K, seed=7 * M + F, n_b=2)
     C = torch.empty((M, F), dtype=torch.bfloat16, device=dev)
     say(f"swiglu epilogue M={M} F={F} K={K} splits={splits}")
