@@ -32,7 +32,7 @@ EXPORTS = ["dit_build_layout", "dit_load_weights", "dit_free", "dit_workspace_by
            "dit_kv_capacity", "dit_kv_cache_bytes", "dit_step_extract", "dit_step_cached",
            "dit_step_cached_noalloc",
            "euler_update", "dit_img_in", "dit_latent_standardize", "dit_debug_mask", "dit_debug_attention",
-           "dit_debug_gemm", "dit_debug_final_out", "dit_debug_stream_copy", "dit_debug_mfma_loop",
+           "dit_debug_gemm", "dit_debug_final_out", "dit_debug_gemv", "dit_debug_stream_copy", "dit_debug_mfma_loop",
            "dit_profile_enable", "dit_profile_read",
            "dit_last_error",
            "dit_version"]
@@ -104,6 +104,7 @@ def _load(path=None):
         "dit_debug_gemm": (i, [P(dit_gemm_desc), vp]),
         "dit_debug_mfma_loop": (i, [vp, vp, i, i, vp]),
         "dit_debug_final_out": (i, [vp, i, i, i, vp, f, vp, vp, vp]),
+        "dit_debug_gemv": (i, [vp, i, i, vp, i, i, vp, vp, vp]),
         "dit_debug_stream_copy": (i, [vp, vp, sz, vp]),
         "dit_profile_enable": (i, [vp, i]),
         "dit_profile_read": (i, [vp, P(C.c_double), P(ll)]),
@@ -320,6 +321,12 @@ def _make_api(_lib):
         _check(_lib.dit_debug_final_out(_ptr(h), int(h.shape[1]), int(h.shape[0]), int(h.shape[1]),
                                         _ptr(scale_out), float(eps), _ptr(w_out), _ptr(v_out),
                                         _stream(stream)))
+
+    def dit_debug_gemv(W, X, Y, Ys=None, stream=None):
+        """W [O, I] bf16, X [nv, I] f32, Y (and Ys) [nv, O] f32; all contiguous device tensors."""
+        O_, I_ = int(W.shape[0]), int(W.shape[1])
+        _check(_lib.dit_debug_gemv(_ptr(W), O_, I_, _ptr(X), I_, int(X.shape[0]), _ptr(Y), _ptr(Ys),
+                                   _stream(stream)))
 
     def dit_debug_stream_copy(src, dst, stream=None):
         _check(_lib.dit_debug_stream_copy(_ptr(src), _ptr(dst), _nbytes(src), _stream(stream)))

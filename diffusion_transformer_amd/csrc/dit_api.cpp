@@ -744,6 +744,19 @@ dit_status dit_debug_final_out(const float* h, int ldh, int rows, int H, const f
 #endif
 }
 
+dit_status dit_debug_gemv(const void* W, int O, int I, const float* X, int ldx, int nv, float* Y,
+                          float* Ys, void* stream) {
+  if (!W || !X || !Y) return fail(DIT_ERR_ARG, "NULL argument");
+  if (nv < 1 || nv > 2) return fail(DIT_ERR_ARG, "nv must be 1 or 2");
+  if (O <= 0 || I <= 0 || I % 8 || I > 4096 || (size_t)O * I * 2 >= 0x80000000u || ldx < I || ldx % 4)
+    return fail(DIT_ERR_SHAPE, "need O > 0, I a multiple of 8 and at most 4096, O*I*2 < 2^31, ldx >= I "
+                               "and a multiple of 4");
+  if ((reinterpret_cast<uintptr_t>(W) | reinterpret_cast<uintptr_t>(X) | reinterpret_cast<uintptr_t>(Y) |
+       reinterpret_cast<uintptr_t>(Ys)) & 15)
+    return fail(DIT_ERR_ARG, "buffers must be 16-byte aligned");
+  return hip_check(launch_gemv(U(W), O, I, X, ldx, nv, Y, O, Ys, static_cast<hipStream_t>(stream)), "gemv");
+}
+
 dit_status dit_debug_stream_copy(const void* src, void* dst, size_t bytes, void* stream) {
   if (!src || !dst) return fail(DIT_ERR_ARG, "NULL argument");
   if (bytes % 16 || ((reinterpret_cast<uintptr_t>(src) | reinterpret_cast<uintptr_t>(dst)) & 15))

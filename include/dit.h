@@ -331,6 +331,18 @@ dit_status dit_debug_gemm(const dit_gemm_desc* d, void* stream);
 dit_status dit_debug_final_out(const float* h, int ldh, int rows, int H, const float* scale_out,
                                float eps, const void* w_out, float* v_out, void* stream);
 
+/* Test hook: the step's GEMV kernel on explicit buffers, Y[v][o] = W[o] · X[v]
+ * for v < nv: the timestep MLP's two linears, the shared modulation linear
+ * and the final scale linear (page 3B §1; page 6B §3), fp32 accumulation of
+ * bf16 weights times fp32 inputs. If Ys is not NULL it also receives
+ * SiLU(Y) (the input of the next linear).
+ *   W [O, I] bf16 row-major, X [nv, I] f32 (row stride ldx), Y and Ys
+ *   [nv, O] f32 (row stride O), all device, 16-byte aligned. nv is 1 or 2,
+ *   I a multiple of 8 and at most 4096, O > 0 and O·I·2 below 2^31 bytes
+ *   (DIT_ERR_SHAPE otherwise). */
+dit_status dit_debug_gemv(const void* W, int O, int I, const float* X, int ldx, int nv, float* Y,
+                          float* Ys, void* stream);
+
 /* Measurement hook: a device-to-device copy of `bytes` (a multiple of 16)
  * with 16-byte accesses, the HBM ceiling the bandwidth-bound kernels are
  * compared with. */

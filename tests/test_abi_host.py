@@ -401,3 +401,15 @@ def test_measurement_and_final_hooks_validation():
     assert f(FAKE, 4096, 10, 4096, FAKE, 0.0, FAKE, FAKE, None) == L.DIT_ERR_ARG
     assert L._lib.dit_debug_stream_copy(FAKE, FAKE, 24, None) == L.DIT_ERR_ARG
     assert L._lib.dit_debug_mfma_loop(FAKE, FAKE, 0, 10, None) == L.DIT_ERR_ARG
+
+
+def test_gemv_hook_validation():
+    f = L._lib.dit_debug_gemv
+    assert f(None, 16, 64, FAKE, 64, 1, FAKE, None, None) == L.DIT_ERR_ARG
+    assert f(FAKE, 16, 64, FAKE, 64, 3, FAKE, None, None) == L.DIT_ERR_ARG        # nv
+    assert f(FAKE, 16, 60, FAKE, 64, 1, FAKE, None, None) == L.DIT_ERR_SHAPE      # I % 8
+    assert f(FAKE, 16, 8192, FAKE, 8192, 1, FAKE, None, None) == L.DIT_ERR_SHAPE  # I > 4096
+    assert f(FAKE, 0, 64, FAKE, 64, 1, FAKE, None, None) == L.DIT_ERR_SHAPE       # O
+    assert f(FAKE, 16, 64, FAKE, 32, 1, FAKE, None, None) == L.DIT_ERR_SHAPE      # ldx < I
+    assert f(FAKE, 1 << 20, 4096, FAKE, 4096, 1, FAKE, None, None) == L.DIT_ERR_SHAPE   # 8 GiB of W
+    assert "I a multiple of 8" in L.dit_last_error()

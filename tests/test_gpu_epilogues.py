@@ -114,6 +114,34 @@ def test_final_adaln_proj_out(dev, rows, H):
     assert np.all(err <= bound)
 
 
+@pytest.mark.parametrize("O,I,nv,silu", [(16384, 4096, 2, False), (4096, 4096, 1, True), (4096, 256, 2, True),
+                                         (37, 24, 1, False), (1001, 520, 2, True)])
+def test_gemv_fp32_accumulation(dev, O, I, nv, silu):
+    """The step's GEMV (timestep MLP, shared modulation, final scale): Y =
+    W X for bf16 W and fp32 X, every output within the fp32 accumulation
+    bound of the fp64 product, and SiLU(Y) where the MLP asks for it. The
+    shapes are the modulation linear [16384 x 4096] on both timestep rows,
+    the MLP's linears, and ragged ones (odd pair count, I not a multiple of
+    the 512 values a wave covers per pass)."""
+    g = torch.Generator().manual_seed(O + I + nv)
+    W = (torch.randn((O, I), generator=g) / np.sqrt(I)).to(torch.bfloat16)
+    X = torch.randn((nv, I), generator=g)
+    Y = torch.empty((nv, O), dtype=torch.float32, device=dev)
+    Ys = torch.empty((nv, O), dtype=torch.float32, device=dev) if silu else None
+    say(f"gemv O={O} I={I} nv={nv} silu={silu}")
+    L.dit_debug_gemv(W.to(dev), X.to(dev), Y, Ys)
+    torch.cuda.synchronize()
+    w, x = host(W), X.double().numpy()
+    ref = x @ w.T
+    bound = ACC * (np.abs(x) @ np.abs(w).T)
+    err = np.abs(Y.cpu().double().numpy() - ref)
+    assert np.all(err <= bound), float((err / np.maximum(bound, 1e-30)).max())
+    if silu:
+        sref = ref / (1.0 + np.exp(-ref))
+        serr = np.abs(Ys.cpu().double().numpy() - sref)
+        assert np.all(serr <= 1.1 * bound + 2e-6 * np.abs(sref) + 1e-7), float(serr.max())
+
+
 @pytest.mark.parametrize("n", [4096, 700, 1])
 def test_img_in_is_fp32_exact(dev, n):
     """img_in (fp32 latents, bf16 weights) through three bf16 MFMAs per block
